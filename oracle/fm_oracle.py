@@ -1,0 +1,337 @@
+"""Plain CPU oracle of the flow-matching denoise loop of a VLA action head.
+
+TEST INFRASTRUCTURE ONLY. This module is the yardstick the HIP path is checked
+against: tests, the package's smoke check and the benchmark's CPU-baseline leg may
+call it; the product path never does. It shares no code with the HIP library and
+imports nothing from it: only numpy. Every step is written out in the order the
+pages state it, one tensor operation at a time, in float64 by default (float32 on
+request), with no fusion, blocking or reordering.
+
+Sources (pages as titled; sections, equations):
+  * vla.cpp: A Unified Inference Runtime for Vision-Language-Action Models,
+    Sec. III-A Eq. (1) (Euler integration over the schedule tau_0..tau_T),
+    Sec. III-B Eq. (2) (softmax attention over cached keys/values),
+    Sec. III-E Eq. (5) (e_inf, e_rel).
+  * pi0.5 Design (TensorRT Edge-LLM): architecture diagram (expert 18 layers,
+    hidden 1024, head_dim 256, one K/V head), sequence diagram (cond -> per-step
+    modulation rows, loop t: 1 -> 0, x += dt * v), "Component contract"
+    (adarms_modulation row layout and (scale, shift, gate) packing; action_pred is
+    the velocity), "Attention and the K/V pool" (suffix K/V appended after the
+    prefix; head fold of all query heads onto the single K/V head).
+  * GR00T N1.7 (TensorRT Edge-LLM): section "action" (32 DiT blocks, odd blocks
+    self-attend over state + action tokens, even blocks cross-attend into the VL
+    context), "Build-time constants" (per-step modulation rows, timestep bias),
+    "vl_backbone" (cross-attention K/V projected once and kept bound).
+  * LoongForge GR00T-N1.7 training optimization blog, Sec. 3.3 (rotate_half RoPE,
+    RMSNorm with fp32 reduction, gate * up MLP pattern).
+
+Readings taken where the pages are silent (each is listed with its reason in the
+design notes of the repository): sinusoid periods 4e-3..4.0 and a two-layer SiLU
+time MLP; (1 + scale) modulation; RMS/Layer norm epsilon 1e-6 without a learned
+weight; tanh-form GELU on the gate branch; RoPE base 10000 on queries and suffix
+keys only (the prefix keys arrive already rotated); biases only on the time MLP,
+modulation Denses and the action/state in/out projections; DiT feed-forward width
+4 x hidden, ungated, behind a plain LayerNorm and an ungated residual.
+
+Parity pins: every function here is checked by `tests/test_oracle.py` against
+closed forms, invariants, library routines or brute force. The numerical values of
+the time embedding and modulation table are "parity unpinned" beyond their
+invariants, because the pages print no worked values for them.
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+ARCH_PREFIX_JOINT = 0
+ARCH_DIT_CROSS = 1
+
+SINUSOID_MIN_PERIOD = 4e-3
+SINUSOID_MAX_PERIOD = 4.0
+
+
+# ----------------------------------------------------------------------------- schedule
+def schedule(steps: int, tau=None, dtype=np.float64) -> np.ndarray:
+    """Integration schedule tau_0..tau_T (vla.cpp Sec. III-A, Eq. (1); pi0.5 Design,
+    sequence diagram: t runs from 1 to 0). Default: uniform, tau_k = 1 - k/T."""
+    if tau is not None:
+        tau = np.asarray(tau, dtype=dtype)
+        if tau.shape != (steps + 1,):
+            raise ValueError(f"schedule needs {steps + 1} values, got {tau.shape}")
+        return tau
+    return np.array([1.0 - k / steps for k in range(steps + 1)], dtype=dtype) if steps > 0 \
+        else np.ones(1, dtype=dtype)
+
+
+# ----------------------------------------------------------------------------- elementwise
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu_tanh(x):
+    """GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    c = math.sqrt(2.0 / math.pi)
+    return 0.5 * x * (1.0 + np.tanh(c * (x + 0.044715 * x * x * x)))
+
+
+def linear(x, w, b=None):
+    """y = x W^T (+ b), nn.Linear convention, W is [out, in]."""
+    y = x @ w.T
+    return y if b is None else y + b
+
+
+# ----------------------------------------------------------------------------- norms
+def rms_norm(h, eps):
+    """h / sqrt(mean(h^2) + eps) over the last axis (LoongForge blog Sec. 3.3: RMSNorm with
+    its reduction kept in full precision). No learned weight: the modulation supplies it."""
+    return h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+
+
+def layer_norm(h, eps):
+    """(h - mean) / sqrt(var + eps), biased variance, no affine (DiT AdaLN base norm)."""
+    mu = np.mean(h, axis=-1, keepdims=True)
+    d = h - mu
+    return d / np.sqrt(np.mean(d * d, axis=-1, keepdims=True) + eps)
+
+
+def modulate(n, scale, shift):
+    """n * (1 + scale) + shift, scale/shift broadcast over tokens."""
+    return n * (1.0 + scale) + shift
+
+
+def split_site(row, D):
+    """A modulation row packs (scale, shift, gate), each of width D (pi0.5 Design,
+    "Component contract", adarms_modulation)."""
+    return row[..., :D], row[..., D:2 * D], row[..., 2 * D:3 * D]
+
+
+# ----------------------------------------------------------------------------- RoPE
+def rope(x, positions, base):
+    """Rotary embedding, rotate_half convention (LoongForge blog Sec. 3.3): for j < d/2,
+    theta_j = base^(-2j/d), the pair (x_j, x_{j+d/2}) at position p rotates by p*theta_j:
+    (a, b) -> (a cos - b sin, b cos + a sin). x: [..., T, d]; positions: [T]."""
+    d = x.shape[-1]
+    half = d // 2
+    j = np.arange(half, dtype=np.float64)
+    theta = base ** (-2.0 * j / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    cos = np.cos(ang).astype(x.dtype)
+    sin = np.sin(ang).astype(x.dtype)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * cos - b * sin, b * cos + a * sin], axis=-1)
+
+
+# ----------------------------------------------------------------------------- attention
+def attention(q, k, v):
+    """softmax(Q K^T / sqrt(d_k)) V with no mask (vla.cpp Eq. (2), M = 0), softmax over keys.
+
+    q: [B, n_q, Tq, d]; k, v: [B, n_kv, Tk, d] with n_kv == 1 (the single K/V head shared by
+    every query head, pi0.5 Design "Attention and the K/V pool") or n_kv == n_q."""
+    d = q.shape[-1]
+    s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(d)
+    s = s - np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / np.sum(p, axis=-1, keepdims=True)
+    return p @ v
+
+
+# ----------------------------------------------------------------------------- time conditioning
+def sinusoidal_embedding(tau, width, min_period=SINUSOID_MIN_PERIOD, max_period=SINUSOID_MAX_PERIOD):
+    """e(tau) = [sin(2 pi tau / p_j)]_j ++ [cos(2 pi tau / p_j)]_j, j < width/2, with periods
+    geometric from min_period to max_period. The time embedder that the pi0.5 cond component
+    hoists out of the step (pi0.5 Design, cond paragraph); the constants are a reading."""
+    tau = np.asarray(tau)
+    half = width // 2
+    frac = np.arange(half, dtype=np.float64) / max(half - 1, 1)
+    period = min_period * (max_period / min_period) ** frac
+    arg = tau[:, None].astype(np.float64) * (2.0 * math.pi / period)[None, :]
+    return np.concatenate([np.sin(arg), np.cos(arg)], axis=-1).astype(tau.dtype)
+
+
+def time_conditioning(w, tau_steps):
+    """c_k = SiLU(W_out SiLU(W_in e(tau_k) + b_in) + b_out) for each evaluated tau_k."""
+    D = w["time_in.w"].shape[0]
+    e = sinusoidal_embedding(tau_steps, D)
+    c = silu(linear(e, w["time_in.w"], w["time_in.b"]))
+    return silu(linear(c, w["time_out.w"], w["time_out.b"]))
+
+
+def modulation_table(cfg, w, tau):
+    """Per-step modulation rows, evaluated once per (steps, batch) off the step path
+    (pi0.5 Design: the optional cond component, evaluated again only on a new step count or
+    batch; GR00T N1.7 "Build-time constants"). Returns (table [T, S, 3D], time_bias [T, D] or None).
+
+    table[k, s] = W_s c_k + b_s. The pages' tensor repeats each step's row once per
+    request ([steps * batch, S, 3D]); every request shares tau_k, so the rows are equal
+    across requests and one per step is kept here."""
+    T = len(tau) - 1
+    if T == 0:
+        return None, None
+    c = time_conditioning(w, tau[:T])                      # [T, D]
+    S, O, D = w["mod.w"].shape
+    table = (w["mod.w"].reshape(S * O, D) @ c.T).T.reshape(T, S, O) + w["mod.b"][None]
+    tb = None
+    if cfg["arch"] == ARCH_DIT_CROSS:
+        tb = linear(c, w["time_bias.w"], w["time_bias.b"])  # [T, D]
+    return table, tb
+
+
+# ----------------------------------------------------------------------------- bind
+def bind(cfg, w, inputs, dtype=np.float64):
+    """Per-observation conditioning, computed once and kept for the whole loop (vla.cpp
+    Sec. III-B, observation reuse; GR00T N1.7 "Who runs what", vl_backbone row).
+
+    pi0.5: the per-layer prefix K/V [B, P, 1, d_h] as given (already rotated by the
+    prefix tower). DiT: cross K/V of each even block, K_c = Z W_K^T, V_c = Z W_V^T, and
+    the state token W_s s + b_s. Arrays are returned read-only: the loop never writes them."""
+    out = {}
+    if cfg["arch"] == ARCH_PREFIX_JOINT:
+        L = cfg["n_layers"]
+        out["k"] = [np.asarray(inputs[f"prefix.k.{l}"], dtype=dtype)[:, :, 0, :][:, None] for l in range(L)]
+        out["v"] = [np.asarray(inputs[f"prefix.v.{l}"], dtype=dtype)[:, :, 0, :][:, None] for l in range(L)]
+        out["prefix_len"] = out["k"][0].shape[2] if L else 0
+    else:
+        nh, dh = cfg["n_heads"], cfg["head_dim"]
+        z = np.asarray(inputs["context"], dtype=dtype)
+        B, S, _ = z.shape
+        out["k"], out["v"] = {}, {}
+        for i in range(0, cfg["n_layers"], 2):
+            kc = linear(z, w[f"blocks.{i}.k.w"].astype(dtype))
+            vc = linear(z, w[f"blocks.{i}.v.w"].astype(dtype))
+            out["k"][i] = kc.reshape(B, S, nh, dh).transpose(0, 2, 1, 3)
+            out["v"][i] = vc.reshape(B, S, nh, dh).transpose(0, 2, 1, 3)
+        s = np.asarray(inputs["state"], dtype=dtype)
+        out["state_token"] = linear(s, w["state_in.w"].astype(dtype), w["state_in.b"].astype(dtype))
+    for key in ("k", "v"):
+        vals = out[key].values() if isinstance(out[key], dict) else out[key]
+        for a in vals:
+            a.flags.writeable = False
+    return out
+
+
+# ----------------------------------------------------------------------------- velocity
+def velocity_prefix_joint(cfg, w, bound, x, row):
+    """One step of the pi0.5-shaped action expert: x [B, H, d_a] -> v [B, H, d_a].
+
+    row: this step's modulation row [2L+1, 3D]; site 2l is layer l's input norm, 2l+1 its
+    post-attention norm, the last site the final norm (pi0.5 Design, "Component contract")."""
+    D, L = cfg["hidden"], cfg["n_layers"]
+    nq, dh, eps = cfg["n_heads"], cfg["head_dim"], cfg["norm_eps"]
+    B, H, _ = x.shape
+    P = bound["prefix_len"]
+    pos = P + np.arange(H)  # suffix positions continue after the compact prefix
+    h = linear(x, w["action_in.w"], w["action_in.b"])
+    for l in range(L):
+        p = f"layers.{l}."
+        scale, shift, gate = split_site(row[2 * l], D)
+        u = modulate(rms_norm(h, eps), scale, shift)
+        q = linear(u, w[p + "q.w"]).reshape(B, H, nq, dh).transpose(0, 2, 1, 3)
+        k = linear(u, w[p + "k.w"]).reshape(B, H, 1, dh).transpose(0, 2, 1, 3)
+        v = linear(u, w[p + "v.w"]).reshape(B, H, 1, dh).transpose(0, 2, 1, 3)
+        if cfg["rope_base"] > 0:
+            q = rope(q, pos, cfg["rope_base"])
+            k = rope(k, pos, cfg["rope_base"])
+        K = np.concatenate([bound["k"][l], k], axis=2)   # suffix appended after the prefix
+        V = np.concatenate([bound["v"][l], v], axis=2)
+        o = attention(q, K, V).transpose(0, 2, 1, 3).reshape(B, H, nq * dh)
+        h = h + gate * linear(o, w[p + "o.w"])
+        scale, shift, gate = split_site(row[2 * l + 1], D)
+        u = modulate(rms_norm(h, eps), scale, shift)
+        if cfg["mlp_gated"]:
+            a = gelu_tanh(linear(u, w[p + "gate.w"])) * linear(u, w[p + "up.w"])
+        else:
+            a = gelu_tanh(linear(u, w[p + "gate.w"]))
+        h = h + gate * linear(a, w[p + "down.w"])
+    scale, shift, _ = split_site(row[2 * L], D)
+    u = modulate(rms_norm(h, eps), scale, shift)
+    return linear(u, w["action_out.w"], w["action_out.b"])
+
+
+def velocity_dit_cross(cfg, w, bound, x, row, time_bias):
+    """One step of the DiT action head (GR00T N1.7, section "action"): the state token is
+    prepended to the action tokens; 0-based even blocks cross-attend into the bound context
+    K/V, odd blocks self-attend over state + action tokens; AdaLN-modulated LayerNorm with a
+    gated attention residual, plain LayerNorm + GELU feed-forward; the output norm uses the
+    last site and only action tokens are projected to the velocity."""
+    D, L = cfg["hidden"], cfg["n_layers"]
+    nh, dh, eps = cfg["n_heads"], cfg["head_dim"], cfg["norm_eps"]
+    B, H, _ = x.shape
+    h_a = linear(x, w["action_in.w"], w["action_in.b"]) + time_bias
+    h = np.concatenate([bound["state_token"], h_a], axis=1)
+    T = h.shape[1]
+    for i in range(L):
+        p = f"blocks.{i}."
+        scale, shift, gate = split_site(row[i], D)
+        u = modulate(layer_norm(h, eps), scale, shift)
+        q = linear(u, w[p + "q.w"]).reshape(B, T, nh, dh).transpose(0, 2, 1, 3)
+        if i % 2 == 0:
+            K, V = bound["k"][i], bound["v"][i]
+        else:
+            K = linear(u, w[p + "k.w"]).reshape(B, T, nh, dh).transpose(0, 2, 1, 3)
+            V = linear(u, w[p + "v.w"]).reshape(B, T, nh, dh).transpose(0, 2, 1, 3)
+        o = attention(q, K, V).transpose(0, 2, 1, 3).reshape(B, T, D)
+        h = h + gate * linear(o, w[p + "o.w"])
+        h = h + linear(gelu_tanh(linear(layer_norm(h, eps), w[p + "ff1.w"])), w[p + "ff2.w"])
+    scale, shift, _ = split_site(row[L], D)
+    u = modulate(layer_norm(h[:, cfg["state_tokens"]:], eps), scale, shift)
+    return linear(u, w["action_out.w"], w["action_out.b"])
+
+
+def velocity(cfg, w, bound, x, table, time_bias, k):
+    """v_theta(X^k, tau_k, C) of vla.cpp Eq. (1), for step k of the scheduled table."""
+    if cfg["arch"] == ARCH_PREFIX_JOINT:
+        return velocity_prefix_joint(cfg, w, bound, x, table[k])
+    return velocity_dit_cross(cfg, w, bound, x, table[k], time_bias[k])
+
+
+# ----------------------------------------------------------------------------- the loop
+def cast_weights(w, dtype=np.float64):
+    return {n: np.asarray(a, dtype=dtype) for n, a in w.items()}
+
+
+def denoise(cfg, w, bound, x0, steps, tau=None, field=None, return_trace=False, dtype=np.float64):
+    """Euler integration X^{k+1} = X^k + (tau_{k+1} - tau_k) v(X^k, tau_k) for k = 0..T-1
+    (vla.cpp Sec. III-A, Eq. (1)); the update is applied to the float32-or-wider chunk and
+    the velocity (not the updated chunk) is what one step of the network produces
+    (pi0.5 Design, action_pred).
+
+    field: optional callable (x, k, tau_k) -> v replacing the network, for closed-form checks.
+    Returns X^T, and with return_trace the list of (X^k, v_k) pairs."""
+    tau = schedule(steps, tau, dtype=dtype)
+    x = np.array(x0, dtype=dtype, copy=True)
+    trace = []
+    if steps > 0 and field is None:
+        table, tb = modulation_table(cfg, w, tau)
+    for k in range(steps):
+        if field is not None:
+            v = field(x, k, tau[k])
+        else:
+            v = velocity(cfg, w, bound, x, table, tb, k)
+        if return_trace:
+            trace.append((x.copy(), v))
+        x = x + (tau[k + 1] - tau[k]) * v
+    return (x, trace) if return_trace else x
+
+
+def run(cfg, weights, inputs, steps=None, tau=None, dtype=np.float64, return_trace=False, field=None):
+    """Cast the seeded weights and inputs to the oracle precision, bind, and denoise x0."""
+    steps = cfg["steps"] if steps is None else steps
+    w = cast_weights(weights, dtype)
+    bound = bind(cfg, w, inputs, dtype=dtype)
+    return denoise(cfg, w, bound, inputs["x0"], steps, tau=tau, field=field,
+                   return_trace=return_trace, dtype=dtype)
+
+
+# ----------------------------------------------------------------------------- metrics
+def e_inf(a, ref):
+    """Maximum absolute error (vla.cpp Sec. III-E, Eq. (5))."""
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(ref, np.float64))))
+
+
+def e_rel(a, ref):
+    """||A - A_ref||_2 / ||A_ref||_2 over the flattened tensors (vla.cpp Eq. (5)); undefined
+    (None) when the reference norm is zero, in which case e_inf is the figure to report."""
+    a = np.asarray(a, np.float64).ravel()
+    r = np.asarray(ref, np.float64).ravel()
+    n = np.linalg.norm(r)
+    return None if n == 0 else float(np.linalg.norm(a - r) / n)

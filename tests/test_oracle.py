@@ -1,0 +1,465 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each check is chosen so that a plausible slip in the oracle (a dropped term, a wrong
+sign or index, a transposed operand) fails it: library routines (torch, float64),
+closed forms of the Euler loop, invariants of RoPE / attention / norms, page-printed
+sizes, and a scalar brute-force re-implementation on micro shapes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from flow_matching_vla_amd import workloads as wl
+
+RNG = np.random.default_rng(12345)
+
+
+def t64(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+# ----------------------------------------------------------------------------- schedule / Euler
+def test_schedule_uniform_one_to_zero():
+    # vla.cpp Eq. (1) schedule; pi0.5 Design loop runs t from 1 to 0.
+    np.testing.assert_array_equal(oracle.schedule(4), [1.0, 0.75, 0.5, 0.25, 0.0])
+    np.testing.assert_array_equal(oracle.schedule(0), [1.0])
+    with pytest.raises(ValueError):
+        oracle.schedule(3, tau=[1.0, 0.0])
+
+
+def _tiny(**kw):
+    return wl.workload("tiny_fp32", **kw)
+
+
+def test_steps_zero_returns_x0():
+    cfg = _tiny()
+    W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+    x = oracle.run(cfg, W, I, steps=0)
+    np.testing.assert_array_equal(x, I["x0"].astype(np.float64))
+
+
+def test_dt_zero_returns_x0_bitwise():
+    # a constant schedule gives dt = 0, and x + 0 * v == x exactly for finite v
+    cfg = _tiny()
+    W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+    x = oracle.run(cfg, W, I, steps=3, tau=[0.4, 0.4, 0.4, 0.4])
+    np.testing.assert_array_equal(x, I["x0"].astype(np.float64))
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "dit_b1"])
+def test_constant_velocity_field_closed_form(name):
+    # W_out = 0, b_out = c makes v == c at every step: X^T = X^0 + (tau_T - tau_0) c = X^0 - c.
+    cfg = wl.workload(name, n_layers=2) if name == "dit_b1" else _tiny()
+    if name == "dit_b1":
+        cfg.update(ctx_len=8)
+    W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+    c = RNG.standard_normal(cfg["action_dim"])
+    W["action_out.w"] = np.zeros_like(W["action_out.w"])
+    W["action_out.b"] = c.astype(np.float32)
+    x = oracle.run(cfg, W, I, steps=cfg["steps"])
+    ref = I["x0"].astype(np.float64) - c.astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(x, ref, rtol=0, atol=1e-12)
+
+
+def test_linear_velocity_field_closed_form():
+    # v = a x integrates by Euler to prod_k (1 + a dt_k) x0 = (1 - a/T)^T x0 on the uniform 1->0 grid.
+    cfg = _tiny()
+    x0 = RNG.standard_normal((2, 5, 3))
+    a, T = 0.7, 6
+    x = oracle.denoise(cfg, None, None, x0, T, field=lambda x, k, t: a * x)
+    np.testing.assert_allclose(x, (1.0 - a / T) ** T * x0, rtol=1e-13)
+    # a time-dependent field sees tau_k at the left end of each interval
+    seen = []
+    oracle.denoise(cfg, None, None, x0, 4, field=lambda x, k, t: seen.append(t) or 0 * x)
+    assert seen == [1.0, 0.75, 0.5, 0.25]
+
+
+# ----------------------------------------------------------------------------- elementwise
+def test_gelu_tanh_and_silu_match_torch():
+    x = np.linspace(-8, 8, 4001)
+    np.testing.assert_allclose(oracle.gelu_tanh(x), F.gelu(t64(x), approximate="tanh").numpy(), rtol=1e-14, atol=1e-15)
+    # the tanh form stays within its known approximation error of the exact erf GELU
+    exact = 0.5 * x * (1 + np.vectorize(math.erf)(x / math.sqrt(2)))
+    assert np.max(np.abs(oracle.gelu_tanh(x) - exact)) < 1e-3
+    np.testing.assert_allclose(oracle.silu(x), F.silu(t64(x)).numpy(), rtol=1e-14, atol=1e-15)
+
+
+def test_linear_matches_torch():
+    x, w, b = RNG.standard_normal((3, 4, 7)), RNG.standard_normal((5, 7)), RNG.standard_normal(5)
+    np.testing.assert_allclose(oracle.linear(x, w, b), F.linear(t64(x), t64(w), t64(b)).numpy(), rtol=1e-13)
+
+
+# ----------------------------------------------------------------------------- norms
+def test_rms_norm_matches_torch_and_invariants():
+    h = RNG.standard_normal((4, 6, 64)) * 3 + 0.5
+    eps = 1e-6
+    np.testing.assert_allclose(oracle.rms_norm(h, eps), F.rms_norm(t64(h), (64,), eps=eps).numpy(), rtol=1e-13)
+    n = oracle.rms_norm(h, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(n * n, axis=-1)), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(oracle.rms_norm(5.0 * h, 0.0), n, rtol=1e-13)
+
+
+def test_layer_norm_matches_torch_and_invariants():
+    h = RNG.standard_normal((4, 6, 48)) * 2 - 1.5
+    eps = 1e-6
+    np.testing.assert_allclose(oracle.layer_norm(h, eps), F.layer_norm(t64(h), (48,), eps=eps).numpy(), rtol=1e-12, atol=1e-13)
+    n = oracle.layer_norm(h, 0.0)
+    np.testing.assert_allclose(n.mean(-1), 0.0, atol=1e-13)
+    np.testing.assert_allclose(n.var(-1), 1.0, rtol=1e-12)
+
+
+def test_modulate_and_site_split():
+    D = 4
+    row = np.arange(3 * D, dtype=np.float64)
+    s, sh, g = oracle.split_site(row, D)
+    np.testing.assert_array_equal(s, [0, 1, 2, 3])
+    np.testing.assert_array_equal(sh, [4, 5, 6, 7])
+    np.testing.assert_array_equal(g, [8, 9, 10, 11])
+    n = RNG.standard_normal((2, D))
+    np.testing.assert_allclose(oracle.modulate(n, 0 * s, 0 * sh), n)
+    np.testing.assert_allclose(oracle.modulate(n, s, sh), n + n * s + sh)
+
+
+# ----------------------------------------------------------------------------- RoPE
+def test_rope_matches_complex_rotation():
+    # independent formulation: z_j = x_j + i x_{j+d/2} multiplied by exp(i p theta_j)
+    d, base = 16, 10000.0
+    x = RNG.standard_normal((2, 5, d))
+    pos = np.array([0, 3, 7, 100, 1023])
+    out = oracle.rope(x, pos, base)
+    theta = base ** (-np.arange(d // 2) * 2.0 / d)
+    z = (x[..., : d // 2] + 1j * x[..., d // 2:]) * np.exp(1j * pos[:, None] * theta[None, :])
+    np.testing.assert_allclose(out, np.concatenate([z.real, z.imag], -1), rtol=1e-12, atol=1e-12)
+
+
+def test_rope_invariants():
+    d = 32
+    q, k = RNG.standard_normal((1, 1, d)), RNG.standard_normal((1, 1, d))
+    np.testing.assert_array_equal(oracle.rope(q, [0], 1e4), q)          # position 0 is the identity
+    np.testing.assert_allclose(np.linalg.norm(oracle.rope(q, [57], 1e4)), np.linalg.norm(q), rtol=1e-13)
+    # <R_m q, R_n k> depends only on m - n
+    def dot(m, n):
+        return float(np.sum(oracle.rope(q, [m], 1e4) * oracle.rope(k, [n], 1e4)))
+    assert abs(dot(10, 3) - dot(817, 810)) < 1e-10
+    assert abs(dot(10, 3) - dot(3, 10)) > 1e-6
+
+
+# ----------------------------------------------------------------------------- attention
+def test_attention_matches_torch_sdpa_head_fold():
+    # one K/V head shared by all query heads == MHA with K/V replicated per head
+    B, nq, Tq, Tk, d = 2, 4, 5, 9, 8
+    q = RNG.standard_normal((B, nq, Tq, d))
+    k, v = RNG.standard_normal((B, 1, Tk, d)), RNG.standard_normal((B, 1, Tk, d))
+    out = oracle.attention(q, k, v)
+    ref = F.scaled_dot_product_attention(t64(q), t64(k).expand(B, nq, Tk, d), t64(v).expand(B, nq, Tk, d)).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    kk, vv = RNG.standard_normal((B, nq, Tk, d)), RNG.standard_normal((B, nq, Tk, d))
+    ref = F.scaled_dot_product_attention(t64(q), t64(kk), t64(vv)).numpy()
+    np.testing.assert_allclose(oracle.attention(q, kk, vv), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_brute_force_and_special_cases():
+    d, Tq, Tk = 3, 2, 4
+    q, k, v = RNG.standard_normal((1, 1, Tq, d)), RNG.standard_normal((1, 1, Tk, d)), RNG.standard_normal((1, 1, Tk, d))
+    out = oracle.attention(q, k, v)
+    for i in range(Tq):
+        w = [math.exp(sum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d)) / math.sqrt(d)) for j in range(Tk)]
+        z = sum(w)
+        for c in range(d):
+            assert abs(out[0, 0, i, c] - sum(w[j] * v[0, 0, j, c] for j in range(Tk)) / z) < 1e-12
+    # a single key returns its value; q = 0 averages the values uniformly
+    np.testing.assert_allclose(oracle.attention(q, k[:, :, :1], v[:, :, :1]), np.broadcast_to(v[:, :, :1], out.shape), rtol=1e-14)
+    np.testing.assert_allclose(oracle.attention(0 * q, k, v), np.broadcast_to(v.mean(2, keepdims=True), out.shape), rtol=1e-13)
+    # permuting keys and values jointly changes nothing; huge logits are stable
+    perm = RNG.permutation(Tk)
+    np.testing.assert_allclose(oracle.attention(q, k[:, :, perm], v[:, :, perm]), out, rtol=1e-13)
+    big = oracle.attention(1e4 * q, k, v)
+    assert np.all(np.isfinite(big))
+
+
+# ----------------------------------------------------------------------------- time conditioning
+def test_sinusoidal_embedding_invariants():
+    D = 64
+    e0 = oracle.sinusoidal_embedding(np.array([0.0]), D)
+    np.testing.assert_array_equal(e0[0, : D // 2], 0.0)
+    np.testing.assert_array_equal(e0[0, D // 2:], 1.0)
+    tau = np.array([0.1, 0.37, 0.9])
+    e = oracle.sinusoidal_embedding(tau, D)
+    np.testing.assert_allclose(e[:, : D // 2] ** 2 + e[:, D // 2:] ** 2, 1.0, rtol=1e-14)
+    # angular frequencies 2 pi / p_j: p_0 = 4e-3 and p_last = 4.0, geometric in between
+    h = 1e-7
+    slope = oracle.sinusoidal_embedding(np.array([h]), D)[0, : D // 2] / h
+    np.testing.assert_allclose(slope[0], 2 * math.pi / 4e-3, rtol=1e-6)
+    np.testing.assert_allclose(slope[-1], 2 * math.pi / 4.0, rtol=1e-9)
+    ratios = slope[1:] / slope[:-1]
+    np.testing.assert_allclose(ratios, ratios[0], rtol=1e-5)
+
+
+def test_modulation_table_sites_and_page_sizes():
+    # pi0.5 Design: 37 AdaRMS Denses [3072, 1024] hoisted, 232.8 MB in fp16.
+    shp = wl.weight_shapes(wl.workload("pi05_b1"))
+    assert shp["mod.w"] == (37, 3072, 1024)
+    assert abs(np.prod(shp["mod.w"]) * 2 / 1e6 - 232.8) < 0.05
+    # GR00T N1.7 Build-time constants: 33 AdaLayerNorm projections [1536, 3072], 311 MB fp16.
+    shp = wl.weight_shapes(wl.workload("dit_b1"))
+    assert shp["mod.w"][0] == 33 and shp["mod.w"][2] == 1536
+    assert abs(33 * 1536 * 3072 * 2 / 1e6 - 311) < 0.5
+    # pi0.5 Design architecture diagram: action expert of 428M (blocks + AdaRMS Denses)
+    cfg = wl.workload("pi05_b1")
+    shp = wl.weight_shapes(cfg)
+    n = sum(np.prod(s) for k, s in shp.items() if k.startswith("layers.") or k == "mod.w")
+    assert abs(n / 1e6 - 428) < 0.5
+
+
+def test_modulation_table_is_per_site_dense_of_time_conditioning():
+    cfg = _tiny()
+    W = oracle.cast_weights(wl.make_weights(cfg))
+    tau = oracle.schedule(4)
+    table, tb = oracle.modulation_table(cfg, W, tau)
+    assert table.shape == (4, 5, 768) and tb is None
+    c = oracle.time_conditioning(W, tau[:4])
+    for k in range(4):
+        for s in range(5):
+            ref = F.linear(t64(c[k]), t64(W["mod.w"][s]), t64(W["mod.b"][s])).numpy()
+            np.testing.assert_allclose(table[k, s], ref, rtol=1e-12, atol=1e-14)
+    # zero weights leave only the bias; the time MLP is two SiLU(Linear) layers
+    Z = dict(W)
+    Z["mod.w"] = np.zeros_like(W["mod.w"])
+    np.testing.assert_array_equal(oracle.modulation_table(cfg, Z, tau)[0][2], W["mod.b"])
+    e = oracle.sinusoidal_embedding(tau[:4], 256)
+    ref = F.silu(F.linear(F.silu(F.linear(t64(e), t64(W["time_in.w"]), t64(W["time_in.b"]))), t64(W["time_out.w"]), t64(W["time_out.b"])))
+    np.testing.assert_allclose(c, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- whole-network pins
+def _zero_gates(cfg, W):
+    W = dict(W)
+    D = cfg["hidden"]
+    mw, mb = W["mod.w"].copy(), W["mod.b"].copy()
+    mw[:, 2 * D:3 * D, :] = 0
+    mb[:, 2 * D:3 * D] = 0
+    W["mod.w"], W["mod.b"] = mw, mb
+    return W
+
+
+def test_all_gates_zero_makes_blocks_identity_pi05():
+    cfg = _tiny()
+    W, I = oracle.cast_weights(_zero_gates(cfg, wl.make_weights(cfg))), wl.make_inputs(cfg)
+    bound = oracle.bind(cfg, W, I)
+    tau = oracle.schedule(4)
+    table, tb = oracle.modulation_table(cfg, W, tau)
+    x = I["x0"].astype(np.float64)
+    v = oracle.velocity(cfg, W, bound, x, table, tb, 2)
+    h = oracle.linear(x, W["action_in.w"], W["action_in.b"])
+    s, sh, _ = oracle.split_site(table[2, -1], cfg["hidden"])
+    ref = oracle.linear(oracle.modulate(oracle.rms_norm(h, 1e-6), s, sh), W["action_out.w"], W["action_out.b"])
+    np.testing.assert_allclose(v, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_all_gates_zero_dit_blocks_identity_when_ff_zero():
+    cfg = wl.workload("dit_b1", n_layers=2, ctx_len=8)
+    W = _zero_gates(cfg, wl.make_weights(cfg))
+    for i in range(2):
+        W[f"blocks.{i}.ff2.w"] = np.zeros_like(W[f"blocks.{i}.ff2.w"])
+    W, I = oracle.cast_weights(W), wl.make_inputs(cfg)
+    bound = oracle.bind(cfg, W, I)
+    tau = oracle.schedule(4)
+    table, tb = oracle.modulation_table(cfg, W, tau)
+    x = I["x0"].astype(np.float64)
+    v = oracle.velocity(cfg, W, bound, x, table, tb, 1)
+    h = oracle.linear(x, W["action_in.w"], W["action_in.b"]) + tb[1]
+    s, sh, _ = oracle.split_site(table[1, -1], cfg["hidden"])
+    ref = oracle.linear(oracle.modulate(oracle.layer_norm(h, 1e-6), s, sh), W["action_out.w"], W["action_out.b"])
+    np.testing.assert_allclose(v, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_prefix_kv_is_never_written_and_reused():
+    cfg = _tiny()
+    W, I = oracle.cast_weights(wl.make_weights(cfg)), wl.make_inputs(cfg)
+    bound = oracle.bind(cfg, W, I)
+    snap = [a.copy() for a in bound["k"] + bound["v"]]
+    with pytest.raises(ValueError):
+        bound["k"][0][0, 0, 0, 0] = 1.0
+    x1 = oracle.denoise(cfg, W, bound, I["x0"], 4)
+    x2 = oracle.denoise(cfg, W, bound, I["x0"], 4)
+    for a, b in zip(snap, bound["k"] + bound["v"]):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(x1, x2)
+
+
+def test_requests_are_independent():
+    cfg = _tiny(batch=3)
+    W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+    xb = oracle.run(cfg, W, I)
+    for b in range(3):
+        Ib = {k: v[b:b + 1] for k, v in I.items()}
+        np.testing.assert_allclose(oracle.run(dict(cfg, batch=1), W, Ib), xb[b:b + 1], rtol=1e-12, atol=1e-13)
+
+
+def test_joint_prefix_permutation_invariance():
+    cfg = _tiny()
+    W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+    perm = RNG.permutation(cfg["prefix_len"])
+    Ip = dict(I)
+    for l in range(cfg["n_layers"]):
+        Ip[f"prefix.k.{l}"] = I[f"prefix.k.{l}"][:, perm]
+        Ip[f"prefix.v.{l}"] = I[f"prefix.v.{l}"][:, perm]
+    np.testing.assert_allclose(oracle.run(cfg, W, Ip), oracle.run(cfg, W, I), rtol=1e-12, atol=1e-13)
+
+
+def test_float32_oracle_agrees_with_float64():
+    for cfg in (_tiny(), wl.workload("pi05_b1", n_layers=2, prefix_len=40, action_horizon=12),
+                wl.workload("dit_b1", n_layers=2, ctx_len=24)):
+        W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+        x64, tr64 = oracle.run(cfg, W, I, return_trace=True)
+        x32, tr32 = oracle.run(cfg, W, I, dtype=np.float32, return_trace=True)
+        assert oracle.e_rel(x32, x64) < 1e-5
+        for (_, v64), (_, v32) in zip(tr64, tr32):
+            assert oracle.e_rel(v32, v64) < 1e-4
+
+
+def test_metrics():
+    a, r = np.array([1.0, 2.0, 3.0]), np.array([1.0, 2.5, 3.0])
+    assert oracle.e_inf(a, r) == 0.5
+    assert abs(oracle.e_rel(a, r) - 0.5 / math.sqrt(1 + 6.25 + 9)) < 1e-15
+    assert oracle.e_rel(a, 0 * r) is None
+
+
+# ----------------------------------------------------------------------------- scalar brute force
+def _brute_velocity_pi05(cfg, W, I, x, row):
+    """Scalar-loop re-statement of one expert step on micro shapes (pure Python floats)."""
+    D, L, nq, dh, F_, eps = cfg["hidden"], cfg["n_layers"], cfg["n_heads"], cfg["head_dim"], cfg["mlp_dim"], cfg["norm_eps"]
+    H, da, P, base = cfg["action_horizon"], cfg["action_dim"], cfg["prefix_len"], cfg["rope_base"]
+
+    def mv(Wm, vec):
+        return [sum(Wm[o][i] * vec[i] for i in range(len(vec))) for o in range(len(Wm))]
+
+    def rot(vec, p):
+        out = list(vec)
+        for j in range(dh // 2):
+            th = p * base ** (-2.0 * j / dh)
+            a, b = vec[j], vec[j + dh // 2]
+            out[j] = a * math.cos(th) - b * math.sin(th)
+            out[j + dh // 2] = b * math.cos(th) + a * math.sin(th)
+        return out
+
+    def nm(vec, site):
+        r = math.sqrt(sum(t * t for t in vec) / D + eps)
+        return [vec[i] / r * (1 + row[site][i]) + row[site][D + i] for i in range(D)]
+
+    h = [[sum(W["action_in.w"][o][i] * x[t][i] for i in range(da)) + W["action_in.b"][o] for o in range(D)] for t in range(H)]
+    for l in range(L):
+        p = f"layers.{l}."
+        u = [nm(h[t], 2 * l) for t in range(H)]
+        q = [mv(W[p + "q.w"], u[t]) for t in range(H)]
+        ks = [rot(mv(W[p + "k.w"], u[t]), P + t) for t in range(H)]
+        vs = [mv(W[p + "v.w"], u[t]) for t in range(H)]
+        keys = I[f"prefix.k.{l}"][0, :, 0].astype(np.float64).tolist() + ks
+        vals = I[f"prefix.v.{l}"][0, :, 0].astype(np.float64).tolist() + vs
+        o = [[0.0] * (nq * dh) for _ in range(H)]
+        for t in range(H):
+            for n in range(nq):
+                qq = rot(q[t][n * dh:(n + 1) * dh], P + t)
+                sc = [sum(qq[c] * kk[c] for c in range(dh)) / math.sqrt(dh) for kk in keys]
+                m = max(sc)
+                e = [math.exp(s - m) for s in sc]
+                z = sum(e)
+                for c in range(dh):
+                    o[t][n * dh + c] = sum(e[j] * vals[j][c] for j in range(len(keys))) / z
+        for t in range(H):
+            y = mv(W[p + "o.w"], o[t])
+            h[t] = [h[t][i] + row[2 * l][2 * D + i] * y[i] for i in range(D)]
+        for t in range(H):
+            u2 = nm(h[t], 2 * l + 1)
+            g, up = mv(W[p + "gate.w"], u2), mv(W[p + "up.w"], u2)
+            a = [0.5 * g[f] * (1 + math.tanh(math.sqrt(2 / math.pi) * (g[f] + 0.044715 * g[f] ** 3))) * up[f] for f in range(F_)]
+            y = mv(W[p + "down.w"], a)
+            h[t] = [h[t][i] + row[2 * l + 1][2 * D + i] * y[i] for i in range(D)]
+    out = []
+    for t in range(H):
+        u = nm(h[t], 2 * L)
+        out.append([sum(W["action_out.w"][o][i] * u[i] for i in range(D)) + W["action_out.b"][o] for o in range(da)])
+    return out
+
+
+def test_scalar_brute_force_pi05_micro():
+    cfg = wl.workload("tiny_fp32", n_layers=2, hidden=8, n_heads=2, head_dim=4, mlp_dim=6,
+                      action_horizon=3, action_dim=2, prefix_len=4, weight_std=0.5)
+    W, I = oracle.cast_weights(wl.make_weights(cfg)), wl.make_inputs(cfg)
+    bound = oracle.bind(cfg, W, I)
+    tau = oracle.schedule(2)
+    table, tb = oracle.modulation_table(cfg, W, tau)
+    x = I["x0"].astype(np.float64)
+    v = oracle.velocity(cfg, W, bound, x, table, tb, 1)
+    Wl = {k: np.asarray(a).tolist() for k, a in W.items()}
+    ref = _brute_velocity_pi05(cfg, Wl, I, x[0].tolist(), table[1].tolist())
+    np.testing.assert_allclose(v[0], np.array(ref), rtol=1e-10, atol=1e-12)
+
+
+def _brute_velocity_dit(cfg, W, I, x, row, tb):
+    D, L, nh, dh, F_, eps = cfg["hidden"], cfg["n_layers"], cfg["n_heads"], cfg["head_dim"], cfg["mlp_dim"], cfg["norm_eps"]
+    H, da = cfg["action_horizon"], cfg["action_dim"]
+    ctx = I["context"][0].astype(np.float64).tolist()
+    st = I["state"][0, 0].astype(np.float64).tolist()
+
+    def mv(Wm, vec):
+        return [sum(Wm[o][i] * vec[i] for i in range(len(vec))) for o in range(len(Wm))]
+
+    def ln(vec):
+        mu = sum(vec) / D
+        var = sum((t - mu) ** 2 for t in vec) / D
+        return [(t - mu) / math.sqrt(var + eps) for t in vec]
+
+    def gelu(g):
+        return 0.5 * g * (1 + math.tanh(math.sqrt(2 / math.pi) * (g + 0.044715 * g ** 3)))
+
+    h = [[a + b for a, b in zip(mv(W["state_in.w"], st), W["state_in.b"])]]
+    for t in range(H):
+        h.append([a + b + c for a, b, c in zip(mv(W["action_in.w"], x[t]), W["action_in.b"], tb)])
+    T = len(h)
+    for i in range(L):
+        p = f"blocks.{i}."
+        u = [[n * (1 + row[i][c]) + row[i][D + c] for c, n in enumerate(ln(h[t]))] for t in range(T)]
+        q = [mv(W[p + "q.w"], u[t]) for t in range(T)]
+        src = ctx if i % 2 == 0 else u
+        ks = [mv(W[p + "k.w"], s) for s in src]
+        vs = [mv(W[p + "v.w"], s) for s in src]
+        o = [[0.0] * D for _ in range(T)]
+        for t in range(T):
+            for n in range(nh):
+                sl = slice(n * dh, (n + 1) * dh)
+                sc = [sum(a * b for a, b in zip(q[t][sl], kk[sl])) / math.sqrt(dh) for kk in ks]
+                m = max(sc)
+                e = [math.exp(s - m) for s in sc]
+                z = sum(e)
+                for c in range(n * dh, (n + 1) * dh):
+                    o[t][c] = sum(e[j] * vs[j][c] for j in range(len(ks))) / z
+        for t in range(T):
+            y = mv(W[p + "o.w"], o[t])
+            h[t] = [h[t][c] + row[i][2 * D + c] * y[c] for c in range(D)]
+        for t in range(T):
+            y = mv(W[p + "ff2.w"], [gelu(g) for g in mv(W[p + "ff1.w"], ln(h[t]))])
+            h[t] = [a + b for a, b in zip(h[t], y)]
+    out = []
+    for t in range(1, T):
+        u = [n * (1 + row[L][c]) + row[L][D + c] for c, n in enumerate(ln(h[t]))]
+        out.append([a + b for a, b in zip(mv(W["action_out.w"], u), W["action_out.b"])])
+    return out
+
+
+def test_scalar_brute_force_dit_micro():
+    cfg = wl.workload("dit_b1", n_layers=2, hidden=8, n_heads=2, head_dim=4, n_kv_heads=2, mlp_dim=12,
+                      action_horizon=3, action_dim=2, state_dim=3, ctx_len=5, ctx_dim=6, weight_std=0.5)
+    W, I = oracle.cast_weights(wl.make_weights(cfg)), wl.make_inputs(cfg)
+    bound = oracle.bind(cfg, W, I)
+    tau = oracle.schedule(2)
+    table, tb = oracle.modulation_table(cfg, W, tau)
+    x = I["x0"].astype(np.float64)
+    v = oracle.velocity(cfg, W, bound, x, table, tb, 0)
+    Wl = {k: np.asarray(a).tolist() for k, a in W.items()}
+    ref = _brute_velocity_dit(cfg, Wl, I, x[0].tolist(), table[0].tolist(), tb[0].tolist())
+    np.testing.assert_allclose(v[0], np.array(ref), rtol=1e-10, atol=1e-12)
