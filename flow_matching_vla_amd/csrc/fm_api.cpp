@@ -1,0 +1,1003 @@
+// Runtime behind the C ABI: validation, weight layout, the K/V pool, the schedule table,
+// the per-step launch sequence and its capture into one hipGraph per (steps, batch,
+// prefix length).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/fm.h"
+#include "fm_kernels.h"
+
+using namespace fm;
+
+namespace {
+
+thread_local std::string g_err;
+
+std::string fmt(const char* f, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, f);
+  vsnprintf(buf, sizeof buf, f, ap);
+  va_end(ap);
+  return buf;
+}
+
+long round_up(long x, long m) { return (x + m - 1) / m * m; }
+
+struct Spec {
+  std::string name;
+  std::vector<int64_t> shape;
+};
+
+int n_sites(const fm_config& c) { return c.arch == FM_ARCH_PREFIX_JOINT ? 2 * c.n_layers + 1 : c.n_layers + 1; }
+
+std::vector<Spec> weight_specs(const fm_config& c) {
+  const int64_t D = c.hidden, F = c.mlp_dim, S = n_sites(c);
+  std::vector<Spec> v = {
+      {"time_in.w", {D, D}}, {"time_in.b", {D}}, {"time_out.w", {D, D}}, {"time_out.b", {D}},
+      {"mod.w", {S, 3 * D, D}}, {"mod.b", {S, 3 * D}}, {"action_in.w", {D, c.action_dim}},
+      {"action_in.b", {D}}, {"action_out.w", {c.action_dim, D}}, {"action_out.b", {c.action_dim}},
+  };
+  if (c.arch == FM_ARCH_PREFIX_JOINT) {
+    const int64_t qd = (int64_t)c.n_heads * c.head_dim, kd = (int64_t)c.n_kv_heads * c.head_dim;
+    for (int l = 0; l < c.n_layers; ++l) {
+      const std::string p = "layers." + std::to_string(l) + ".";
+      v.push_back({p + "q.w", {qd, D}});
+      v.push_back({p + "k.w", {kd, D}});
+      v.push_back({p + "v.w", {kd, D}});
+      v.push_back({p + "o.w", {D, qd}});
+      v.push_back({p + "gate.w", {F, D}});
+      if (c.mlp_gated) v.push_back({p + "up.w", {F, D}});
+      v.push_back({p + "down.w", {D, F}});
+    }
+  } else {
+    v.push_back({"time_bias.w", {D, D}});
+    v.push_back({"time_bias.b", {D}});
+    v.push_back({"state_in.w", {D, c.state_dim}});
+    v.push_back({"state_in.b", {D}});
+    for (int i = 0; i < c.n_layers; ++i) {
+      const std::string p = "blocks." + std::to_string(i) + ".";
+      const int64_t kin = (i % 2 == 0) ? c.ctx_dim : D;
+      v.push_back({p + "q.w", {D, D}});
+      v.push_back({p + "k.w", {D, kin}});
+      v.push_back({p + "v.w", {D, kin}});
+      v.push_back({p + "o.w", {D, D}});
+      v.push_back({p + "ff1.w", {F, D}});
+      v.push_back({p + "ff2.w", {D, F}});
+    }
+  }
+  return v;
+}
+
+// Config validation (host only).
+fm_status check_config(const fm_config* c, std::string& msg) {
+  if (!c) { msg = "config is NULL"; return FM_ERR_INVALID_ARG; }
+  if (c->arch != FM_ARCH_PREFIX_JOINT && c->arch != FM_ARCH_DIT_CROSS) { msg = fmt("arch %d unknown", c->arch); return FM_ERR_INVALID_ARG; }
+  if (c->dtype != FM_F32 && c->dtype != FM_BF16) { msg = fmt("dtype %d unknown", c->dtype); return FM_ERR_INVALID_ARG; }
+  if (c->n_layers < 1 || c->hidden < 64 || c->n_heads < 1 || c->head_dim < 1 || c->mlp_dim < 1 ||
+      c->action_horizon < 1 || c->action_dim < 1 || c->max_batch < 1 || c->max_steps < 1 || c->n_kv_heads < 1) {
+    msg = "n_layers, hidden (>= 64), heads, head_dim, mlp_dim, action_horizon, action_dim, n_kv_heads, max_batch and max_steps must be positive";
+    return FM_ERR_INVALID_ARG;
+  }
+  if (c->hidden % 64 != 0) { msg = fmt("hidden %d must be a multiple of 64", c->hidden); return FM_ERR_UNSUPPORTED; }
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) {
+    msg = fmt("head_dim %d not in {64, 128, 256}", c->head_dim);
+    return FM_ERR_UNSUPPORTED;
+  }
+  if (c->dtype == FM_F32 && c->head_dim == 256) { msg = "fp32 head_dim 256 is not built"; return FM_ERR_UNSUPPORTED; }
+  const int kq = c->dtype == FM_BF16 ? 32 : 16;
+  if (c->mlp_dim % kq != 0) { msg = fmt("mlp_dim %d must be a multiple of %d", c->mlp_dim, kq); return FM_ERR_UNSUPPORTED; }
+  if (!(c->norm_eps >= 0.f) || !(c->rope_base >= 0.f)) { msg = "norm_eps and rope_base must be >= 0"; return FM_ERR_INVALID_ARG; }
+  if (c->arch == FM_ARCH_PREFIX_JOINT) {
+    if (c->n_kv_heads != 1) {
+      msg = fmt("prefix-joint expert needs exactly one K/V head (got %d): the pool is one flat [capacity, head_dim] plane per request", c->n_kv_heads);
+      return FM_ERR_UNSUPPORTED;
+    }
+    if (c->max_prefix_len < 0) { msg = "max_prefix_len must be >= 0"; return FM_ERR_INVALID_ARG; }
+    if (c->state_tokens != 0 || c->ctx_len_max != 0) { msg = "state_tokens and ctx_len_max must be 0 for the prefix-joint expert"; return FM_ERR_INVALID_ARG; }
+  } else {
+    if (c->n_kv_heads != c->n_heads) { msg = fmt("DiT head needs n_kv_heads == n_heads (%d vs %d)", c->n_kv_heads, c->n_heads); return FM_ERR_UNSUPPORTED; }
+    if (c->n_heads * c->head_dim != c->hidden) { msg = fmt("n_heads * head_dim (%d) must equal hidden (%d)", c->n_heads * c->head_dim, c->hidden); return FM_ERR_INVALID_ARG; }
+    if (c->state_tokens < 0 || c->state_tokens > 8 || (c->state_tokens > 0 && c->state_dim < 1)) { msg = "state_tokens in [0, 8] with state_dim >= 1"; return FM_ERR_INVALID_ARG; }
+    if (c->ctx_len_max < 1 || c->ctx_dim < 1 || c->ctx_dim % kq != 0) { msg = fmt("ctx_len_max >= 1 and ctx_dim a multiple of %d", kq); return FM_ERR_INVALID_ARG; }
+    if (c->rope_base != 0.f) { msg = "RoPE is not used by the DiT head"; return FM_ERR_UNSUPPORTED; }
+    if (c->mlp_gated) { msg = "the DiT feed-forward is not gated"; return FM_ERR_UNSUPPORTED; }
+  }
+  if (c->arch == FM_ARCH_PREFIX_JOINT && c->mlp_gated != 0 && c->mlp_gated != 1) { msg = "mlp_gated must be 0 or 1"; return FM_ERR_INVALID_ARG; }
+  const int qcols = c->n_heads * c->head_dim;
+  if (qcols % kq != 0) { msg = "n_heads * head_dim must be a multiple of the k chunk"; return FM_ERR_UNSUPPORTED; }
+  return FM_OK;
+}
+
+int pool_capacity(const fm_config& c) { return (int)round_up((long)c.max_prefix_len + c.action_horizon, 256); }
+
+struct Op {
+  enum Kind { GEMM, ATTN, INPROJ, TRACE } kind;
+  GemmArgs g;
+  AttnArgs at;
+  InProjArgs ip;
+  int trace_layer;
+};
+
+}  // namespace
+
+struct fm_ctx {
+  fm_config c;
+  hipStream_t stream = nullptr, cap_stream = nullptr;
+  int device = 0, num_cus = 256, elem = ET_BF16, esz = 2;
+  std::string err;
+  bool poisoned = false;
+
+  // device memory owned by the context
+  std::vector<void*> allocs;
+  bool loaded = false;
+  struct Layer { void *qkv = nullptr, *q = nullptr, *kx = nullptr, *vx = nullptr, *o = nullptr, *gu = nullptr, *down = nullptr; };
+  std::vector<Layer> L;
+  void *w_tin = nullptr, *w_tout = nullptr, *w_mod = nullptr, *w_tb = nullptr, *w_in = nullptr, *w_out = nullptr, *w_state = nullptr;
+  float *b_tin = nullptr, *b_tout = nullptr, *b_mod = nullptr, *b_tb = nullptr, *b_in = nullptr, *b_out = nullptr, *b_state = nullptr;
+
+  // schedule
+  int steps = -1, sched_batch = 0;
+  std::vector<float> tau;
+  float *table = nullptr, *tbias = nullptr;
+  void *e_buf = nullptr, *c1_buf = nullptr, *c_buf = nullptr;
+
+  // binding
+  int bound_batch = 0, prefix_len = -1;
+  int cap = 0, spad = 0, tpad = 0;
+  void* pool = nullptr;       // PREFIX_JOINT: [L][2][Bmax][cap][dh]; K plane RoPE-interleaved, V plane transposed
+  void* cross_k = nullptr;    // DIT: [ceil(L/2)][Bmax][ctx_max][D]
+  void* cross_vt = nullptr;   // DIT: [ceil(L/2)][Bmax][D][spad]
+  float* state_tok = nullptr; // DIT: [Bmax*st][D]
+  float2* rope_cs = nullptr;  // [H][dh/2]
+
+  // activations
+  float *h = nullptr, *x = nullptr;
+  float2* stats = nullptr;
+  void *qbuf = nullptr, *obuf = nullptr, *abuf = nullptr, *kself = nullptr, *vtself = nullptr;
+
+  // split-K / split-key workspace
+  float* ws = nullptr;
+  size_t ws_bytes = 0;
+  unsigned* counters = nullptr;
+  static constexpr int kCounters = 1 << 16;
+
+  // captured loop
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  bool graph_valid = false;
+
+  int rows_per_req() const { return c.state_tokens + c.action_horizon; }
+};
+
+namespace {
+
+fm_status fail(fm_ctx* x, fm_status s, const std::string& m) {
+  x->err = m;
+  if (s == FM_ERR_DEVICE) x->poisoned = true;
+  return s;
+}
+
+#define HIPCK(call)                                                                       \
+  do {                                                                                    \
+    hipError_t e_ = (call);                                                               \
+    if (e_ != hipSuccess) return fail(ctx, FM_ERR_DEVICE, fmt("%s failed: %s (%s:%d)", #call, \
+                                                              hipGetErrorString(e_), __FILE__, __LINE__)); \
+  } while (0)
+
+fm_status dalloc(fm_ctx* ctx, void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return FM_OK;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *p = nullptr;
+    return fail(ctx, FM_ERR_OOM, fmt("hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e)));
+  }
+  ctx->allocs.push_back(*p);
+  return FM_OK;
+}
+
+void dfree(fm_ctx* ctx, void* p) {
+  if (!p) return;
+  for (size_t i = 0; i < ctx->allocs.size(); ++i)
+    if (ctx->allocs[i] == p) { ctx->allocs.erase(ctx->allocs.begin() + i); break; }
+  (void)hipFree(p);
+}
+
+void invalidate_graph(fm_ctx* ctx) {
+  if (ctx->gexec) { (void)hipGraphExecDestroy(ctx->gexec); ctx->gexec = nullptr; }
+  if (ctx->graph) { (void)hipGraphDestroy(ctx->graph); ctx->graph = nullptr; }
+  ctx->graph_valid = false;
+}
+
+GemmArgs gemm_base(int M, int N, int K, const void* W) {
+  GemmArgs a;
+  memset(&a, 0, sizeof a);
+  a.M = M; a.N = N; a.K = K; a.W = W;
+  a.row_group = 1 << 30; a.row_gstride = 0; a.row_off = 0;
+  a.splits = 1; a.k_split = K;
+  return a;
+}
+
+void set_norm(fm_ctx* ctx, GemmArgs& a, int kind, const float* scale, const float* shift, int rows_h) {
+  a.norm = kind;
+  a.H = ctx->h; a.ldh = ctx->c.hidden;
+  a.stats = ctx->stats; a.nparts = ctx->c.hidden / kStatCols; a.stats_ld = rows_h;
+  a.mscale = scale; a.mshift = shift; a.eps = ctx->c.norm_eps;
+}
+
+// The launch sequence of Euler step k. vout: velocity output (then x is not updated);
+// trace: residual stream copies after the in-projection and after every layer.
+std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
+  const fm_config& c = ctx->c;
+  const int B = ctx->bound_batch, H = c.action_horizon, D = c.hidden, F = c.mlp_dim;
+  const int st = c.state_tokens, Mh = B * (st + H), Ma = B * H;
+  const int S = n_sites(c);
+  const float* row = ctx->table + (size_t)k * S * 3 * D;
+  auto site = [&](int s, int part) { return row + (size_t)s * 3 * D + (size_t)part * D; };
+  std::vector<Op> ops;
+  Op op;
+  memset(&op, 0, sizeof op);
+
+  // action (and state) tokens -> h
+  op.kind = Op::INPROJ;
+  InProjArgs& ip = op.ip;
+  ip.x = ctx->x; ip.da = c.action_dim; ip.w = ctx->w_in; ip.b = ctx->b_in;
+  ip.tb = c.arch == FM_ARCH_DIT_CROSS ? ctx->tbias + (size_t)k * D : nullptr;
+  ip.state_tok = ctx->state_tok; ip.B = B; ip.Ha = H; ip.st = st; ip.D = D;
+  ip.h = ctx->h; ip.stats = ctx->stats; ip.stats_ld = Mh;
+  ops.push_back(op);
+  if (trace) { Op t; memset(&t, 0, sizeof t); t.kind = Op::TRACE; t.trace_layer = 0; ops.push_back(t); }
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    const auto& W = ctx->L[l];
+    if (c.arch == FM_ARCH_PREFIX_JOINT) {
+      const int nq = c.n_heads, dh = c.head_dim, qd = nq * dh;
+      const size_t plane = (size_t)c.max_batch * ctx->cap * dh * ctx->esz;
+      char* kpl = (char*)ctx->pool + (size_t)(2 * l) * plane;
+      char* vpl = (char*)ctx->pool + (size_t)(2 * l + 1) * plane;
+      // QKV + RoPE + append into pool slots [P, P+H)
+      GemmArgs g = gemm_base(Ma, qd + 2 * dh, D, W.qkv);
+      set_norm(ctx, g, NORM_RMS, site(2 * l, 0), site(2 * l, 1), Mh);
+      g.epi = EPI_QKV; g.out = ctx->qbuf; g.ldo = qd;
+      g.q_cols = qd; g.kv_cols = dh; g.tq = H; g.kv_off = ctx->prefix_len;
+      g.rope = c.rope_base > 0.f; g.half_dh = dh / 2; g.rope_cs = ctx->rope_cs;
+      g.kdst = kpl; g.k_bs = (long)ctx->cap * dh; g.k_rs = dh;
+      g.vdst = vpl; g.v_bs = (long)dh * ctx->cap; g.v_ds = ctx->cap;
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      // attention over [prefix ; suffix]
+      AttnArgs at;
+      memset(&at, 0, sizeof at);
+      at.q = ctx->qbuf; at.q_bs = (long)H * qd; at.q_rs = qd;
+      at.k = kpl; at.k_bs = (long)ctx->cap * dh; at.k_rs = dh; at.k_hs = 0;
+      at.vt = vpl; at.v_bs = (long)dh * ctx->cap; at.v_hs = 0; at.v_ds = ctx->cap;
+      at.o = ctx->obuf; at.o_bs = (long)H * qd; at.o_rs = qd;
+      at.B = B; at.Tq = H; at.n_heads = nq; at.heads_per_kv = nq; at.n_keys = ctx->prefix_len + H; at.dh = dh;
+      at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+      memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.at = at; ops.push_back(op);
+      // O projection + gated residual
+      g = gemm_base(Ma, D, qd, W.o);
+      g.A = ctx->obuf; g.lda = qd;
+      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      // gate/up + GELU * up
+      g = gemm_base(Ma, c.mlp_gated ? 2 * F : F, D, W.gu);
+      set_norm(ctx, g, NORM_RMS, site(2 * l + 1, 0), site(2 * l + 1, 1), Mh);
+      g.out = ctx->abuf; g.ldo = F;
+      if (c.mlp_gated) g.epi = EPI_GELU_MUL; else { g.epi = EPI_STORE; g.act = ACT_GELU; }
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      // down + gated residual
+      g = gemm_base(Ma, D, F, W.down);
+      g.A = ctx->abuf; g.lda = F;
+      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l + 1, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+    } else {
+      const int nh = c.n_heads, dh = c.head_dim, Tq = st + H;
+      const bool cross = (l % 2) == 0;
+      AttnArgs at;
+      memset(&at, 0, sizeof at);
+      at.q = ctx->qbuf; at.q_bs = (long)Tq * D; at.q_rs = D;
+      at.o = ctx->obuf; at.o_bs = (long)Tq * D; at.o_rs = D;
+      at.B = B; at.Tq = Tq; at.n_heads = nh; at.heads_per_kv = 1; at.dh = dh;
+      at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+      GemmArgs g;
+      if (cross) {
+        const int ci = l / 2;
+        g = gemm_base(Mh, D, D, W.q);
+        set_norm(ctx, g, NORM_LN, site(l, 0), site(l, 1), Mh);
+        g.epi = EPI_STORE; g.out = ctx->qbuf; g.ldo = D;
+        memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+        at.k = (char*)ctx->cross_k + (size_t)ci * c.max_batch * c.ctx_len_max * D * ctx->esz;
+        at.k_bs = (long)c.ctx_len_max * D; at.k_rs = D; at.k_hs = dh;
+        at.vt = (char*)ctx->cross_vt + (size_t)ci * c.max_batch * D * ctx->spad * ctx->esz;
+        at.v_bs = (long)D * ctx->spad; at.v_hs = (long)dh * ctx->spad; at.v_ds = ctx->spad;
+        at.n_keys = ctx->prefix_len;
+      } else {
+        g = gemm_base(Mh, 3 * D, D, W.qkv);
+        set_norm(ctx, g, NORM_LN, site(l, 0), site(l, 1), Mh);
+        g.epi = EPI_QKV; g.out = ctx->qbuf; g.ldo = D;
+        g.q_cols = D; g.kv_cols = D; g.tq = Tq; g.kv_off = 0; g.rope = 0;
+        g.kdst = ctx->kself; g.k_bs = (long)Tq * D; g.k_rs = D;
+        g.vdst = ctx->vtself; g.v_bs = (long)D * ctx->tpad; g.v_ds = ctx->tpad;
+        memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+        at.k = ctx->kself; at.k_bs = (long)Tq * D; at.k_rs = D; at.k_hs = dh;
+        at.vt = ctx->vtself; at.v_bs = (long)D * ctx->tpad; at.v_hs = (long)dh * ctx->tpad; at.v_ds = ctx->tpad;
+        at.n_keys = Tq;
+      }
+      memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.at = at; ops.push_back(op);
+      g = gemm_base(Mh, D, D, W.o);
+      g.A = ctx->obuf; g.lda = D;
+      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(l, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      g = gemm_base(Mh, F, D, W.gu);
+      set_norm(ctx, g, NORM_LN, nullptr, nullptr, Mh);
+      g.epi = EPI_STORE; g.act = ACT_GELU; g.out = ctx->abuf; g.ldo = F;
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      g = gemm_base(Mh, D, F, W.down);
+      g.A = ctx->abuf; g.lda = F;
+      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = nullptr; g.stats_out = ctx->stats; g.stats_out_ld = Mh;
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+    }
+    if (trace) { Op t; memset(&t, 0, sizeof t); t.kind = Op::TRACE; t.trace_layer = l + 1; ops.push_back(t); }
+  }
+  // final modulated norm + velocity projection + Euler update
+  GemmArgs g = gemm_base(Ma, c.action_dim, D, ctx->w_out);
+  set_norm(ctx, g, c.arch == FM_ARCH_PREFIX_JOINT ? NORM_RMS : NORM_LN, site(S - 1, 0), site(S - 1, 1), Mh);
+  if (st > 0) { g.row_group = H; g.row_gstride = st + H; g.row_off = st; }
+  g.epi = EPI_EULER; g.bias = ctx->b_out; g.ldo = c.action_dim;
+  if (vout) { g.vout = vout; g.x = nullptr; g.dt = 0.f; }
+  else { g.x = ctx->x; g.dt = ctx->tau[k + 1] - ctx->tau[k]; g.vout = nullptr; }
+  memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+  return ops;
+}
+
+// Plan tile shapes / splits and make sure the shared workspace covers every op.
+fm_status plan_ops(fm_ctx* ctx, std::vector<Op>& ops) {
+  size_t need = 0;
+  for (auto& op : ops) {
+    if (op.kind == Op::GEMM) {
+      gemm_plan(op.g, ctx->elem, ctx->num_cus);
+      need = std::max(need, gemm_ws_bytes(op.g));
+      if (op.g.splits > 1 && gemm_num_tiles(op.g) > fm_ctx::kCounters) return fail(ctx, FM_ERR_UNSUPPORTED, "too many split tiles");
+    } else if (op.kind == Op::ATTN) {
+      attn_plan(op.at, ctx->elem, ctx->num_cus);
+      need = std::max(need, attn_ws_bytes(op.at));
+      if (op.at.splits > 1 && attn_num_items(op.at) > fm_ctx::kCounters) return fail(ctx, FM_ERR_UNSUPPORTED, "too many attention tiles");
+    }
+  }
+  if (need > ctx->ws_bytes) {
+    HIPCK(hipStreamSynchronize(ctx->stream));
+    dfree(ctx, ctx->ws);
+    ctx->ws = nullptr;
+    ctx->ws_bytes = 0;
+    void* p;
+    fm_status s = dalloc(ctx, &p, need);
+    if (s != FM_OK) return s;
+    ctx->ws = (float*)p;
+    ctx->ws_bytes = need;
+  }
+  for (auto& op : ops) {
+    if (op.kind == Op::GEMM) { op.g.ws = ctx->ws; op.g.counters = ctx->counters; }
+    else if (op.kind == Op::ATTN) { op.at.ws = ctx->ws; op.at.counters = ctx->counters; }
+  }
+  return FM_OK;
+}
+
+fm_status enqueue_ops(fm_ctx* ctx, const std::vector<Op>& ops, hipStream_t s, float* trace) {
+  const size_t hsz = (size_t)ctx->bound_batch * ctx->rows_per_req() * ctx->c.hidden;
+  for (const auto& op : ops) {
+    switch (op.kind) {
+      case Op::GEMM: HIPCK(gemm_launch(op.g, ctx->elem, s)); break;
+      case Op::ATTN: HIPCK(attn_launch(op.at, ctx->elem, s)); break;
+      case Op::INPROJ: HIPCK(inproj_launch(op.ip, ctx->elem, s)); break;
+      case Op::TRACE:
+        HIPCK(hipMemcpyAsync(trace + (size_t)op.trace_layer * hsz, ctx->h, hsz * sizeof(float), hipMemcpyDeviceToDevice, s));
+        break;
+    }
+  }
+  return FM_OK;
+}
+
+fm_status check_ready(fm_ctx* ctx) {
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  if (!ctx->loaded) return fail(ctx, FM_ERR_STATE, "weights are not loaded");
+  if (ctx->steps < 0) return fail(ctx, FM_ERR_STATE, "no schedule: call fm_set_schedule first");
+  if (ctx->prefix_len < 0) return fail(ctx, FM_ERR_STATE, "nothing bound: call fm_bind_prefix_kv first");
+  if (ctx->sched_batch != ctx->bound_batch)
+    return fail(ctx, FM_ERR_SCHEDULE, fmt("scheduled batch %d differs from bound batch %d", ctx->sched_batch, ctx->bound_batch));
+  return FM_OK;
+}
+
+}  // namespace
+
+// =======================================================================================
+// C ABI
+// =======================================================================================
+extern "C" {
+
+fm_status fm_query(const fm_config* cfg, fm_plan_info* info, char* msg, int32_t msg_len) {
+  std::string m;
+  fm_status s = check_config(cfg, m);
+  if (msg && msg_len > 0) { strncpy(msg, m.c_str(), msg_len - 1); msg[msg_len - 1] = 0; }
+  if (s != FM_OK) { g_err = m; return s; }
+  if (info) {
+    const fm_config& c = *cfg;
+    const int esz = c.dtype == FM_BF16 ? 2 : 4;
+    memset(info, 0, sizeof *info);
+    info->n_sites = n_sites(c);
+    info->pool_capacity = c.arch == FM_ARCH_PREFIX_JOINT ? pool_capacity(c) : 0;
+    auto specs = weight_specs(c);
+    info->n_weights = (int32_t)specs.size();
+    int64_t wb = 0;
+    for (auto& sp : specs) {
+      int64_t n = 1;
+      for (auto d : sp.shape) n *= d;
+      wb += n * esz;
+    }
+    info->weight_bytes = wb;
+    if (c.arch == FM_ARCH_PREFIX_JOINT)
+      info->pool_bytes = (int64_t)c.n_layers * 2 * c.max_batch * pool_capacity(c) * c.head_dim * esz;
+    else
+      info->pool_bytes = (int64_t)((c.n_layers + 1) / 2) * c.max_batch * c.hidden * (c.ctx_len_max + round_up(c.ctx_len_max, 8)) * esz;
+  }
+  return FM_OK;
+}
+
+fm_status fm_weight_spec(const fm_config* cfg, int32_t i, const char** name, int32_t* ndim, int64_t shape[4]) {
+  std::string m;
+  fm_status s = check_config(cfg, m);
+  if (s != FM_OK) { g_err = m; return s; }
+  static thread_local std::vector<Spec> cache;
+  cache = weight_specs(*cfg);
+  if (i < 0 || i >= (int32_t)cache.size()) { g_err = fmt("weight index %d out of range [0, %zu)", i, cache.size()); return FM_ERR_INVALID_ARG; }
+  if (name) *name = cache[i].name.c_str();
+  if (ndim) *ndim = (int32_t)cache[i].shape.size();
+  if (shape) for (size_t d = 0; d < 4; ++d) shape[d] = d < cache[i].shape.size() ? cache[i].shape[d] : 0;
+  return FM_OK;
+}
+
+const char* fm_last_error(const fm_ctx* ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
+  std::string m;
+  if (!out) { g_err = "out is NULL"; return FM_ERR_INVALID_ARG; }
+  *out = nullptr;
+  fm_status s = check_config(cfg, m);
+  if (s != FM_OK) { g_err = m; return s; }
+  fm_ctx* ctx = new fm_ctx();
+  ctx->c = *cfg;
+  ctx->stream = (hipStream_t)stream;
+  ctx->elem = cfg->dtype == FM_BF16 ? ET_BF16 : ET_F32;
+  ctx->esz = cfg->dtype == FM_BF16 ? 2 : 4;
+  auto bail = [&](fm_status st) { g_err = ctx->err; fm_destroy(ctx); return st; };
+  hipError_t e = hipGetDevice(&ctx->device);
+  if (e != hipSuccess) { ctx->err = fmt("hipGetDevice: %s", hipGetErrorString(e)); return bail(FM_ERR_DEVICE); }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, ctx->device);
+  if (e != hipSuccess) { ctx->err = fmt("hipGetDeviceProperties: %s", hipGetErrorString(e)); return bail(FM_ERR_DEVICE); }
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) { ctx->err = fmt("device is %s; this library is built for gfx950", prop.gcnArchName); return bail(FM_ERR_UNSUPPORTED); }
+  ctx->num_cus = prop.multiProcessorCount;
+  e = hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) { ctx->err = fmt("hipStreamCreate: %s", hipGetErrorString(e)); return bail(FM_ERR_DEVICE); }
+
+  const fm_config& c = *cfg;
+  const size_t B = c.max_batch, D = c.hidden, F = c.mlp_dim, H = c.action_horizon, st = c.state_tokens;
+  const size_t rows = B * (st + H);
+  const size_t esz = ctx->esz;
+  const size_t qd = (size_t)c.n_heads * c.head_dim;
+  void* p;
+#define ALLOC(field, bytes, type)                               \
+  do {                                                          \
+    if ((s = dalloc(ctx, &p, (bytes))) != FM_OK) return bail(s); \
+    ctx->field = (type)p;                                       \
+  } while (0)
+  ALLOC(h, rows * D * 4, float*);
+  ALLOC(x, B * H * c.action_dim * 4, float*);
+  ALLOC(stats, (D / kStatCols) * rows * sizeof(float2), float2*);
+  ALLOC(qbuf, rows * std::max(qd, D) * esz, void*);
+  ALLOC(obuf, rows * std::max(qd, D) * esz, void*);
+  ALLOC(abuf, rows * F * esz, void*);
+  ALLOC(table, (size_t)c.max_steps * n_sites(c) * 3 * D * 4, float*);
+  ALLOC(e_buf, (size_t)c.max_steps * D * esz, void*);
+  ALLOC(c1_buf, (size_t)c.max_steps * D * esz, void*);
+  ALLOC(c_buf, (size_t)c.max_steps * D * esz, void*);
+  ALLOC(counters, fm_ctx::kCounters * sizeof(unsigned), unsigned*);
+  if (c.arch == FM_ARCH_PREFIX_JOINT) {
+    ctx->cap = pool_capacity(c);
+    ALLOC(pool, (size_t)c.n_layers * 2 * B * ctx->cap * c.head_dim * esz, void*);
+    ALLOC(rope_cs, H * (c.head_dim / 2) * sizeof(float2), float2*);
+  } else {
+    const size_t nc = (c.n_layers + 1) / 2;
+    ctx->spad = (int)round_up(c.ctx_len_max, 8);
+    ctx->tpad = (int)round_up(st + H, 8);
+    ALLOC(cross_k, nc * B * c.ctx_len_max * D * esz, void*);
+    ALLOC(cross_vt, nc * B * D * ctx->spad * esz, void*);
+    ALLOC(kself, rows * D * esz, void*);
+    ALLOC(vtself, B * D * ctx->tpad * esz, void*);
+    ALLOC(tbias, (size_t)c.max_steps * D * 4, float*);
+    if (st > 0) ALLOC(state_tok, B * st * D * 4, float*);
+  }
+#undef ALLOC
+  e = hipMemsetAsync(ctx->counters, 0, fm_ctx::kCounters * sizeof(unsigned), ctx->stream);
+  if (e == hipSuccess && ctx->pool) e = hipMemsetAsync(ctx->pool, 0, (size_t)c.n_layers * 2 * B * ctx->cap * c.head_dim * esz, ctx->stream);
+  if (e == hipSuccess && ctx->vtself) e = hipMemsetAsync(ctx->vtself, 0, B * D * ctx->tpad * esz, ctx->stream);
+  if (e == hipSuccess && ctx->cross_vt) e = hipMemsetAsync(ctx->cross_vt, 0, ((c.n_layers + 1) / 2) * B * D * ctx->spad * esz, ctx->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+  if (e != hipSuccess) { ctx->err = fmt("initial clear: %s", hipGetErrorString(e)); return bail(FM_ERR_DEVICE); }
+  ctx->L.resize(c.n_layers);
+  *out = ctx;
+  return FM_OK;
+}
+
+fm_status fm_destroy(fm_ctx* ctx) {
+  if (!ctx) return FM_OK;
+  (void)hipStreamSynchronize(ctx->stream);
+  invalidate_graph(ctx);
+  for (void* p : ctx->allocs) (void)hipFree(p);
+  ctx->allocs.clear();
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  delete ctx;
+  return FM_OK;
+}
+
+fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  if (!t || n < 0) return fail(ctx, FM_ERR_INVALID_ARG, "tensor table is NULL");
+  const fm_config& c = ctx->c;
+  auto specs = weight_specs(c);
+  std::map<std::string, const fm_tensor*> byname;
+  for (int i = 0; i < n; ++i) {
+    if (!t[i].name) return fail(ctx, FM_ERR_INVALID_ARG, fmt("tensor %d has no name", i));
+    if (byname.count(t[i].name)) return fail(ctx, FM_ERR_SHAPE, fmt("tensor '%s' given twice", t[i].name));
+    byname[t[i].name] = &t[i];
+  }
+  for (auto& sp : specs) {
+    auto it = byname.find(sp.name);
+    if (it == byname.end()) return fail(ctx, FM_ERR_SHAPE, fmt("missing weight '%s'", sp.name.c_str()));
+    const fm_tensor* w = it->second;
+    if (w->dtype != c.dtype) return fail(ctx, FM_ERR_SHAPE, fmt("weight '%s': dtype %d, expected %d", sp.name.c_str(), w->dtype, c.dtype));
+    bool ok = w->ndim == (int)sp.shape.size();
+    for (size_t d = 0; ok && d < sp.shape.size(); ++d) ok = w->shape[d] == sp.shape[d];
+    if (!ok) {
+      std::string got = "[", exp = "[";
+      for (int d = 0; d < w->ndim && d < 4; ++d) got += std::to_string(w->shape[d]) + (d + 1 < w->ndim ? "," : "");
+      for (size_t d = 0; d < sp.shape.size(); ++d) exp += std::to_string(sp.shape[d]) + (d + 1 < sp.shape.size() ? "," : "");
+      return fail(ctx, FM_ERR_SHAPE, fmt("weight '%s': shape %s], expected %s]", sp.name.c_str(), got.c_str(), exp.c_str()));
+    }
+    if (!w->data) return fail(ctx, FM_ERR_INVALID_ARG, fmt("weight '%s' has no data", sp.name.c_str()));
+    byname.erase(it);
+  }
+  if (!byname.empty()) return fail(ctx, FM_ERR_SHAPE, fmt("unexpected weight '%s'", byname.begin()->first.c_str()));
+  for (int i = 0; i < n; ++i) byname[t[i].name] = &t[i];
+
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  invalidate_graph(ctx);
+  // drop previous weights
+  auto drop = [&](void*& p) { dfree(ctx, p); p = nullptr; };
+  for (auto& l : ctx->L) { drop(l.qkv); drop(l.q); drop(l.kx); drop(l.vx); drop(l.o); drop(l.gu); drop(l.down); }
+  drop(ctx->w_tin); drop(ctx->w_tout); drop(ctx->w_mod); drop(ctx->w_tb); drop(ctx->w_in); drop(ctx->w_out); drop(ctx->w_state);
+  { void* bp[] = {ctx->b_tin, ctx->b_tout, ctx->b_mod, ctx->b_tb, ctx->b_in, ctx->b_out, ctx->b_state}; for (void* q : bp) dfree(ctx, q); }
+  ctx->b_tin = ctx->b_tout = ctx->b_mod = ctx->b_tb = ctx->b_in = ctx->b_out = ctx->b_state = nullptr;
+  ctx->loaded = false;
+  ctx->steps = -1;
+
+  const int elem = ctx->elem;
+  const size_t esz = ctx->esz;
+  const int D = c.hidden, F = c.mlp_dim;
+  fm_status s;
+  auto data = [&](const char* nm) { return byname[nm]->data; };
+  auto swz = [&](void** dst, const void* src, const int* rows, int N, int K) -> fm_status {
+    fm_status st2 = dalloc(ctx, dst, swizzled_bytes(N, K, elem));
+    if (st2 != FM_OK) return st2;
+    HIPCK(swizzle_weight(*dst, src, rows, N, K, K, elem, ctx->stream));
+    return FM_OK;
+  };
+  auto bias = [&](float** dst, const void* src, long nel) -> fm_status {
+    void* p;
+    fm_status st2 = dalloc(ctx, &p, nel * 4);
+    if (st2 != FM_OK) return st2;
+    *dst = (float*)p;
+    HIPCK(convert_to_f32(*dst, src, nel, elem, ctx->stream));
+    return FM_OK;
+  };
+  auto plain = [&](void** dst, const void* src, size_t bytes) -> fm_status {
+    fm_status st2 = dalloc(ctx, dst, bytes);
+    if (st2 != FM_OK) return st2;
+    HIPCK(hipMemcpyAsync(*dst, src, bytes, hipMemcpyDeviceToDevice, ctx->stream));
+    return FM_OK;
+  };
+  const int S = n_sites(c);
+  if ((s = swz(&ctx->w_tin, data("time_in.w"), nullptr, D, D)) != FM_OK) return s;
+  if ((s = swz(&ctx->w_tout, data("time_out.w"), nullptr, D, D)) != FM_OK) return s;
+  if ((s = swz(&ctx->w_mod, data("mod.w"), nullptr, S * 3 * D, D)) != FM_OK) return s;
+  if ((s = swz(&ctx->w_out, data("action_out.w"), nullptr, c.action_dim, D)) != FM_OK) return s;
+  if ((s = plain(&ctx->w_in, data("action_in.w"), (size_t)D * c.action_dim * esz)) != FM_OK) return s;
+  if ((s = bias(&ctx->b_tin, data("time_in.b"), D)) != FM_OK) return s;
+  if ((s = bias(&ctx->b_tout, data("time_out.b"), D)) != FM_OK) return s;
+  if ((s = bias(&ctx->b_mod, data("mod.b"), (long)S * 3 * D)) != FM_OK) return s;
+  if ((s = bias(&ctx->b_in, data("action_in.b"), D)) != FM_OK) return s;
+  if ((s = bias(&ctx->b_out, data("action_out.b"), c.action_dim)) != FM_OK) return s;
+
+  // staging buffer for concatenated row blocks, and device row-index lists
+  size_t stage_rows = 0;
+  if (c.arch == FM_ARCH_PREFIX_JOINT) stage_rows = std::max((size_t)(c.n_heads + 2) * c.head_dim, (size_t)2 * F);
+  else stage_rows = 3 * (size_t)D;
+  void* stage = nullptr;
+  int* rowidx = nullptr;
+  std::vector<int> rows;
+  if ((s = dalloc(ctx, &stage, stage_rows * D * esz)) != FM_OK) return s;
+
+  if (c.arch == FM_ARCH_PREFIX_JOINT) {
+    const int nq = c.n_heads, dh = c.head_dim, qd = nq * dh, N = qd + 2 * dh;
+    const bool rope = c.rope_base > 0.f;
+    // QKV rows: within each q / k head, output row 2j <- j and 2j+1 <- j + dh/2 (RoPE pairs
+    // adjacent); v rows unchanged. Gate/up rows interleaved: 2f <- gate f, 2f+1 <- up f.
+    rows.assign(N + 2 * F, 0);
+    for (int r = 0; r < N; ++r) {
+      const int head0 = (r / dh) * dh, dp = r % dh;
+      rows[r] = (r < qd + dh && rope) ? head0 + ((dp & 1) ? dp / 2 + dh / 2 : dp / 2) : r;
+    }
+    for (int f = 0; f < F; ++f) { rows[N + 2 * f] = f; rows[N + 2 * f + 1] = F + f; }
+    {
+      void* p;
+      if ((s = dalloc(ctx, &p, rows.size() * sizeof(int))) != FM_OK) return s;
+      rowidx = (int*)p;
+    }
+    HIPCK(hipMemcpyAsync(rowidx, rows.data(), rows.size() * sizeof(int), hipMemcpyHostToDevice, ctx->stream));
+    HIPCK(hipStreamSynchronize(ctx->stream));
+    for (int l = 0; l < c.n_layers; ++l) {
+      const std::string p = "layers." + std::to_string(l) + ".";
+      auto& W = ctx->L[l];
+      HIPCK(hipMemcpyAsync(stage, data((p + "q.w").c_str()), (size_t)qd * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
+      HIPCK(hipMemcpyAsync((char*)stage + (size_t)qd * D * esz, data((p + "k.w").c_str()), (size_t)dh * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
+      HIPCK(hipMemcpyAsync((char*)stage + (size_t)(qd + dh) * D * esz, data((p + "v.w").c_str()), (size_t)dh * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
+      if ((s = swz(&W.qkv, stage, rowidx, N, D)) != FM_OK) return s;
+      if ((s = swz(&W.o, data((p + "o.w").c_str()), nullptr, D, qd)) != FM_OK) return s;
+      if ((s = swz(&W.down, data((p + "down.w").c_str()), nullptr, D, F)) != FM_OK) return s;
+      if (c.mlp_gated) {
+        HIPCK(hipMemcpyAsync(stage, data((p + "gate.w").c_str()), (size_t)F * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
+        HIPCK(hipMemcpyAsync((char*)stage + (size_t)F * D * esz, data((p + "up.w").c_str()), (size_t)F * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
+        if ((s = swz(&W.gu, stage, rowidx + N, 2 * F, D)) != FM_OK) return s;
+      } else {
+        if ((s = swz(&W.gu, data((p + "gate.w").c_str()), nullptr, F, D)) != FM_OK) return s;
+      }
+    }
+  } else {
+    if ((s = swz(&ctx->w_tb, data("time_bias.w"), nullptr, D, D)) != FM_OK) return s;
+    if ((s = bias(&ctx->b_tb, data("time_bias.b"), D)) != FM_OK) return s;
+    if ((s = plain(&ctx->w_state, data("state_in.w"), (size_t)D * c.state_dim * esz)) != FM_OK) return s;
+    if ((s = bias(&ctx->b_state, data("state_in.b"), D)) != FM_OK) return s;
+    for (int i = 0; i < c.n_layers; ++i) {
+      const std::string p = "blocks." + std::to_string(i) + ".";
+      auto& W = ctx->L[i];
+      if (i % 2 == 0) {
+        if ((s = swz(&W.q, data((p + "q.w").c_str()), nullptr, D, D)) != FM_OK) return s;
+        if ((s = swz(&W.kx, data((p + "k.w").c_str()), nullptr, D, c.ctx_dim)) != FM_OK) return s;
+        if ((s = swz(&W.vx, data((p + "v.w").c_str()), nullptr, D, c.ctx_dim)) != FM_OK) return s;
+      } else {
+        HIPCK(hipMemcpyAsync(stage, data((p + "q.w").c_str()), (size_t)D * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
+        HIPCK(hipMemcpyAsync((char*)stage + (size_t)D * D * esz, data((p + "k.w").c_str()), (size_t)D * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
+        HIPCK(hipMemcpyAsync((char*)stage + (size_t)2 * D * D * esz, data((p + "v.w").c_str()), (size_t)D * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
+        if ((s = swz(&W.qkv, stage, nullptr, 3 * D, D)) != FM_OK) return s;
+        HIPCK(hipStreamSynchronize(ctx->stream));
+      }
+      if ((s = swz(&W.o, data((p + "o.w").c_str()), nullptr, D, D)) != FM_OK) return s;
+      if ((s = swz(&W.gu, data((p + "ff1.w").c_str()), nullptr, F, D)) != FM_OK) return s;
+      if ((s = swz(&W.down, data((p + "ff2.w").c_str()), nullptr, D, F)) != FM_OK) return s;
+    }
+  }
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  dfree(ctx, stage);
+  dfree(ctx, rowidx);
+  ctx->loaded = true;
+  ctx->prefix_len = -1;  // a binding may depend on the previous weights (DiT projections)
+  return FM_OK;
+}
+
+fm_status fm_set_schedule(fm_ctx* ctx, int32_t steps, int32_t batch, const float* tau_host) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  if (!ctx->loaded) return fail(ctx, FM_ERR_STATE, "weights are not loaded");
+  const fm_config& c = ctx->c;
+  if (steps < 0 || steps > c.max_steps) return fail(ctx, FM_ERR_INVALID_ARG, fmt("steps %d outside [0, %d]", steps, c.max_steps));
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, FM_ERR_INVALID_ARG, fmt("batch %d outside [1, %d]", batch, c.max_batch));
+  std::vector<float> tau(steps + 1);
+  for (int k = 0; k <= steps; ++k) {
+    tau[k] = tau_host ? tau_host[k] : (steps > 0 ? (float)(1.0 - (double)k / steps) : 1.f);
+    if (!std::isfinite(tau[k])) return fail(ctx, FM_ERR_INVALID_ARG, fmt("tau[%d] is not finite", k));
+  }
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  invalidate_graph(ctx);
+  ctx->tau = tau;
+  ctx->steps = steps;
+  ctx->sched_batch = batch;
+  if (steps == 0) return FM_OK;
+  const int D = c.hidden, S = n_sites(c), T = steps;
+  // sinusoidal time embedding of tau_0..tau_{T-1}, evaluated in double on the host:
+  // [sin(2 pi tau / p_j)] ++ [cos(2 pi tau / p_j)], periods geometric from 4e-3 to 4
+  std::vector<float> e((size_t)T * D);
+  const int half = D / 2;
+  for (int k = 0; k < T; ++k)
+    for (int j = 0; j < half; ++j) {
+      const double frac = half > 1 ? (double)j / (half - 1) : 0.0;
+      const double period = 4e-3 * std::pow(4.0 / 4e-3, frac);
+      const double arg = (double)tau[k] * 2.0 * 3.14159265358979323846 / period;
+      e[(size_t)k * D + j] = (float)std::sin(arg);
+      e[(size_t)k * D + half + j] = (float)std::cos(arg);
+    }
+  float* e32 = nullptr;
+  {
+    void* p;
+    fm_status s = dalloc(ctx, &p, e.size() * 4);
+    if (s != FM_OK) return s;
+    e32 = (float*)p;
+  }
+  HIPCK(hipMemcpyAsync(e32, e.data(), e.size() * 4, hipMemcpyHostToDevice, ctx->stream));
+  HIPCK(convert_from_f32(ctx->e_buf, e32, (long)T * D, ctx->elem, ctx->stream));
+  std::vector<Op> ops;
+  Op op;
+  auto add = [&](GemmArgs g) { memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op); };
+  GemmArgs g = gemm_base(T, D, D, ctx->w_tin);
+  g.A = ctx->e_buf; g.lda = D; g.epi = EPI_STORE; g.bias = ctx->b_tin; g.act = ACT_SILU; g.out = ctx->c1_buf; g.ldo = D;
+  add(g);
+  g = gemm_base(T, D, D, ctx->w_tout);
+  g.A = ctx->c1_buf; g.lda = D; g.epi = EPI_STORE; g.bias = ctx->b_tout; g.act = ACT_SILU; g.out = ctx->c_buf; g.ldo = D;
+  add(g);
+  g = gemm_base(T, S * 3 * D, D, ctx->w_mod);
+  g.A = ctx->c_buf; g.lda = D; g.epi = EPI_STORE; g.bias = ctx->b_mod; g.out = ctx->table; g.ldo = (long)S * 3 * D; g.out_f32 = 1;
+  add(g);
+  if (c.arch == FM_ARCH_DIT_CROSS) {
+    g = gemm_base(T, D, D, ctx->w_tb);
+    g.A = ctx->c_buf; g.lda = D; g.epi = EPI_STORE; g.bias = ctx->b_tb; g.out = ctx->tbias; g.ldo = D; g.out_f32 = 1;
+    add(g);
+  }
+  fm_status s = plan_ops(ctx, ops);
+  if (s != FM_OK) return s;
+  if ((s = enqueue_ops(ctx, ops, ctx->stream, nullptr)) != FM_OK) return s;
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  dfree(ctx, e32);
+  return FM_OK;
+}
+
+fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void* const* k_dev,
+                            const void* const* v_dev, const void* ctx_dev, const void* state_dev) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  if (!ctx->loaded) return fail(ctx, FM_ERR_STATE, "weights are not loaded");
+  const fm_config& c = ctx->c;
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, FM_ERR_INVALID_ARG, fmt("batch %d outside [1, %d]", batch, c.max_batch));
+  const int D = c.hidden, H = c.action_horizon;
+  if (c.arch == FM_ARCH_PREFIX_JOINT) {
+    if (plen < 0 || plen > c.max_prefix_len) return fail(ctx, FM_ERR_INVALID_ARG, fmt("prefix_len %d outside [0, %d]", plen, c.max_prefix_len));
+    if (ctx_dev || state_dev) return fail(ctx, FM_ERR_INVALID_ARG, "ctx_dev / state_dev must be NULL for the prefix-joint expert");
+    if (plen > 0 && (!k_dev || !v_dev)) return fail(ctx, FM_ERR_INVALID_ARG, "k_dev / v_dev are NULL");
+    for (int l = 0; plen > 0 && l < c.n_layers; ++l)
+      if (!k_dev[l] || !v_dev[l]) return fail(ctx, FM_ERR_INVALID_ARG, fmt("prefix K/V of layer %d is NULL", l));
+    HIPCK(hipStreamSynchronize(ctx->stream));
+    invalidate_graph(ctx);
+    const int dh = c.head_dim;
+    const size_t plane = (size_t)c.max_batch * ctx->cap * dh * ctx->esz;
+    for (int l = 0; plen > 0 && l < c.n_layers; ++l) {
+      HIPCK(prefix_k_copy((char*)ctx->pool + 2 * l * plane, (long)ctx->cap * dh, k_dev[l], batch, plen, dh, c.rope_base > 0.f, ctx->elem, ctx->stream));
+      HIPCK(prefix_v_copy_t((char*)ctx->pool + (2 * l + 1) * plane, (long)dh * ctx->cap, ctx->cap, v_dev[l], batch, plen, dh, ctx->elem, ctx->stream));
+    }
+    // cos/sin of the chunk positions plen + i (rotate_half pairs j, j + dh/2), in double
+    std::vector<float2> cs((size_t)H * (dh / 2));
+    for (int i = 0; i < H; ++i)
+      for (int j = 0; j < dh / 2; ++j) {
+        const double th = c.rope_base > 0.f ? std::pow((double)c.rope_base, -2.0 * j / dh) : 0.0;
+        const double ang = (double)(plen + i) * th;
+        cs[(size_t)i * (dh / 2) + j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+      }
+    HIPCK(hipMemcpyAsync(ctx->rope_cs, cs.data(), cs.size() * sizeof(float2), hipMemcpyHostToDevice, ctx->stream));
+    HIPCK(hipStreamSynchronize(ctx->stream));
+  } else {
+    if (plen < 1 || plen > c.ctx_len_max) return fail(ctx, FM_ERR_INVALID_ARG, fmt("context length %d outside [1, %d]", plen, c.ctx_len_max));
+    if (k_dev || v_dev) return fail(ctx, FM_ERR_INVALID_ARG, "k_dev / v_dev must be NULL for the DiT head");
+    if (!ctx_dev) return fail(ctx, FM_ERR_INVALID_ARG, "ctx_dev is NULL");
+    if (c.state_tokens > 0 && !state_dev) return fail(ctx, FM_ERR_INVALID_ARG, "state_dev is NULL");
+    HIPCK(hipStreamSynchronize(ctx->stream));
+    invalidate_graph(ctx);
+    std::vector<Op> ops;
+    Op op;
+    for (int i = 0; i < c.n_layers; i += 2) {
+      const int ci = i / 2;
+      GemmArgs g = gemm_base(batch * plen, D, c.ctx_dim, ctx->L[i].kx);
+      g.A = ctx_dev; g.lda = c.ctx_dim;
+      g.epi = EPI_STORE; g.out = (char*)ctx->cross_k + (size_t)ci * c.max_batch * c.ctx_len_max * D * ctx->esz;
+      g.ldo = D;
+      // rows b*plen + s -> b*ctx_len_max + s
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g;
+      if (plen != c.ctx_len_max) {
+        // one launch per request keeps the [b][ctx_len_max][D] layout
+        for (int b = 0; b < batch; ++b) {
+          Op o2 = op;
+          o2.g.M = plen;
+          o2.g.A = (const char*)ctx_dev + (size_t)b * plen * c.ctx_dim * ctx->esz;
+          o2.g.out = (char*)g.out + (size_t)b * c.ctx_len_max * D * ctx->esz;
+          ops.push_back(o2);
+        }
+      } else {
+        ops.push_back(op);
+      }
+      g = gemm_base(batch * plen, D, c.ctx_dim, ctx->L[i].vx);
+      g.A = ctx_dev; g.lda = c.ctx_dim;
+      g.epi = EPI_VT; g.out = (char*)ctx->cross_vt + (size_t)ci * c.max_batch * D * ctx->spad * ctx->esz;
+      g.vt_group = plen; g.vt_bs = (long)D * ctx->spad; g.vt_ds = ctx->spad;
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+    }
+    if (c.state_tokens > 0) {
+      memset(&op, 0, sizeof op);
+      op.kind = Op::INPROJ;
+      op.ip.x = (const float*)state_dev; op.ip.da = c.state_dim; op.ip.w = ctx->w_state; op.ip.b = ctx->b_state;
+      op.ip.B = batch * c.state_tokens; op.ip.Ha = 1; op.ip.st = 0; op.ip.D = D; op.ip.h = ctx->state_tok; op.ip.stats = nullptr;
+      ops.push_back(op);
+    }
+    fm_status s = plan_ops(ctx, ops);
+    if (s != FM_OK) return s;
+    if ((s = enqueue_ops(ctx, ops, ctx->stream, nullptr)) != FM_OK) return s;
+    HIPCK(hipStreamSynchronize(ctx->stream));
+  }
+  ctx->bound_batch = batch;
+  ctx->prefix_len = plen;
+  return FM_OK;
+}
+
+static fm_status capture_loop(fm_ctx* ctx) {
+  invalidate_graph(ctx);
+  std::vector<std::vector<Op>> steps;
+  for (int k = 0; k < ctx->steps; ++k) {
+    steps.push_back(build_step(ctx, k, nullptr, nullptr));
+    fm_status s = plan_ops(ctx, steps.back());
+    if (s != FM_OK) return s;
+  }
+  HIPCK(hipStreamBeginCapture(ctx->cap_stream, hipStreamCaptureModeThreadLocal));
+  for (auto& ops : steps) {
+    fm_status s = enqueue_ops(ctx, ops, ctx->cap_stream, nullptr);
+    if (s != FM_OK) {
+      hipGraph_t g;
+      (void)hipStreamEndCapture(ctx->cap_stream, &g);
+      if (g) (void)hipGraphDestroy(g);
+      return s;
+    }
+  }
+  HIPCK(hipStreamEndCapture(ctx->cap_stream, &ctx->graph));
+  HIPCK(hipGraphInstantiate(&ctx->gexec, ctx->graph, nullptr, nullptr, 0));
+  ctx->graph_valid = true;
+  return FM_OK;
+}
+
+fm_status fm_denoise(fm_ctx* ctx, const float* x0, int32_t steps, float* out) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  fm_status s = check_ready(ctx);
+  if (s != FM_OK) return s;
+  if (!x0 || !out) return fail(ctx, FM_ERR_INVALID_ARG, "x0 / out is NULL");
+  if (steps != ctx->steps)
+    return fail(ctx, FM_ERR_SCHEDULE, fmt("steps %d differs from the scheduled %d", steps, ctx->steps));
+  const size_t xbytes = (size_t)ctx->bound_batch * ctx->c.action_horizon * ctx->c.action_dim * sizeof(float);
+  if (steps == 0) {
+    if (out != x0) HIPCK(hipMemcpyAsync(out, x0, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+    return FM_OK;
+  }
+  if (!ctx->graph_valid && (s = capture_loop(ctx)) != FM_OK) return s;
+  HIPCK(hipMemcpyAsync(ctx->x, x0, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+  HIPCK(hipGraphLaunch(ctx->gexec, ctx->stream));
+  HIPCK(hipMemcpyAsync(out, ctx->x, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+  return FM_OK;
+}
+
+static fm_status step_eager(fm_ctx* ctx, const float* xin, int32_t k, float* v, float* trace) {
+  fm_status s = check_ready(ctx);
+  if (s != FM_OK) return s;
+  if (!xin || !v) return fail(ctx, FM_ERR_INVALID_ARG, "x / v is NULL");
+  if (k < 0 || k >= ctx->steps) return fail(ctx, FM_ERR_SCHEDULE, fmt("step %d outside the scheduled [0, %d)", k, ctx->steps));
+  const size_t xbytes = (size_t)ctx->bound_batch * ctx->c.action_horizon * ctx->c.action_dim * sizeof(float);
+  std::vector<Op> ops = build_step(ctx, k, v, trace);
+  if ((s = plan_ops(ctx, ops)) != FM_OK) return s;
+  HIPCK(hipMemcpyAsync(ctx->x, xin, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+  return enqueue_ops(ctx, ops, ctx->stream, trace);
+}
+
+fm_status fm_step_velocity(fm_ctx* ctx, const float* x, int32_t k, float* v) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  return step_eager(ctx, x, k, v, nullptr);
+}
+
+fm_status fm_step_trace(fm_ctx* ctx, const float* x, int32_t k, float* v, float* trace) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (!trace) return fail(ctx, FM_ERR_INVALID_ARG, "h_trace is NULL");
+  return step_eager(ctx, x, k, v, trace);
+}
+
+// ---------------------------------------------------------------------------------------
+// Kernel-level entry points (own scratch, synchronous).
+// ---------------------------------------------------------------------------------------
+fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, const void* W,
+                       const float* bias, int32_t act, void* out, int32_t out_f32, void* stream) {
+  const int elem = dtype == FM_BF16 ? ET_BF16 : ET_F32;
+  const int kq = dtype == FM_BF16 ? 32 : 16;
+  if ((dtype != FM_F32 && dtype != FM_BF16) || M < 0 || N < 1 || K < kq || K % kq != 0 || !A || !W || !out ||
+      act < 0 || act > 2) {
+    g_err = fmt("fm_op_linear: bad arguments (M %d N %d K %d, K a multiple of %d)", M, N, K, kq);
+    return FM_ERR_INVALID_ARG;
+  }
+  if (M == 0) return FM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) { g_err = "no device"; return FM_ERR_DEVICE; }
+  GemmArgs g = gemm_base(M, N, K, nullptr);
+  g.A = A; g.lda = K; g.epi = EPI_STORE; g.bias = bias; g.act = act; g.out = out; g.ldo = N; g.out_f32 = out_f32;
+  gemm_plan(g, elem, prop.multiProcessorCount);
+  void *wsw = nullptr, *ws = nullptr, *cnt = nullptr;
+  hipError_t e = hipMalloc(&wsw, swizzled_bytes(N, K, elem));
+  const size_t wsb = gemm_ws_bytes(g);
+  if (e == hipSuccess && wsb) e = hipMalloc(&ws, wsb);
+  if (e == hipSuccess) e = hipMalloc(&cnt, fm_ctx::kCounters * sizeof(unsigned));
+  if (e == hipSuccess) e = hipMemsetAsync(cnt, 0, fm_ctx::kCounters * sizeof(unsigned), s);
+  if (e == hipSuccess) e = swizzle_weight(wsw, W, nullptr, N, K, K, elem, s);
+  g.W = wsw; g.ws = (float*)ws; g.counters = (unsigned*)cnt;
+  if (e == hipSuccess && g.splits > 1 && gemm_num_tiles(g) > fm_ctx::kCounters) e = hipErrorInvalidValue;
+  if (e == hipSuccess) e = gemm_launch(g, elem, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  hipError_t e2 = hipSuccess;
+  if (wsw) e2 = hipFree(wsw);
+  if (ws) (void)hipFree(ws);
+  if (cnt) (void)hipFree(cnt);
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) { g_err = fmt("fm_op_linear: %s", hipGetErrorString(e)); return FM_ERR_DEVICE; }
+  return FM_OK;
+}
+
+fm_status fm_op_attention(int32_t dtype, int32_t B, int32_t Tq, int32_t nh, int32_t nkv, int32_t nk, int32_t dh,
+                          const void* q, const void* k, const void* v, void* o, void* stream) {
+  const int elem = dtype == FM_BF16 ? ET_BF16 : ET_F32;
+  if ((dtype != FM_F32 && dtype != FM_BF16) || B < 1 || Tq < 1 || nh < 1 || nk < 1 || (nkv != 1 && nkv != nh) ||
+      !q || !k || !v || !o || (dh != 64 && dh != 128 && dh != 256) || (dtype == FM_F32 && dh == 256)) {
+    g_err = "fm_op_attention: bad arguments";
+    return FM_ERR_INVALID_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) { g_err = "no device"; return FM_ERR_DEVICE; }
+  const size_t esz = elem == ET_BF16 ? 2 : 4;
+  const int kpad = (int)round_up(nk, 8);
+  AttnArgs at;
+  memset(&at, 0, sizeof at);
+  at.q = q; at.q_bs = (long)Tq * nh * dh; at.q_rs = (long)nh * dh;
+  at.k = k; at.k_bs = (long)nkv * nk * dh; at.k_rs = dh; at.k_hs = (long)nk * dh;
+  at.o = o; at.o_bs = at.q_bs; at.o_rs = at.q_rs;
+  at.v_bs = (long)nkv * dh * kpad; at.v_hs = (long)dh * kpad; at.v_ds = kpad;
+  at.B = B; at.Tq = Tq; at.n_heads = nh; at.heads_per_kv = nh / nkv; at.n_keys = nk; at.dh = dh;
+  at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  attn_plan(at, elem, prop.multiProcessorCount);
+  void *vt = nullptr, *ws = nullptr, *cnt = nullptr;
+  hipError_t e = hipMalloc(&vt, (size_t)B * nkv * dh * kpad * esz);
+  const size_t wsb = attn_ws_bytes(at);
+  if (e == hipSuccess && wsb) e = hipMalloc(&ws, wsb);
+  if (e == hipSuccess) e = hipMalloc(&cnt, fm_ctx::kCounters * sizeof(unsigned));
+  if (e == hipSuccess) e = hipMemsetAsync(cnt, 0, fm_ctx::kCounters * sizeof(unsigned), s);
+  if (e == hipSuccess) e = hipMemsetAsync(vt, 0, (size_t)B * nkv * dh * kpad * esz, s);
+  if (e == hipSuccess) e = prefix_v_copy_t(vt, (long)dh * kpad, kpad, v, B * nkv, nk, dh, elem, s);
+  at.vt = vt; at.ws = (float*)ws; at.counters = (unsigned*)cnt;
+  if (e == hipSuccess && at.splits > 1 && attn_num_items(at) > fm_ctx::kCounters) e = hipErrorInvalidValue;
+  if (e == hipSuccess) e = attn_launch(at, elem, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (vt) (void)hipFree(vt);
+  if (ws) (void)hipFree(ws);
+  if (cnt) (void)hipFree(cnt);
+  if (e != hipSuccess) { g_err = fmt("fm_op_attention: %s", hipGetErrorString(e)); return FM_ERR_DEVICE; }
+  return FM_OK;
+}
+
+}  // extern "C"

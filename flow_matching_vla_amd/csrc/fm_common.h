@@ -1,0 +1,96 @@
+// Internal definitions shared by the HIP kernels of the denoise loop (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+namespace fm {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------------------
+// MFMA traits. Both element types move operands as one 16-byte fragment per lane per
+// k-chunk: lane l holds the (l / 16)-th run of VEC consecutive k of row (A) or column (B)
+// (l % 16). The bf16 chunk is one v_mfma_f32_16x16x32_bf16; the fp32 chunk is four
+// v_mfma_f32_16x16x4_f32, element j of every lane feeding instruction j. A and B use the
+// same k assignment, so every chunk computes the exact 16x16 block product. The 16x16
+// fp32 result: lane l, element i holds row 4 * (l / 16) + i, column l % 16.
+// ---------------------------------------------------------------------------------------
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int VEC = 8;   // elements per 16-byte fragment
+  static constexpr int KC = 32;   // k covered by one fragment pair
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int VEC = 4;
+  static constexpr int KC = 16;
+  typedef f32x4 frag;
+  static __device__ __forceinline__ f32x4 mma(const frag& a, const frag& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+    return c;
+  }
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// 16-byte vector of T as raw storage
+struct alignas(16) V16 { uint32_t w[4]; };
+
+template <typename T> __device__ __forceinline__ void unpack(const V16& v, float* out);
+template <> __device__ __forceinline__ void unpack<float>(const V16& v, float* out) {
+  for (int j = 0; j < 4; ++j) out[j] = __uint_as_float(v.w[j]);
+}
+template <> __device__ __forceinline__ void unpack<bf16>(const V16& v, float* out) {
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = __uint_as_float(v.w[j] << 16);
+    out[2 * j + 1] = __uint_as_float(v.w[j] & 0xffff0000u);
+  }
+}
+template <typename T> __device__ __forceinline__ V16 pack(const float* in);
+template <> __device__ __forceinline__ V16 pack<float>(const float* in) {
+  V16 v;
+  for (int j = 0; j < 4; ++j) v.w[j] = __float_as_uint(in[j]);
+  return v;
+}
+template <> __device__ __forceinline__ V16 pack<bf16>(const float* in) {
+  V16 v;
+  for (int j = 0; j < 4; ++j) {
+    bf16 lo = (bf16)in[2 * j], hi = (bf16)in[2 * j + 1];
+    v.w[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return v;
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float c = 0.7978845608028654f;  // sqrt(2 / pi)
+  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+}
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Map a linear workgroup id so that consecutive logical ids land on the same XCD:
+// the hardware deals workgroups round-robin over the 8 XCDs.
+__device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
+  const int nx = 8;
+  if (nblocks < nx || nblocks % nx != 0) return bid;
+  return (bid % nx) * (nblocks / nx) + bid / nx;
+}
+
+}  // namespace fm

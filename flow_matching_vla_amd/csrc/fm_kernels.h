@@ -1,0 +1,97 @@
+// Internal launch interfaces of the denoise-loop kernels (not part of the public C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fm {
+
+enum ElemType { ET_F32 = 0, ET_BF16 = 1 };
+enum EpiKind { EPI_STORE = 0, EPI_GELU_MUL = 1, EPI_QKV = 2, EPI_RESID = 3, EPI_EULER = 4, EPI_VT = 5 };
+enum Act { ACT_NONE = 0, ACT_SILU = 1, ACT_GELU = 2 };
+enum NormKind { NORM_NONE = 0, NORM_RMS = 1, NORM_LN = 2 };
+
+// Columns per partial row-statistic slot written by the residual epilogue and the
+// in-projection, and read by the normalizing A-loader.
+constexpr int kStatCols = 64;
+
+// C[M x N] = A[M x K] * W^T, W stored fragment-major (see swizzle_weight).
+struct GemmArgs {
+  int M, N, K;
+  // A operand: a row-major T matrix, or fp32 residual rows normalized on load.
+  const void* A; long lda;
+  int norm;                                   // NormKind
+  const float* H; long ldh;                   // residual rows for the normalizing loader
+  const float2* stats; int nparts; long stats_ld;  // (mean, M2) per kStatCols-wide slot, [part][row]
+  const float* mscale; const float* mshift;   // modulation (may be null): u = n(h)(1+scale)+shift
+  float eps;
+  int row_group, row_gstride, row_off;        // A row r -> H row (r/row_group)*row_gstride+row_off+r%row_group
+  // B operand: fragment-major weights of [Npad x K]
+  const void* W;
+  // split-K
+  int splits, k_split;
+  float* ws; unsigned* counters;
+  // epilogue
+  int epi;
+  void* out; long ldo; const float* bias; int act; int out_f32;
+  float* h; long ldh_out; const float* gate; float2* stats_out; long stats_out_ld;
+  int q_cols, kv_cols, tq, kv_off, rope, half_dh; const float2* rope_cs;
+  void* kdst; long k_bs, k_rs; void* vdst; long v_bs, v_ds;
+  float* x; float dt; float* vout;
+  int vt_group; long vt_bs, vt_ds;
+  // launch shape chosen by the planner
+  int cfg;
+};
+
+enum GemmCfg { GEMM_64x64 = 0, GEMM_128x128 = 1, GEMM_32x64 = 2 };
+
+// Plan tile shape and split-K for an M x N x K problem; fills cfg/splits/k_split.
+void gemm_plan(GemmArgs& a, int elem, int num_cus);
+size_t gemm_ws_bytes(const GemmArgs& a);        // split-K partial workspace bytes
+int gemm_num_tiles(const GemmArgs& a);
+hipError_t gemm_launch(const GemmArgs& a, int elem, hipStream_t s);
+
+// Attention (vla.cpp Eq. (2), no mask) over groups of query rows sharing one K/V head.
+struct AttnArgs {
+  const void* q; long q_bs, q_rs;             // q[b*q_bs + t*q_rs + n*dh + d]
+  const void* k; long k_bs, k_rs, k_hs;       // k[b*k_bs + g*k_hs + j*k_rs + d]
+  const void* vt; long v_bs, v_hs, v_ds;      // v stored transposed: vt[b*v_bs + g*v_hs + d*v_ds + j]
+  void* o; long o_bs, o_rs;                   // o[b*o_bs + t*o_rs + n*dh + d]
+  int B, Tq, n_heads, heads_per_kv, n_keys, dh;
+  float scale_log2;                            // log2(e) / sqrt(dh)
+  int splits, keys_per_split;
+  float* ws; unsigned* counters;
+  int cfg;
+};
+void attn_plan(AttnArgs& a, int elem, int num_cus);
+size_t attn_ws_bytes(const AttnArgs& a);
+int attn_num_items(const AttnArgs& a);
+hipError_t attn_launch(const AttnArgs& a, int elem, hipStream_t s);
+
+// Fragment-major weight layout: dst holds ceil(N/16) x (K/KC) fragments of 64 x 16 bytes.
+// src is [N x K] row-major; rows listed by src_rows (device, length N; -1 = zero row) or identity.
+hipError_t swizzle_weight(void* dst, const void* src, const int* src_rows, int N, int K, long ld_src,
+                          int elem, hipStream_t s);
+size_t swizzled_bytes(int N, int K, int elem);
+
+// h rows of the in-projection, with per-slot row statistics for the first norm.
+struct InProjArgs {
+  const float* x; int da;                     // x [B*Ha x da] fp32
+  const void* w; const float* b;              // w [D x da] (T, row-major), bias fp32 [D]
+  const float* tb;                            // per-step time bias fp32 [D] or null
+  const float* state_tok;                     // [B*st x D] fp32 or null
+  int B, Ha, st, D;                           // rows per request = st + Ha
+  float* h; float2* stats; long stats_ld;
+};
+hipError_t inproj_launch(const InProjArgs& a, int elem, hipStream_t s);
+
+hipError_t convert_to_f32(float* dst, const void* src, long n, int elem, hipStream_t s);
+hipError_t convert_from_f32(void* dst, const float* src, long n, int elem, hipStream_t s);
+// Prefix K into the pool with RoPE pair interleave (d' = 2j <- j, 2j+1 <- j + dh/2) when rope.
+hipError_t prefix_k_copy(void* pool, long pool_bs, const void* src, int B, int P, int dh, int rope,
+                         int elem, hipStream_t s);
+// Prefix V into the pool transposed: pool[b*pool_bs + d*cap + j] = src[(b*P + j)*dh + d].
+hipError_t prefix_v_copy_t(void* pool, long pool_bs, int cap, const void* src, int B, int P, int dh,
+                           int elem, hipStream_t s);
+hipError_t fill_f32(float* dst, float v, long n, hipStream_t s);
+
+}  // namespace fm

@@ -1,0 +1,257 @@
+"""Python binding of the C ABI in include/fm.h (ctypes). Argument marshalling only: every
+step of the loop runs in the HIP library; torch supplies device memory and the stream.
+The binding refuses to run when the library has not been built."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfmvla.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fm.h")
+
+FM_OK = 0
+STATUS = {0: "FM_OK", 1: "FM_ERR_INVALID_ARG", 2: "FM_ERR_SHAPE", 3: "FM_ERR_STATE", 4: "FM_ERR_SCHEDULE",
+          5: "FM_ERR_UNSUPPORTED", 6: "FM_ERR_OOM", 7: "FM_ERR_DEVICE"}
+F32, BF16 = 0, 1
+
+
+class FMError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class fm_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "arch", "dtype", "n_layers", "hidden", "n_heads", "head_dim", "n_kv_heads", "mlp_dim", "mlp_gated",
+        "action_horizon", "action_dim", "state_tokens", "state_dim", "ctx_len_max", "ctx_dim",
+        "max_prefix_len", "max_batch", "max_steps")] + [("rope_base", C.c_float), ("norm_eps", C.c_float)]
+
+
+class fm_tensor(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("dtype", C.c_int32), ("ndim", C.c_int32), ("shape", C.c_int64 * 4),
+                ("data", C.c_void_p)]
+
+
+class fm_plan_info(C.Structure):
+    _fields_ = [("n_sites", C.c_int32), ("pool_capacity", C.c_int32), ("n_weights", C.c_int32),
+                ("weight_bytes", C.c_int64), ("pool_bytes", C.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libfmvla.so; raise if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with flow_matching_vla_amd.build.build()")
+    try:  # load torch's HIP runtime first so the library binds to the same one (same SONAME)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    L = C.CDLL(LIB_PATH)
+    P, I32, VP = C.POINTER, C.c_int32, C.c_void_p
+    sig = {
+        "fm_query": ([P(fm_config), P(fm_plan_info), C.c_char_p, I32], I32),
+        "fm_weight_spec": ([P(fm_config), I32, P(C.c_char_p), P(I32), P(C.c_int64)], I32),
+        "fm_create": ([P(fm_config), VP, P(VP)], I32),
+        "fm_destroy": ([VP], I32),
+        "fm_last_error": ([VP], C.c_char_p),
+        "fm_load_weights": ([VP, P(fm_tensor), I32], I32),
+        "fm_set_schedule": ([VP, I32, I32, P(C.c_float)], I32),
+        "fm_bind_prefix_kv": ([VP, I32, I32, P(VP), P(VP), VP, VP], I32),
+        "fm_denoise": ([VP, VP, I32, VP], I32),
+        "fm_step_velocity": ([VP, VP, I32, VP], I32),
+        "fm_step_trace": ([VP, VP, I32, VP, VP], I32),
+        "fm_op_linear": ([I32, I32, I32, I32, VP, VP, VP, I32, VP, I32, VP], I32),
+        "fm_op_attention": ([I32, I32, I32, I32, I32, I32, I32, VP, VP, VP, VP, VP], I32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes, f.restype = args, res
+    _lib = L
+    return L
+
+
+def header_symbols():
+    """Names of the functions include/fm.h declares."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fm_status|const char\*)\s+(fm_\w+)\s*\(", txt, re.M)))
+
+
+def make_config(cfg: dict) -> fm_config:
+    c = fm_config()
+    c.arch, c.dtype, c.n_layers, c.hidden = cfg["arch"], cfg["dtype"], cfg["n_layers"], cfg["hidden"]
+    c.n_heads, c.head_dim, c.n_kv_heads = cfg["n_heads"], cfg["head_dim"], cfg["n_kv_heads"]
+    c.mlp_dim, c.mlp_gated = cfg["mlp_dim"], cfg["mlp_gated"]
+    c.action_horizon, c.action_dim = cfg["action_horizon"], cfg["action_dim"]
+    c.state_tokens, c.state_dim = cfg.get("state_tokens", 0), cfg.get("state_dim", 0)
+    c.ctx_len_max, c.ctx_dim = cfg.get("ctx_len_max", cfg.get("ctx_len", 0)), cfg.get("ctx_dim", 0)
+    c.max_prefix_len = cfg.get("max_prefix_len", cfg.get("prefix_len", 0))
+    c.max_batch = cfg.get("max_batch", cfg.get("batch", 1))
+    c.max_steps = cfg.get("max_steps", max(cfg.get("steps", 1), 1))
+    c.rope_base, c.norm_eps = cfg.get("rope_base", 0.0), cfg.get("norm_eps", 1e-6)
+    return c
+
+
+def _check(st: int, ctx=None):
+    if st != FM_OK:
+        msg = lib().fm_last_error(ctx)
+        raise FMError(st, msg.decode() if msg else "")
+
+
+def query(cfg: dict) -> dict:
+    info = fm_plan_info()
+    buf = C.create_string_buffer(512)
+    st = lib().fm_query(C.byref(make_config(cfg)), C.byref(info), buf, 512)
+    if st != FM_OK:
+        raise FMError(st, buf.value.decode())
+    return {f: getattr(info, f) for f, _ in fm_plan_info._fields_}
+
+
+def weight_spec(cfg: dict) -> list:
+    c = make_config(cfg)
+    n = query(cfg)["n_weights"]
+    out = []
+    for i in range(n):
+        name, nd, shp = C.c_char_p(), C.c_int32(), (C.c_int64 * 4)()
+        _check(lib().fm_weight_spec(C.byref(c), i, C.byref(name), C.byref(nd), shp))
+        out.append((name.value.decode(), tuple(shp[:nd.value])))
+    return out
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(arr: np.ndarray, dtype: int, device="cuda"):
+    """Host array (float32 values) -> contiguous device tensor of the config dtype."""
+    torch = _torch()
+    t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    if dtype == BF16:
+        t = t.to(torch.bfloat16)
+    return t.to(device).contiguous()
+
+
+class Context:
+    """One fm_ctx on the current torch stream (or `stream`)."""
+
+    def __init__(self, cfg: dict, stream=None):
+        torch = _torch()
+        self.cfg = dict(cfg)
+        self.dtype = cfg["dtype"]
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        self.stream = stream
+        self._c = make_config(cfg)
+        h = C.c_void_p()
+        _check(lib().fm_create(C.byref(self._c), C.c_void_p(stream.cuda_stream), C.byref(h)))
+        self.h = h
+        self._keep = []
+
+    def close(self):
+        if self.h:
+            lib().fm_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    def last_error(self) -> str:
+        return lib().fm_last_error(self.h).decode()
+
+    def load_weights(self, weights: dict):
+        """weights: name -> device tensor (config dtype, contiguous)."""
+        arr = (fm_tensor * len(weights))()
+        names = []
+        for i, (n, t) in enumerate(weights.items()):
+            nb = n.encode()
+            names.append(nb)
+            arr[i].name = nb
+            arr[i].dtype = BF16 if str(t.dtype) == "torch.bfloat16" else F32
+            arr[i].ndim = t.dim()
+            for d in range(t.dim()):
+                arr[i].shape[d] = t.shape[d]
+            arr[i].data = t.data_ptr()
+        _check(lib().fm_load_weights(self.h, arr, len(weights)), self.h)
+
+    def set_schedule(self, steps: int, batch: int, tau=None):
+        tp = None
+        if tau is not None:
+            ta = np.ascontiguousarray(tau, dtype=np.float32)
+            tp = ta.ctypes.data_as(C.POINTER(C.c_float))
+        _check(lib().fm_set_schedule(self.h, steps, batch, tp), self.h)
+
+    def bind_prefix_kv(self, batch: int, prefix_len: int, k=None, v=None, context=None, state=None):
+        kp = vp = None
+        if k is not None:
+            kp = (C.c_void_p * len(k))(*[t.data_ptr() for t in k])
+            vp = (C.c_void_p * len(v))(*[t.data_ptr() for t in v])
+        _check(lib().fm_bind_prefix_kv(self.h, batch, prefix_len, kp, vp, _ptr(context), _ptr(state)), self.h)
+
+    def denoise(self, x0, steps: int, out=None):
+        torch = _torch()
+        if out is None:
+            out = torch.empty_like(x0)
+        _check(lib().fm_denoise(self.h, _ptr(x0), steps, _ptr(out)), self.h)
+        return out
+
+    def step_velocity(self, x, k: int, v=None):
+        torch = _torch()
+        if v is None:
+            v = torch.empty_like(x)
+        _check(lib().fm_step_velocity(self.h, _ptr(x), k, _ptr(v)), self.h)
+        return v
+
+    def step_trace(self, x, k: int):
+        torch = _torch()
+        c = self.cfg
+        rows = x.shape[0] * (c.get("state_tokens", 0) + c["action_horizon"])
+        tr = torch.empty((c["n_layers"] + 1, rows, c["hidden"]), dtype=torch.float32, device=x.device)
+        v = torch.empty_like(x)
+        _check(lib().fm_step_trace(self.h, _ptr(x), k, _ptr(v), _ptr(tr)), self.h)
+        return v, tr
+
+
+def op_linear(A, W, bias=None, act: int = 0, out_f32: bool = False):
+    torch = _torch()
+    dt = BF16 if A.dtype == torch.bfloat16 else F32
+    M, K = A.shape
+    N = W.shape[0]
+    out = torch.empty((M, N), dtype=torch.float32 if out_f32 else A.dtype, device=A.device)
+    s = torch.cuda.current_stream().cuda_stream
+    _check(lib().fm_op_linear(dt, M, N, K, _ptr(A), _ptr(W), _ptr(bias), act, _ptr(out), int(out_f32), C.c_void_p(s)))
+    return out
+
+
+def op_attention(q, k, v):
+    """q [B, Tq, nh, dh]; k, v [B, nkv, nk, dh]."""
+    torch = _torch()
+    dt = BF16 if q.dtype == torch.bfloat16 else F32
+    B, Tq, nh, dh = q.shape
+    nkv, nk = k.shape[1], k.shape[2]
+    o = torch.empty_like(q)
+    s = torch.cuda.current_stream().cuda_stream
+    _check(lib().fm_op_attention(dt, B, Tq, nh, nkv, nk, dh, _ptr(q), _ptr(k), _ptr(v), _ptr(o), C.c_void_p(s)))
+    return o

@@ -80,7 +80,8 @@ def weight_shapes(cfg) -> dict:
             shp[p + "v.w"] = (nkv * dh, D)
             shp[p + "o.w"] = (D, nq * dh)
             shp[p + "gate.w"] = (F, D)
-            shp[p + "up.w"] = (F, D)
+            if cfg["mlp_gated"]:
+                shp[p + "up.w"] = (F, D)
             shp[p + "down.w"] = (D, F)
     else:
         shp["time_bias.w"] = (D, D)
@@ -113,11 +114,17 @@ def bf16_bits(a: np.ndarray) -> np.ndarray:
 
 
 def _draw(seed: int, shape, std: float, bf16: bool) -> np.ndarray:
-    rng = np.random.Generator(np.random.PCG64(seed))
-    a = rng.standard_normal(size=shape, dtype=np.float32)
+    """Standard normal draws of one tensor from torch's CPU generator (Mersenne Twister,
+    seeded per tensor), times std, rounded to bf16 (ties to even) when asked."""
+    import torch
+
+    g = torch.Generator().manual_seed(int(seed))
+    t = torch.randn(tuple(int(d) for d in shape), generator=g, dtype=torch.float32)
     if std != 1.0:
-        a *= np.float32(std)
-    return round_bf16(a) if bf16 else a
+        t.mul_(float(std))
+    if bf16:
+        t = t.to(torch.bfloat16).to(torch.float32)
+    return t.numpy()
 
 
 def input_shapes(cfg) -> dict:

@@ -1,0 +1,188 @@
+/*
+ * fm.h - C ABI of the flow-matching denoise loop of a VLA action head (MI355X / gfx950).
+ *
+ * What it computes. An action chunk X in R^{B x H x d_a} is integrated by explicit Euler
+ * steps X^{k+1} = X^k + (tau_{k+1} - tau_k) v(X^k, tau_k, C) for k = 0..T-1 (vla.cpp: A
+ * Unified Inference Runtime for Vision-Language-Action Models, Sec. III-A, Eq. (1)). The
+ * velocity v is one pass of a modulated action-expert transformer over the chunk tokens,
+ * attending to conditioning C bound once per observation (vla.cpp Sec. III-B, Eq. (2)):
+ *   - FM_ARCH_PREFIX_JOINT: pi0.5-shaped expert (pi0.5 Design page: architecture diagram,
+ *     sequence diagram, "Component contract", "Attention and the K/V pool"). Per layer:
+ *     AdaRMS-modulated norm, Q/K/V with RoPE at positions P + i, attention over the bound
+ *     prefix K/V followed by the chunk's own K/V through ONE shared K/V head, gated
+ *     residual, AdaRMS norm, gated-GELU MLP, gated residual; final AdaRMS norm and the
+ *     velocity projection.
+ *   - FM_ARCH_DIT_CROSS: GR00T-style DiT head (GR00T N1.7 page, section "action" and
+ *     "Build-time constants"): a state token then the action tokens; even blocks
+ *     cross-attend into a context projected to K/V once at bind, odd blocks self-attend;
+ *     AdaLN-modulated LayerNorm with a gated attention residual; plain LayerNorm + GELU
+ *     feed-forward; AdaLN output norm and the velocity projection.
+ * The per-step modulation rows (scale, shift, gate) come from a time embedding passed
+ * through a time MLP and one Dense per norm site; they depend only on the schedule and
+ * are computed by fm_set_schedule, off the step path (pi0.5 Design: the cond component).
+ *
+ * Threading and streams. One context per caller thread; a context is not thread-safe.
+ * Every call enqueues its device work on the stream given to fm_create and returns
+ * without waiting, except where stated. An error returns a status, sets the message read
+ * by fm_last_error and never aborts; after FM_ERR_DEVICE the context is poisoned and every
+ * later call but fm_destroy / fm_last_error returns FM_ERR_DEVICE.
+ *
+ * Memory. Pointers documented "device" are HIP device pointers (e.g. torch tensors'
+ * data_ptr()); "host" pointers are ordinary host memory. Weights, prefix K/V and context
+ * are consumed (copied / projected) into library-owned, address-stable device memory by
+ * work enqueued on the context stream: the caller may free or reuse its buffers once that
+ * stream has passed the call. The library never retains caller pointers across calls.
+ */
+#ifndef FM_H_
+#define FM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fm_ctx fm_ctx;
+
+typedef enum {
+  FM_OK = 0,
+  FM_ERR_INVALID_ARG = 1, /* null pointer, out-of-range count or config field */
+  FM_ERR_SHAPE = 2,       /* tensor name/rank/shape/dtype mismatch at load */
+  FM_ERR_STATE = 3,       /* call order: weights, schedule or binding missing */
+  FM_ERR_SCHEDULE = 4,    /* steps or batch disagree with the schedule / binding */
+  FM_ERR_UNSUPPORTED = 5, /* a configuration this build does not implement */
+  FM_ERR_OOM = 6,         /* device allocation failed */
+  FM_ERR_DEVICE = 7       /* a HIP call failed; the context is poisoned */
+} fm_status;
+
+enum { FM_ARCH_PREFIX_JOINT = 0, FM_ARCH_DIT_CROSS = 1 };
+enum { FM_F32 = 0, FM_BF16 = 1 };
+
+/* Model and capacity description, fixed for the life of a context.
+ *  arch            FM_ARCH_PREFIX_JOINT or FM_ARCH_DIT_CROSS
+ *  dtype           FM_F32 or FM_BF16: weights, K/V and GEMM operands; accumulation, the
+ *                  residual stream, the modulation table, x and v are always fp32
+ *  n_layers        expert layers (DiT: blocks; even 0-based blocks cross-attend)
+ *  hidden          D, a multiple of 64
+ *  n_heads, head_dim, n_kv_heads
+ *                  PREFIX_JOINT requires n_kv_heads == 1 (the pages' pool constraint);
+ *                  DIT_CROSS requires n_kv_heads == n_heads; head_dim in {64, 128, 256}
+ *  mlp_dim         F; mlp_gated = 1: GELU(gate) * up (PREFIX_JOINT), 0: GELU (DiT)
+ *  action_horizon  H tokens per request; action_dim d_a
+ *  state_tokens, state_dim   DiT state token(s) prepended to the action tokens (0 otherwise)
+ *  ctx_len_max, ctx_dim      DiT context capacity and width (0 otherwise)
+ *  max_prefix_len  capacity of the prefix part of the K/V pool (PREFIX_JOINT)
+ *  max_batch, max_steps      capacity of a binding and a schedule
+ *  rope_base       RoPE base (0 = no RoPE); norm_eps    epsilon of every norm */
+typedef struct {
+  int32_t arch, dtype, n_layers, hidden, n_heads, head_dim, n_kv_heads, mlp_dim, mlp_gated,
+      action_horizon, action_dim, state_tokens, state_dim, ctx_len_max, ctx_dim,
+      max_prefix_len, max_batch, max_steps;
+  float rope_base, norm_eps;
+} fm_config;
+
+/* One named weight tensor: dtype must equal the config dtype, shape in nn.Linear
+ * convention [out, in], data a contiguous row-major DEVICE buffer. */
+typedef struct {
+  const char* name;
+  int32_t dtype;
+  int32_t ndim;
+  int64_t shape[4];
+  const void* data;
+} fm_tensor;
+
+/* Sizes derived from a config, computed on the host without touching a device. */
+typedef struct {
+  int32_t n_sites;        /* modulation sites: 2L+1 (PREFIX_JOINT) or L+1 (DIT_CROSS) */
+  int32_t pool_capacity;  /* K/V slots per request: max_prefix_len + H rounded up to 256 */
+  int32_t n_weights;      /* number of weight tensors fm_load_weights expects */
+  int64_t weight_bytes;   /* device bytes of weights after load */
+  int64_t pool_bytes;     /* device bytes of the K/V pool / bound context */
+} fm_plan_info;
+
+/* Validate a config and report derived sizes. Host only; needs no GPU.
+ * Returns FM_ERR_INVALID_ARG / FM_ERR_UNSUPPORTED with a message in msg (may be NULL). */
+fm_status fm_query(const fm_config* cfg, fm_plan_info* info, char* msg, int32_t msg_len);
+
+/* Name of the i-th weight tensor expected by fm_load_weights, in a fixed order, and its
+ * shape. Host only. Returns FM_ERR_INVALID_ARG for i out of range. */
+fm_status fm_weight_spec(const fm_config* cfg, int32_t i, const char** name, int32_t* ndim, int64_t shape[4]);
+
+/* Create a context on the current HIP device. hip_stream: a hipStream_t (NULL = the
+ * default stream) on which all of this context's work runs. Allocates the pool and the
+ * activation buffers for max_batch. */
+fm_status fm_create(const fm_config* cfg, void* hip_stream, fm_ctx** out);
+
+/* Synchronize the context stream and release every device allocation. NULL is a no-op. */
+fm_status fm_destroy(fm_ctx* ctx);
+
+/* Message of the last failed call on ctx (or of the last failed fm_create / fm_query when
+ * ctx is NULL). Valid until the next call on the same context. */
+const char* fm_last_error(const fm_ctx* ctx);
+
+/* Load all weights (fm_weight_spec lists names and shapes). Each tensor is validated
+ * (name, dtype, rank, shape: a mismatch names expected vs got and returns FM_ERR_SHAPE)
+ * and then copied into the library's layout. Biases are converted to fp32. Calling it
+ * again replaces the weights and invalidates schedule and captured graphs. */
+fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* tensors, int32_t n);
+
+/* Build the per-step modulation table for `steps` Euler steps and `batch` requests
+ * (pi0.5 Design: the cond component, evaluated again only when the step count or batch
+ * changes). tau_host: steps + 1 HOST floats tau_0..tau_T, or NULL for tau_k = 1 - k/T
+ * (t from 1 to 0). The table rows are equal across requests and are stored once per step.
+ * 0 <= steps <= max_steps, 1 <= batch <= max_batch, else FM_ERR_INVALID_ARG. Requires
+ * loaded weights (FM_ERR_STATE). Synchronizes the context stream before returning. */
+fm_status fm_set_schedule(fm_ctx* ctx, int32_t steps, int32_t batch, const float* tau_host);
+
+/* Bind the conditioning of one observation batch, kept for the whole loop and never
+ * written by it (vla.cpp Sec. III-B observation reuse).
+ * PREFIX_JOINT: k_dev[l], v_dev[l] for l < n_layers are DEVICE buffers [batch, prefix_len,
+ *   1, head_dim] in the config dtype: the prefix keys (already rotated by the prefix
+ *   tower) and values, copied into pool slots [0, prefix_len) of each request (pi0.5
+ *   Design, "Attention and the K/V pool"); the chunk's own K/V is appended at
+ *   [prefix_len, prefix_len + H) on every step. ctx_dev / state_dev must be NULL.
+ *   0 <= prefix_len <= max_prefix_len.
+ * DIT_CROSS: ctx_dev is a DEVICE buffer [batch, prefix_len, ctx_dim] (config dtype), the
+ *   VL context, projected here to the cross-attention K/V of every even block; state_dev is
+ *   a DEVICE fp32 buffer [batch, state_tokens, state_dim], embedded here to the state
+ *   token(s). k_dev / v_dev must be NULL. 1 <= prefix_len <= ctx_len_max.
+ * 1 <= batch <= max_batch. Requires loaded weights. */
+fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t prefix_len, const void* const* k_dev,
+                            const void* const* v_dev, const void* ctx_dev, const void* state_dev);
+
+/* Run the whole Euler loop: out_dev = X^T for X^0 = x0_dev. Both are DEVICE fp32 buffers
+ * [batch, H, d_a] (the bound batch); out_dev may equal x0_dev. steps must equal the
+ * scheduled step count (FM_ERR_SCHEDULE otherwise), and the scheduled batch must equal the
+ * bound batch; steps == 0 copies x0 to out. The T steps replay as one captured hipGraph,
+ * built on the first call after a schedule, bind or load changed the loop. */
+fm_status fm_denoise(fm_ctx* ctx, const float* x0_dev, int32_t steps, float* out_dev);
+
+/* One step's velocity v(X, tau_k) without the Euler update (pi0.5 Design: the action
+ * component returns the velocity), for teacher-forced checks: x_dev, v_dev DEVICE fp32
+ * [batch, H, d_a]; 0 <= k < scheduled steps. Runs eagerly on the context stream. */
+fm_status fm_step_velocity(fm_ctx* ctx, const float* x_dev, int32_t k, float* v_dev);
+
+/* Like fm_step_velocity, and also copies the fp32 residual stream after the in-projection
+ * and after every layer into h_trace_dev: DEVICE fp32 [n_layers + 1, rows, hidden], rows =
+ * batch * (state_tokens + H). Intermediate tensors localize a discrepancy (vla.cpp
+ * Sec. III-E). */
+fm_status fm_step_trace(fm_ctx* ctx, const float* x_dev, int32_t k, float* v_dev, float* h_trace_dev);
+
+/* Kernel-level entry points on caller buffers, used to check single kernels.
+ * fm_op_linear: out[M, N] = act(A[M, K] W[N, K]^T + bias) with the library GEMM (split-K
+ *   and tile choice as the loop would plan them). A, W DEVICE in `dtype`, row-major; bias
+ *   DEVICE fp32 [N] or NULL; act 0 none, 1 SiLU, 2 GELU (tanh); out DEVICE, fp32 when
+ *   out_f32 else `dtype`. K must be a multiple of 32 (bf16) or 16 (fp32). Allocates and
+ *   frees its scratch; synchronizes `hip_stream`.
+ * fm_op_attention: o = softmax(q k^T / sqrt(dh)) v per head (vla.cpp Eq. (2), no mask).
+ *   q, o DEVICE [B, Tq, n_heads, dh]; k, v DEVICE [B, n_kv, n_keys, dh] with n_kv = 1 or
+ *   n_heads; all in `dtype`. Allocates and frees its scratch; synchronizes `hip_stream`. */
+fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, const void* W,
+                       const float* bias, int32_t act, void* out, int32_t out_f32, void* hip_stream);
+fm_status fm_op_attention(int32_t dtype, int32_t B, int32_t Tq, int32_t n_heads, int32_t n_kv, int32_t n_keys,
+                          int32_t dh, const void* q, const void* k, const void* v, void* o, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FM_H_ */

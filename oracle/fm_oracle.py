@@ -210,7 +210,7 @@ def bind(cfg, w, inputs, dtype=np.float64):
 
 
 # ----------------------------------------------------------------------------- velocity
-def velocity_prefix_joint(cfg, w, bound, x, row):
+def velocity_prefix_joint(cfg, w, bound, x, row, trace=None):
     """One step of the pi0.5-shaped action expert: x [B, H, d_a] -> v [B, H, d_a].
 
     row: this step's modulation row [2L+1, 3D]; site 2l is layer l's input norm, 2l+1 its
@@ -221,6 +221,8 @@ def velocity_prefix_joint(cfg, w, bound, x, row):
     P = bound["prefix_len"]
     pos = P + np.arange(H)  # suffix positions continue after the compact prefix
     h = linear(x, w["action_in.w"], w["action_in.b"])
+    if trace is not None:
+        trace.append(h)
     for l in range(L):
         p = f"layers.{l}."
         scale, shift, gate = split_site(row[2 * l], D)
@@ -242,12 +244,14 @@ def velocity_prefix_joint(cfg, w, bound, x, row):
         else:
             a = gelu_tanh(linear(u, w[p + "gate.w"]))
         h = h + gate * linear(a, w[p + "down.w"])
+        if trace is not None:
+            trace.append(h)
     scale, shift, _ = split_site(row[2 * L], D)
     u = modulate(rms_norm(h, eps), scale, shift)
     return linear(u, w["action_out.w"], w["action_out.b"])
 
 
-def velocity_dit_cross(cfg, w, bound, x, row, time_bias):
+def velocity_dit_cross(cfg, w, bound, x, row, time_bias, trace=None):
     """One step of the DiT action head (GR00T N1.7, section "action"): the state token is
     prepended to the action tokens; 0-based even blocks cross-attend into the bound context
     K/V, odd blocks self-attend over state + action tokens; AdaLN-modulated LayerNorm with a
@@ -259,6 +263,8 @@ def velocity_dit_cross(cfg, w, bound, x, row, time_bias):
     h_a = linear(x, w["action_in.w"], w["action_in.b"]) + time_bias
     h = np.concatenate([bound["state_token"], h_a], axis=1)
     T = h.shape[1]
+    if trace is not None:
+        trace.append(h)
     for i in range(L):
         p = f"blocks.{i}."
         scale, shift, gate = split_site(row[i], D)
@@ -272,16 +278,20 @@ def velocity_dit_cross(cfg, w, bound, x, row, time_bias):
         o = attention(q, K, V).transpose(0, 2, 1, 3).reshape(B, T, D)
         h = h + gate * linear(o, w[p + "o.w"])
         h = h + linear(gelu_tanh(linear(layer_norm(h, eps), w[p + "ff1.w"])), w[p + "ff2.w"])
+        if trace is not None:
+            trace.append(h)
     scale, shift, _ = split_site(row[L], D)
     u = modulate(layer_norm(h[:, cfg["state_tokens"]:], eps), scale, shift)
     return linear(u, w["action_out.w"], w["action_out.b"])
 
 
-def velocity(cfg, w, bound, x, table, time_bias, k):
-    """v_theta(X^k, tau_k, C) of vla.cpp Eq. (1), for step k of the scheduled table."""
+def velocity(cfg, w, bound, x, table, time_bias, k, trace=None):
+    """v_theta(X^k, tau_k, C) of vla.cpp Eq. (1), for step k of the scheduled table.
+    trace: optional list that receives the residual stream after the in-projection and
+    after every layer (vla.cpp Sec. III-E: intermediate tensors localize discrepancies)."""
     if cfg["arch"] == ARCH_PREFIX_JOINT:
-        return velocity_prefix_joint(cfg, w, bound, x, table[k])
-    return velocity_dit_cross(cfg, w, bound, x, table[k], time_bias[k])
+        return velocity_prefix_joint(cfg, w, bound, x, table[k], trace)
+    return velocity_dit_cross(cfg, w, bound, x, table[k], time_bias[k], trace)
 
 
 # ----------------------------------------------------------------------------- the loop

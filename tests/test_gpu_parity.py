@@ -1,0 +1,187 @@
+"""End-to-end parity of the HIP denoise loop against the CPU oracle on the seeded
+workloads, plus the loop's invariants (vla.cpp Eq. (1) and Eq. (5); tolerances: relative
+L2 <= 1e-4 for the fp32 workload; <= 1e-2 per-step velocity, teacher-forced, and <= 2e-2 on
+the final chunk for bf16 workloads)."""
+import numpy as np
+import pytest
+
+import oracle
+from flow_matching_vla_amd import workloads as wl
+from gpu_util import Case, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _teacher_forced(case, tol_v, requests=None, layers_trace=False):
+    """GPU velocity at the GPU's own trajectory x_k vs the oracle velocity at the same x_k."""
+    x = case.I["x0"].astype(np.float32)
+    worst = 0.0
+    for k in range(case.steps):
+        v_gpu = case.gpu_velocity(x, k)
+        v_ref = case.oracle_velocity(x, k, requests=requests)
+        vg = v_gpu if requests is None else v_gpu[requests]
+        e = oracle.e_rel(vg, v_ref)
+        say(f"  step {k}: velocity e_rel {e:.3e} e_inf {oracle.e_inf(vg, v_ref):.3e}")
+        worst = max(worst, e)
+        x = (x + np.float32(case.tau64[k + 1] - case.tau64[k]) * v_gpu).astype(np.float32)
+    assert worst <= tol_v, worst
+    return worst
+
+
+def _chunk(case, tol_x, requests=None):
+    x_gpu = case.gpu_denoise()
+    I = case.I
+    if requests is not None:
+        x_ref = oracle.denoise(dict(case.cfg, batch=len(requests)), case.w64,
+                               {k: ([a[requests] for a in v] if isinstance(v, list) else
+                                    ({i: a[requests] for i, a in v.items()} if isinstance(v, dict) else
+                                     (v[requests] if isinstance(v, np.ndarray) else v)))
+                                for k, v in case.bound.items()},
+                               I["x0"][requests], case.steps, tau=case.tau)
+        x_gpu = x_gpu[requests]
+    else:
+        x_ref = oracle.denoise(case.cfg, case.w64, case.bound, I["x0"], case.steps, tau=case.tau)
+    e = oracle.e_rel(x_gpu, x_ref)
+    say(f"  chunk e_rel {e:.3e} e_inf {oracle.e_inf(x_gpu, x_ref):.3e}")
+    assert e <= tol_x, e
+    return x_gpu
+
+
+# ----------------------------------------------------------------------------- fp32 tiny expert
+@pytest.fixture(scope="module")
+def tiny():
+    c = Case(wl.workload("tiny_fp32"))
+    yield c
+    c.close()
+
+
+def test_tiny_fp32_chunk_and_velocity(tiny):
+    _teacher_forced(tiny, 1e-4)
+    _chunk(tiny, 1e-4)
+
+
+def test_tiny_fp32_layer_trace(tiny):
+    import torch
+    x = tiny.I["x0"].astype(np.float32)
+    v, tr = tiny.ctx.step_trace(torch.from_numpy(x).cuda(), 1)
+    ref = []
+    vr = tiny.oracle_velocity(x, 1, trace=ref)
+    tr = tr.cpu().numpy()
+    assert len(ref) == tr.shape[0]
+    for i, h in enumerate(ref):
+        e = oracle.e_rel(tr[i], h.reshape(tr[i].shape))
+        assert e < 1e-5, (i, e)
+    assert oracle.e_rel(v.cpu().numpy(), vr) < 1e-4
+
+
+def test_replay_is_deterministic_and_prefix_untouched(tiny):
+    a = tiny.gpu_denoise()
+    b = tiny.gpu_denoise()
+    np.testing.assert_array_equal(a, b)
+    # the step velocity after two loops equals the one before (pool prefix unchanged)
+    x = tiny.I["x0"].astype(np.float32)
+    v1 = tiny.gpu_velocity(x, 2)
+    tiny.gpu_denoise()
+    np.testing.assert_array_equal(v1, tiny.gpu_velocity(x, 2))
+
+
+def test_graph_matches_eager_steps(tiny):
+    x = tiny.I["x0"].astype(np.float32)
+    for k in range(tiny.steps):
+        x = (x + np.float32(tiny.tau64[k + 1] - tiny.tau64[k]) * tiny.gpu_velocity(x, k)).astype(np.float32)
+    g = tiny.gpu_denoise()
+    assert np.max(np.abs(g - x)) < 1e-5
+
+
+def test_steps_zero_and_dt_zero():
+    import torch
+    cfg = wl.workload("tiny_fp32")
+    c = Case(cfg, steps=3, tau=[0.5, 0.5, 0.5, 0.5])
+    out = c.gpu_denoise()
+    np.testing.assert_array_equal(out, c.I["x0"])  # dt = 0: x + 0 * v == x bitwise
+    c.ctx.set_schedule(0, 1)
+    o2 = c.ctx.denoise(c.x0, 0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o2.cpu().numpy(), c.I["x0"])
+    c.close()
+
+
+def test_errors_are_reported():
+    import torch
+    from flow_matching_vla_amd import fm
+    c = Case(wl.workload("tiny_fp32"))
+    with pytest.raises(fm.FMError) as e:
+        c.ctx.denoise(c.x0, 3)
+    assert "FM_ERR_SCHEDULE" in str(e.value)
+    with pytest.raises(fm.FMError):
+        c.ctx.set_schedule(99, 1)
+    bad = {n: fm.to_device(a, fm.F32) for n, a in c.W.items()}
+    bad["layers.0.q.w"] = bad["layers.0.q.w"][:, :128].contiguous()
+    with pytest.raises(fm.FMError) as e:
+        c.ctx.load_weights(bad)
+    assert "FM_ERR_SHAPE" in str(e.value) and "layers.0.q.w" in str(e.value)
+    torch.cuda.synchronize()
+    c.close()
+
+
+@pytest.mark.parametrize("P,H", [(0, 16), (1, 5), (63, 1), (200, 33)])
+def test_tiny_ragged_prefix_and_horizon(P, H):
+    cfg = wl.workload("tiny_fp32", prefix_len=P, action_horizon=H, steps=2)
+    c = Case(cfg)
+    _teacher_forced(c, 1e-4)
+    _chunk(c, 1e-4)
+    c.close()
+
+
+def test_tiny_fp32_batch_independence():
+    cfg = wl.workload("tiny_fp32", batch=3)
+    c = Case(cfg)
+    _chunk(c, 1e-4)
+    full = c.gpu_denoise()
+    c.close()
+    for b in (0, 2):
+        Ib = {k: v[b:b + 1] for k, v in c.I.items()}
+        cb = Case(dict(cfg, batch=1), W=c.W, I=Ib)
+        np.testing.assert_allclose(cb.gpu_denoise(), full[b:b + 1], rtol=0, atol=2e-6)
+        cb.close()
+
+
+# ----------------------------------------------------------------------------- bf16 workloads
+def test_pi05_b1():
+    c = Case(wl.workload("pi05_b1"))
+    _teacher_forced(c, 1e-2)
+    _chunk(c, 2e-2)
+    c.close()
+
+
+def test_pi05_sharp_attention_two_layers():
+    # larger query weights make the softmax peaky, so the velocity leans on attention
+    cfg = wl.workload("pi05_b1", n_layers=2, steps=3)
+    W = wl.make_weights(cfg)
+    for l in range(2):
+        W[f"layers.{l}.q.w"] = wl.round_bf16(W[f"layers.{l}.q.w"] * 8)
+        W[f"layers.{l}.o.w"] = wl.round_bf16(W[f"layers.{l}.o.w"] * 8)
+    c = Case(cfg, W=W)
+    _teacher_forced(c, 1e-2)
+    c.close()
+
+
+def test_pi05_b8_sampled_requests():
+    c = Case(wl.workload("pi05_b8"))
+    _teacher_forced(c, 1e-2, requests=[0, 5])
+    _chunk(c, 2e-2, requests=[0, 5])
+    c.close()
+
+
+def test_dit_b1():
+    c = Case(wl.workload("dit_b1"))
+    _teacher_forced(c, 1e-2)
+    _chunk(c, 2e-2)
+    c.close()
+
+
+def test_pi05_b64_sampled_requests():
+    c = Case(wl.workload("pi05_b64"))
+    _teacher_forced(c, 1e-2, requests=[0, 37, 63])
+    _chunk(c, 2e-2, requests=[0, 63])
+    c.close()

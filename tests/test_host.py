@@ -1,0 +1,88 @@
+"""Host-side checks of the C ABI: the library loads, exports every function include/fm.h
+declares, validates configs, derives the pool capacity the pages' rule gives, and lists
+the weight tensors the seeded workloads draw. No compute calls: these run without a GPU."""
+import ctypes as C
+import os
+
+import pytest
+
+from flow_matching_vla_amd import fm, workloads as wl
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fm.LIB_PATH):
+        from flow_matching_vla_amd import build
+        build.build(verbose=False)
+    return fm.lib()
+
+
+def test_exports_every_header_symbol(lib):
+    syms = fm.header_symbols()
+    assert len(syms) >= 11
+    for s in ("fm_load_weights", "fm_bind_prefix_kv", "fm_set_schedule", "fm_denoise"):
+        assert s in syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_weight_spec_matches_workload_shapes(lib, idx):
+    cfg = wl.workload(idx)
+    spec = dict(fm.weight_spec(cfg))
+    assert spec == {k: tuple(v) for k, v in wl.weight_shapes(cfg).items()}
+
+
+def test_pool_capacity_rule(lib):
+    # pi0.5 Design, "Attention and the K/V pool": capacity = max prefix + horizon rounded up
+    # to 256 keys; a 976-token prefix gives 1024 for horizons 10 and 15, 1280 for 50.
+    for H, cap in ((10, 1024), (15, 1024), (50, 1280)):
+        cfg = wl.workload("pi05_b1", prefix_len=976, action_horizon=H)
+        assert fm.query(cfg)["pool_capacity"] == cap
+    assert fm.query(wl.workload("pi05_b1"))["pool_capacity"] == 1024
+
+
+def test_plan_info_sizes(lib):
+    q = fm.query(wl.workload("pi05_b1"))
+    assert q["n_sites"] == 37 and q["n_weights"] == 18 * 7 + 10
+    assert q["weight_bytes"] == 2 * wl.param_count(wl.workload("pi05_b1"))
+    assert fm.query(wl.workload("dit_b1"))["n_sites"] == 33
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_kv_heads", 2, fm.STATUS[5]), ("dtype", 7, fm.STATUS[1]), ("hidden", 100, fm.STATUS[5]),
+    ("head_dim", 96, fm.STATUS[5]), ("max_batch", 0, fm.STATUS[1]), ("arch", 3, fm.STATUS[1]),
+    ("norm_eps", -1.0, fm.STATUS[1]),
+])
+def test_config_validation(lib, field, value, status):
+    cfg = dict(wl.workload("pi05_b1"), **{field: value})
+    with pytest.raises(fm.FMError) as e:
+        fm.query(cfg)
+    assert str(e.value).startswith(status)
+
+
+def test_dit_config_validation(lib):
+    with pytest.raises(fm.FMError):
+        fm.query(dict(wl.workload("dit_b1"), n_kv_heads=1))
+    with pytest.raises(fm.FMError):
+        fm.query(dict(wl.workload("dit_b1"), rope_base=10000.0))
+    fm.query(wl.workload("dit_b1"))
+
+
+def test_null_and_range_arguments_fail_cleanly(lib):
+    assert lib.fm_query(None, None, None, 0) == 1
+    assert lib.fm_destroy(None) == 0
+    assert lib.fm_load_weights(None, None, 0) == 1
+    assert lib.fm_set_schedule(None, 1, 1, None) == 1
+    assert lib.fm_denoise(None, None, 1, None) == 1
+    cfg = fm.make_config(wl.workload("tiny_fp32"))
+    name = C.c_char_p()
+    assert lib.fm_weight_spec(C.byref(cfg), 10_000, C.byref(name), None, None) == 1
+    assert lib.fm_op_linear(0, 4, 4, 7, None, None, None, 0, None, 0, None) == 1
+
+
+def test_binding_refuses_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fm, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fm, "_lib", None)
+    with pytest.raises(RuntimeError):
+        fm.lib()
