@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Throughput of the flow-matching denoise loop on one MI355X.
+
+One bench step is one fm_denoise call: the whole T-step Euler loop of the action expert
+over one batch of seeded synthetic inputs already resident in HBM (weights, bound prefix
+K/V, x0), replayed as one hipGraph. The default workload is the pi0.5-shaped expert at
+batch 1, prefix 816, horizon 50, 10 Euler steps. Prints one JSON line.
+
+Besides chunks/s it reports: a linear fit of latency over the step count T (the model
+latency P + T E of the vla.cpp paper, Sec. III-B Eq. (3)); the whole loop's algorithmic
+HBM rate; a roofline entry for the kernel role that takes the most time, timed with HIP
+events around each of its launches on the context stream; and the CPU oracle timed on the
+host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+METRIC = "action chunks/sec (10-step denoise) + per-step latency; % HBM / MFMA peak"
+
+DESCRIPTIONS = {
+    "tiny_fp32": "tiny fp32 expert: 2 layers, hidden 256, 4x64 q heads, 1 KV head, prefix 64, horizon 16, dim 7, 4 steps",
+    "pi05_b1": "pi0.5-shaped action expert: 18 layers, hidden 1024, 8x256 q heads, 1 KV head, gated-GELU 4096, RoPE, prefix 816, horizon 50, dim 32, batch 1, 10 Euler steps",
+    "pi05_b8": "pi0.5-shaped action expert, batch 8, prefix 816, 10 Euler steps",
+    "dit_b1": "DiT action head: 32 blocks, hidden 1536, 24x64 heads, AdaLN, cross-attention to 600x2048 context, horizon 40 + 1 state token, batch 1, 4 Euler steps",
+    "pi05_b64": "pi0.5-shaped action expert, batch 64, prefix 1024, 10 Euler steps",
+}
+
+
+def role_bytes_flops(cfg, role):
+    """Algorithmic bytes and flops of one launch of a role at one Euler step: weights (and the
+    bound K/V for attention) read once, plus the modulation vectors; activations between
+    kernels are not counted (they can stay on chip)."""
+    e = 2 if cfg["dtype"] == 1 else 4
+    D, F, L = cfg["hidden"], cfg["mlp_dim"], cfg["n_layers"]
+    B, H, da = cfg["batch"], cfg["action_horizon"], cfg["action_dim"]
+    nq, dh = cfg["n_heads"], cfg["head_dim"]
+    st = cfg.get("state_tokens", 0)
+    M = B * (st + H)
+    if cfg["arch"] == 0:
+        qd = nq * dh
+        keys = cfg["prefix_len"] + H
+        shapes = {
+            "qkv": ((qd + 2 * dh) * D, 2 * D), "oproj": (D * qd, D), "mlp_up": (2 * F * D if cfg["mlp_gated"] else F * D, 2 * D),
+            "mlp_down": (D * F, D), "out": (da * D, 2 * D), "inproj": (D * da, 0),
+        }
+        if role == "attn":
+            return B * keys * dh * 2 * e, B * 4 * nq * H * keys * dh
+        w, mod = shapes[role]
+        Mr = B * H
+        return w * e + mod * 4, 2 * w * Mr
+    # DiT: per-role averages over the two block kinds
+    S = cfg["ctx_len"]
+    if role == "qkv":
+        w = (D * D + 3 * D * D) / 2
+        return w * e + 2 * D * 4, 2 * w * M
+    if role == "attn":
+        kv = (B * S * D * 2 * e + 0) / 2
+        fl = (4 * B * (st + H) * S * D + 4 * B * (st + H) ** 2 * D) / 2
+        return kv, fl
+    w = {"oproj": D * D, "mlp_up": F * D, "mlp_down": D * F, "out": da * D, "inproj": D * da}[role]
+    return w * e, 2 * w * M
+
+
+def step_bytes_flops(cfg):
+    """Algorithmic bytes / flops of one Euler step (all layers)."""
+    L = cfg["n_layers"]
+    tb, tf = 0.0, 0.0
+    for r in ("qkv", "attn", "oproj", "mlp_up", "mlp_down"):
+        b, f = role_bytes_flops(cfg, r)
+        tb += L * b
+        tf += L * f
+    for r in ("out", "inproj"):
+        b, f = role_bytes_flops(cfg, r)
+        tb += b
+        tf += f
+    return tb, tf
+
+
+def cpu_baseline(cfg, W, I, budget_s=12.0):
+    """The oracle as it stands, timed on the host: whole chunks (all Euler steps) of the same
+    workload until about budget_s of CPU work has been done (at least one chunk)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info() if p.get("user_api") == "blas"}))
+    except Exception:
+        threads, blas = os.cpu_count(), "unknown"
+    w = oracle.cast_weights(W)
+    bound = oracle.bind(cfg, w, I)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        oracle.denoise(cfg, w, bound, I["x0"], cfg["steps"])
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(cfg["batch"] * n / dt, 4), "unit": "chunks/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{n} chunk(s) of {cfg['name']} ({cfg['steps']} Euler steps, batch {cfg['batch']}), float64 numpy "
+                  f"({blas}, {threads} threads; {os.cpu_count()} CPUs visible), table and bind excluded, {dt:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50, help="timed fm_denoise calls")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="pi05_b1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fit", action="store_true")
+    ap.add_argument("--no-roles", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
+              "the loop shards by request with no exchange, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from flow_matching_vla_amd import fm, workloads as wl
+
+    cfg = wl.workload(args.workload)
+    T, B = cfg["steps"], cfg["batch"]
+    dt = cfg["dtype"]
+    print(f"[bench] {cfg['name']}: generating seeded inputs", file=sys.stderr, flush=True)
+    W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+    torch.cuda.set_device(0)
+    ctx = fm.Context(cfg)
+    wt = {n: fm.to_device(a, dt) for n, a in W.items()}
+    ctx.load_weights(wt)
+    del wt
+    if cfg["arch"] == 0:
+        L = cfg["n_layers"]
+        kk = [fm.to_device(I[f"prefix.k.{l}"], dt) for l in range(L)]
+        vv = [fm.to_device(I[f"prefix.v.{l}"], dt) for l in range(L)]
+        ctx.bind_prefix_kv(B, cfg["prefix_len"], kk, vv)
+        torch.cuda.synchronize()
+        del kk, vv
+    else:
+        ctx.bind_prefix_kv(B, cfg["ctx_len"], context=fm.to_device(I["context"], dt), state=fm.to_device(I["state"], fm.F32))
+    ctx.set_schedule(T, B)
+    x0 = torch.from_numpy(I["x0"]).cuda()
+    out = torch.empty_like(x0)
+    stream = ctx.stream
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        ctx.denoise(x0, T, out)
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        ctx.denoise(x0, T, out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = B * args.steps / wall
+    print(f"[bench] {ms:.3f} ms per chunk call ({value:.1f} chunks/s)", file=sys.stderr, flush=True)
+
+    step_b, step_f = step_bytes_flops(cfg)
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": "chunks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if dt == 1 else "f32", "data": "synthetic (seeded, random-init)",
+        "config": {"workload": f"{cfg['name']}: {DESCRIPTIONS[cfg['name']]}", "batch": B, "euler_steps": T,
+                   "prefix_len": cfg["prefix_len"], "action_horizon": cfg["action_horizon"],
+                   "action_dim": cfg["action_dim"], "parallelism": "none (1 GPU)"},
+        "per_euler_step_us": round(1000 * ms / T, 2),
+        "loop": {"alg_bytes_per_euler_step": int(step_b), "alg_flops_per_euler_step": int(step_f),
+                 "achieved_GBps": round(step_b * T / (ms * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(step_b * T / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "achieved_TFLOPs": round(step_f * T / (ms * 1e-3) / 1e12, 2),
+                 "mfma_frac": round(step_f * T / (ms * 1e-3) / 1e12 / (BF16_PEAK_TFLOPS if dt == 1 else FP32_PEAK_TFLOPS), 4)},
+    }
+    # latency vs step count: L(T) = P + T E
+    if not args.no_fit and T > 1:
+        pts = []
+        for t in sorted({1, 2, max(1, T // 2), T}):
+            ctx.set_schedule(t, B)
+            for _ in range(5):
+                ctx.denoise(x0, t, out)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(20):
+                ctx.denoise(x0, t, out)
+            b.record(stream)
+            torch.cuda.synchronize()
+            pts.append((t, a.elapsed_time(b) / 20))
+        ts = np.array([p[0] for p in pts], float)
+        ls = np.array([p[1] for p in pts], float)
+        E, P0 = np.polyfit(ts, ls, 1)
+        res["latency_fit"] = {"points_ms": [[int(t), round(l, 4)] for t, l in pts], "P_ms": round(float(P0), 4),
+                              "E_us_per_step": round(float(E) * 1000, 2)}
+        ctx.set_schedule(T, B)
+    # per-role kernel time inside the loop (eager launches with events on the context stream)
+    if not args.no_roles:
+        roles = {}
+        for r in ("inproj", "qkv", "attn", "oproj", "mlp_up", "mlp_down", "out"):
+            ctx.denoise(x0, T, out)
+            tot = 0.0
+            nl = 0
+            for _ in range(3):
+                m, n = fm.profile_loop(ctx, x0, T, r, out)
+                tot += m
+                nl += n
+            roles[r] = (tot / nl, nl // 3)
+        res["roles_us_per_launch"] = {r: round(v[0] * 1000, 2) for r, v in roles.items()}
+        dom = max(roles, key=lambda r: roles[r][0] * roles[r][1])
+        nbytes, nflops = role_bytes_flops(cfg, dom)
+        avg_s = roles[dom][0] * 1e-3
+        intensity = nflops / max(nbytes, 1)
+        ridge = (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+        if intensity < ridge:
+            ach = nbytes / avg_s / 1e9
+            res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel_role": dom,
+                               "alg_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2),
+                               "launches_per_chunk": roles[dom][1]}
+        else:
+            peak = BF16_PEAK_TFLOPS if dt == 1 else FP32_PEAK_TFLOPS
+            ach = nflops / avg_s / 1e12
+            res["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                               "frac": round(ach / peak, 4), "traffic": None, "kernel_role": dom,
+                               "alg_flops_per_launch": int(nflops), "avg_launch_us": round(avg_s * 1e6, 2),
+                               "launches_per_chunk": roles[dom][1]}
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg, W, I)
+    ctx.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -120,6 +120,7 @@ int pool_capacity(const fm_config& c) { return (int)round_up((long)c.max_prefix_
 
 struct Op {
   enum Kind { GEMM, ATTN, INPROJ, TRACE } kind;
+  int role;  // FM_OP_* of include/fm.h
   GemmArgs g;
   AttnArgs at;
   InProjArgs ip;
@@ -147,7 +148,12 @@ struct fm_ctx {
   int steps = -1, sched_batch = 0;
   std::vector<float> tau;
   float *table = nullptr, *tbias = nullptr;
-  void *e_buf = nullptr, *c1_buf = nullptr, *c_buf = nullptr;
+  void *e_buf = nullptr, *c1_buf = nullptr, *c_buf = nullptr, *row_buf = nullptr;
+  // per step and norm site: c = shift W^T and (LayerNorm) d = (1 + scale) W^T of the
+  // site's consumer weights, [max_steps][csum]; site s starts at c_off[s]
+  float *cbuf = nullptr, *dbuf = nullptr, *dff = nullptr;
+  std::vector<long> c_off;
+  long csum = 0;
 
   // binding
   int bound_batch = 0, prefix_len = -1;
@@ -160,6 +166,7 @@ struct fm_ctx {
 
   // activations
   float *h = nullptr, *x = nullptr;
+  void* hs = nullptr;         // T copy of h scaled by (1 + scale) of the next norm site
   float2* stats = nullptr;
   void *qbuf = nullptr, *obuf = nullptr, *abuf = nullptr, *kself = nullptr, *vtself = nullptr;
 
@@ -227,11 +234,34 @@ GemmArgs gemm_base(int M, int N, int K, const void* W) {
   return a;
 }
 
-void set_norm(fm_ctx* ctx, GemmArgs& a, int kind, const float* scale, const float* shift, int rows_h) {
+// Consumer of norm site s at step k: A = hs, per-row (mu, rinv) from the statistics,
+// epilogue y = rinv (acc - mu d) + c.
+void set_consumer(fm_ctx* ctx, GemmArgs& a, int kind, int k, int s, const float* dvec_override, int rows_h) {
+  a.A = ctx->hs; a.lda = ctx->c.hidden;
   a.norm = kind;
-  a.H = ctx->h; a.ldh = ctx->c.hidden;
   a.stats = ctx->stats; a.nparts = ctx->c.hidden / kStatCols; a.stats_ld = rows_h;
-  a.mscale = scale; a.mshift = shift; a.eps = ctx->c.norm_eps;
+  a.eps = ctx->c.norm_eps;
+  if (s >= 0) {
+    a.cvec = ctx->cbuf + (size_t)k * ctx->csum + ctx->c_off[s];
+    a.dvec = kind == NORM_LN ? ctx->dbuf + (size_t)k * ctx->csum + ctx->c_off[s] : nullptr;
+  } else {
+    a.cvec = nullptr;
+    a.dvec = dvec_override;
+  }
+}
+
+// Weights consuming norm site s (the output of that norm), and their row count.
+std::pair<const void*, int> site_consumer(fm_ctx* ctx, int s) {
+  const fm_config& c = ctx->c;
+  if (c.arch == FM_ARCH_PREFIX_JOINT) {
+    if (s == 2 * c.n_layers) return {ctx->w_out, c.action_dim};
+    const auto& W = ctx->L[s / 2];
+    if (s % 2 == 0) return {W.qkv, c.n_heads * c.head_dim + 2 * c.head_dim};
+    return {W.gu, c.mlp_gated ? 2 * c.mlp_dim : c.mlp_dim};
+  }
+  if (s == c.n_layers) return {ctx->w_out, c.action_dim};
+  const auto& W = ctx->L[s];
+  return s % 2 == 0 ? std::pair<const void*, int>{W.q, c.hidden} : std::pair<const void*, int>{W.qkv, 3 * c.hidden};
 }
 
 // The launch sequence of Euler step k. vout: velocity output (then x is not updated);
@@ -254,6 +284,8 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
   ip.tb = c.arch == FM_ARCH_DIT_CROSS ? ctx->tbias + (size_t)k * D : nullptr;
   ip.state_tok = ctx->state_tok; ip.B = B; ip.Ha = H; ip.st = st; ip.D = D;
   ip.h = ctx->h; ip.stats = ctx->stats; ip.stats_ld = Mh;
+  ip.hs = ctx->hs; ip.hscale = site(0, 0);
+  op.role = FM_OP_INPROJ;
   ops.push_back(op);
   if (trace) { Op t; memset(&t, 0, sizeof t); t.kind = Op::TRACE; t.trace_layer = 0; ops.push_back(t); }
 
@@ -266,13 +298,13 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       char* vpl = (char*)ctx->pool + (size_t)(2 * l + 1) * plane;
       // QKV + RoPE + append into pool slots [P, P+H)
       GemmArgs g = gemm_base(Ma, qd + 2 * dh, D, W.qkv);
-      set_norm(ctx, g, NORM_RMS, site(2 * l, 0), site(2 * l, 1), Mh);
+      set_consumer(ctx, g, NORM_RMS, k, 2 * l, nullptr, Mh);
       g.epi = EPI_QKV; g.out = ctx->qbuf; g.ldo = qd;
       g.q_cols = qd; g.kv_cols = dh; g.tq = H; g.kv_off = ctx->prefix_len;
       g.rope = c.rope_base > 0.f; g.half_dh = dh / 2; g.rope_cs = ctx->rope_cs;
       g.kdst = kpl; g.k_bs = (long)ctx->cap * dh; g.k_rs = dh;
       g.vdst = vpl; g.v_bs = (long)dh * ctx->cap; g.v_ds = ctx->cap;
-      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_QKV; op.g = g; ops.push_back(op);
       // attention over [prefix ; suffix]
       AttnArgs at;
       memset(&at, 0, sizeof at);
@@ -282,23 +314,25 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       at.o = ctx->obuf; at.o_bs = (long)H * qd; at.o_rs = qd;
       at.B = B; at.Tq = H; at.n_heads = nq; at.heads_per_kv = nq; at.n_keys = ctx->prefix_len + H; at.dh = dh;
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
-      memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.at = at; ops.push_back(op);
+      memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.role = FM_OP_ATTN; op.at = at; ops.push_back(op);
       // O projection + gated residual
       g = gemm_base(Ma, D, qd, W.o);
       g.A = ctx->obuf; g.lda = qd;
       g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
-      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      g.hs = ctx->hs; g.hscale = site(2 * l + 1, 0);
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_OPROJ; op.g = g; ops.push_back(op);
       // gate/up + GELU * up
       g = gemm_base(Ma, c.mlp_gated ? 2 * F : F, D, W.gu);
-      set_norm(ctx, g, NORM_RMS, site(2 * l + 1, 0), site(2 * l + 1, 1), Mh);
+      set_consumer(ctx, g, NORM_RMS, k, 2 * l + 1, nullptr, Mh);
       g.out = ctx->abuf; g.ldo = F;
       if (c.mlp_gated) g.epi = EPI_GELU_MUL; else { g.epi = EPI_STORE; g.act = ACT_GELU; }
-      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_UP; op.g = g; ops.push_back(op);
       // down + gated residual
       g = gemm_base(Ma, D, F, W.down);
       g.A = ctx->abuf; g.lda = F;
       g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l + 1, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
-      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      g.hs = ctx->hs; g.hscale = site(2 * l + 2, 0);
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_DOWN; op.g = g; ops.push_back(op);
     } else {
       const int nh = c.n_heads, dh = c.head_dim, Tq = st + H;
       const bool cross = (l % 2) == 0;
@@ -312,9 +346,9 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       if (cross) {
         const int ci = l / 2;
         g = gemm_base(Mh, D, D, W.q);
-        set_norm(ctx, g, NORM_LN, site(l, 0), site(l, 1), Mh);
+        set_consumer(ctx, g, NORM_LN, k, l, nullptr, Mh);
         g.epi = EPI_STORE; g.out = ctx->qbuf; g.ldo = D;
-        memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+        memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_QKV; op.g = g; ops.push_back(op);
         at.k = (char*)ctx->cross_k + (size_t)ci * c.max_batch * c.ctx_len_max * D * ctx->esz;
         at.k_bs = (long)c.ctx_len_max * D; at.k_rs = D; at.k_hs = dh;
         at.vt = (char*)ctx->cross_vt + (size_t)ci * c.max_batch * D * ctx->spad * ctx->esz;
@@ -322,40 +356,42 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
         at.n_keys = ctx->prefix_len;
       } else {
         g = gemm_base(Mh, 3 * D, D, W.qkv);
-        set_norm(ctx, g, NORM_LN, site(l, 0), site(l, 1), Mh);
+        set_consumer(ctx, g, NORM_LN, k, l, nullptr, Mh);
         g.epi = EPI_QKV; g.out = ctx->qbuf; g.ldo = D;
         g.q_cols = D; g.kv_cols = D; g.tq = Tq; g.kv_off = 0; g.rope = 0;
         g.kdst = ctx->kself; g.k_bs = (long)Tq * D; g.k_rs = D;
         g.vdst = ctx->vtself; g.v_bs = (long)D * ctx->tpad; g.v_ds = ctx->tpad;
-        memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+        memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_QKV; op.g = g; ops.push_back(op);
         at.k = ctx->kself; at.k_bs = (long)Tq * D; at.k_rs = D; at.k_hs = dh;
         at.vt = ctx->vtself; at.v_bs = (long)D * ctx->tpad; at.v_hs = (long)dh * ctx->tpad; at.v_ds = ctx->tpad;
         at.n_keys = Tq;
       }
-      memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.at = at; ops.push_back(op);
+      memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.role = FM_OP_ATTN; op.at = at; ops.push_back(op);
       g = gemm_base(Mh, D, D, W.o);
       g.A = ctx->obuf; g.lda = D;
       g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(l, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
-      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      g.hs = ctx->hs; g.hscale = nullptr;  // the feed-forward LayerNorm carries no modulation
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_OPROJ; op.g = g; ops.push_back(op);
       g = gemm_base(Mh, F, D, W.gu);
-      set_norm(ctx, g, NORM_LN, nullptr, nullptr, Mh);
+      set_consumer(ctx, g, NORM_LN, k, -1, ctx->dff + (size_t)l * F, Mh);
       g.epi = EPI_STORE; g.act = ACT_GELU; g.out = ctx->abuf; g.ldo = F;
-      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_UP; op.g = g; ops.push_back(op);
       g = gemm_base(Mh, D, F, W.down);
       g.A = ctx->abuf; g.lda = F;
       g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = nullptr; g.stats_out = ctx->stats; g.stats_out_ld = Mh;
-      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      g.hs = ctx->hs; g.hscale = site(l + 1, 0);
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_DOWN; op.g = g; ops.push_back(op);
     }
     if (trace) { Op t; memset(&t, 0, sizeof t); t.kind = Op::TRACE; t.trace_layer = l + 1; ops.push_back(t); }
   }
   // final modulated norm + velocity projection + Euler update
   GemmArgs g = gemm_base(Ma, c.action_dim, D, ctx->w_out);
-  set_norm(ctx, g, c.arch == FM_ARCH_PREFIX_JOINT ? NORM_RMS : NORM_LN, site(S - 1, 0), site(S - 1, 1), Mh);
+  set_consumer(ctx, g, c.arch == FM_ARCH_PREFIX_JOINT ? NORM_RMS : NORM_LN, k, S - 1, nullptr, Mh);
   if (st > 0) { g.row_group = H; g.row_gstride = st + H; g.row_off = st; }
   g.epi = EPI_EULER; g.bias = ctx->b_out; g.ldo = c.action_dim;
   if (vout) { g.vout = vout; g.x = nullptr; g.dt = 0.f; }
   else { g.x = ctx->x; g.dt = ctx->tau[k + 1] - ctx->tau[k]; g.vout = nullptr; }
-  memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+  memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_OUT; op.g = g; ops.push_back(op);
   return ops;
 }
 
@@ -500,7 +536,8 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
     ctx->field = (type)p;                                       \
   } while (0)
   ALLOC(h, rows * D * 4, float*);
-  ALLOC(x, B * H * c.action_dim * 4, float*);
+  ALLOC(hs, rows * D * esz, void*);
+  ALLOC(x, B * H * c.action_dim * 4 + 64, float*);  // padded: the Euler epilogue reads 4 floats at a time
   ALLOC(stats, (D / kStatCols) * rows * sizeof(float2), float2*);
   ALLOC(qbuf, rows * std::max(qd, D) * esz, void*);
   ALLOC(obuf, rows * std::max(qd, D) * esz, void*);
@@ -509,6 +546,28 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
   ALLOC(e_buf, (size_t)c.max_steps * D * esz, void*);
   ALLOC(c1_buf, (size_t)c.max_steps * D * esz, void*);
   ALLOC(c_buf, (size_t)c.max_steps * D * esz, void*);
+  ALLOC(row_buf, (size_t)std::max(c.max_steps, 1) * D * esz, void*);
+  {
+    // consumer row counts per norm site, in site order
+    const int S = n_sites(c);
+    ctx->c_off.assign(S, 0);
+    long off = 0;
+    for (int s2 = 0; s2 < S; ++s2) {
+      int n;
+      if (c.arch == FM_ARCH_PREFIX_JOINT)
+        n = s2 == 2 * c.n_layers ? c.action_dim : (s2 % 2 == 0 ? c.n_heads * c.head_dim + 2 * c.head_dim : (c.mlp_gated ? 2 : 1) * c.mlp_dim);
+      else
+        n = s2 == c.n_layers ? c.action_dim : (s2 % 2 == 0 ? c.hidden : 3 * c.hidden);
+      ctx->c_off[s2] = off;
+      off += round_up(n, 4);
+    }
+    ctx->csum = off;
+  }
+  ALLOC(cbuf, (size_t)c.max_steps * ctx->csum * 4, float*);
+  if (c.arch == FM_ARCH_DIT_CROSS) {
+    ALLOC(dbuf, (size_t)c.max_steps * ctx->csum * 4, float*);
+    ALLOC(dff, (size_t)c.n_layers * F * 4, float*);
+  }
   ALLOC(counters, fm_ctx::kCounters * sizeof(unsigned), unsigned*);
   if (c.arch == FM_ARCH_PREFIX_JOINT) {
     ctx->cap = pool_capacity(c);
@@ -603,7 +662,7 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
   };
   auto bias = [&](float** dst, const void* src, long nel) -> fm_status {
     void* p;
-    fm_status st2 = dalloc(ctx, &p, nel * 4);
+    fm_status st2 = dalloc(ctx, &p, round_up(nel, 4) * 4);  // padded: epilogues read 4 floats at a time
     if (st2 != FM_OK) return st2;
     *dst = (float*)p;
     HIPCK(convert_to_f32(*dst, src, nel, elem, ctx->stream));
@@ -695,6 +754,22 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
       if ((s = swz(&W.down, data((p + "ff2.w").c_str()), nullptr, D, F)) != FM_OK) return s;
     }
   }
+  if (c.arch == FM_ARCH_DIT_CROSS) {
+    // d of the feed-forward LayerNorm (no modulation): row sums of the FF1 weights
+    HIPCK(fill_f32((float*)stage, 1.f, D, ctx->stream));
+    HIPCK(rows_from_f32(ctx->row_buf, D, (const float*)stage, D, 1, D, 0.f, elem, ctx->stream));
+    for (int i = 0; i < c.n_layers; ++i) {
+      std::vector<Op> one(1);
+      memset(&one[0], 0, sizeof(Op));
+      one[0].kind = Op::GEMM;
+      GemmArgs& gg = one[0].g;
+      gg = gemm_base(1, F, D, ctx->L[i].gu);
+      gg.A = ctx->row_buf; gg.lda = D; gg.epi = EPI_STORE; gg.out_f32 = 1; gg.ldo = F;
+      gg.out = ctx->dff + (size_t)i * F;
+      if ((s = plan_ops(ctx, one)) != FM_OK) return s;
+      if ((s = enqueue_ops(ctx, one, ctx->stream, nullptr)) != FM_OK) return s;
+    }
+  }
   HIPCK(hipStreamSynchronize(ctx->stream));
   dfree(ctx, stage);
   dfree(ctx, rowidx);
@@ -763,6 +838,23 @@ fm_status fm_set_schedule(fm_ctx* ctx, int32_t steps, int32_t batch, const float
   fm_status s = plan_ops(ctx, ops);
   if (s != FM_OK) return s;
   if ((s = enqueue_ops(ctx, ops, ctx->stream, nullptr)) != FM_OK) return s;
+  // per site: c = shift W^T and, for LayerNorm, d = (1 + scale) W^T of the consumer weights
+  for (int site = 0; site < S; ++site) {
+    auto cw = site_consumer(ctx, site);
+    for (int which = 0; which < (c.arch == FM_ARCH_DIT_CROSS ? 2 : 1); ++which) {
+      const float* src = ctx->table + (size_t)site * 3 * D + (which == 0 ? D : 0);
+      HIPCK(rows_from_f32(ctx->row_buf, D, src, (long)S * 3 * D, T, D, which == 0 ? 0.f : 1.f, ctx->elem, ctx->stream));
+      std::vector<Op> one(1);
+      memset(&one[0], 0, sizeof(Op));
+      one[0].kind = Op::GEMM;
+      GemmArgs& gg = one[0].g;
+      gg = gemm_base(T, cw.second, D, cw.first);
+      gg.A = ctx->row_buf; gg.lda = D; gg.epi = EPI_STORE; gg.out_f32 = 1; gg.ldo = ctx->csum;
+      gg.out = (which == 0 ? ctx->cbuf : ctx->dbuf) + ctx->c_off[site];
+      if ((s = plan_ops(ctx, one)) != FM_OK) return s;
+      if ((s = enqueue_ops(ctx, one, ctx->stream, nullptr)) != FM_OK) return s;
+    }
+  }
   HIPCK(hipStreamSynchronize(ctx->stream));
   dfree(ctx, e32);
   return FM_OK;
@@ -918,6 +1010,49 @@ fm_status fm_step_trace(fm_ctx* ctx, const float* x, int32_t k, float* v, float*
   return step_eager(ctx, x, k, v, trace);
 }
 
+fm_status fm_profile_loop(fm_ctx* ctx, const float* x0, int32_t steps, float* out, int32_t role, float* ms,
+                          int32_t* launches) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  fm_status s = check_ready(ctx);
+  if (s != FM_OK) return s;
+  if (!x0 || !out || !ms || !launches || role < FM_OP_INPROJ || role > FM_OP_OUT)
+    return fail(ctx, FM_ERR_INVALID_ARG, "fm_profile_loop: bad arguments");
+  if (steps != ctx->steps || steps < 1)
+    return fail(ctx, FM_ERR_SCHEDULE, fmt("steps %d differs from the scheduled %d", steps, ctx->steps));
+  const size_t xbytes = (size_t)ctx->bound_batch * ctx->c.action_horizon * ctx->c.action_dim * sizeof(float);
+  std::vector<std::vector<Op>> all;
+  size_t count = 0;
+  for (int k = 0; k < steps; ++k) {
+    all.push_back(build_step(ctx, k, nullptr, nullptr));
+    if ((s = plan_ops(ctx, all.back())) != FM_OK) return s;
+    for (auto& op : all.back()) count += op.role == role;
+  }
+  std::vector<hipEvent_t> ev(2 * count);
+  for (auto& e : ev) HIPCK(hipEventCreate(&e));
+  HIPCK(hipMemcpyAsync(ctx->x, x0, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+  size_t i = 0;
+  for (auto& ops : all)
+    for (auto& op : ops) {
+      const bool hit = op.role == role;
+      if (hit) HIPCK(hipEventRecord(ev[2 * i], ctx->stream));
+      std::vector<Op> one(1, op);
+      if ((s = enqueue_ops(ctx, one, ctx->stream, nullptr)) != FM_OK) return s;
+      if (hit) { HIPCK(hipEventRecord(ev[2 * i + 1], ctx->stream)); ++i; }
+    }
+  HIPCK(hipMemcpyAsync(out, ctx->x, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  double tot = 0;
+  for (size_t j = 0; j < count; ++j) {
+    float e = 0;
+    HIPCK(hipEventElapsedTime(&e, ev[2 * j], ev[2 * j + 1]));
+    tot += e;
+  }
+  for (auto& e : ev) (void)hipEventDestroy(e);
+  *ms = (float)tot;
+  *launches = (int32_t)count;
+  return FM_OK;
+}
+
 // ---------------------------------------------------------------------------------------
 // Kernel-level entry points (own scratch, synchronous).
 // ---------------------------------------------------------------------------------------
@@ -938,9 +1073,15 @@ fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const voi
   GemmArgs g = gemm_base(M, N, K, nullptr);
   g.A = A; g.lda = K; g.epi = EPI_STORE; g.bias = bias; g.act = act; g.out = out; g.ldo = N; g.out_f32 = out_f32;
   gemm_plan(g, elem, prop.multiProcessorCount);
-  void *wsw = nullptr, *ws = nullptr, *cnt = nullptr;
+  void *wsw = nullptr, *ws = nullptr, *cnt = nullptr, *bpad = nullptr;
   hipError_t e = hipMalloc(&wsw, swizzled_bytes(N, K, elem));
   const size_t wsb = gemm_ws_bytes(g);
+  if (e == hipSuccess && bias) {
+    e = hipMalloc(&bpad, (size_t)round_up(N, 4) * 4);
+    if (e == hipSuccess) e = hipMemsetAsync(bpad, 0, (size_t)round_up(N, 4) * 4, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(bpad, bias, (size_t)N * 4, hipMemcpyDeviceToDevice, s);
+    g.bias = (const float*)bpad;
+  }
   if (e == hipSuccess && wsb) e = hipMalloc(&ws, wsb);
   if (e == hipSuccess) e = hipMalloc(&cnt, fm_ctx::kCounters * sizeof(unsigned));
   if (e == hipSuccess) e = hipMemsetAsync(cnt, 0, fm_ctx::kCounters * sizeof(unsigned), s);
@@ -951,6 +1092,7 @@ fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const voi
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   hipError_t e2 = hipSuccess;
   if (wsw) e2 = hipFree(wsw);
+  if (bpad) (void)hipFree(bpad);
   if (ws) (void)hipFree(ws);
   if (cnt) (void)hipFree(cnt);
   if (e == hipSuccess) e = e2;

@@ -48,18 +48,15 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   const T* vbase = (const T*)a.vt + (long)b * a.v_bs + (long)g * a.v_hs;
 
   // this lane's query row for the Q fragments
+  // (loads are unconditional from clamped addresses: rows past R produce outputs that are
+  // never stored, keys past the range are masked in the softmax and zeroed in V)
   frag qf[DCH];
   {
-    const int r = rt * ROWS + wave * 16 + (lane % 16);
-    if (r < R) {
-      const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
-      const T* qp = (const T*)a.q + (long)b * a.q_bs + (long)t * a.q_rs + (long)n * a.dh + (lane / 16) * VEC;
+    const int r = min(rt * ROWS + wave * 16 + (lane % 16), R - 1);
+    const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
+    const T* qp = (const T*)a.q + (long)b * a.q_bs + (long)t * a.q_rs + (long)n * a.dh + (lane / 16) * VEC;
 #pragma unroll
-      for (int c = 0; c < DCH; ++c) qf[c] = __builtin_bit_cast(frag, *(const V16*)(qp + c * KC));
-    } else {
-#pragma unroll
-      for (int c = 0; c < DCH; ++c) qf[c] = __builtin_bit_cast(frag, V16{{0, 0, 0, 0}});
-    }
+    for (int c = 0; c < DCH; ++c) qf[c] = __builtin_bit_cast(frag, *(const V16*)(qp + c * KC));
   }
 
   f32x4 o[DB];
@@ -71,28 +68,49 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
 
   T* pw = (T*)(sP + wave * P_V16);
 
-  for (int kt = key_beg; kt < key_end; kt += BK) {
-    // stage K tile (fragment-major for the B operand of Q K^T) and V^T tile
-    for (int c = tid; c < K_V16; c += NT) {
+  // K / V^T tiles: the next tile's global loads are issued before the current tile's MFMA
+  // work, so one memory round trip per tile is hidden behind compute.
+  constexpr int KPT = (K_V16 + NT - 1) / NT;
+  V16 rk[KPT], rv[KPT];
+  auto load_kv = [&](int kt) {
+    const int jlast = ((key_end - 1) / VEC) * VEC;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int c = min(tid + q * NT, K_V16 - 1);
       const int j = c / (DH / VEC), ds = c % (DH / VEC);
-      V16 v = {{0, 0, 0, 0}};
-      if (kt + j < key_end) v = *(const V16*)(kbase + (long)(kt + j) * a.k_rs + ds * VEC);
-      sK[((j / 16) * DCH + ds / SEG) * 64 + (j % 16) + 16 * (ds % SEG)] = v;
-    }
-    for (int c = tid; c < K_V16; c += NT) {
+      rk[q] = *(const V16*)(kbase + (long)min(kt + j, key_end - 1) * a.k_rs + ds * VEC);
       const int d = c / (BK / VEC), ks = c % (BK / VEC);
       const int j0 = kt + ks * VEC;
-      V16 v = {{0, 0, 0, 0}};
-      if (j0 < key_end) {
-        v = *(const V16*)(vbase + (long)d * a.v_ds + j0);
-        if (j0 + VEC > key_end) {  // zero the keys past the end inside this chunk
-          T* e = (T*)&v;
-          for (int q = key_end - j0; q < VEC; ++q) e[q] = from_f32<T>(0.f);
-        }
+      V16 v = *(const V16*)(vbase + (long)d * a.v_ds + min(j0, jlast));
+      const int nv = key_end - j0;  // keys of this chunk inside the range (may be <= 0)
+      constexpr int EPW = VEC / 4;  // elements per 32-bit word
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int e0 = w * EPW;
+        const uint32_t keep = (e0 + EPW <= nv) ? 0xffffffffu : (e0 < nv ? 0x0000ffffu : 0u);
+        v[w] &= keep;
       }
-      sV[((d / 16) * KCH + ks / SEG) * 64 + (d % 16) + 16 * (ks % SEG)] = v;
+      rv[q] = v;
     }
+  };
+  auto store_kv = [&]() {
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int c = tid + q * NT;
+      if (c < K_V16) {
+        const int j = c / (DH / VEC), ds = c % (DH / VEC);
+        sK[((j / 16) * DCH + ds / SEG) * 64 + (j % 16) + 16 * (ds % SEG)] = rk[q];
+        const int d = c / (BK / VEC), ks = c % (BK / VEC);
+        sV[((d / 16) * KCH + ks / SEG) * 64 + (d % 16) + 16 * (ks % SEG)] = rv[q];
+      }
+    }
+  };
+
+  if (key_beg < key_end) load_kv(key_beg);
+  for (int kt = key_beg; kt < key_end; kt += BK) {
+    store_kv();
     __syncthreads();
+    if (kt + BK < key_end) load_kv(kt + BK);
 
     // S = Q K^T for 16 rows x BK keys
     f32x4 s[KB];
@@ -181,7 +199,8 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
     return;
   }
 
-  // split keys: partial (O, m, l) to the workspace, last arriver merges in split order
+  // split keys: partial (O, m, l) to the workspace with device-scope stores (coherent
+  // across XCDs without an L2 write-back); the last arriver merges them in split order
   const long per = (long)ROWS * DH + 2L * ROWS;
   float* wt = a.ws + (long)tile_id * a.splits * per;
   {
@@ -190,35 +209,57 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int rl = wave * 16 + 4 * (lane / 16) + e;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) wo[(long)rl * DH + db * 16 + (lane % 16)] = o[db][e];
+      for (int db = 0; db < DB; ++db) st_dev1(wo + (long)rl * DH + db * 16 + (lane % 16), o[db][e]);
       if ((lane % 16) == 0) {
-        wo[(long)ROWS * DH + rl] = mrow[e];
-        wo[(long)ROWS * DH + ROWS + rl] = lrow[e];
+        st_dev1(wo + (long)ROWS * DH + rl, mrow[e]);
+        st_dev1(wo + (long)ROWS * DH + ROWS + rl, lrow[e]);
       }
     }
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(a.counters + tile_id, 1u) == (unsigned)a.splits - 1u);
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(a.counters + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.splits - 1u;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int rl = wave * 16 + 4 * (lane / 16) + e;
     const int r = rt * ROWS + rl;
     float mx = -INFINITY;
-    for (int q = 0; q < a.splits; ++q) mx = fmaxf(mx, wt[(long)q * per + (long)ROWS * DH + rl]);
+    for (int q0 = 0; q0 < a.splits; q0 += 8) {
+      float mv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float m_u = ld_dev1(wt + (long)min(q0 + u, a.splits - 1) * per + (long)ROWS * DH + rl);
+        mv[u] = q0 + u < a.splits ? m_u : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mx = fmaxf(mx, mv[u]);
+    }
     float den = 0.f;
     float acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = 0.f;
-    for (int q = 0; q < a.splits; ++q) {
-      const float* wq = wt + (long)q * per;
-      const float w = exp2f(wq[(long)ROWS * DH + rl] - mx);
-      den += w * wq[(long)ROWS * DH + ROWS + rl];
+    for (int q0 = 0; q0 < a.splits; q0 += 2) {
+      float w[2], lv[2], ov[2][DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] += w * wq[(long)rl * DH + db * 16 + (lane % 16)];
+      for (int u = 0; u < 2; ++u) {
+        const bool ok = q0 + u < a.splits;
+        const float* wq = wt + (long)(ok ? q0 + u : 0) * per;
+        const float m_u = ld_dev1(wq + (long)ROWS * DH + rl);
+        w[u] = ok ? m_u : -INFINITY;
+        lv[u] = ld_dev1(wq + (long)ROWS * DH + ROWS + rl);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) ov[u][db] = ld_dev1(wq + (long)rl * DH + db * 16 + (lane % 16));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float wt_u = exp2f(w[u] - mx);
+        den += wt_u * lv[u];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] += wt_u * ov[u][db];
+      }
     }
     if (r < R) {
       const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
@@ -228,7 +269,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
       for (int db = 0; db < DB; ++db) op[db * 16 + (lane % 16)] = from_f32<T>(acc[db] * inv);
     }
   }
-  if (tid == 0) a.counters[tile_id] = 0u;
+  if (tid == 0) __hip_atomic_store(a.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 static int attn_rows(int elem, int dh) { (void)elem; (void)dh; return 64; }

@@ -51,39 +51,55 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
 
-// 16-byte vector of T as raw storage
-struct alignas(16) V16 { uint32_t w[4]; };
+// 16 bytes of T as a native vector (kept in registers; no struct-with-array)
+typedef uint32_t V16 __attribute__((ext_vector_type(4)));
 
 template <typename T> __device__ __forceinline__ void unpack(const V16& v, float* out);
 template <> __device__ __forceinline__ void unpack<float>(const V16& v, float* out) {
-  for (int j = 0; j < 4; ++j) out[j] = __uint_as_float(v.w[j]);
+  out[0] = __uint_as_float(v[0]); out[1] = __uint_as_float(v[1]);
+  out[2] = __uint_as_float(v[2]); out[3] = __uint_as_float(v[3]);
 }
 template <> __device__ __forceinline__ void unpack<bf16>(const V16& v, float* out) {
+#pragma unroll
   for (int j = 0; j < 4; ++j) {
-    out[2 * j] = __uint_as_float(v.w[j] << 16);
-    out[2 * j + 1] = __uint_as_float(v.w[j] & 0xffff0000u);
+    out[2 * j] = __uint_as_float(v[j] << 16);
+    out[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
   }
 }
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) { return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x); }
 template <typename T> __device__ __forceinline__ V16 pack(const float* in);
 template <> __device__ __forceinline__ V16 pack<float>(const float* in) {
   V16 v;
-  for (int j = 0; j < 4; ++j) v.w[j] = __float_as_uint(in[j]);
+  v[0] = __float_as_uint(in[0]); v[1] = __float_as_uint(in[1]);
+  v[2] = __float_as_uint(in[2]); v[3] = __float_as_uint(in[3]);
   return v;
 }
 template <> __device__ __forceinline__ V16 pack<bf16>(const float* in) {
   V16 v;
-  for (int j = 0; j < 4; ++j) {
-    bf16 lo = (bf16)in[2 * j], hi = (bf16)in[2 * j + 1];
-    v.w[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = bf16_bits_rne(in[2 * j]) | (bf16_bits_rne(in[2 * j + 1]) << 16);
   return v;
 }
+__device__ __forceinline__ V16 vzero() { return V16{0u, 0u, 0u, 0u}; }
 
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float c = 0.7978845608028654f;  // sqrt(2 / pi)
   return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
 }
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Sixteen zero bytes to read in place of an absent optional operand: kernels load from
+// (p ? p + i : g_zeros) unconditionally, because a load under a branch, even a uniform
+// one, is waited on before the branch rejoins and so costs a memory round trip of its own.
+static __device__ __attribute__((aligned(16))) float g_zeros[4] = {0.f, 0.f, 0.f, 0.f};
+
+// Device-scope (sc1) scalar accesses for data exchanged between workgroups of one kernel.
+__device__ __forceinline__ void st_dev1(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev1(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Map a linear workgroup id so that consecutive logical ids land on the same XCD:
 // the hardware deals workgroups round-robin over the 8 XCDs.

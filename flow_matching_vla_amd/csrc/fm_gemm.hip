@@ -7,6 +7,13 @@
 #include "fm_common.h"
 #include "fm_kernels.h"
 
+#ifdef FM_PHASE_TIMING
+extern __device__ unsigned long long* g_phase;
+#define FM_PHASE(i) do { if (threadIdx.x == 0 && g_phase) g_phase[blockIdx.x * 8 + (i)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define FM_PHASE(i) do { } while (0)
+#endif
+
 namespace fm {
 
 // ---------------------------------------------------------------------------------------
@@ -26,7 +33,7 @@ __global__ void k_swizzle(T* __restrict__ dst, const T* __restrict__ src, const 
     const int nb = (int)(f / KB), kc = (int)(f % KB);
     const int n = nb * 16 + (l % 16);
     const int k = kc * KC + (l / 16) * VEC;
-    V16 v = {{0, 0, 0, 0}};
+    V16 v = vzero();
     if (n < N) {
       const int sr = rows ? rows[n] : n;
       if (sr >= 0) v = *(const V16*)(src + (long)sr * ld + k);
@@ -51,123 +58,240 @@ hipError_t swizzle_weight(void* dst, const void* src, const int* rows, int N, in
 }
 
 // ---------------------------------------------------------------------------------------
-// Row statistics: (mean, M2) over a run of columns, merged pairwise (Chan et al.).
+// Row statistics: (mean, M2) over runs of columns, merged pairwise (Chan et al.); empty
+// sides are skipped so the merge is exact for any split of the columns.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void stat_merge(float& mean, float& m2, float n, float mean_b, float m2_b, float n_b) {
+__device__ __forceinline__ void stat_merge(float& mean, float& m2, float& n, float mean_b, float m2_b, float n_b) {
+  // branch-free: an empty side (count 0, M2 0) leaves the other unchanged
   const float tot = n + n_b;
+  const float f = n_b / fmaxf(tot, 1e-30f);
   const float d = mean_b - mean;
-  mean += d * (n_b / tot);
-  m2 += m2_b + d * d * (n * n_b / tot);
+  mean += d * f;
+  m2 += m2_b + d * d * (n * f);
+  n = tot;
+}
+
+__device__ __forceinline__ int a_row(const GemmArgs& a, int m) {
+  return (m / a.row_group) * a.row_gstride + a.row_off + m % a.row_group;
+}
+
+// Per-row (mu, rinv) of the BM rows starting at m0, from the producer's per-slot partial
+// statistics. NT / BM threads share a row; each merges a strided subset of the slots, and
+// the subsets are merged across adjacent lanes. Split in two so that the slot loads can be
+// issued ahead of the operand loads and merged after them: every load is unconditional
+// (clamped index), PPT per thread, covering up to kMaxParts slots.
+constexpr int kMaxParts = 128;   // hidden <= 2048
+template <int BM, int NT>
+struct RowStats {
+  static constexpr int TPR = NT / BM;
+  static constexpr int PPT = kMaxParts / TPR;
+  static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0 && TPR <= 64, "threads per row");
+  float2 v[PPT];
+  __device__ __forceinline__ void load(const GemmArgs& a, int m0) {
+    const int tid = threadIdx.x;
+    const int r = tid / TPR, q = tid % TPR;
+    const long hr = a_row(a, min(m0 + r, a.M - 1));
+    const int np = max(a.nparts, 1);
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const float2* p = a.stats ? a.stats + (long)min(q + u * TPR, np - 1) * a.stats_ld + hr : (const float2*)g_zeros;
+      v[u] = *p;
+    }
+  }
+  __device__ __forceinline__ void merge(const GemmArgs& a, int m0, float* s_mean, float* s_rinv) {
+    // every slot covers kStatCols columns: mean = average of slot means, and
+    // M2 = sum of slot M2 + kStatCols * sum (slot mean - mean)^2 (no divisions, short chains)
+    const int tid = threadIdx.x;
+    const int r = tid / TPR, q = tid % TPR;
+    float sm = 0.f;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) sm += (q + u * TPR < a.nparts) ? v[u].x : 0.f;
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) sm += __shfl_xor(sm, off, 64);
+    const float np = (float)max(a.nparts, 1);
+    const float mu = sm / np;
+    float m2 = 0.f;
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      const float d = v[u].x - mu;
+      m2 += (q + u * TPR < a.nparts) ? v[u].y + (float)kStatCols * d * d : 0.f;
+    }
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) m2 += __shfl_xor(m2, off, 64);
+    if (q == 0 && r < BM) {
+      const float cnt = np * (float)kStatCols;
+      const bool ok = m0 + r < a.M;
+      float mean = 0.f, rinv;
+      if (a.norm == NORM_RMS) {
+        rinv = rsqrtf((m2 + cnt * mu * mu) / cnt + a.eps);
+      } else {
+        rinv = rsqrtf(m2 / cnt + a.eps);
+        mean = mu;
+      }
+      s_mean[r] = ok ? mean : 0.f;
+      s_rinv[r] = ok ? rinv : 0.f;
+    }
+  }
+};
+
+// device-scope (sc1) accesses for data exchanged between workgroups inside one kernel:
+// coherent across XCDs without write-back or invalidation of the whole L2.
+__device__ __forceinline__ void st_dev(float* p, f32x4 v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) __hip_atomic_store(p + j, v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 ld_dev(const float* p) {
+  f32x4 v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
 }
 
 // ---------------------------------------------------------------------------------------
-// Epilogue over a BM x BN fp32 tile held in LDS (row stride LDC). Items are 4-column
-// runs; the 16 consecutive lanes that share a row cover 64 columns = one statistic slot.
+// Epilogue over a BM x BN fp32 tile held in LDS (row stride ldc). Items are 4-column runs;
+// four consecutive lanes of a row cover one 16-column statistic slot. Every global input
+// (bias, modulation vectors, residual, x, RoPE table) is loaded for all of the thread's
+// items before any is used.
 // ---------------------------------------------------------------------------------------
 template <typename T, int BM, int BN, int NT, int EPI>
-__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C, int ldc, int m0, int n0) {
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C, int ldc, int m0, int n0,
+                                              const float* s_mean, const float* s_rinv) {
   constexpr int C4 = BN / 4;
+  constexpr int TOT = BM * C4;
+  constexpr int ITEMS = (TOT + NT - 1) / NT;
+  static_assert(TOT % 64 == 0 && C4 % 4 == 0, "epilogue items");
   const int tid = threadIdx.x;
-  for (int it = tid; it < BM * C4; it += NT) {
+  const bool consumer = a.norm != NORM_NONE;
+  f32x4 pc[ITEMS], pd[ITEMS], p0[ITEMS], p1[ITEMS], p2[ITEMS];
+  // Loads use clamped indices and are unconditional (a divergent conditional load costs a
+  // full memory round trip of its own); values outside the tile are never used. Per-column
+  // vectors (bias, c, d) are padded to a multiple of four floats by their owners.
+  auto vec4 = [&](const float* p, long i) -> f32x4 { return *(const f32x4*)(p ? p + i : g_zeros); };
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    const int it = min(tid + q * NT, TOT - 1);
     const int r = it / C4, c4 = it % C4;
-    const int m = m0 + r;
-    const int n = n0 + c4 * 4;
+    const int mc = min(m0 + r, a.M - 1), n = min(n0 + c4 * 4, ((a.N - 1) / 4) * 4);
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+    pc[q] = z; pd[q] = z; p0[q] = z; p1[q] = z; p2[q] = z;
+    pc[q] = vec4(a.cvec, n);
+    pd[q] = vec4(a.dvec, n);
+    if constexpr (EPI == EPI_STORE || EPI == EPI_EULER) {
+      p0[q] = vec4(a.bias, n);
+      if constexpr (EPI == EPI_EULER) p1[q] = vec4(a.x, (long)mc * a.ldo + n);
+    } else if constexpr (EPI == EPI_RESID) {
+      p0[q] = vec4(a.h, (long)mc * a.ldh_out + n);
+      const f32x4 gv = vec4(a.gate, n);
+      p1[q] = a.gate ? gv : f32x4{1.f, 1.f, 1.f, 1.f};
+      p2[q] = vec4(a.hscale, n);
+    } else if constexpr (EPI == EPI_QKV) {
+      const int nr = max(min(n, a.q_cols + a.kv_cols - 4), 0);
+      const int c = nr < a.q_cols ? nr : nr - a.q_cols;
+      const int jj = (c % max(2 * a.half_dh, 1)) / 2;   // even: pairs jj, jj + 1 are adjacent
+      p0[q] = vec4((const float*)a.rope_cs, 2L * ((long)(mc % a.tq) * a.half_dh + jj));
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < ITEMS; ++q) {
+    const int it = tid + q * NT;
+    if (it >= TOT) continue;   // uniform per wave (TOT is a multiple of 64)
+    const int r = it / C4, c4 = it % C4;
+    const int m = m0 + r, n = n0 + c4 * 4;
     const bool mok = m < a.M;
-    float v[4];
-    {
-      const f32x4 cv = *(const f32x4*)(C + r * ldc + c4 * 4);
-      v[0] = cv[0]; v[1] = cv[1]; v[2] = cv[2]; v[3] = cv[3];
+    f32x4 v = *(const f32x4*)(C + r * ldc + c4 * 4);
+    if (consumer) {
+      const float mu = s_mean[r], ri = s_rinv[r];
+      v = ri * (v - mu * pd[q]) + pc[q];   // absent c / d read as zeros
     }
     if constexpr (EPI == EPI_STORE) {
       if (mok) {
+        float y[4];
+#pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (n + j >= a.N) break;
-          float y = v[j] + (a.bias ? a.bias[n + j] : 0.f);
-          if (a.act == ACT_SILU) y = silu(y);
-          else if (a.act == ACT_GELU) y = gelu_tanh(y);
-          if (a.out_f32) ((float*)a.out)[(long)m * a.ldo + n + j] = y;
-          else ((T*)a.out)[(long)m * a.ldo + n + j] = from_f32<T>(y);
+          y[j] = v[j] + p0[q][j];
+          if (a.act == ACT_SILU) y[j] = silu(y[j]);
+          else if (a.act == ACT_GELU) y[j] = gelu_tanh(y[j]);
+        }
+        const long base = (long)m * a.ldo + n;
+        if (a.out_f32) {
+          float* o = (float*)a.out + base;
+          if (n + 3 < a.N && (base & 3) == 0) *(f32x4*)o = f32x4{y[0], y[1], y[2], y[3]};
+          else for (int j = 0; j < 4; ++j) if (n + j < a.N) o[j] = y[j];
+        } else {
+          T* o = (T*)a.out + base;
+          for (int j = 0; j < 4; ++j) if (n + j < a.N) o[j] = from_f32<T>(y[j]);
         }
       }
     } else if constexpr (EPI == EPI_GELU_MUL) {
-      // columns interleave (gate_f, up_f) pairs: output f = n / 2
-      if (mok) {
-        for (int j = 0; j < 4; j += 2) {
-          if (n + j + 1 >= a.N + 1) break;
-          const float y = gelu_tanh(v[j]) * v[j + 1];
-          ((T*)a.out)[(long)m * a.ldo + (n + j) / 2] = from_f32<T>(y);
-        }
+      // columns interleave (gate_f, up_f): outputs f = n / 2 and n / 2 + 1
+      if (mok && n < a.N) {
+        T* o = (T*)a.out + (long)m * a.ldo + n / 2;
+        o[0] = from_f32<T>(gelu_tanh(v[0]) * v[1]);
+        if (n + 2 < a.N) o[1] = from_f32<T>(gelu_tanh(v[2]) * v[3]);
       }
     } else if constexpr (EPI == EPI_QKV) {
       if (mok) {
         const int b = m / a.tq, i = m % a.tq;
-        if (n < a.q_cols + a.kv_cols && a.rope) {
-          // pairs (2j, 2j + 1) of the interleaved head layout rotate together
-          const int c = n < a.q_cols ? n : n - a.q_cols;
-          const int dh = 2 * a.half_dh;
-          for (int j = 0; j < 4; j += 2) {
-            const int jj = ((c + j) % dh) / 2;
-            const float2 cs = a.rope_cs[(long)i * a.half_dh + jj];
-            const float x0 = v[j], x1 = v[j + 1];
-            v[j] = x0 * cs.x - x1 * cs.y;
-            v[j + 1] = x1 * cs.x + x0 * cs.y;
-          }
+        if (a.rope && n < a.q_cols + a.kv_cols) {
+          const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+          v[0] = x0 * p0[q][0] - x1 * p0[q][1];
+          v[1] = x1 * p0[q][0] + x0 * p0[q][1];
+          v[2] = x2 * p0[q][2] - x3 * p0[q][3];
+          v[3] = x3 * p0[q][2] + x2 * p0[q][3];
         }
-        for (int j = 0; j < 4; ++j) {
-          const int nn = n + j;
-          if (nn >= a.N) break;
-          if (nn < a.q_cols) {
-            ((T*)a.out)[(long)m * a.ldo + nn] = from_f32<T>(v[j]);
-          } else if (nn < a.q_cols + a.kv_cols) {
-            const int c = nn - a.q_cols;
-            ((T*)a.kdst)[(long)b * a.k_bs + (long)(a.kv_off + i) * a.k_rs + c] = from_f32<T>(v[j]);
-          } else {
-            const int c = nn - a.q_cols - a.kv_cols;
-            ((T*)a.vdst)[(long)b * a.v_bs + (long)c * a.v_ds + a.kv_off + i] = from_f32<T>(v[j]);
-          }
+        if (n < a.q_cols) {
+          T* o = (T*)a.out + (long)m * a.ldo + n;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(v[j]);
+        } else if (n < a.q_cols + a.kv_cols) {
+          T* o = (T*)a.kdst + (long)b * a.k_bs + (long)(a.kv_off + i) * a.k_rs + (n - a.q_cols);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(v[j]);
+        } else if (n < a.N) {
+          const int c = n - a.q_cols - a.kv_cols;
+          T* o = (T*)a.vdst + (long)b * a.v_bs + a.kv_off + i;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[(long)(c + j) * a.v_ds] = from_f32<T>(v[j]);
         }
       }
     } else if constexpr (EPI == EPI_VT) {
       if (mok) {
-        const int b = m / a.vt_group, s = m % a.vt_group;
-        for (int j = 0; j < 4; ++j) {
-          if (n + j >= a.N) break;
-          ((T*)a.out)[(long)b * a.vt_bs + (long)(n + j) * a.vt_ds + s] = from_f32<T>(v[j]);
-        }
+        const int b = m / a.vt_group, sidx = m % a.vt_group;
+        for (int j = 0; j < 4; ++j)
+          if (n + j < a.N) ((T*)a.out)[(long)b * a.vt_bs + (long)(n + j) * a.vt_ds + sidx] = from_f32<T>(v[j]);
       }
     } else if constexpr (EPI == EPI_RESID) {
-      // h += gate * acc, then (mean, M2) of the updated 64-column slot for the next norm.
-      // N is a multiple of BN here, so every item is in range column-wise.
-      float hv[4] = {0.f, 0.f, 0.f, 0.f};
+      // h += gate * y; hs = T(h (1 + next scale)); (mean, M2) of the 16-column slot.
+      // N is a multiple of 16 here and every item is in range column-wise.
+      f32x4 hv = mok ? p0[q] + p1[q] * v : f32x4{0.f, 0.f, 0.f, 0.f};
       if (mok) {
-        float* hp = a.h + (long)m * a.ldh_out + n;
-        const f32x4 ho = *(const f32x4*)hp;
-        for (int j = 0; j < 4; ++j) hv[j] = ho[j] + (a.gate ? a.gate[n + j] : 1.f) * v[j];
-        f32x4 hn; hn[0] = hv[0]; hn[1] = hv[1]; hn[2] = hv[2]; hn[3] = hv[3];
-        *(f32x4*)hp = hn;
+        *(f32x4*)(a.h + (long)m * a.ldh_out + n) = hv;
+        float hsv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hsv[j] = hv[j] * (1.f + p2[q][j]);
+        T* o = (T*)a.hs + (long)m * a.ldh_out + n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(hsv[j]);
       }
       float mean = 0.25f * (hv[0] + hv[1] + hv[2] + hv[3]);
       float m2 = 0.f;
+#pragma unroll
       for (int j = 0; j < 4; ++j) m2 += (hv[j] - mean) * (hv[j] - mean);
       float cnt = 4.f;
-      for (int off = 1; off < 16; off <<= 1) {
-        const float mb = __shfl_xor(mean, off, 64);
-        const float qb = __shfl_xor(m2, off, 64);
-        stat_merge(mean, m2, cnt, mb, qb, cnt);
-        cnt *= 2.f;
+#pragma unroll
+      for (int off = 1; off < 4; off <<= 1) {
+        float mb = __shfl_xor(mean, off, 64), qb = __shfl_xor(m2, off, 64), nb = __shfl_xor(cnt, off, 64);
+        stat_merge(mean, m2, cnt, mb, qb, nb);
       }
-      if (mok && (c4 % 16) == 0) {
-        const int part = n / kStatCols;
-        a.stats_out[(long)part * a.stats_out_ld + m] = make_float2(mean, m2);
-      }
+      if (mok && (c4 % 4) == 0) a.stats_out[(long)(n / kStatCols) * a.stats_out_ld + m] = make_float2(mean, m2);
     } else if constexpr (EPI == EPI_EULER) {
       if (mok) {
         for (int j = 0; j < 4; ++j) {
           if (n + j >= a.N) break;
-          const float vel = v[j] + (a.bias ? a.bias[n + j] : 0.f);
+          const float vel = v[j] + p0[q][j];
           const long idx = (long)m * a.ldo + n + j;
           if (a.vout) a.vout[idx] = vel;
-          if (a.x) a.x[idx] += a.dt * vel;
+          if (a.x) a.x[idx] = p1[q][j] + a.dt * vel;
         }
       }
     }
@@ -175,18 +299,19 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C,
 }
 
 // ---------------------------------------------------------------------------------------
-// The GEMM kernel. Workgroup = WM x WN waves; tile BM x BN; k-tile BK; two LDS stages in
-// fragment-major order (conflict-free 16-byte reads); optional split-K over workgroups with
-// the last-arriving workgroup of a tile summing the partials in split order.
+// Tiled kernel (M > 64): workgroup = WM x WN waves, tile BM x BN, k-tile BK. Global loads
+// of k-tiles run two tiles ahead in registers; two LDS stages in fragment-major order
+// (conflict-free 16-byte reads). Optional split-K over workgroups: partial tiles go to the
+// workspace with device-scope stores and the last-arriving workgroup of a tile sums them
+// in split order (deterministic) and runs the epilogue.
 // ---------------------------------------------------------------------------------------
 template <typename T, int BM, int BN, int BK, int WM, int WN, int EPI>
 __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
-  using MT = Mma<T>;
+  typedef Mma<T> MT;
   typedef typename MT::frag frag;
   constexpr int NT = WM * WN * 64;
   constexpr int VEC = MT::VEC, KC = MT::KC;
-  constexpr int KCH = BK / KC;                // k-chunks per k-tile
-  constexpr int SEG = KC / VEC;               // 16-byte segments per chunk row (4)
+  constexpr int KCH = BK / KC, SEG = KC / VEC;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int A_CH = BM * BK / VEC, B_CH = BN * BK / VEC;
@@ -209,79 +334,36 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   const int split = bid / tiles, t = bid % tiles;
   const int tn = t % ntn, tm = t / ntn;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int KB = a.K / KC;                    // k-chunks in the full K (weights layout)
+  const int KB = a.K / KC;
   const int kbeg = split * a.k_split;
   const int kend = min(a.K, kbeg + a.k_split);
   const int nkt = (kend - kbeg + BK - 1) / BK;
-  const bool normed = a.norm != NORM_NONE;
-
-  if (normed) {
-    for (int r = tid; r < BM; r += NT) {
-      const int m = m0 + r;
-      float mean = 0.f, rinv = 0.f;
-      if (m < a.M) {
-        const int hr = (m / a.row_group) * a.row_gstride + a.row_off + m % a.row_group;
-        float mu = 0.f, m2 = 0.f, cnt = 0.f;
-        for (int p = 0; p < a.nparts; ++p) {
-          const float2 st = a.stats[(long)p * a.stats_ld + hr];
-          if (p == 0) { mu = st.x; m2 = st.y; cnt = (float)kStatCols; }
-          else { stat_merge(mu, m2, cnt, st.x, st.y, (float)kStatCols); cnt += (float)kStatCols; }
-        }
-        if (a.norm == NORM_RMS) {
-          const float ms = (m2 + cnt * mu * mu) / cnt;
-          rinv = rsqrtf(ms + a.eps);
-          mean = 0.f;
-        } else {
-          rinv = rsqrtf(m2 / cnt + a.eps);
-          mean = mu;
-        }
-      }
-      s_mean[r] = mean;
-      s_rinv[r] = rinv;
-    }
-    __syncthreads();
-  }
-
-  V16 ra[A_PT][2];
-  V16 rb[B_PT];
   V16* lds = (V16*)smem;
 
-  auto load_tile = [&](int k0) {
+  struct Regs { V16 a[A_PT]; V16 b[B_PT]; };
+  auto load_tile = [&](Regs& R, int k0) {
+    // unconditional loads from clamped addresses; k beyond the split is zeroed by select
 #pragma unroll
     for (int p = 0; p < A_PT; ++p) {
-      const int c = tid + p * NT;
-      ra[p][0] = V16{{0, 0, 0, 0}};
-      ra[p][1] = V16{{0, 0, 0, 0}};
-      if (c < A_CH) {
-        const int r = c / (BK / VEC), ks = c % (BK / VEC);
-        const int m = m0 + r, k = k0 + ks * VEC;
-        if (m < a.M && k < kend) {
-          if (!normed) {
-            ra[p][0] = *(const V16*)((const T*)a.A + (long)m * a.lda + k);
-          } else {
-            const int hr = (m / a.row_group) * a.row_gstride + a.row_off + m % a.row_group;
-            const float* hp = a.H + (long)hr * a.ldh + k;
-            ra[p][0] = *(const V16*)hp;
-            if (VEC == 8) ra[p][1] = *(const V16*)(hp + 4);
-          }
-        }
-      }
+      const int c = min(tid + p * NT, A_CH - 1);
+      const int r = c / (BK / VEC), ks = c % (BK / VEC);
+      const int m = min(m0 + r, a.M - 1), k = k0 + ks * VEC;
+      const bool kok = k < kend;
+      const V16 v = *(const V16*)((const T*)a.A + (long)a_row(a, m) * a.lda + (kok ? k : kbeg));
+      R.a[p] = kok ? v : vzero();
     }
 #pragma unroll
     for (int p = 0; p < B_PT; ++p) {
-      const int c = tid + p * NT;
-      rb[p] = V16{{0, 0, 0, 0}};
-      if (c < B_CH) {
-        const int f = c / 64, slot = c % 64;
-        const int nbl = f / KCH, kcl = f % KCH;
-        const int nb = n0 / 16 + nbl, kc = k0 / KC + kcl;
-        if (nb * 16 < a.N && kc * KC < kend)
-          rb[p] = *((const V16*)a.W + ((long)nb * KB + kc) * 64 + slot);
-      }
+      const int c = min(tid + p * NT, B_CH - 1);
+      const int f = c / 64, slot = c % 64;
+      const int nbl = f / KCH, kcl = f % KCH;
+      const int nb = min(n0 / 16 + nbl, (a.N - 1) / 16), kc = k0 / KC + kcl;
+      const bool kok = kc * KC < kend;
+      const V16 v = *((const V16*)a.W + ((long)nb * KB + (kok ? kc : kbeg / KC)) * 64 + slot);
+      R.b[p] = kok ? v : vzero();
     }
   };
-
-  auto store_tile = [&](int stage, int k0) {
+  auto store_tile = [&](const Regs& R, int stage) {
     V16* As = lds + stage * STAGE_V16;
     V16* Bs = As + A_CH;
 #pragma unroll
@@ -289,35 +371,13 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
       const int c = tid + p * NT;
       if (c < A_CH) {
         const int r = c / (BK / VEC), ks = c % (BK / VEC);
-        V16 val = ra[p][0];
-        if (normed) {
-          const int m = m0 + r, k = k0 + ks * VEC;
-          float f[8];
-          if (m < a.M && k < kend) {
-            unpack<float>(ra[p][0], f);
-            if (VEC == 8) unpack<float>(ra[p][1], f + 4);
-            const float mu = s_mean[r], ri = s_rinv[r];
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-              float u = (f[j] - mu) * ri;
-              if (a.mscale) u = u * (1.f + a.mscale[k + j]) + a.mshift[k + j];
-              f[j] = u;
-            }
-          } else {
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) f[j] = 0.f;
-          }
-          val = pack<T>(f);
-        }
-        const int frag_i = (r / 16) * KCH + ks / SEG;
-        const int slot = (r % 16) + 16 * (ks % SEG);
-        As[frag_i * 64 + slot] = val;
+        As[((r / 16) * KCH + ks / SEG) * 64 + (r % 16) + 16 * (ks % SEG)] = R.a[p];
       }
     }
 #pragma unroll
     for (int p = 0; p < B_PT; ++p) {
       const int c = tid + p * NT;
-      if (c < B_CH) Bs[c] = rb[p];
+      if (c < B_CH) Bs[c] = R.b[p];
     }
   };
 
@@ -326,41 +386,48 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int stage) {
+    const V16* As = lds + stage * STAGE_V16;
+    const V16* Bs = As + A_CH;
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) {
+      frag af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = __builtin_bit_cast(frag, As[((wm * FM + i) * KCH + kc) * 64 + lane]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = __builtin_bit_cast(frag, Bs[((wn * FN + j) * KCH + kc) * 64 + lane]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = MT::mma(af[i], bfr[j], acc[i][j]);
+    }
+  };
 
+  if (a.norm != NORM_NONE) {
+    RowStats<BM, NT> st;
+    st.load(a, m0);
+    st.merge(a, m0, s_mean, s_rinv);
+  }
+  Regs R0, R1;
+  if (nkt > 0) load_tile(R0, kbeg);
+  if (nkt > 1) load_tile(R1, kbeg + BK);
   if (nkt > 0) {
-    load_tile(kbeg);
-    store_tile(0, kbeg);
+    store_tile(R0, 0);
     __syncthreads();
-    for (int it = 0; it < nkt; ++it) {
-      const int cur = it & 1;
-      const int knext = kbeg + (it + 1) * BK;
-      if (it + 1 < nkt) load_tile(knext);
-      const V16* As = lds + cur * STAGE_V16;
-      const V16* Bs = As + A_CH;
-#pragma unroll
-      for (int kc = 0; kc < KCH; ++kc) {
-        frag af[FM], bfr[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const V16 v = As[((wm * FM + i) * KCH + kc) * 64 + lane];
-          af[i] = __builtin_bit_cast(frag, v);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const V16 v = Bs[((wn * FN + j) * KCH + kc) * 64 + lane];
-          bfr[j] = __builtin_bit_cast(frag, v);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = MT::mma(af[i], bfr[j], acc[i][j]);
-      }
-      if (it + 1 < nkt) store_tile(cur ^ 1, knext);
+    for (int it = 0; it < nkt; it += 2) {
+      compute(0);
+      if (it + 1 < nkt) store_tile(R1, 1);
+      if (it + 2 < nkt) load_tile(R0, kbeg + (it + 2) * BK);
       __syncthreads();
+      if (it + 1 < nkt) {
+        compute(1);
+        if (it + 2 < nkt) store_tile(R0, 0);
+        if (it + 3 < nkt) load_tile(R1, kbeg + (it + 3) * BK);
+        __syncthreads();
+      }
     }
   }
 
-  // accumulators -> LDS tile (row-major, fp32)
   float* C = (float*)smem;
   __syncthreads();
 #pragma unroll
@@ -376,30 +443,209 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   __syncthreads();
 
   if (a.splits > 1) {
+    constexpr int Q4 = BM * BN / 4 / NT;
+    static_assert((BM * BN / 4) % NT == 0, "split items");
     float* wst = a.ws + (long)t * a.splits * BM * BN;
-    for (int it = tid; it < BM * BN / 4; it += NT) {
+#pragma unroll
+    for (int q = 0; q < Q4; ++q) {
+      const int it = tid + q * NT;
       const int r = it / (BN / 4), c4 = it % (BN / 4);
-      *(f32x4*)(wst + (long)split * BM * BN + r * BN + c4 * 4) = *(const f32x4*)(C + r * LDC + c4 * 4);
+      st_dev(wst + (long)split * BM * BN + r * BN + c4 * 4, *(const f32x4*)(C + r * LDC + c4 * 4));
     }
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = atomicAdd(a.counters + t, 1u);
-      s_last = (prev == (unsigned)a.splits - 1u);
-    }
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.splits - 1u;
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    for (int it = tid; it < BM * BN / 4; it += NT) {
+#pragma unroll
+    for (int q = 0; q < Q4; ++q) {
+      const int it = tid + q * NT;
       const int r = it / (BN / 4), c4 = it % (BN / 4);
-      f32x4 s = *(const f32x4*)(wst + r * BN + c4 * 4);
-      for (int sp = 1; sp < a.splits; ++sp) s += *(const f32x4*)(wst + (long)sp * BM * BN + r * BN + c4 * 4);
-      *(f32x4*)(C + r * LDC + c4 * 4) = s;
+      const float* src = wst + r * BN + c4 * 4;
+      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < a.splits; s0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const f32x4 t4 = ld_dev(src + (long)min(s0 + u, a.splits - 1) * BM * BN);
+          v[u] = s0 + u < a.splits ? t4 : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+      }
+      *(f32x4*)(C + r * LDC + c4 * 4) = sum;
     }
-    if (tid == 0) a.counters[t] = 0u;
+    if (tid == 0) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
   }
-  epilogue_tile<T, BM, BN, NT, EPI>(a, C, LDC, m0, n0);
+  epilogue_tile<T, BM, BN, NT, EPI>(a, C, LDC, m0, n0, s_mean, s_rinv);
+}
+
+// ---------------------------------------------------------------------------------------
+// Skinny kernel (M <= 64, the weight-streaming regime). A workgroup covers all rows and
+// 16*NB output columns over 1/splits of K; its four waves split that K range further. Each
+// wave streams its weight fragments (contiguous 1 KB runs) and the matching activation
+// fragments straight into registers, CB k-chunks per batch with two batches in flight. The
+// wave partials are summed in LDS in wave order; with splits > 1 the workgroup partials
+// are exchanged through device-scope stores and the last-arriving workgroup of the column
+// tile sums them in split order before the shared epilogue.
+// ---------------------------------------------------------------------------------------
+template <typename T, int NB, int EPI>
+__global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs a) {
+  typedef Mma<T> MT;
+  typedef typename MT::frag frag;
+  constexpr int KW = 4, NT = KW * 64, VEC = MT::VEC, KC = MT::KC;
+  constexpr int BM = 64, BN = 16 * NB, MB = 4, CB = 4;
+  constexpr int LDR = BN + 4;
+  constexpr int RED = KW * BM * LDR;
+  __shared__ __attribute__((aligned(16))) float red[RED];
+  __shared__ float s_mean[BM], s_rinv[BM];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ntn = (a.N + BN - 1) / BN;
+  const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int tile = bid % ntn, split = bid / ntn;
+  const int n0 = tile * BN;
+  const int KCt = a.K / KC;
+  const int CPS = (KCt + a.splits - 1) / a.splits;
+  const int s_beg = split * CPS, s_end = min(KCt, s_beg + CPS);
+  const int CPW = (s_end - s_beg + KW - 1) / KW;
+  const int c_beg = s_beg + w * CPW, c_end = min(s_end, c_beg + CPW);
+  const int nbat = c_end > c_beg ? (c_end - c_beg + CB - 1) / CB : 0;
+  const int NBt = (a.N + 15) / 16;
+
+  long arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    // rows past M read row M-1: their products land in discarded output rows
+    const int r = min(16 * mb + (lane % 16), a.M - 1);
+    arow[mb] = (long)a_row(a, r) * a.lda;
+  }
+  const T* Ab = (const T*)a.A + (lane / 16) * VEC;
+  const V16* Wf = (const V16*)a.W + lane;
+
+  V16 ra0[CB][MB], rb0[CB][NB], ra1[CB][MB], rb1[CB][NB];
+  auto load_batch = [&](V16 (&ra)[CB][MB], V16 (&rb)[CB][NB], int bi) {
+    // unconditional loads (clamped addresses): chunks past the wave's range are zeroed
+    // on the weight side by select; columns past N land in discarded output columns
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = c_beg + bi * CB + cb;
+      const bool cok = c < c_end;
+      const int cc = cok ? c : c_beg;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) ra[cb][mb] = *(const V16*)(Ab + arow[mb] + (long)cc * KC);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int nbg = min(n0 / 16 + nb, NBt - 1);
+        const V16 v = Wf[((long)nbg * KCt + cc) * 64];
+        rb[cb][nb] = cok ? v : vzero();
+      }
+    }
+  };
+  f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute_batch = [&](const V16 (&ra)[CB][MB], const V16 (&rb)[CB][NB]) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = MT::mma(__builtin_bit_cast(frag, ra[cb][mb]), __builtin_bit_cast(frag, rb[cb][nb]), acc[mb][nb]);
+  };
+
+  // statistic slots first, then two operand batches; the merge waits only for the slots
+  FM_PHASE(0);
+  RowStats<BM, NT> st;
+  st.load(a, 0);   // unconditional (zeros when there is no norm to fold)
+  if (nbat > 0) load_batch(ra0, rb0, 0);
+  if (nbat > 1) load_batch(ra1, rb1, 1);
+  FM_PHASE(1);
+  if (a.norm != NORM_NONE) st.merge(a, 0, s_mean, s_rinv);
+  FM_PHASE(2);
+  for (int bi = 0; bi < nbat; bi += 2) {
+    compute_batch(ra0, rb0);
+    if (bi + 2 < nbat) load_batch(ra0, rb0, bi + 2);
+    if (bi + 1 < nbat) {
+      compute_batch(ra1, rb1);
+      if (bi + 3 < nbat) load_batch(ra1, rb1, bi + 3);
+    }
+  }
+
+  FM_PHASE(3);
+  // wave partials -> LDS, summed in wave order into wave 0's region
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        red[(w * BM + 16 * mb + 4 * (lane / 16) + e) * LDR + 16 * nb + (lane % 16)] = acc[mb][nb][e];
+  __syncthreads();
+  constexpr int Q4 = (BM * BN / 4 + NT - 1) / NT;
+  f32x4 part[Q4];
+#pragma unroll
+  for (int q = 0; q < Q4; ++q) {
+    const int i = tid + q * NT;
+    part[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < BM * BN / 4) {
+      const int r = i / (BN / 4), c4 = i % (BN / 4);
+#pragma unroll
+      for (int w2 = 0; w2 < KW; ++w2) part[q] += *(const f32x4*)(red + (w2 * BM + r) * LDR + c4 * 4);
+    }
+  }
+  FM_PHASE(4);
+  if (a.splits > 1) {
+    float* wst = a.ws + (long)tile * a.splits * BM * BN;
+#pragma unroll
+    for (int q = 0; q < Q4; ++q) {
+      const int i = tid + q * NT;
+      if (i < BM * BN / 4) st_dev(wst + (long)split * BM * BN + i * 4, part[q]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.splits - 1u;
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int q = 0; q < Q4; ++q) {
+      const int i = tid + q * NT;
+      if (i >= BM * BN / 4) continue;
+      f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < a.splits; s0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const f32x4 t4 = ld_dev(wst + (long)min(s0 + u, a.splits - 1) * BM * BN + i * 4);
+          v[u] = s0 + u < a.splits ? t4 : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += v[u];
+      }
+      part[q] = sum;
+    }
+    if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  FM_PHASE(5);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < Q4; ++q) {
+    const int i = tid + q * NT;
+    if (i < BM * BN / 4) {
+      const int r = i / (BN / 4), c4 = i % (BN / 4);
+      *(f32x4*)(red + r * LDR + c4 * 4) = part[q];
+    }
+  }
+  __syncthreads();
+  epilogue_tile<T, BM, BN, NT, EPI>(a, red, LDR, 0, n0, s_mean, s_rinv);
+  FM_PHASE(6);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -414,28 +660,43 @@ static CfgShape cfg_shape(int cfg, int elem) {
     default: return {64, 64, bk};
   }
 }
+static int skinny_bn(int cfg) { return cfg == SK_N32 ? 32 : 16; }
 
 int gemm_num_tiles(const GemmArgs& a) {
-  const CfgShape c = cfg_shape(a.cfg, a.epi == EPI_RESID ? ET_BF16 : ET_BF16);
+  if (a.kind == GEMM_SKINNY) return (a.N + skinny_bn(a.cfg) - 1) / skinny_bn(a.cfg);
+  const CfgShape c = cfg_shape(a.cfg, ET_BF16);
   return ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
 }
 
 void gemm_plan(GemmArgs& a, int elem, int num_cus) {
-  // Large M: 128 x 128 tiles. Small M: 64-row (or 32-row) tiles with split-K until the
-  // launch covers the chip about twice.
+  const int kq = elem == ET_BF16 ? 32 : 16;
+  if (a.M <= 64) {
+    // 16 or 32 columns per workgroup; split K over workgroups until the launch covers the
+    // chip, keeping at least 16 k-chunks (four per wave) per workgroup
+    a.kind = GEMM_SKINNY;
+    const int bn = (a.N / 32 >= num_cus) ? 32 : 16;
+    a.cfg = bn == 32 ? SK_N32 : SK_N16;
+    const int tiles = (a.N + bn - 1) / bn;
+    const int kct = a.K / kq;
+    int splits = 1;
+    while (tiles * splits < num_cus && kct / (2 * splits) >= 16 && splits < 16) splits *= 2;
+    a.splits = splits;
+    a.k_split = ((kct + splits - 1) / splits) * kq;
+    return;
+  }
+  a.kind = GEMM_TILED;
   if (elem == ET_BF16 && a.M >= 256 && a.N >= 512) a.cfg = GEMM_128x128;
-  else if (a.M <= 32) a.cfg = GEMM_32x64;
   else a.cfg = GEMM_64x64;
   const CfgShape c = cfg_shape(a.cfg, elem);
   const int tiles = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
   const int nk = (a.K + c.bk - 1) / c.bk;
   int splits = 1;
-  const int target = 2 * num_cus;
+  const int target = num_cus;
   if (tiles < target) {
     splits = (target + tiles - 1) / tiles;
-    const int max_splits = nk / 2 > 0 ? nk / 2 : 1;   // at least two k-tiles per split
+    const int max_splits = nk / 4 > 0 ? nk / 4 : 1;   // at least four k-tiles per split
     if (splits > max_splits) splits = max_splits;
-    if (splits > 32) splits = 32;
+    if (splits > 16) splits = 16;
   }
   int kt_per = (nk + splits - 1) / splits;
   splits = (nk + kt_per - 1) / kt_per;
@@ -445,40 +706,60 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
 
 size_t gemm_ws_bytes(const GemmArgs& a) {
   if (a.splits <= 1) return 0;
+  if (a.kind == GEMM_SKINNY) return (size_t)gemm_num_tiles(a) * a.splits * 64 * skinny_bn(a.cfg) * sizeof(float);
   const CfgShape c = cfg_shape(a.cfg, ET_BF16);
   const int tiles = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
   return (size_t)tiles * a.splits * c.bm * c.bn * sizeof(float);
 }
 
+#define FM_EPI_SWITCH(KERNEL, GRID, BLOCK)                                                       \
+  switch (a.epi) {                                                                             \
+    case EPI_STORE: hipLaunchKernelGGL(KERNEL(EPI_STORE), GRID, BLOCK, 0, s, a); break;         \
+    case EPI_GELU_MUL: hipLaunchKernelGGL(KERNEL(EPI_GELU_MUL), GRID, BLOCK, 0, s, a); break;   \
+    case EPI_QKV: hipLaunchKernelGGL(KERNEL(EPI_QKV), GRID, BLOCK, 0, s, a); break;             \
+    case EPI_RESID: hipLaunchKernelGGL(KERNEL(EPI_RESID), GRID, BLOCK, 0, s, a); break;         \
+    case EPI_EULER: hipLaunchKernelGGL(KERNEL(EPI_EULER), GRID, BLOCK, 0, s, a); break;         \
+    case EPI_VT: hipLaunchKernelGGL(KERNEL(EPI_VT), GRID, BLOCK, 0, s, a); break;               \
+    default: return hipErrorInvalidValue;                                                      \
+  }
+
 template <typename T, int BM, int BN, int BK, int WM, int WN>
-static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const dim3 grid(tiles * a.splits), block(WM * WN * 64);
-  switch (a.epi) {
-    case EPI_STORE: hipLaunchKernelGGL((k_gemm<T, BM, BN, BK, WM, WN, EPI_STORE>), grid, block, 0, s, a); break;
-    case EPI_GELU_MUL: hipLaunchKernelGGL((k_gemm<T, BM, BN, BK, WM, WN, EPI_GELU_MUL>), grid, block, 0, s, a); break;
-    case EPI_QKV: hipLaunchKernelGGL((k_gemm<T, BM, BN, BK, WM, WN, EPI_QKV>), grid, block, 0, s, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((k_gemm<T, BM, BN, BK, WM, WN, EPI_RESID>), grid, block, 0, s, a); break;
-    case EPI_EULER: hipLaunchKernelGGL((k_gemm<T, BM, BN, BK, WM, WN, EPI_EULER>), grid, block, 0, s, a); break;
-    case EPI_VT: hipLaunchKernelGGL((k_gemm<T, BM, BN, BK, WM, WN, EPI_VT>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
+#define K_TILED(E) (k_gemm<T, BM, BN, BK, WM, WN, E>)
+  FM_EPI_SWITCH(K_TILED, grid, block)
+#undef K_TILED
   return hipGetLastError();
+}
+
+template <typename T, int NB>
+static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(((a.N + 16 * NB - 1) / (16 * NB)) * a.splits), block(256);
+#define K_SKINNY(E) (k_gemm_skinny<T, NB, E>)
+  FM_EPI_SWITCH(K_SKINNY, grid, block)
+#undef K_SKINNY
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_skinny_cfg(const GemmArgs& a, hipStream_t s) {
+  return a.cfg == SK_N32 ? launch_skinny<T, 2>(a, s) : launch_skinny<T, 1>(a, s);
 }
 
 hipError_t gemm_launch(const GemmArgs& a, int elem, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.kind == GEMM_SKINNY) {
+    if (a.M > 64) return hipErrorInvalidValue;
+    return elem == ET_BF16 ? launch_skinny_cfg<bf16>(a, s) : launch_skinny_cfg<float>(a, s);
+  }
   if (elem == ET_BF16) {
     switch (a.cfg) {
-      case GEMM_128x128: return launch_cfg<bf16, 128, 128, 64, 2, 2>(a, s);
-      case GEMM_32x64: return launch_cfg<bf16, 32, 64, 64, 1, 4>(a, s);
-      default: return launch_cfg<bf16, 64, 64, 64, 2, 2>(a, s);
+      case GEMM_128x128: return launch_tiled<bf16, 128, 128, 64, 2, 2>(a, s);
+      default: return launch_tiled<bf16, 64, 64, 64, 2, 2>(a, s);
     }
   }
-  switch (a.cfg) {
-    case GEMM_32x64: return launch_cfg<float, 32, 64, 32, 1, 4>(a, s);
-    default: return launch_cfg<float, 64, 64, 32, 2, 2>(a, s);
-  }
+  return launch_tiled<float, 64, 64, 32, 2, 2>(a, s);
 }
 
 }  // namespace fm

@@ -11,40 +11,51 @@ enum Act { ACT_NONE = 0, ACT_SILU = 1, ACT_GELU = 2 };
 enum NormKind { NORM_NONE = 0, NORM_RMS = 1, NORM_LN = 2 };
 
 // Columns per partial row-statistic slot written by the residual epilogue and the
-// in-projection, and read by the normalizing A-loader.
-constexpr int kStatCols = 64;
+// in-projection, and read by the consumer GEMMs of the next modulated norm.
+constexpr int kStatCols = 16;
 
 // C[M x N] = A[M x K] * W^T, W stored fragment-major (see swizzle_weight).
+//
+// Modulated norms are folded around the GEMM: with u = (h - mu) rinv (1 + s) + t,
+//   u W^T = rinv (hs W^T - mu d) + c,   hs = h (1 + s),  d = (1 + s) W^T,  c = t W^T,
+// so the producer of h also writes hs (rounded to T) and per-slot row statistics, the
+// schedule precomputes c and d per step, and the consumer's epilogue applies rinv, mu, c, d.
 struct GemmArgs {
   int M, N, K;
-  // A operand: a row-major T matrix, or fp32 residual rows normalized on load.
+  // A operand: a row-major T matrix; row r is read from row (r/row_group)*row_gstride +
+  // row_off + r%row_group
   const void* A; long lda;
-  int norm;                                   // NormKind
-  const float* H; long ldh;                   // residual rows for the normalizing loader
-  const float2* stats; int nparts; long stats_ld;  // (mean, M2) per kStatCols-wide slot, [part][row]
-  const float* mscale; const float* mshift;   // modulation (may be null): u = n(h)(1+scale)+shift
+  int row_group, row_gstride, row_off;
+  // consumer side of a modulated norm (norm != NORM_NONE): per-row (mu, rinv) merged from
+  // stats [part][row] of the A rows; y = rinv (acc - mu d[n]) + c[n] (d only for LayerNorm)
+  int norm;
+  const float2* stats; int nparts; long stats_ld;
+  const float* cvec; const float* dvec;
   float eps;
-  int row_group, row_gstride, row_off;        // A row r -> H row (r/row_group)*row_gstride+row_off+r%row_group
   // B operand: fragment-major weights of [Npad x K]
   const void* W;
-  // split-K
+  // split-K (tiled kernel only)
   int splits, k_split;
   float* ws; unsigned* counters;
   // epilogue
   int epi;
   void* out; long ldo; const float* bias; int act; int out_f32;
-  float* h; long ldh_out; const float* gate; float2* stats_out; long stats_out_ld;
+  // residual producer: h += gate * y; hs = T(h (1 + hscale)); stats of h per 64 columns
+  float* h; long ldh_out; const float* gate; void* hs; const float* hscale; float2* stats_out; long stats_out_ld;
   int q_cols, kv_cols, tq, kv_off, rope, half_dh; const float2* rope_cs;
   void* kdst; long k_bs, k_rs; void* vdst; long v_bs, v_ds;
   float* x; float dt; float* vout;
   int vt_group; long vt_bs, vt_ds;
   // launch shape chosen by the planner
-  int cfg;
+  int kind;          // GEMM_SKINNY / GEMM_TILED
+  int cfg;           // tile configuration of that kind
 };
 
+enum GemmKind { GEMM_SKINNY = 0, GEMM_TILED = 1 };
 enum GemmCfg { GEMM_64x64 = 0, GEMM_128x128 = 1, GEMM_32x64 = 2 };
+enum SkinnyCfg { SK_N16 = 0, SK_N32 = 1 };
 
-// Plan tile shape and split-K for an M x N x K problem; fills cfg/splits/k_split.
+// Plan kernel, tile shape and split-K for an M x N x K problem.
 void gemm_plan(GemmArgs& a, int elem, int num_cus);
 size_t gemm_ws_bytes(const GemmArgs& a);        // split-K partial workspace bytes
 int gemm_num_tiles(const GemmArgs& a);
@@ -81,6 +92,7 @@ struct InProjArgs {
   const float* state_tok;                     // [B*st x D] fp32 or null
   int B, Ha, st, D;                           // rows per request = st + Ha
   float* h; float2* stats; long stats_ld;
+  void* hs; const float* hscale;              // hs = T(h (1 + hscale)) (hscale may be null)
 };
 hipError_t inproj_launch(const InProjArgs& a, int elem, hipStream_t s);
 
@@ -93,5 +105,8 @@ hipError_t prefix_k_copy(void* pool, long pool_bs, const void* src, int B, int P
 hipError_t prefix_v_copy_t(void* pool, long pool_bs, int cap, const void* src, int B, int P, int dh,
                            int elem, hipStream_t s);
 hipError_t fill_f32(float* dst, float v, long n, hipStream_t s);
+// dst[r*dld + c] = T(src[r*sld + c] + add) for r < rows, c < cols.
+hipError_t rows_from_f32(void* dst, long dld, const float* src, long sld, int rows, int cols, float add, int elem,
+                         hipStream_t s);
 
 }  // namespace fm

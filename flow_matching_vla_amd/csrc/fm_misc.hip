@@ -6,42 +6,89 @@
 
 namespace fm {
 
-// One workgroup (256 threads) per h row. Columns n = tid + 256 j; wave w of pass j covers
-// statistic slot 4 j + w (64 columns), reduced across the wave with pairwise merges.
+// Workgroup = 64 h rows x one 64-column statistic slot. The slot's weight rows and the
+// rows' inputs are staged in LDS with every global load issued up front; thread (row r,
+// 16-column group g) computes 16 outputs, stores them, and merges the slot's (mean, M2)
+// across the four lanes of its row.
+constexpr int kInMaxK = 64;
 template <typename T>
 __global__ void __launch_bounds__(256) k_inproj(InProjArgs a) {
-  const int hr = blockIdx.x;
+  __shared__ float sw[64][kInMaxK + 1];
+  __shared__ float sx[64][kInMaxK + 1];
   const int per = a.st + a.Ha;
-  const int b = hr / per, t = hr % per;
-  const int lane = threadIdx.x & 63;
-  for (int n0 = 0; n0 < a.D; n0 += 256) {
-    const int n = n0 + threadIdx.x;
-    float v = 0.f;
-    if (n < a.D) {
-      if (t < a.st) {
-        v = a.state_tok[(long)(b * a.st + t) * a.D + n];
-      } else {
-        const float* xr = a.x + (long)(b * a.Ha + t - a.st) * a.da;
-        const T* wr = (const T*)a.w + (long)n * a.da;
-        float acc = 0.f;
-        for (int k = 0; k < a.da; ++k) acc += xr[k] * to_f32(wr[k]);
-        v = acc + a.b[n] + (a.tb ? a.tb[n] : 0.f);
-      }
-      a.h[(long)hr * a.D + n] = v;
+  const int rows = a.B * per;
+  const int n0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  constexpr int LPT = 64 * kInMaxK / 256;
+  float wv[LPT], xv[LPT];
+  // unconditional loads from clamped indices; entries with k >= da are never read and
+  // state-token rows ignore x
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) {
+    const int idx = tid + q * 256;
+    const int rr = idx / kInMaxK, k = min(idx % kInMaxK, a.da - 1);
+    wv[q] = to_f32(((const T*)a.w)[(long)(n0 + rr) * a.da + k]);
+    const int hr = min(r0 + rr, rows - 1);
+    const int b = hr / per, t = max(hr % per - a.st, 0);
+    xv[q] = a.x[(long)(b * a.Ha + t) * a.da + k];
+  }
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) {
+    const int idx = tid + q * 256;
+    sw[idx / kInMaxK][idx % kInMaxK] = wv[q];
+    sx[idx / kInMaxK][idx % kInMaxK] = xv[q];
+  }
+  const int r = tid / 4, g = tid % 4;
+  const int hr = r0 + r;
+  const bool rok = hr < rows;
+  const int b = rok ? hr / per : 0, t = rok ? hr % per : 0;
+  float bias[16], st[16], hsc[16];
+  const int tst = min(t, a.st > 0 ? a.st - 1 : 0);
+#pragma unroll
+  for (int c = 0; c < 16; c += 4) {
+    // unconditional loads; absent optional vectors read as zeros
+    const int n = n0 + g * 16 + c;   // D is a multiple of 64: always in range
+    const f32x4 bv = *(const f32x4*)(a.b + n);
+    const f32x4 tv = *(const f32x4*)(a.tb ? a.tb + n : g_zeros);
+    const f32x4 sv = *(const f32x4*)(a.hscale ? a.hscale + n : g_zeros);
+    const f32x4 stv = *(const f32x4*)(a.state_tok ? a.state_tok + (long)(b * a.st + tst) * a.D + n : g_zeros);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bias[c + j] = bv[j] + tv[j];
+      hsc[c + j] = sv[j];
+      st[c + j] = stv[j];
+    }
+  }
+  __syncthreads();
+  float y[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) y[c] = 0.f;
+  for (int k = 0; k < a.da; ++k) {
+    const float xk = sx[r][k];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) y[c] += xk * sw[g * 16 + c][k];
+  }
+#pragma unroll
+  for (int c = 0; c < 16; ++c) y[c] = (rok && t < a.st) ? st[c] : y[c] + bias[c];
+  if (rok && n0 + g * 16 < a.D) {
+    float* hp = a.h + (long)hr * a.D + n0 + g * 16;
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) *(f32x4*)(hp + c) = f32x4{y[c], y[c + 1], y[c + 2], y[c + 3]};
+    if (a.hs) {
+      T* hq = (T*)a.hs + (long)hr * a.D + n0 + g * 16;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) hq[c] = from_f32<T>(y[c] * (1.f + hsc[c]));
     }
     if (a.stats) {
-      float mean = v, m2 = 0.f, cnt = 1.f;
-      for (int off = 1; off < 64; off <<= 1) {
-        const float mb = __shfl_xor(mean, off, 64);
-        const float qb = __shfl_xor(m2, off, 64);
-        const float tot = 2.f * cnt;
-        const float d = mb - mean;
-        mean += d * 0.5f;
-        m2 += qb + d * d * (cnt * cnt / tot);
-        cnt = tot;
-      }
-      const int slot = (n0 + (threadIdx.x & ~63)) / kStatCols;
-      if (lane == 0 && n0 + (threadIdx.x & ~63) < a.D) a.stats[(long)slot * a.stats_ld + hr] = make_float2(mean, m2);
+      // the thread's 16 columns are one statistic slot
+      float mean = 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) mean += y[c];
+      mean *= (1.f / 16.f);
+      float m2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) m2 += (y[c] - mean) * (y[c] - mean);
+      a.stats[(long)((n0 + g * 16) / kStatCols) * a.stats_ld + hr] = make_float2(mean, m2);
     }
   }
 }
@@ -49,8 +96,10 @@ __global__ void __launch_bounds__(256) k_inproj(InProjArgs a) {
 hipError_t inproj_launch(const InProjArgs& a, int elem, hipStream_t s) {
   const int rows = a.B * (a.st + a.Ha);
   if (rows == 0) return hipSuccess;
-  if (elem == ET_BF16) hipLaunchKernelGGL(k_inproj<bf16>, dim3(rows), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_inproj<float>, dim3(rows), dim3(256), 0, s, a);
+  if (a.da > kInMaxK || a.D % 64 != 0) return hipErrorInvalidValue;
+  const dim3 grid(a.D / 64, (rows + 63) / 64);
+  if (elem == ET_BF16) hipLaunchKernelGGL(k_inproj<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_inproj<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -63,6 +112,14 @@ template <typename T>
 __global__ void k_from_f32(T* dst, const float* src, long n) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
     dst[i] = from_f32<T>(src[i]);
+}
+template <typename T>
+__global__ void k_rows_from_f32(T* dst, long dld, const float* src, long sld, int rows, int cols, float add) {
+  const long n = (long)rows * cols;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const long r = i / cols, c = i % cols;
+    dst[r * dld + c] = from_f32<T>(src[r * sld + c] + add);
+  }
 }
 __global__ void k_fill(float* dst, float v, long n) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) dst[i] = v;
@@ -80,6 +137,16 @@ hipError_t convert_from_f32(void* dst, const float* src, long n, int elem, hipSt
   if (n <= 0) return hipSuccess;
   if (elem == ET_BF16) hipLaunchKernelGGL(k_from_f32<bf16>, dim3(grid_for(n)), dim3(256), 0, s, (bf16*)dst, src, n);
   else hipLaunchKernelGGL(k_from_f32<float>, dim3(grid_for(n)), dim3(256), 0, s, (float*)dst, src, n);
+  return hipGetLastError();
+}
+hipError_t rows_from_f32(void* dst, long dld, const float* src, long sld, int rows, int cols, float add, int elem,
+                         hipStream_t s) {
+  const long n = (long)rows * cols;
+  if (n <= 0) return hipSuccess;
+  if (elem == ET_BF16)
+    hipLaunchKernelGGL(k_rows_from_f32<bf16>, dim3(grid_for(n)), dim3(256), 0, s, (bf16*)dst, dld, src, sld, rows, cols, add);
+  else
+    hipLaunchKernelGGL(k_rows_from_f32<float>, dim3(grid_for(n)), dim3(256), 0, s, (float*)dst, dld, src, sld, rows, cols, add);
   return hipGetLastError();
 }
 hipError_t fill_f32(float* dst, float v, long n, hipStream_t s) {

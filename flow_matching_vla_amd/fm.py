@@ -70,6 +70,7 @@ def lib():
         "fm_denoise": ([VP, VP, I32, VP], I32),
         "fm_step_velocity": ([VP, VP, I32, VP], I32),
         "fm_step_trace": ([VP, VP, I32, VP, VP], I32),
+        "fm_profile_loop": ([VP, VP, I32, VP, I32, P(C.c_float), P(I32)], I32),
         "fm_op_linear": ([I32, I32, I32, I32, VP, VP, VP, I32, VP, I32, VP], I32),
         "fm_op_attention": ([I32, I32, I32, I32, I32, I32, I32, VP, VP, VP, VP, VP], I32),
     }
@@ -232,6 +233,19 @@ class Context:
         v = torch.empty_like(x)
         _check(lib().fm_step_trace(self.h, _ptr(x), k, _ptr(v), _ptr(tr)), self.h)
         return v, tr
+
+
+OP_ROLES = {"inproj": 0, "qkv": 1, "attn": 2, "oproj": 3, "mlp_up": 4, "mlp_down": 5, "out": 6}
+
+
+def profile_loop(ctx: "Context", x0, steps: int, role: str, out=None):
+    """Eager run of the loop with events around every launch of `role`; (total ms, launches)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(x0)
+    ms, n = C.c_float(), C.c_int32()
+    _check(lib().fm_profile_loop(ctx.h, _ptr(x0), steps, _ptr(out), OP_ROLES[role], C.byref(ms), C.byref(n)), ctx.h)
+    return ms.value, n.value
 
 
 def op_linear(A, W, bias=None, act: int = 0, out_f32: bool = False):

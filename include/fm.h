@@ -168,6 +168,24 @@ fm_status fm_step_velocity(fm_ctx* ctx, const float* x_dev, int32_t k, float* v_
  * Sec. III-E). */
 fm_status fm_step_trace(fm_ctx* ctx, const float* x_dev, int32_t k, float* v_dev, float* h_trace_dev);
 
+/* Launch roles inside one Euler step, for fm_profile_loop. */
+enum {
+  FM_OP_INPROJ = 0,   /* action (and state) tokens -> residual stream */
+  FM_OP_QKV = 1,      /* modulated norm + Q/K/V projection (+ RoPE, K/V append); DiT cross: Q */
+  FM_OP_ATTN = 2,     /* attention over bound + own K/V */
+  FM_OP_OPROJ = 3,    /* output projection + gated residual */
+  FM_OP_MLP_UP = 4,   /* modulated norm + gate/up (or FF1) + GELU */
+  FM_OP_MLP_DOWN = 5, /* down (or FF2) projection + residual */
+  FM_OP_OUT = 6       /* final modulated norm + velocity projection + Euler update */
+};
+
+/* Run the same loop as fm_denoise, eagerly, with a hipEvent pair on the context stream
+ * around every launch of `role`; returns the summed duration in *ms (milliseconds) and
+ * the number of those launches in *launches. Synchronizes the context stream. Arguments
+ * and results as fm_denoise (steps must be the scheduled count, >= 1). For measurement. */
+fm_status fm_profile_loop(fm_ctx* ctx, const float* x0_dev, int32_t steps, float* out_dev, int32_t role, float* ms,
+                          int32_t* launches);
+
 /* Kernel-level entry points on caller buffers, used to check single kernels.
  * fm_op_linear: out[M, N] = act(A[M, K] W[N, K]^T + bias) with the library GEMM (split-K
  *   and tile choice as the loop would plan them). A, W DEVICE in `dtype`, row-major; bias
