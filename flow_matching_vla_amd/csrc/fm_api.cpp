@@ -311,6 +311,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       at.q = ctx->qbuf; at.q_bs = (long)H * qd; at.q_rs = qd;
       at.k = kpl; at.k_bs = (long)ctx->cap * dh; at.k_rs = dh; at.k_hs = 0;
       at.vt = vpl; at.v_bs = (long)dh * ctx->cap; at.v_hs = 0; at.v_ds = ctx->cap;
+      at.k_len = at.v_len = (long)c.max_batch * ctx->cap * dh;
       at.o = ctx->obuf; at.o_bs = (long)H * qd; at.o_rs = qd;
       at.B = B; at.Tq = H; at.n_heads = nq; at.heads_per_kv = nq; at.n_keys = ctx->prefix_len + H; at.dh = dh;
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
@@ -353,6 +354,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
         at.k_bs = (long)c.ctx_len_max * D; at.k_rs = D; at.k_hs = dh;
         at.vt = (char*)ctx->cross_vt + (size_t)ci * c.max_batch * D * ctx->spad * ctx->esz;
         at.v_bs = (long)D * ctx->spad; at.v_hs = (long)dh * ctx->spad; at.v_ds = ctx->spad;
+        at.k_len = (long)c.max_batch * c.ctx_len_max * D; at.v_len = (long)c.max_batch * D * ctx->spad;
         at.n_keys = ctx->prefix_len;
       } else {
         g = gemm_base(Mh, 3 * D, D, W.qkv);
@@ -364,6 +366,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
         memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_QKV; op.g = g; ops.push_back(op);
         at.k = ctx->kself; at.k_bs = (long)Tq * D; at.k_rs = D; at.k_hs = dh;
         at.vt = ctx->vtself; at.v_bs = (long)D * ctx->tpad; at.v_hs = (long)dh * ctx->tpad; at.v_ds = ctx->tpad;
+        at.k_len = (long)c.max_batch * Tq * D; at.v_len = (long)c.max_batch * D * ctx->tpad;
         at.n_keys = Tq;
       }
       memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.role = FM_OP_ATTN; op.at = at; ops.push_back(op);
@@ -406,7 +409,6 @@ fm_status plan_ops(fm_ctx* ctx, std::vector<Op>& ops) {
     } else if (op.kind == Op::ATTN) {
       attn_plan(op.at, ctx->elem, ctx->num_cus);
       need = std::max(need, attn_ws_bytes(op.at));
-      if (op.at.splits > 1 && attn_num_items(op.at) > fm_ctx::kCounters) return fail(ctx, FM_ERR_UNSUPPORTED, "too many attention tiles");
     }
   }
   if (need > ctx->ws_bytes) {
@@ -422,7 +424,7 @@ fm_status plan_ops(fm_ctx* ctx, std::vector<Op>& ops) {
   }
   for (auto& op : ops) {
     if (op.kind == Op::GEMM) { op.g.ws = ctx->ws; op.g.counters = ctx->counters; }
-    else if (op.kind == Op::ATTN) { op.at.ws = ctx->ws; op.at.counters = ctx->counters; }
+    else if (op.kind == Op::ATTN) op.at.ws = ctx->ws;
   }
   return FM_OK;
 }
@@ -575,8 +577,9 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
     ALLOC(rope_cs, H * (c.head_dim / 2) * sizeof(float2), float2*);
   } else {
     const size_t nc = (c.n_layers + 1) / 2;
-    ctx->spad = (int)round_up(c.ctx_len_max, 8);
-    ctx->tpad = (int)round_up(st + H, 8);
+    // transposed V planes hold whole key tiles (and the permuted slots of each)
+    ctx->spad = (int)round_up(c.ctx_len_max, 64);
+    ctx->tpad = (int)round_up(st + H, 64);
     ALLOC(cross_k, nc * B * c.ctx_len_max * D * esz, void*);
     ALLOC(cross_vt, nc * B * D * ctx->spad * esz, void*);
     ALLOC(kself, rows * D * esz, void*);
@@ -1113,7 +1116,7 @@ fm_status fm_op_attention(int32_t dtype, int32_t B, int32_t Tq, int32_t nh, int3
   hipDeviceProp_t prop;
   if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) { g_err = "no device"; return FM_ERR_DEVICE; }
   const size_t esz = elem == ET_BF16 ? 2 : 4;
-  const int kpad = (int)round_up(nk, 8);
+  const int kpad = (int)round_up(nk, 64);   // whole key tiles in the transposed V plane
   AttnArgs at;
   memset(&at, 0, sizeof at);
   at.q = q; at.q_bs = (long)Tq * nh * dh; at.q_rs = (long)nh * dh;
@@ -1121,23 +1124,20 @@ fm_status fm_op_attention(int32_t dtype, int32_t B, int32_t Tq, int32_t nh, int3
   at.o = o; at.o_bs = at.q_bs; at.o_rs = at.q_rs;
   at.v_bs = (long)nkv * dh * kpad; at.v_hs = (long)dh * kpad; at.v_ds = kpad;
   at.B = B; at.Tq = Tq; at.n_heads = nh; at.heads_per_kv = nh / nkv; at.n_keys = nk; at.dh = dh;
+  at.k_len = (long)B * nkv * nk * dh; at.v_len = (long)B * nkv * dh * kpad;
   at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   attn_plan(at, elem, prop.multiProcessorCount);
-  void *vt = nullptr, *ws = nullptr, *cnt = nullptr;
+  void *vt = nullptr, *ws = nullptr;
   hipError_t e = hipMalloc(&vt, (size_t)B * nkv * dh * kpad * esz);
   const size_t wsb = attn_ws_bytes(at);
   if (e == hipSuccess && wsb) e = hipMalloc(&ws, wsb);
-  if (e == hipSuccess) e = hipMalloc(&cnt, fm_ctx::kCounters * sizeof(unsigned));
-  if (e == hipSuccess) e = hipMemsetAsync(cnt, 0, fm_ctx::kCounters * sizeof(unsigned), s);
   if (e == hipSuccess) e = hipMemsetAsync(vt, 0, (size_t)B * nkv * dh * kpad * esz, s);
   if (e == hipSuccess) e = prefix_v_copy_t(vt, (long)dh * kpad, kpad, v, B * nkv, nk, dh, elem, s);
-  at.vt = vt; at.ws = (float*)ws; at.counters = (unsigned*)cnt;
-  if (e == hipSuccess && at.splits > 1 && attn_num_items(at) > fm_ctx::kCounters) e = hipErrorInvalidValue;
+  at.vt = vt; at.ws = (float*)ws;
   if (e == hipSuccess) e = attn_launch(at, elem, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (vt) (void)hipFree(vt);
   if (ws) (void)hipFree(ws);
-  if (cnt) (void)hipFree(cnt);
   if (e != hipSuccess) { g_err = fmt("fm_op_attention: %s", hipGetErrorString(e)); return FM_ERR_DEVICE; }
   return FM_OK;
 }

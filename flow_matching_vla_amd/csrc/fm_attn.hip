@@ -2,54 +2,120 @@
 // (vla.cpp Eq. (2) with M = 0). Query rows of every head that shares a K/V head are
 // folded into one row set (pi0.5 Design, "Attention and the K/V pool": the query heads
 // fold onto the single K/V head), so each K/V tile is staged once in LDS and used by all
-// of them. Scores and P.V run on MFMA; the softmax is computed online with wave-level
-// row reductions; a long key range can be split over workgroups, whose partial (O, m, l)
-// are merged in split order by the last workgroup of the row tile. V is read from a
-// transposed layout (key index contiguous) so both products take 16-byte fragments.
+// of them.
+//
+// Everything is computed transposed: the score tile is S^T = K Q^T (keys as MFMA rows,
+// queries as columns) and the output O^T = V^T P^T. A lane then owns one query column,
+// so the softmax max and sum need only two cross-lane steps, the per-query rescale of O
+// needs none, and the probabilities leave the S^T accumulators directly as the B operand
+// of the P.V product, in the key order that the transposed V plane stores (vt_slot).
+// K and V^T tiles are copied into LDS with buffer loads that write LDS directly (no
+// register staging), double-buffered; reads past the K / V extents return zeros.
+//
+// A long key range can be split over workgroups; their unnormalised (O, m, l) go to a
+// workspace and a second, wide kernel merges them in split order.
 #include "fm_common.h"
 #include "fm_kernels.h"
 
+#ifdef FM_PHASE_TIMING
+extern __device__ unsigned long long* g_phase;
+#define FM_PHASE(i) do { if (threadIdx.x == 0 && g_phase) g_phase[blockIdx.x * 8 + (i)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define FM_PHASE(i) do { } while (0)
+#endif
+
 namespace fm {
 
-constexpr int kKeyTile = 64;
+constexpr int kKeyTile = 32;
+constexpr int kAttnWaves = 4;
+constexpr int kAttnRows = 16 * kAttnWaves;   // query rows per workgroup
+constexpr int kMaxAttnSplits = 16;
+
+constexpr int kAttnStages = 4;                 // LDS tile buffers (tiles in flight + 1)
+
+// s_waitcnt with vmcnt <= n (n < 64) and the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14])
+#define FM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+// wait until at most `pend` tiles of FPW copies each are still in flight (pend < stages)
+template <int FPW, int NST>
+__device__ __forceinline__ void wait_tiles(int pend) {
+  static_assert((NST - 1) * FPW < 64, "vmcnt range");
+  if (pend >= 3 && NST > 3) FM_WAIT_VMCNT(3 * FPW);
+  else if (pend == 2 && NST > 2) FM_WAIT_VMCNT(2 * FPW);
+  else if (pend == 1) FM_WAIT_VMCNT(FPW);
+  else FM_WAIT_VMCNT(0);
+}
 
 template <typename T, int DH, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   using MT = Mma<T>;
   typedef typename MT::frag frag;
-  constexpr int NT = WAVES * 64;
-  constexpr int VEC = MT::VEC, KC = MT::KC, SEG = KC / VEC;
+  constexpr int VEC = MT::VEC, KC = MT::KC;
   constexpr int BK = kKeyTile;
-  constexpr int DCH = DH / KC;                 // d-chunks (QK^T reduction)
-  constexpr int KCH = BK / KC;                 // key-chunks (PV reduction)
   constexpr int KB = BK / 16, DB = DH / 16;
-  constexpr int K_V16 = BK * DH / VEC;         // 16-byte chunks per K (and per V) tile
-  constexpr int P_V16 = 16 * BK / VEC;         // per wave
+  constexpr int DCH = DH / KC;                 // k-chunks of S^T = K Q^T (over d)
+  constexpr int KCH = BK / KC;                 // k-chunks of O^T = V^T P^T (over keys)
+  constexpr int FK = KB * DCH, FV = DB * KCH;  // 1 KB fragments per K / V^T tile
+  constexpr int FT = FK + FV;
+  constexpr int FPW = FT / WAVES;
   constexpr int ROWS = 16 * WAVES;
-  __shared__ __attribute__((aligned(16))) V16 sK[K_V16];
-  __shared__ __attribute__((aligned(16))) V16 sV[K_V16];
-  __shared__ __attribute__((aligned(16))) V16 sP[WAVES * P_V16];
-  __shared__ int s_last;
+  static_assert(FT % WAVES == 0 && FPW <= 15, "tile fragments per wave");
+  static_assert(KB == 2 * KCH || KB == KCH, "P fragment packing");
+  constexpr int NST = kAttnStages;
+  static_assert(NST >= 2 && NST <= 4, "stages");
+  __shared__ __attribute__((aligned(16))) V16 sbuf[NST][FT * 64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave index made provably uniform: it selects LDS destinations (M0) of the tile copies
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = a.heads_per_kv * a.Tq;
   const int rtiles = (R + ROWS - 1) / ROWS;
   const int groups = a.n_heads / a.heads_per_kv;
-  const int item = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int sp = item % a.splits;
-  const int tile_id = item / a.splits;          // (b, g, rt)
-  const int rt = tile_id % rtiles;
-  const int g = (tile_id / rtiles) % groups;
-  const int b = tile_id / (rtiles * groups);
+  // Work units are (request, K/V head, key split); each unit's row tiles run on one XCD
+  // (workgroup b is dispatched to XCD b mod 8) so that its K/V range is fetched from HBM
+  // once and then served from that XCD's L2.
+  const int units = a.B * groups * a.splits;
+  const int xcd = blockIdx.x % 8, j8 = blockIdx.x / 8;
+  const int unit = xcd + 8 * (j8 / rtiles);
+  const int rt = j8 % rtiles;
+  if (unit >= units) return;
+  const int sp = unit % a.splits;
+  const int g = (unit / a.splits) % groups;
+  const int b = unit / (a.splits * groups);
+  const int tile_id = (b * groups + g) * rtiles + rt;
   const int key_beg = sp * a.keys_per_split;
   const int key_end = min(a.n_keys, key_beg + a.keys_per_split);
+  const int ntile = (key_end - key_beg + BK - 1) / BK;
 
-  const T* kbase = (const T*)a.k + (long)b * a.k_bs + (long)g * a.k_hs;
-  const T* vbase = (const T*)a.vt + (long)b * a.v_bs + (long)g * a.v_hs;
+  FM_PHASE(0);
+  // K / V^T tile copies: fragment f of a tile is 64 lanes x 16 bytes. K fragment (kb, c):
+  // lane l carries key kb 16 + l % 16, d = c KC + (l / 16) VEC ... (A operand of S^T).
+  // V^T fragment (db, kc): lane l carries d = db 16 + l % 16, stored key slots
+  // kc KC + (l / 16) VEC ... (A operand of O^T). Each wave issues FPW of them per tile.
+  const V16 rk = make_desc(a.k, (uint32_t)(a.k_len * (long)sizeof(T)));
+  const V16 rv = make_desc(a.vt, (uint32_t)(a.v_len * (long)sizeof(T)));
+  const uint32_t lds0 = lds_addr(&sbuf[0][0]) + (uint32_t)wave * FPW * 1024u;
+  const uint32_t k_lane = (uint32_t)(((long)b * a.k_bs + (long)g * a.k_hs + (long)(lane % 16) * a.k_rs + (lane / 16) * VEC) * sizeof(T));
+  const uint32_t v_lane = (uint32_t)(((long)b * a.v_bs + (long)g * a.v_hs + (long)(lane % 16) * a.v_ds + (lane / 16) * VEC) * sizeof(T));
+  const uint32_t k_row = (uint32_t)(a.k_rs * sizeof(T)), v_row16 = (uint32_t)(16 * a.v_ds * sizeof(T));
+  auto issue = [&](int kt, int buf) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+      const int f = wave * FPW + i;
+      if (f < FK) {   // uniform per wave
+        const int kb = f / DCH, c = f % DCH;
+        const uint32_t off = k_lane + (uint32_t)(kt + 16 * kb) * k_row + (uint32_t)(c * KC * sizeof(T));
+        dma16_lds(rk, lds0 + (uint32_t)buf * (FT * 1024u) + i * 1024u, off);
+      } else {
+        const int fv = f - FK, db = fv / KCH, kc = fv % KCH;
+        const uint32_t off = v_lane + (uint32_t)db * v_row16 + (uint32_t)((kt + kc * KC) * sizeof(T));
+        dma16_lds(rv, lds0 + (uint32_t)buf * (FT * 1024u) + i * 1024u, off);
+      }
+    }
+  };
+  if (ntile > 0) issue(key_beg, 0);   // tile 0 first, the other prefetched tiles after Q
 
-  // this lane's query row for the Q fragments
-  // (loads are unconditional from clamped addresses: rows past R produce outputs that are
-  // never stored, keys past the range are masked in the softmax and zeroed in V)
+  // Q^T fragments (B operand of S^T): lane l carries query row l % 16 of this wave, d
+  // run l / 16 of every d-chunk. Rows past R read row R-1; their outputs are not stored.
   frag qf[DCH];
   {
     const int r = min(rt * ROWS + wave * 16 + (lane % 16), R - 1);
@@ -58,236 +124,207 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < DCH; ++c) qf[c] = __builtin_bit_cast(frag, *(const V16*)(qp + c * KC));
   }
+  // Q and the first tile's copies complete here; the loop below then waits only on the
+  // copies it issues itself (the compiler cannot see those: they are inline asm)
+  FM_WAIT_VMCNT(0);
+#pragma unroll
+  for (int p = 1; p < NST - 1; ++p)
+    if (p < ntile) issue(key_beg + p * BK, p);
+  FM_PHASE(1);
 
-  f32x4 o[DB];
+  f32x4 o[DB];   // O^T: lane l, element e holds d = 16 db + 4 (l / 16) + e of query l % 16
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { mrow[e] = -INFINITY; lrow[e] = 0.f; }
+  float m_run = -INFINITY, l_run = 0.f;   // of this lane's query, base-2 logits
 
-  T* pw = (T*)(sP + wave * P_V16);
-
-  // K / V^T tiles: the next tile's global loads are issued before the current tile's MFMA
-  // work, so one memory round trip per tile is hidden behind compute.
-  constexpr int KPT = (K_V16 + NT - 1) / NT;
-  V16 rk[KPT], rv[KPT];
-  auto load_kv = [&](int kt) {
-    const int jlast = ((key_end - 1) / VEC) * VEC;
-#pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-      const int c = min(tid + q * NT, K_V16 - 1);
-      const int j = c / (DH / VEC), ds = c % (DH / VEC);
-      rk[q] = *(const V16*)(kbase + (long)min(kt + j, key_end - 1) * a.k_rs + ds * VEC);
-      const int d = c / (BK / VEC), ks = c % (BK / VEC);
-      const int j0 = kt + ks * VEC;
-      V16 v = *(const V16*)(vbase + (long)d * a.v_ds + min(j0, jlast));
-      const int nv = key_end - j0;  // keys of this chunk inside the range (may be <= 0)
-      constexpr int EPW = VEC / 4;  // elements per 32-bit word
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int e0 = w * EPW;
-        const uint32_t keep = (e0 + EPW <= nv) ? 0xffffffffu : (e0 < nv ? 0x0000ffffu : 0u);
-        v[w] &= keep;
-      }
-      rv[q] = v;
-    }
-  };
-  auto store_kv = [&]() {
-#pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-      const int c = tid + q * NT;
-      if (c < K_V16) {
-        const int j = c / (DH / VEC), ds = c % (DH / VEC);
-        sK[((j / 16) * DCH + ds / SEG) * 64 + (j % 16) + 16 * (ds % SEG)] = rk[q];
-        const int d = c / (BK / VEC), ks = c % (BK / VEC);
-        sV[((d / 16) * KCH + ks / SEG) * 64 + (d % 16) + 16 * (ks % SEG)] = rv[q];
-      }
-    }
-  };
-
-  if (key_beg < key_end) load_kv(key_beg);
-  for (int kt = key_beg; kt < key_end; kt += BK) {
-    store_kv();
+  for (int t = 0; t < ntile; ++t) {
+    const int kt = key_beg + t * BK;
+    if (t + NST - 1 < ntile) issue(kt + (NST - 1) * BK, (t + NST - 1) % NST);
+    // tile t's copies are done once at most the tiles issued after it are in flight
+    wait_tiles<FPW, NST>(min(NST - 1, ntile - 1 - t));
     __syncthreads();
-    if (kt + BK < key_end) load_kv(kt + BK);
+    if (t == 0) FM_PHASE(2);
+    const V16* sK = sbuf[t % NST];
+    const V16* sV = sK + FK * 64;
 
-    // S = Q K^T for 16 rows x BK keys
+    // S^T = K Q^T: 16 keys x 16 queries per kb, two partial chains per kb. A key block's
+    // fragments are all read from LDS before its MFMAs, so the reads overlap each other
+    // instead of each MFMA waiting on its own read.
     f32x4 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      V16 kf[DCH];
 #pragma unroll
-      for (int c = 0; c < DCH; ++c)
-        s[kb] = MT::mma(qf[c], __builtin_bit_cast(frag, sK[(kb * DCH + c) * 64 + lane]), s[kb]);
+      for (int c = 0; c < DCH; ++c) kf[c] = sK[(kb * DCH + c) * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
+      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+      for (int c = 0; c < DCH; c += 2) {
+        s0 = MT::mma(__builtin_bit_cast(frag, kf[c]), qf[c], s0);
+        if (c + 1 < DCH) s1 = MT::mma(__builtin_bit_cast(frag, kf[c + 1]), qf[c + 1], s1);
+      }
+      s[kb] = s0 + s1;
     }
-    // online softmax (base 2): lane holds rows 4 (l/16) + e, key 16 kb + l % 16
-    float mt[4];
+    // V^T fragments read now; their LDS latency hides behind the softmax
+    V16 vf[FV];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) mt[e] = -INFINITY;
+    for (int f = 0; f < FV; ++f) vf[f] = sV[f * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+    // online softmax of this lane's query over keys kt + 16 kb + 4 (l / 16) + e
+    const int kl = kt + 4 * (lane / 16);
+    float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const bool valid = kt + kb * 16 + (lane % 16) < key_end;
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v = valid ? s[kb][e] * a.scale_log2 : -INFINITY;
+        const float v = (kl + 16 * kb + e < key_end) ? s[kb][e] * a.scale_log2 : -INFINITY;
         s[kb][e] = v;
-        mt[e] = fmaxf(mt[e], v);
+        mt = fmaxf(mt, v);
       }
-    }
+    mt = group4_max(mt);
+    // The reference max moves only when a score exceeds it by more than 2^8: until then
+    // p = 2^(s - m_run) <= 256 stays exact in fp32 / bf16 and O, l need no rescale. The
+    // final O / l is the same for any reference, so this changes no result.
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.f)) {   // wave-uniform
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      for (int off = 1; off < 16; off <<= 1) mt[e] = fmaxf(mt[e], __shfl_xor(mt[e], off, 64));
-    float alpha[4], ls[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float mn = fmaxf(mrow[e], mt[e]);
-      alpha[e] = exp2f(mrow[e] - mn);
-      mrow[e] = mn;
-      ls[e] = 0.f;
+      for (int i = 0; i < DB; ++i) o[i] *= alpha;
     }
+    float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = exp2f(s[kb][e] - mrow[e]);
+        const float p = exp2f(s[kb][e] - m_run);
         s[kb][e] = p;
-        ls[e] += p;
+        ls += p;
       }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      for (int off = 1; off < 16; off <<= 1) ls[e] += __shfl_xor(ls[e], off, 64);
-      lrow[e] = lrow[e] * alpha[e] + ls[e];
-    }
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[i][e] *= alpha[e];
-    // P -> LDS in A-fragment order: element (row r, key c) of chunk c / KC
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * (lane / 16) + e, c = kb * 16 + (lane % 16);
-        const int slot = r + 16 * ((c % KC) / VEC);
-        pw[((c / KC) * 64 + slot) * VEC + (c % VEC)] = from_f32<T>(s[kb][e]);
-      }
-    __syncthreads();
-    // O += P V
+    ls = group4_sum(ls);
+    l_run += ls;
+
+    // P^T fragments: keys 16 h + 4 (l / 16) + r of chunk kc, h over the chunk's key blocks
+    frag pf[KCH];
 #pragma unroll
     for (int kc = 0; kc < KCH; ++kc) {
-      const frag pf = __builtin_bit_cast(frag, sP[wave * P_V16 + kc * 64 + lane]);
+      if constexpr (sizeof(T) == 2) {
+        const f32x4 p0 = s[2 * kc], p1 = s[2 * kc + 1];
+        pf[kc] = frag{(bf16)p0[0], (bf16)p0[1], (bf16)p0[2], (bf16)p0[3], (bf16)p1[0], (bf16)p1[1], (bf16)p1[2], (bf16)p1[3]};
+      } else {
+        pf[kc] = __builtin_bit_cast(frag, s[kc]);
+      }
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        o[db] = MT::mma(pf, __builtin_bit_cast(frag, sV[(db * KCH + kc) * 64 + lane]), o[db]);
-    }
-    __syncthreads();
+        o[db] = MT::mma(__builtin_bit_cast(frag, vf[db * KCH + kc]), pf[kc], o[db]);
+    __syncthreads();   // this buffer is refilled by the next iteration's copies
   }
+  FM_PHASE(3);
 
-  const int row0 = rt * ROWS + wave * 16 + 4 * (lane / 16);
+  const int rq = rt * ROWS + wave * 16 + (lane % 16);   // this lane's query row
   if (a.splits == 1) {
+    if (rq < R) {
+      const int n = g * a.heads_per_kv + rq / a.Tq, t = rq % a.Tq;
+      T* op = (T*)a.o + (long)b * a.o_bs + (long)t * a.o_rs + (long)n * a.dh + 4 * (lane / 16);
+      const float inv = 1.f / l_run;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = row0 + e;
-      if (r >= R) continue;
-      const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
-      T* op = (T*)a.o + (long)b * a.o_bs + (long)t * a.o_rs + (long)n * a.dh;
-      const float inv = 1.f / lrow[e];
-#pragma unroll
-      for (int db = 0; db < DB; ++db) op[db * 16 + (lane % 16)] = from_f32<T>(o[db][e] * inv);
+      for (int db = 0; db < DB; ++db) {
+        if constexpr (sizeof(T) == 2) {
+          *(bf16x4*)(op + db * 16) = bf16x4{(bf16)(o[db][0] * inv), (bf16)(o[db][1] * inv), (bf16)(o[db][2] * inv), (bf16)(o[db][3] * inv)};
+        } else {
+          *(f32x4*)(op + db * 16) = o[db] * inv;
+        }
+      }
     }
     return;
   }
 
-  // split keys: partial (O, m, l) to the workspace with device-scope stores (coherent
-  // across XCDs without an L2 write-back); the last arriver merges them in split order
-  const long per = (long)ROWS * DH + 2L * ROWS;
-  float* wt = a.ws + (long)tile_id * a.splits * per;
-  {
-    float* wo = wt + (long)sp * per;
+  // split keys: unnormalised O^T in the MFMA output layout ([wave][db][lane][e], one
+  // 16-byte store per lane and d-block) and (m, l) of each query row
+  float* wo = a.ws + ((long)tile_id * a.splits + sp) * (ROWS * DH);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rl = wave * 16 + 4 * (lane / 16) + e;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) st_dev1(wo + (long)rl * DH + db * 16 + (lane % 16), o[db][e]);
-      if ((lane % 16) == 0) {
-        st_dev1(wo + (long)ROWS * DH + rl, mrow[e]);
-        st_dev1(wo + (long)ROWS * DH + ROWS + rl, lrow[e]);
-      }
-    }
+  for (int db = 0; db < DB; ++db) *(f32x4*)(wo + ((wave * DB + db) * 64 + lane) * 4) = o[db];
+  if (lane < 16) {
+    float2* wml = (float2*)(a.ws + (long)a.B * groups * rtiles * a.splits * (ROWS * DH)) + ((long)tile_id * a.splits + sp) * ROWS;
+    wml[wave * 16 + lane] = make_float2(m_run, l_run);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(a.counters + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.splits - 1u;
-  __syncthreads();
-  if (!s_last) return;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int rl = wave * 16 + 4 * (lane / 16) + e;
-    const int r = rt * ROWS + rl;
-    float mx = -INFINITY;
-    for (int q0 = 0; q0 < a.splits; q0 += 8) {
-      float mv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float m_u = ld_dev1(wt + (long)min(q0 + u, a.splits - 1) * per + (long)ROWS * DH + rl);
-        mv[u] = q0 + u < a.splits ? m_u : -INFINITY;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) mx = fmaxf(mx, mv[u]);
-    }
-    float den = 0.f;
-    float acc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = 0.f;
-    for (int q0 = 0; q0 < a.splits; q0 += 2) {
-      float w[2], lv[2], ov[2][DB];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bool ok = q0 + u < a.splits;
-        const float* wq = wt + (long)(ok ? q0 + u : 0) * per;
-        const float m_u = ld_dev1(wq + (long)ROWS * DH + rl);
-        w[u] = ok ? m_u : -INFINITY;
-        lv[u] = ld_dev1(wq + (long)ROWS * DH + ROWS + rl);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) ov[u][db] = ld_dev1(wq + (long)rl * DH + db * 16 + (lane % 16));
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float wt_u = exp2f(w[u] - mx);
-        den += wt_u * lv[u];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] += wt_u * ov[u][db];
-      }
-    }
-    if (r < R) {
-      const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
-      T* op = (T*)a.o + (long)b * a.o_bs + (long)t * a.o_rs + (long)n * a.dh;
-      const float inv = 1.f / den;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) op[db * 16 + (lane % 16)] = from_f32<T>(acc[db] * inv);
-    }
-  }
-  if (tid == 0) __hip_atomic_store(a.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  FM_PHASE(4);
 }
 
-static int attn_rows(int elem, int dh) { (void)elem; (void)dh; return 64; }
+// Merge of the key splits: thread = (row tile, wave, d-block, lane) of the partial layout,
+// i.e. four consecutive d of one query row. All NS (>= splits) partials and (m, l) pairs
+// are loaded before any is used (clamped split index, weight 0 past the split count).
+template <typename T, int DH, int ROWS, int NS>
+__global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
+  constexpr int DB = DH / 16, PER_TILE = ROWS * DH / 4;
+  const int R = a.heads_per_kv * a.Tq;
+  const int rtiles = (R + ROWS - 1) / ROWS;
+  const int groups = a.n_heads / a.heads_per_kv;
+  const long ntiles = (long)a.B * groups * rtiles;
+  const long it = blockIdx.x * 256L + threadIdx.x;
+  if (it >= ntiles * PER_TILE) return;
+  const int tile_id = (int)(it / PER_TILE), w = (int)(it % PER_TILE);
+  const int lane = w % 64, db = (w / 64) % DB, wave = w / (64 * DB);
+  const int rt = tile_id % rtiles, g = (tile_id / rtiles) % groups, b = tile_id / (rtiles * groups);
+  const int rl = wave * 16 + (lane % 16);
+  const int S = a.splits;
+  const float* wo = a.ws + (long)tile_id * S * (ROWS * DH) + (long)w * 4;
+  const float2* wml = (const float2*)(a.ws + ntiles * S * (ROWS * DH)) + (long)tile_id * S * ROWS + rl;
+  f32x4 ov[NS];
+  float2 ml[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int sc = min(s, S - 1);
+    ov[s] = *(const f32x4*)(wo + (long)sc * (ROWS * DH));
+    ml[s] = wml[(long)sc * ROWS];
+  }
+  float mx = ml[0].x;
+#pragma unroll
+  for (int s = 1; s < NS; ++s) mx = fmaxf(mx, ml[s].x);   // clamped copies repeat a real split
+  f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float wgt = s < S ? exp2f(ml[s].x - mx) : 0.f;
+    num += wgt * ov[s];
+    den += wgt * ml[s].y;
+  }
+  const int r = rt * ROWS + rl;
+  if (r >= R) return;
+  const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
+  T* op = (T*)a.o + (long)b * a.o_bs + (long)t * a.o_rs + (long)n * a.dh + db * 16 + 4 * (lane / 16);
+  const float inv = 1.f / den;
+  if constexpr (sizeof(T) == 2) {
+    *(bf16x4*)op = bf16x4{(bf16)(num[0] * inv), (bf16)(num[1] * inv), (bf16)(num[2] * inv), (bf16)(num[3] * inv)};
+  } else {
+    *(f32x4*)op = num * inv;
+  }
+}
 
 int attn_num_items(const AttnArgs& a) {
-  const int rows = attn_rows(0, a.dh);
   const int R = a.heads_per_kv * a.Tq;
-  return a.B * (a.n_heads / a.heads_per_kv) * ((R + rows - 1) / rows);
+  return a.B * (a.n_heads / a.heads_per_kv) * ((R + kAttnRows - 1) / kAttnRows);
 }
 
 void attn_plan(AttnArgs& a, int elem, int num_cus) {
+  // Split the keys only when the row tiles alone leave most of the chip idle. The merge
+  // reads every split's partial O (4 bytes per row and head dim), so splits keep at least
+  // two key tiles and the launch stays near a quarter of the CUs.
   a.cfg = 0;
   const int items = attn_num_items(a);
   const int ktiles = (a.n_keys + kKeyTile - 1) / kKeyTile;
   int splits = 1;
-  if (items < num_cus) {
-    splits = (num_cus + items - 1) / items;
-    if (splits > ktiles) splits = ktiles;
+  const int target = num_cus / 4 > 0 ? num_cus / 4 : 1;
+  if (items < target) {
+    splits = (target + items - 1) / items;
+    const int max_splits = ktiles / 2 > 1 ? ktiles / 2 : 1;
+    if (splits > max_splits) splits = max_splits;
+    if (splits > kMaxAttnSplits) splits = kMaxAttnSplits;
   }
   const int per = (ktiles + splits - 1) / splits;
   a.splits = (ktiles + per - 1) / per;
@@ -297,21 +334,39 @@ void attn_plan(AttnArgs& a, int elem, int num_cus) {
 
 size_t attn_ws_bytes(const AttnArgs& a) {
   if (a.splits <= 1) return 0;
-  const int rows = attn_rows(0, a.dh);
-  return (size_t)attn_num_items(a) * a.splits * ((size_t)rows * a.dh + 2 * rows) * sizeof(float);
+  return (size_t)attn_num_items(a) * a.splits * ((size_t)kAttnRows * a.dh + 2 * kAttnRows) * sizeof(float);
+}
+
+template <typename T, int DH>
+static void launch_attn(const AttnArgs& a, hipStream_t s) {
+  const int R = a.heads_per_kv * a.Tq;
+  const int rtiles = (R + kAttnRows - 1) / kAttnRows;
+  const int units = a.B * (a.n_heads / a.heads_per_kv) * a.splits;
+  const dim3 grid(8 * ((units + 7) / 8) * rtiles);
+  hipLaunchKernelGGL((k_attn<T, DH, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, s, a);
+  if (a.splits > 1) {
+    const long threads = (long)attn_num_items(a) * kAttnRows * DH / 4;
+    const dim3 cgrid((unsigned)((threads + 255) / 256));
+    if (a.splits <= 4) hipLaunchKernelGGL((k_attn_combine<T, DH, kAttnRows, 4>), cgrid, dim3(256), 0, s, a);
+    else if (a.splits <= 8) hipLaunchKernelGGL((k_attn_combine<T, DH, kAttnRows, 8>), cgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_combine<T, DH, kAttnRows, 16>), cgrid, dim3(256), 0, s, a);
+  }
 }
 
 hipError_t attn_launch(const AttnArgs& a, int elem, hipStream_t s) {
-  const dim3 grid(attn_num_items(a) * a.splits), block(256);
-  if (grid.x == 0) return hipSuccess;
+  if (attn_num_items(a) == 0) return hipSuccess;
+  if (a.splits < 1 || a.splits > kMaxAttnSplits || a.keys_per_split % kKeyTile != 0) return hipErrorInvalidValue;
+  // K / V^T are addressed through 32-bit byte offsets
+  const long esz = elem == ET_BF16 ? 2 : 4;
+  if (a.k_len <= 0 || a.v_len <= 0 || a.k_len * esz >= (1L << 31) || a.v_len * esz >= (1L << 31)) return hipErrorInvalidValue;
   if (elem == ET_BF16) {
-    if (a.dh == 256) hipLaunchKernelGGL((k_attn<bf16, 256, 4>), grid, block, 0, s, a);
-    else if (a.dh == 64) hipLaunchKernelGGL((k_attn<bf16, 64, 4>), grid, block, 0, s, a);
-    else if (a.dh == 128) hipLaunchKernelGGL((k_attn<bf16, 128, 4>), grid, block, 0, s, a);
+    if (a.dh == 256) launch_attn<bf16, 256>(a, s);
+    else if (a.dh == 64) launch_attn<bf16, 64>(a, s);
+    else if (a.dh == 128) launch_attn<bf16, 128>(a, s);
     else return hipErrorInvalidValue;
   } else {
-    if (a.dh == 64) hipLaunchKernelGGL((k_attn<float, 64, 4>), grid, block, 0, s, a);
-    else if (a.dh == 128) hipLaunchKernelGGL((k_attn<float, 128, 4>), grid, block, 0, s, a);
+    if (a.dh == 64) launch_attn<float, 64>(a, s);
+    else if (a.dh == 128) launch_attn<float, 128>(a, s);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

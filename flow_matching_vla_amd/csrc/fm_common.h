@@ -101,6 +101,67 @@ __device__ __forceinline__ float ld_dev1(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Buffer resources (raw, stride 0): loads at a byte offset at or past `bytes` return zeros
+// and touch no memory, so edge tiles need neither clamped addresses nor selects.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ V16 bload16(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+// Raw buffer descriptor as four SGPRs (base, stride 0, byte extent, gfx9 format word).
+__device__ __forceinline__ V16 make_desc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  return V16{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+// 16 bytes per lane copied from a buffer straight into LDS: lane l's bytes land at
+// lds + 16 l (lds wave-uniform). Issued as inline asm so the compiler does not treat every
+// later LDS read as dependent on it; callers order it with explicit vmcnt waits and
+// barriers. M0 (the LDS base of the copy) is saved and restored around it.
+__device__ __forceinline__ void dma16_lds(const V16& desc, uint32_t lds, uint32_t off) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(off), "s"(desc)
+      : "memory");
+}
+
+// Storage slot of key j in a transposed V plane ([d][key]). For bf16 each aligned run of 32
+// keys is permuted so that the eight keys one lane feeds to the P.V product, keys
+// 16 h + 4 q + r (h = 0, 1; r = 0..3) for lane group q, sit contiguously at 8 q + 4 h + r;
+// the attention kernel produces P in exactly that order from its transposed score tile.
+// fp32 fragments hold four keys, 4 q + r, already contiguous.
+template <typename T> __host__ __device__ __forceinline__ int vt_slot(int j);
+template <> __host__ __device__ __forceinline__ int vt_slot<float>(int j) { return j; }
+template <> __host__ __device__ __forceinline__ int vt_slot<bf16>(int j) {
+  return (j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four lane groups that hold one
+// column of a 16x16 MFMA result), with VALU lane swaps instead of LDS permutes. Swapping a
+// value with itself across 16-lane rows gives the pair (row 2i, row 2i+1) in every lane of
+// both rows; across 32-lane halves, the pair (low half, high half). The result is the same
+// in all four lanes.
+__device__ __forceinline__ float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Map a linear workgroup id so that consecutive logical ids land on the same XCD:
 // the hardware deals workgroups round-robin over the 8 XCDs.
 __device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {

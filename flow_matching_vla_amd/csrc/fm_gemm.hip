@@ -249,7 +249,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C,
           for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(v[j]);
         } else if (n < a.N) {
           const int c = n - a.q_cols - a.kv_cols;
-          T* o = (T*)a.vdst + (long)b * a.v_bs + a.kv_off + i;
+          T* o = (T*)a.vdst + (long)b * a.v_bs + vt_slot<T>(a.kv_off + i);
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[(long)(c + j) * a.v_ds] = from_f32<T>(v[j]);
         }
@@ -258,7 +258,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C,
       if (mok) {
         const int b = m / a.vt_group, sidx = m % a.vt_group;
         for (int j = 0; j < 4; ++j)
-          if (n + j < a.N) ((T*)a.out)[(long)b * a.vt_bs + (long)(n + j) * a.vt_ds + sidx] = from_f32<T>(v[j]);
+          if (n + j < a.N) ((T*)a.out)[(long)b * a.vt_bs + (long)(n + j) * a.vt_ds + vt_slot<T>(sidx)] = from_f32<T>(v[j]);
       }
     } else if constexpr (EPI == EPI_RESID) {
       // h += gate * y; hs = T(h (1 + next scale)); (mean, M2) of the 16-column slot.

@@ -65,12 +65,13 @@ hipError_t gemm_launch(const GemmArgs& a, int elem, hipStream_t s);
 struct AttnArgs {
   const void* q; long q_bs, q_rs;             // q[b*q_bs + t*q_rs + n*dh + d]
   const void* k; long k_bs, k_rs, k_hs;       // k[b*k_bs + g*k_hs + j*k_rs + d]
-  const void* vt; long v_bs, v_hs, v_ds;      // v stored transposed: vt[b*v_bs + g*v_hs + d*v_ds + j]
+  const void* vt; long v_bs, v_hs, v_ds;      // v transposed: vt[b*v_bs + g*v_hs + d*v_ds + vt_slot(j)]
+  long k_len, v_len;                          // elements readable from k / vt (reads past them give 0)
   void* o; long o_bs, o_rs;                   // o[b*o_bs + t*o_rs + n*dh + d]
   int B, Tq, n_heads, heads_per_kv, n_keys, dh;
   float scale_log2;                            // log2(e) / sqrt(dh)
   int splits, keys_per_split;
-  float* ws; unsigned* counters;
+  float* ws;                                   // split partials (attn_ws_bytes), merged by a second kernel
   int cfg;
 };
 void attn_plan(AttnArgs& a, int elem, int num_cus);
@@ -101,7 +102,7 @@ hipError_t convert_from_f32(void* dst, const float* src, long n, int elem, hipSt
 // Prefix K into the pool with RoPE pair interleave (d' = 2j <- j, 2j+1 <- j + dh/2) when rope.
 hipError_t prefix_k_copy(void* pool, long pool_bs, const void* src, int B, int P, int dh, int rope,
                          int elem, hipStream_t s);
-// Prefix V into the pool transposed: pool[b*pool_bs + d*cap + j] = src[(b*P + j)*dh + d].
+// Prefix V into the pool transposed: pool[b*pool_bs + d*cap + vt_slot(j)] = src[(b*P + j)*dh + d].
 hipError_t prefix_v_copy_t(void* pool, long pool_bs, int cap, const void* src, int B, int P, int dh,
                            int elem, hipStream_t s);
 hipError_t fill_f32(float* dst, float v, long n, hipStream_t s);

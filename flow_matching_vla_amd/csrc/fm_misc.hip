@@ -167,7 +167,7 @@ __global__ void k_prefix_k(T* pool, long pool_bs, const T* src, int B, int P, in
     pool[(long)b * pool_bs + (long)j * dh + dp] = src[row * dh + d];
   }
 }
-// pool[b*pool_bs + d*cap + j] = src[(b*P + j)*dh + d]
+// pool[b*pool_bs + d*cap + vt_slot(j)] = src[(b*P + j)*dh + d]
 template <typename T>
 __global__ void k_prefix_vt(T* pool, long pool_bs, int cap, const T* src, int B, int P, int dh) {
   const long n = (long)B * P * dh;
@@ -175,7 +175,7 @@ __global__ void k_prefix_vt(T* pool, long pool_bs, int cap, const T* src, int B,
     const int j = (int)(i % P);
     const long r = i / P;
     const int d = (int)(r % dh), b = (int)(r / dh);
-    pool[(long)b * pool_bs + (long)d * cap + j] = src[((long)b * P + j) * dh + d];
+    pool[(long)b * pool_bs + (long)d * cap + vt_slot<T>(j)] = src[((long)b * P + j) * dh + d];
   }
 }
 
