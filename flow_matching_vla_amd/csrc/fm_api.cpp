@@ -86,7 +86,7 @@ fm_status check_config(const fm_config* c, std::string& msg) {
     msg = "n_layers, hidden (>= 64), heads, head_dim, mlp_dim, action_horizon, action_dim, n_kv_heads, max_batch and max_steps must be positive";
     return FM_ERR_INVALID_ARG;
   }
-  if (c->hidden % 64 != 0) { msg = fmt("hidden %d must be a multiple of 64", c->hidden); return FM_ERR_UNSUPPORTED; }
+  if (c->hidden % 64 != 0 || c->hidden / kStatCols > kMaxStatSlots) { msg = fmt("hidden %d must be a multiple of 64 and at most %d", c->hidden, kStatCols * kMaxStatSlots); return FM_ERR_UNSUPPORTED; }
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) {
     msg = fmt("head_dim %d not in {64, 128, 256}", c->head_dim);
     return FM_ERR_UNSUPPORTED;
@@ -168,6 +168,7 @@ struct fm_ctx {
   float *h = nullptr, *x = nullptr;
   void* hs = nullptr;         // T copy of h scaled by (1 + scale) of the next norm site
   float2* stats = nullptr;
+  float *zeros = nullptr, *ones = nullptr;   // kVecPad each: stand-ins for absent vectors
   void *qbuf = nullptr, *obuf = nullptr, *abuf = nullptr, *kself = nullptr, *vtself = nullptr;
 
   // split-K / split-key workspace
@@ -239,7 +240,8 @@ GemmArgs gemm_base(int M, int N, int K, const void* W) {
 void set_consumer(fm_ctx* ctx, GemmArgs& a, int kind, int k, int s, const float* dvec_override, int rows_h) {
   a.A = ctx->hs; a.lda = ctx->c.hidden;
   a.norm = kind;
-  a.stats = ctx->stats; a.nparts = ctx->c.hidden / kStatCols; a.stats_ld = rows_h;
+  a.stats = ctx->stats; a.nparts = ctx->c.hidden / kStatCols; a.stats_ld = ctx->c.hidden / kStatCols;
+  (void)rows_h;
   a.eps = ctx->c.norm_eps;
   if (s >= 0) {
     a.cvec = ctx->cbuf + (size_t)k * ctx->csum + ctx->c_off[s];
@@ -283,7 +285,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
   ip.x = ctx->x; ip.da = c.action_dim; ip.w = ctx->w_in; ip.b = ctx->b_in;
   ip.tb = c.arch == FM_ARCH_DIT_CROSS ? ctx->tbias + (size_t)k * D : nullptr;
   ip.state_tok = ctx->state_tok; ip.B = B; ip.Ha = H; ip.st = st; ip.D = D;
-  ip.h = ctx->h; ip.stats = ctx->stats; ip.stats_ld = Mh;
+  ip.h = ctx->h; ip.stats = ctx->stats; ip.stats_ld = D / kStatCols; ip.zeros = ctx->zeros;
   ip.hs = ctx->hs; ip.hscale = site(0, 0);
   op.role = FM_OP_INPROJ;
   ops.push_back(op);
@@ -319,7 +321,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       // O projection + gated residual
       g = gemm_base(Ma, D, qd, W.o);
       g.A = ctx->obuf; g.lda = qd;
-      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
+      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l, 2); g.stats_out = ctx->stats; g.stats_out_ld = D / kStatCols;
       g.hs = ctx->hs; g.hscale = site(2 * l + 1, 0);
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_OPROJ; op.g = g; ops.push_back(op);
       // gate/up + GELU * up
@@ -331,7 +333,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       // down + gated residual
       g = gemm_base(Ma, D, F, W.down);
       g.A = ctx->abuf; g.lda = F;
-      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l + 1, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
+      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l + 1, 2); g.stats_out = ctx->stats; g.stats_out_ld = D / kStatCols;
       g.hs = ctx->hs; g.hscale = site(2 * l + 2, 0);
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_DOWN; op.g = g; ops.push_back(op);
     } else {
@@ -372,7 +374,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.role = FM_OP_ATTN; op.at = at; ops.push_back(op);
       g = gemm_base(Mh, D, D, W.o);
       g.A = ctx->obuf; g.lda = D;
-      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(l, 2); g.stats_out = ctx->stats; g.stats_out_ld = Mh;
+      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(l, 2); g.stats_out = ctx->stats; g.stats_out_ld = D / kStatCols;
       g.hs = ctx->hs; g.hscale = nullptr;  // the feed-forward LayerNorm carries no modulation
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_OPROJ; op.g = g; ops.push_back(op);
       g = gemm_base(Mh, F, D, W.gu);
@@ -381,7 +383,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_UP; op.g = g; ops.push_back(op);
       g = gemm_base(Mh, D, F, W.down);
       g.A = ctx->abuf; g.lda = F;
-      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = nullptr; g.stats_out = ctx->stats; g.stats_out_ld = Mh;
+      g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = nullptr; g.stats_out = ctx->stats; g.stats_out_ld = D / kStatCols;
       g.hs = ctx->hs; g.hscale = site(l + 1, 0);
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_DOWN; op.g = g; ops.push_back(op);
     }
@@ -423,7 +425,7 @@ fm_status plan_ops(fm_ctx* ctx, std::vector<Op>& ops) {
     ctx->ws_bytes = need;
   }
   for (auto& op : ops) {
-    if (op.kind == Op::GEMM) { op.g.ws = ctx->ws; op.g.counters = ctx->counters; }
+    if (op.kind == Op::GEMM) { op.g.ws = ctx->ws; op.g.counters = ctx->counters; op.g.zeros = ctx->zeros; op.g.ones = ctx->ones; }
     else if (op.kind == Op::ATTN) op.at.ws = ctx->ws;
   }
   return FM_OK;
@@ -540,7 +542,10 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
   ALLOC(h, rows * D * 4, float*);
   ALLOC(hs, rows * D * esz, void*);
   ALLOC(x, B * H * c.action_dim * 4 + 64, float*);  // padded: the Euler epilogue reads 4 floats at a time
-  ALLOC(stats, (D / kStatCols) * rows * sizeof(float2), float2*);
+  // [row][slot]; the tail pads the consumers' fixed-width slot reads past the last row
+  ALLOC(stats, ((D / kStatCols) * rows + 2 * kMaxStatSlots) * sizeof(float2), float2*);
+  ALLOC(zeros, kVecPad * sizeof(float), float*);
+  ALLOC(ones, kVecPad * sizeof(float), float*);
   ALLOC(qbuf, rows * std::max(qd, D) * esz, void*);
   ALLOC(obuf, rows * std::max(qd, D) * esz, void*);
   ALLOC(abuf, rows * F * esz, void*);
@@ -589,6 +594,9 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
   }
 #undef ALLOC
   e = hipMemsetAsync(ctx->counters, 0, fm_ctx::kCounters * sizeof(unsigned), ctx->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(ctx->zeros, 0, kVecPad * sizeof(float), ctx->stream);
+  if (e == hipSuccess) e = fill_f32(ctx->ones, 1.f, kVecPad, ctx->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(ctx->stats, 0, ((D / kStatCols) * rows + 2 * kMaxStatSlots) * sizeof(float2), ctx->stream);
   if (e == hipSuccess && ctx->pool) e = hipMemsetAsync(ctx->pool, 0, (size_t)c.n_layers * 2 * B * ctx->cap * c.head_dim * esz, ctx->stream);
   if (e == hipSuccess && ctx->vtself) e = hipMemsetAsync(ctx->vtself, 0, B * D * ctx->tpad * esz, ctx->stream);
   if (e == hipSuccess && ctx->cross_vt) e = hipMemsetAsync(ctx->cross_vt, 0, ((c.n_layers + 1) / 2) * B * D * ctx->spad * esz, ctx->stream);
@@ -934,7 +942,7 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void
       memset(&op, 0, sizeof op);
       op.kind = Op::INPROJ;
       op.ip.x = (const float*)state_dev; op.ip.da = c.state_dim; op.ip.w = ctx->w_state; op.ip.b = ctx->b_state;
-      op.ip.B = batch * c.state_tokens; op.ip.Ha = 1; op.ip.st = 0; op.ip.D = D; op.ip.h = ctx->state_tok; op.ip.stats = nullptr;
+      op.ip.B = batch * c.state_tokens; op.ip.Ha = 1; op.ip.st = 0; op.ip.D = D; op.ip.h = ctx->state_tok; op.ip.stats = nullptr; op.ip.zeros = ctx->zeros;
       ops.push_back(op);
     }
     fm_status s = plan_ops(ctx, ops);
@@ -1076,8 +1084,12 @@ fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const voi
   GemmArgs g = gemm_base(M, N, K, nullptr);
   g.A = A; g.lda = K; g.epi = EPI_STORE; g.bias = bias; g.act = act; g.out = out; g.ldo = N; g.out_f32 = out_f32;
   gemm_plan(g, elem, prop.multiProcessorCount);
-  void *wsw = nullptr, *ws = nullptr, *cnt = nullptr, *bpad = nullptr;
+  void *wsw = nullptr, *ws = nullptr, *cnt = nullptr, *bpad = nullptr, *zo = nullptr;
   hipError_t e = hipMalloc(&wsw, swizzled_bytes(N, K, elem));
+  if (e == hipSuccess) e = hipMalloc(&zo, 2 * kVecPad * sizeof(float));
+  if (e == hipSuccess) e = hipMemsetAsync(zo, 0, kVecPad * sizeof(float), s);
+  if (e == hipSuccess) e = fill_f32((float*)zo + kVecPad, 1.f, kVecPad, s);
+  g.zeros = (const float*)zo; g.ones = (const float*)zo + kVecPad;
   const size_t wsb = gemm_ws_bytes(g);
   if (e == hipSuccess && bias) {
     e = hipMalloc(&bpad, (size_t)round_up(N, 4) * 4);
@@ -1098,6 +1110,7 @@ fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const voi
   if (bpad) (void)hipFree(bpad);
   if (ws) (void)hipFree(ws);
   if (cnt) (void)hipFree(cnt);
+  if (zo) (void)hipFree(zo);
   if (e == hipSuccess) e = e2;
   if (e != hipSuccess) { g_err = fmt("fm_op_linear: %s", hipGetErrorString(e)); return FM_ERR_DEVICE; }
   return FM_OK;

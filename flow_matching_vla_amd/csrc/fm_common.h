@@ -144,6 +144,25 @@ template <> __host__ __device__ __forceinline__ int vt_slot<bf16>(int j) {
   return (j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3);
 }
 
+// Data-parallel-primitive (DPP) lane moves: VALU operands read from another lane of the
+// same 16-lane row, no LDS traffic. quad_perm [1,0,3,2] / [2,3,0,1] swap neighbours and
+// pairs within a quad; the half-row mirror maps lane i to 7 - i within each 8 lanes and
+// the row mirror i to 15 - i.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// Sum over each aligned group of G consecutive lanes (G = 1, 2, 4, 8 or 16); every lane
+// of the group gets the same total (each step adds values that the partners hold equally).
+template <int G> __device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+  if constexpr (G >= 2) x += dpp_mov<kDppXor1>(x);
+  if constexpr (G >= 4) x += dpp_mov<kDppXor2>(x);
+  if constexpr (G >= 8) x += dpp_mov<kDppHalfMirror>(x);
+  if constexpr (G >= 16) x += dpp_mov<kDppMirror>(x);
+  return x;
+}
+
 // Reductions over the four lanes l, l^16, l^32, l^48 (the four lane groups that hold one
 // column of a 16x16 MFMA result), with VALU lane swaps instead of LDS permutes. Swapping a
 // value with itself across 16-lane rows gives the pair (row 2i, row 2i+1) in every lane of

@@ -57,67 +57,47 @@ hipError_t swizzle_weight(void* dst, const void* src, const int* rows, int N, in
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------------------
-// Row statistics: (mean, M2) over runs of columns, merged pairwise (Chan et al.); empty
-// sides are skipped so the merge is exact for any split of the columns.
-// ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void stat_merge(float& mean, float& m2, float& n, float mean_b, float m2_b, float n_b) {
-  // branch-free: an empty side (count 0, M2 0) leaves the other unchanged
-  const float tot = n + n_b;
-  const float f = n_b / fmaxf(tot, 1e-30f);
-  const float d = mean_b - mean;
-  mean += d * f;
-  m2 += m2_b + d * d * (n * f);
-  n = tot;
-}
-
 __device__ __forceinline__ int a_row(const GemmArgs& a, int m) {
   return (m / a.row_group) * a.row_gstride + a.row_off + m % a.row_group;
 }
 
 // Per-row (mu, rinv) of the BM rows starting at m0, from the producer's per-slot partial
-// statistics. NT / BM threads share a row; each merges a strided subset of the slots, and
-// the subsets are merged across adjacent lanes. Split in two so that the slot loads can be
-// issued ahead of the operand loads and merged after them: every load is unconditional
-// (clamped index), PPT per thread, covering up to kMaxParts slots.
-constexpr int kMaxParts = 128;   // hidden <= 2048
+// statistics stats[row][slot] (slots of kStatCols columns). TPR = NT / BM threads share a
+// row; each reads PPT 16-byte slot pairs at a stride of TPR pairs and the partial sums are
+// merged across the row's lanes. Split in two so that the slot loads are issued together
+// with the operand loads and merged after them. Loads past the row's slots read the next
+// row (or the buffer's tail padding) and are masked out.
 template <int BM, int NT>
 struct RowStats {
   static constexpr int TPR = NT / BM;
-  static constexpr int PPT = kMaxParts / TPR;
+  static constexpr int PPT = (kMaxStatSlots / 2 + TPR - 1) / TPR;
   static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0 && TPR <= 64, "threads per row");
-  float2 v[PPT];
+  f32x4 v[PPT];
   __device__ __forceinline__ void load(const GemmArgs& a, int m0) {
     const int tid = threadIdx.x;
     const int r = tid / TPR, q = tid % TPR;
-    const long hr = a_row(a, min(m0 + r, a.M - 1));
-    const int np = max(a.nparts, 1);
+    const float2* rp = a.stats + (long)a_row(a, min(m0 + r, a.M - 1)) * a.stats_ld + 2 * q;
 #pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const float2* p = a.stats ? a.stats + (long)min(q + u * TPR, np - 1) * a.stats_ld + hr : (const float2*)g_zeros;
-      v[u] = *p;
-    }
+    for (int u = 0; u < PPT; ++u) v[u] = *(const f32x4*)(rp + 2 * u * TPR);
   }
   __device__ __forceinline__ void merge(const GemmArgs& a, int m0, float* s_mean, float* s_rinv) {
     // every slot covers kStatCols columns: mean = average of slot means, and
-    // M2 = sum of slot M2 + kStatCols * sum (slot mean - mean)^2 (no divisions, short chains)
+    // M2 = sum of slot M2 + kStatCols * sum (slot mean - mean)^2
     const int tid = threadIdx.x;
     const int r = tid / TPR, q = tid % TPR;
     float sm = 0.f;
 #pragma unroll
-    for (int u = 0; u < PPT; ++u) sm += (q + u * TPR < a.nparts) ? v[u].x : 0.f;
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) sm += __shfl_xor(sm, off, 64);
-    const float np = (float)max(a.nparts, 1);
+    for (int u = 0; u < PPT; ++u) sm += (2 * (q + u * TPR) < a.nparts) ? v[u][0] + v[u][2] : 0.f;
+    sm = group_sum<TPR>(sm);
+    const float np = (float)a.nparts;
     const float mu = sm / np;
     float m2 = 0.f;
 #pragma unroll
     for (int u = 0; u < PPT; ++u) {
-      const float d = v[u].x - mu;
-      m2 += (q + u * TPR < a.nparts) ? v[u].y + (float)kStatCols * d * d : 0.f;
+      const float d0 = v[u][0] - mu, d1 = v[u][2] - mu;
+      m2 += (2 * (q + u * TPR) < a.nparts) ? v[u][1] + v[u][3] + (float)kStatCols * (d0 * d0 + d1 * d1) : 0.f;
     }
-#pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) m2 += __shfl_xor(m2, off, 64);
+    m2 = group_sum<TPR>(m2);
     if (q == 0 && r < BM) {
       const float cnt = np * (float)kStatCols;
       const bool ok = m0 + r < a.M;
@@ -134,17 +114,16 @@ struct RowStats {
   }
 };
 
-// device-scope (sc1) accesses for data exchanged between workgroups inside one kernel:
-// coherent across XCDs without write-back or invalidation of the whole L2.
-__device__ __forceinline__ void st_dev(float* p, f32x4 v) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) __hip_atomic_store(p + j, v[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Device-scope (sc1) 16-byte accesses for partial tiles exchanged between workgroups of one
+// kernel: written through to, and read back from, the device-coherent level without a
+// write-back or invalidation of the whole L2. Offsets are in bytes from the workspace base.
+constexpr int kCpolSc1 = 16;             // cache-policy operand: sc1
+constexpr uint32_t kOob = 0x80000000u;   // byte offset past every buffer extent (all < 2^31)
+__device__ __forceinline__ void st_dev(const Rsrc& r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V16, v), r, off, 0, kCpolSc1);
 }
-__device__ __forceinline__ f32x4 ld_dev(const float* p) {
-  f32x4 v;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) v[j] = __hip_atomic_load(p + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v;
+__device__ __forceinline__ f32x4 ld_dev(const Rsrc& r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1));
 }
 
 // ---------------------------------------------------------------------------------------
@@ -154,19 +133,22 @@ __device__ __forceinline__ f32x4 ld_dev(const float* p) {
 // items before any is used.
 // ---------------------------------------------------------------------------------------
 template <typename T, int BM, int BN, int NT, int EPI>
-__device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C, int ldc, int m0, int n0,
-                                              const float* s_mean, const float* s_rinv) {
-  constexpr int C4 = BN / 4;
-  constexpr int TOT = BM * C4;
-  constexpr int ITEMS = (TOT + NT - 1) / NT;
+struct Epilogue {
+  static constexpr int C4 = BN / 4;
+  static constexpr int TOT = BM * C4;
+  static constexpr int ITEMS = (TOT + NT - 1) / NT;
   static_assert(TOT % 64 == 0 && C4 % 4 == 0, "epilogue items");
-  const int tid = threadIdx.x;
-  const bool consumer = a.norm != NORM_NONE;
+  static_assert(EPI != EPI_RESID || BN % kStatCols == 0, "residual tiles cover whole statistic slots");
   f32x4 pc[ITEMS], pd[ITEMS], p0[ITEMS], p1[ITEMS], p2[ITEMS];
+
+  // the epilogue's global inputs for the thread's items (issued early by the caller)
+  __device__ __forceinline__ void prefetch(const GemmArgs& a, int m0, int n0) {
+  const int tid = threadIdx.x;
   // Loads use clamped indices and are unconditional (a divergent conditional load costs a
   // full memory round trip of its own); values outside the tile are never used. Per-column
-  // vectors (bias, c, d) are padded to a multiple of four floats by their owners.
-  auto vec4 = [&](const float* p, long i) -> f32x4 { return *(const f32x4*)(p ? p + i : g_zeros); };
+  // vectors (bias, c, d) are padded to a multiple of four floats by their owners, and the
+  // launcher has replaced every absent one by a zeros (gate: ones) buffer.
+  auto vec4 = [&](const float* p, long i) -> f32x4 { return *(const f32x4*)(p + i); };
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q) {
     const int it = min(tid + q * NT, TOT - 1);
@@ -181,8 +163,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C,
       if constexpr (EPI == EPI_EULER) p1[q] = vec4(a.x, (long)mc * a.ldo + n);
     } else if constexpr (EPI == EPI_RESID) {
       p0[q] = vec4(a.h, (long)mc * a.ldh_out + n);
-      const f32x4 gv = vec4(a.gate, n);
-      p1[q] = a.gate ? gv : f32x4{1.f, 1.f, 1.f, 1.f};
+      p1[q] = vec4(a.gate, n);
       p2[q] = vec4(a.hscale, n);
     } else if constexpr (EPI == EPI_QKV) {
       const int nr = max(min(n, a.q_cols + a.kv_cols - 4), 0);
@@ -191,6 +172,13 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C,
       p0[q] = vec4((const float*)a.rope_cs, 2L * ((long)(mc % a.tq) * a.half_dh + jj));
     }
   }
+  }
+
+  // y from the fp32 tile C (row stride ldc), then the kind's transform and stores
+  __device__ __forceinline__ void apply(const GemmArgs& a, const float* C, int ldc, int m0, int n0,
+                                        const float* s_mean, const float* s_rinv) {
+  const int tid = threadIdx.x;
+  const bool consumer = a.norm != NORM_NONE;
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q) {
     const int it = tid + q * NT;
@@ -261,8 +249,8 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C,
           if (n + j < a.N) ((T*)a.out)[(long)b * a.vt_bs + (long)(n + j) * a.vt_ds + vt_slot<T>(sidx)] = from_f32<T>(v[j]);
       }
     } else if constexpr (EPI == EPI_RESID) {
-      // h += gate * y; hs = T(h (1 + next scale)); (mean, M2) of the 16-column slot.
-      // N is a multiple of 16 here and every item is in range column-wise.
+      // h += gate * y; hs = T(h (1 + next scale)); (mean, M2) of the kStatCols-column slot
+      // (eight consecutive lanes of the row). N is a multiple of kStatCols here.
       f32x4 hv = mok ? p0[q] + p1[q] * v : f32x4{0.f, 0.f, 0.f, 0.f};
       if (mok) {
         *(f32x4*)(a.h + (long)m * a.ldh_out + n) = hv;
@@ -273,17 +261,15 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C,
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(hsv[j]);
       }
-      float mean = 0.25f * (hv[0] + hv[1] + hv[2] + hv[3]);
+      // the slot's lanes hold four columns each: its mean is the mean of their sums, and
+      // M2 the sum of their squared deviations from it (two reductions over the group)
+      constexpr int G = kStatCols / 4;
+      const float mean = group_sum<G>(hv[0] + hv[1] + hv[2] + hv[3]) * (1.f / kStatCols);
       float m2 = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) m2 += (hv[j] - mean) * (hv[j] - mean);
-      float cnt = 4.f;
-#pragma unroll
-      for (int off = 1; off < 4; off <<= 1) {
-        float mb = __shfl_xor(mean, off, 64), qb = __shfl_xor(m2, off, 64), nb = __shfl_xor(cnt, off, 64);
-        stat_merge(mean, m2, cnt, mb, qb, nb);
-      }
-      if (mok && (c4 % 4) == 0) a.stats_out[(long)(n / kStatCols) * a.stats_out_ld + m] = make_float2(mean, m2);
+      m2 = group_sum<G>(m2);
+      if (mok && (c4 % (kStatCols / 4)) == 0) a.stats_out[(long)m * a.stats_out_ld + n / kStatCols] = make_float2(mean, m2);
     } else if constexpr (EPI == EPI_EULER) {
       if (mok) {
         for (int j = 0; j < 4; ++j) {
@@ -291,12 +277,13 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& a, const float* C,
           const float vel = v[j] + p0[q][j];
           const long idx = (long)m * a.ldo + n + j;
           if (a.vout) a.vout[idx] = vel;
-          if (a.x) a.x[idx] = p1[q][j] + a.dt * vel;
+          else a.x[idx] = p1[q][j] + a.dt * vel;
         }
       }
     }
   }
-}
+  }
+};
 
 // ---------------------------------------------------------------------------------------
 // Tiled kernel (M > 64): workgroup = WM x WN waves, tile BM x BN, k-tile BK. Global loads
@@ -445,12 +432,13 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   if (a.splits > 1) {
     constexpr int Q4 = BM * BN / 4 / NT;
     static_assert((BM * BN / 4) % NT == 0, "split items");
-    float* wst = a.ws + (long)t * a.splits * BM * BN;
+    const Rsrc rws = make_rsrc(a.ws, a.ws_bytes);
+    const uint32_t tbase = (uint32_t)t * (uint32_t)a.splits * (BM * BN * 4);
 #pragma unroll
     for (int q = 0; q < Q4; ++q) {
       const int it = tid + q * NT;
       const int r = it / (BN / 4), c4 = it % (BN / 4);
-      st_dev(wst + (long)split * BM * BN + r * BN + c4 * 4, *(const f32x4*)(C + r * LDC + c4 * 4));
+      st_dev(rws, tbase + (uint32_t)split * (BM * BN * 4) + it * 16, *(const f32x4*)(C + r * LDC + c4 * 4));
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -462,15 +450,12 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
     for (int q = 0; q < Q4; ++q) {
       const int it = tid + q * NT;
       const int r = it / (BN / 4), c4 = it % (BN / 4);
-      const float* src = wst + r * BN + c4 * 4;
       f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int s0 = 0; s0 < a.splits; s0 += 8) {
         f32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const f32x4 t4 = ld_dev(src + (long)min(s0 + u, a.splits - 1) * BM * BN);
-          v[u] = s0 + u < a.splits ? t4 : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int u = 0; u < 8; ++u)
+          v[u] = ld_dev(rws, s0 + u < a.splits ? tbase + (uint32_t)(s0 + u) * (BM * BN * 4) + it * 16 : kOob);
 #pragma unroll
         for (int u = 0; u < 8; ++u) sum += v[u];
       }
@@ -479,107 +464,91 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
     if (tid == 0) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
   }
-  epilogue_tile<T, BM, BN, NT, EPI>(a, C, LDC, m0, n0, s_mean, s_rinv);
+  Epilogue<T, BM, BN, NT, EPI> ep;
+  ep.prefetch(a, m0, n0);
+  ep.apply(a, C, LDC, m0, n0, s_mean, s_rinv);
 }
 
 // ---------------------------------------------------------------------------------------
 // Skinny kernel (M <= 64, the weight-streaming regime). A workgroup covers all rows and
-// 16*NB output columns over 1/splits of K; its four waves split that K range further. Each
-// wave streams its weight fragments (contiguous 1 KB runs) and the matching activation
-// fragments straight into registers, CB k-chunks per batch with two batches in flight. The
-// wave partials are summed in LDS in wave order; with splits > 1 the workgroup partials
-// are exchanged through device-scope stores and the last-arriving workgroup of the column
-// tile sums them in split order before the shared epilogue.
+// 16*NB output columns over 1/splits of K; its KW waves split that range again into CPW
+// k-chunks each. Every wave issues all of its loads at once: the weight fragments
+// (contiguous 1 KB runs) and the matching activation fragments, through buffer
+// descriptors with 32-bit offsets (rows past M and chunks past the wave's range read zeros
+// through out-of-range offsets, so nothing is clamped or selected). The wave partials are
+// summed in LDS in wave order; with splits > 1 the workgroup partials are exchanged through
+// device-scope stores and the last-arriving workgroup of the column tile sums them in split
+// order before the shared epilogue. NORM: the A operand is a modulated-norm input whose row
+// statistics are loaded with the operands and merged before the epilogue.
 // ---------------------------------------------------------------------------------------
-template <typename T, int NB, int EPI>
-__global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs a) {
+template <typename T, int KW, int NB, int CPW, int EPI, bool NORM>
+__global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   typedef Mma<T> MT;
   typedef typename MT::frag frag;
-  constexpr int KW = 4, NT = KW * 64, VEC = MT::VEC, KC = MT::KC;
-  constexpr int BM = 64, BN = 16 * NB, MB = 4, CB = 4;
+  constexpr int NT = KW * 64, VEC = MT::VEC, KC = MT::KC;
+  constexpr int BM = 64, BN = 16 * NB, MB = 4;
   constexpr int LDR = BN + 4;
   constexpr int RED = KW * BM * LDR;
   __shared__ __attribute__((aligned(16))) float red[RED];
   __shared__ float s_mean[BM], s_rinv[BM];
   __shared__ int s_last;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntn = (a.N + BN - 1) / BN;
   const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
   const int tile = bid % ntn, split = bid / ntn;
   const int n0 = tile * BN;
   const int KCt = a.K / KC;
-  const int CPS = (KCt + a.splits - 1) / a.splits;
-  const int s_beg = split * CPS, s_end = min(KCt, s_beg + CPS);
-  const int CPW = (s_end - s_beg + KW - 1) / KW;
-  const int c_beg = s_beg + w * CPW, c_end = min(s_end, c_beg + CPW);
-  const int nbat = c_end > c_beg ? (c_end - c_beg + CB - 1) / CB : 0;
-  const int NBt = (a.N + 15) / 16;
+  const int c_beg = (split * KW + w) * CPW;   // this wave's chunks: [c_beg, c_beg + CPW) within K
 
-  long arow[MB];
+  FM_PHASE(0);
+  // activation fragments: lane l reads row 16 mb + l % 16, k run l / 16 of every chunk
+  const Rsrc ra = make_rsrc(a.A, a.a_bytes);
+  uint32_t aoff[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    // rows past M read row M-1: their products land in discarded output rows
-    const int r = min(16 * mb + (lane % 16), a.M - 1);
-    arow[mb] = (long)a_row(a, r) * a.lda;
+    const int r = 16 * mb + (lane % 16);
+    aoff[mb] = r < a.M ? (uint32_t)(((long)a_row(a, r) * a.lda + (lane / 16) * VEC) * sizeof(T)) : kOob;
   }
-  const T* Ab = (const T*)a.A + (lane / 16) * VEC;
-  const V16* Wf = (const V16*)a.W + lane;
+  // weight fragments: fragment (nb, c) is 1 KB at ((nb * KCt + c) * 64 + lane) * 16 bytes
+  const Rsrc rw = make_rsrc(a.W, a.w_bytes);
+  const uint32_t wbase = (uint32_t)((n0 / 16) * KCt * 1024 + lane * 16);
 
-  V16 ra0[CB][MB], rb0[CB][NB], ra1[CB][MB], rb1[CB][NB];
-  auto load_batch = [&](V16 (&ra)[CB][MB], V16 (&rb)[CB][NB], int bi) {
-    // unconditional loads (clamped addresses): chunks past the wave's range are zeroed
-    // on the weight side by select; columns past N land in discarded output columns
+  V16 ra_[CPW][MB], rb_[CPW][NB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int c = c_beg + bi * CB + cb;
-      const bool cok = c < c_end;
-      const int cc = cok ? c : c_beg;
+  for (int c = 0; c < CPW; ++c) {
+    const int cc = c_beg + c;
+    const bool cok = cc < KCt;   // uniform per wave
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) ra[cb][mb] = *(const V16*)(Ab + arow[mb] + (long)cc * KC);
+    for (int mb = 0; mb < MB; ++mb) ra_[c][mb] = bload16(ra, aoff[mb] + (uint32_t)(cc * KC * sizeof(T)));
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int nbg = min(n0 / 16 + nb, NBt - 1);
-        const V16 v = Wf[((long)nbg * KCt + cc) * 64];
-        rb[cb][nb] = cok ? v : vzero();
-      }
-    }
-  };
+    for (int nb = 0; nb < NB; ++nb) rb_[c][nb] = bload16(rw, cok ? wbase + (uint32_t)((nb * KCt + cc) * 1024) : kOob);
+  }
+  RowStats<BM, NT> st;
+  if constexpr (NORM) st.load(a, 0);
+  Epilogue<T, BM, BN, NT, EPI> ep;
+  ep.prefetch(a, 0, n0);
+  // all loads are in flight before the first MFMA waits on one (the scheduler would
+  // otherwise interleave them with the MFMAs and keep only a few outstanding)
+  __builtin_amdgcn_sched_barrier(0);
+  FM_PHASE(1);
+
   f32x4 acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute_batch = [&](const V16 (&ra)[CB][MB], const V16 (&rb)[CB][NB]) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+  for (int c = 0; c < CPW; ++c)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = MT::mma(__builtin_bit_cast(frag, ra[cb][mb]), __builtin_bit_cast(frag, rb[cb][nb]), acc[mb][nb]);
-  };
-
-  // statistic slots first, then two operand batches; the merge waits only for the slots
-  FM_PHASE(0);
-  RowStats<BM, NT> st;
-  st.load(a, 0);   // unconditional (zeros when there is no norm to fold)
-  if (nbat > 0) load_batch(ra0, rb0, 0);
-  if (nbat > 1) load_batch(ra1, rb1, 1);
-  FM_PHASE(1);
-  if (a.norm != NORM_NONE) st.merge(a, 0, s_mean, s_rinv);
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = MT::mma(__builtin_bit_cast(frag, ra_[c][mb]), __builtin_bit_cast(frag, rb_[c][nb]), acc[mb][nb]);
+  if constexpr (NORM) st.merge(a, 0, s_mean, s_rinv);
   FM_PHASE(2);
-  for (int bi = 0; bi < nbat; bi += 2) {
-    compute_batch(ra0, rb0);
-    if (bi + 2 < nbat) load_batch(ra0, rb0, bi + 2);
-    if (bi + 1 < nbat) {
-      compute_batch(ra1, rb1);
-      if (bi + 3 < nbat) load_batch(ra1, rb1, bi + 3);
-    }
-  }
 
-  FM_PHASE(3);
-  // wave partials -> LDS, summed in wave order into wave 0's region
+  // wave partials -> LDS, summed in wave order
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -600,13 +569,14 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs a) {
       for (int w2 = 0; w2 < KW; ++w2) part[q] += *(const f32x4*)(red + (w2 * BM + r) * LDR + c4 * 4);
     }
   }
-  FM_PHASE(4);
+  FM_PHASE(3);
   if (a.splits > 1) {
-    float* wst = a.ws + (long)tile * a.splits * BM * BN;
+    const Rsrc rws = make_rsrc(a.ws, a.ws_bytes);
+    const uint32_t tbase = (uint32_t)tile * (uint32_t)a.splits * (BM * BN * 4);
 #pragma unroll
     for (int q = 0; q < Q4; ++q) {
       const int i = tid + q * NT;
-      if (i < BM * BN / 4) st_dev(wst + (long)split * BM * BN + i * 4, part[q]);
+      if (i < BM * BN / 4) st_dev(rws, tbase + (uint32_t)split * (BM * BN * 4) + i * 16, part[q]);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -622,10 +592,8 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs a) {
       for (int s0 = 0; s0 < a.splits; s0 += 8) {
         f32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const f32x4 t4 = ld_dev(wst + (long)min(s0 + u, a.splits - 1) * BM * BN + i * 4);
-          v[u] = s0 + u < a.splits ? t4 : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int u = 0; u < 8; ++u)
+          v[u] = ld_dev(rws, s0 + u < a.splits ? tbase + (uint32_t)(s0 + u) * (BM * BN * 4) + i * 16 : kOob);
 #pragma unroll
         for (int u = 0; u < 8; ++u) sum += v[u];
       }
@@ -633,7 +601,7 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs a) {
     }
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  FM_PHASE(5);
+  FM_PHASE(4);
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < Q4; ++q) {
@@ -644,8 +612,8 @@ __global__ void __launch_bounds__(256) k_gemm_skinny(GemmArgs a) {
     }
   }
   __syncthreads();
-  epilogue_tile<T, BM, BN, NT, EPI>(a, red, LDR, 0, n0, s_mean, s_rinv);
-  FM_PHASE(6);
+  ep.apply(a, red, LDR, 0, n0, s_mean, s_rinv);
+  FM_PHASE(5);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -670,18 +638,44 @@ int gemm_num_tiles(const GemmArgs& a) {
 
 void gemm_plan(GemmArgs& a, int elem, int num_cus) {
   const int kq = elem == ET_BF16 ? 32 : 16;
+  const int esz = elem == ET_BF16 ? 2 : 4;
   if (a.M <= 64) {
-    // 16 or 32 columns per workgroup; split K over workgroups until the launch covers the
-    // chip, keeping at least 16 k-chunks (four per wave) per workgroup
+    // Weight streaming: pick the waves per workgroup (4 / 8), the column width (16 / 32),
+    // the chunks per wave (2 / 4 / 8, all loaded at once) and the k-split over workgroups
+    // that minimise a simple estimate: bytes each CU loads (activations are re-read by
+    // every column tile) at ~105 GB/s (4 waves) or ~125 GB/s (8 waves) per CU, plus the
+    // split-K exchange (a fixed round-trip cost and the last workgroup's reads of every
+    // partial). Residual epilogues need whole kStatCols-column slots (32 columns).
     a.kind = GEMM_SKINNY;
-    const int bn = (a.N / 32 >= num_cus) ? 32 : 16;
-    a.cfg = bn == 32 ? SK_N32 : SK_N16;
-    const int tiles = (a.N + bn - 1) / bn;
     const int kct = a.K / kq;
-    int splits = 1;
-    while (tiles * splits < num_cus && kct / (2 * splits) >= 16 && splits < 16) splits *= 2;
-    a.splits = splits;
-    a.k_split = ((kct + splits - 1) / splits) * kq;
+    double best = 1e30;
+    int bkw = 4, bnb = 1, bs = 1, bc = 8;
+    for (int kw = 4; kw <= 8; kw *= 2) {
+      if (kw == 8 && elem != ET_BF16) continue;
+      for (int nb = 1; nb <= 2; ++nb) {
+        if (a.epi == EPI_RESID && nb * 16 < kStatCols) continue;
+        if (elem != ET_BF16 && nb > 1 && a.epi != EPI_RESID) continue;
+        for (int cpw = 2; cpw <= 8; cpw *= 2) {
+          if ((nb == 2 || kw == 8) && cpw > 4) continue;   // register budget
+          const int per_wg = kw * cpw;
+          const int splits = (kct + per_wg - 1) / per_wg;
+          if (splits > 16) continue;
+          const int tiles = (a.N + 16 * nb - 1) / (16 * nb);
+          const int wgs = tiles * splits;
+          const double kb = (double)(16 * nb + a.M) * (per_wg * kq) * esz / 1024.0;   // KB per workgroup
+          const double per_cu = (double)((wgs + num_cus - 1) / num_cus) * kb;
+          const double bw = kw == 8 ? 125.0 : 105.0;   // KB per microsecond per CU
+          const double xchg = splits > 1 ? 2.0 + 0.02 * splits * (16 * nb * 64 * 4 / 1024.0) : 0.0;
+          const double est = per_cu / bw + xchg + 0.02 * cpw;
+          if (est < best) { best = est; bkw = kw; bnb = nb; bs = splits; bc = cpw; }
+        }
+      }
+    }
+    a.cfg = bnb == 2 ? SK_N32 : SK_N16;
+    a.cpw = bc;
+    a.kw = bkw;
+    a.splits = bs;
+    a.k_split = bkw * bc * kq;
     return;
   }
   a.kind = GEMM_TILED;
@@ -733,25 +727,80 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int NB>
-static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-  const dim3 grid(((a.N + 16 * NB - 1) / (16 * NB)) * a.splits), block(256);
-#define K_SKINNY(E) (k_gemm_skinny<T, NB, E>)
-  FM_EPI_SWITCH(K_SKINNY, grid, block)
-#undef K_SKINNY
+// Skinny instantiations: the residual epilogue never consumes a norm; the others can.
+template <typename T, int KW, int NB, int CPW>
+static hipError_t launch_skinny_cpw(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid(((a.N + 16 * NB - 1) / (16 * NB)) * a.splits), block(KW * 64);
+  const bool norm = a.norm != NORM_NONE;
+#define K_SK(E, NRM) hipLaunchKernelGGL((k_gemm_skinny<T, KW, NB, CPW, E, NRM>), grid, block, 0, s, a)
+  switch (a.epi) {
+    case EPI_STORE: if (norm) K_SK(EPI_STORE, true); else K_SK(EPI_STORE, false); break;
+    case EPI_GELU_MUL: if (norm) K_SK(EPI_GELU_MUL, true); else K_SK(EPI_GELU_MUL, false); break;
+    case EPI_QKV: if (norm) K_SK(EPI_QKV, true); else K_SK(EPI_QKV, false); break;
+    case EPI_EULER: if (norm) K_SK(EPI_EULER, true); else K_SK(EPI_EULER, false); break;
+    case EPI_RESID:
+      if constexpr ((16 * NB) % kStatCols == 0) {
+        if (norm) return hipErrorInvalidValue;
+        K_SK(EPI_RESID, false);
+      } else {
+        return hipErrorInvalidValue;
+      }
+      break;
+    case EPI_VT: if (norm) return hipErrorInvalidValue; K_SK(EPI_VT, false); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef K_SK
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_skinny_cfg(const GemmArgs& a, hipStream_t s) {
-  return a.cfg == SK_N32 ? launch_skinny<T, 2>(a, s) : launch_skinny<T, 1>(a, s);
+template <typename T, int KW, int NB>
+static hipError_t launch_skinny_nb(const GemmArgs& a, hipStream_t s) {
+  switch (a.cpw) {
+    case 2: return launch_skinny_cpw<T, KW, NB, 2>(a, s);
+    case 4: return launch_skinny_cpw<T, KW, NB, 4>(a, s);
+    case 8:
+      if constexpr (NB == 1 && KW == 4) return launch_skinny_cpw<T, KW, NB, 8>(a, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
 }
 
-hipError_t gemm_launch(const GemmArgs& a, int elem, hipStream_t s) {
-  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+template <typename T>
+static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (a.kw == 8) return a.cfg == SK_N32 ? launch_skinny_nb<T, 8, 2>(a, s) : launch_skinny_nb<T, 8, 1>(a, s);
+  }
+  if (a.kw != 4) return hipErrorInvalidValue;
+  return a.cfg == SK_N32 ? launch_skinny_nb<T, 4, 2>(a, s) : launch_skinny_nb<T, 4, 1>(a, s);
+}
+
+hipError_t gemm_launch(const GemmArgs& in, int elem, hipStream_t s) {
+  if (in.M <= 0 || in.N <= 0) return hipSuccess;
+  // absent optional vectors read the zeros (gate: ones) buffers; descriptor extents
+  GemmArgs a = in;
+  if (!a.zeros || !a.ones) return hipErrorInvalidValue;
+  if (!a.cvec) a.cvec = a.zeros;
+  if (!a.dvec) a.dvec = a.zeros;
+  if (!a.bias) a.bias = a.zeros;
+  if (!a.hscale) a.hscale = a.zeros;
+  if (!a.gate) a.gate = a.ones;
+  if (!a.rope_cs) a.rope_cs = (const float2*)a.zeros;
+  if (!a.x) a.x = const_cast<float*>(a.zeros);
+  if (!a.h) a.h = const_cast<float*>(a.zeros);
+  if (!a.stats) a.stats = (const float2*)a.zeros;
+  // every vector index stays below N + 4 (matrices: M rows of ldo / ldh_out)
+  const long vec_need = (long)a.N + 4;
+  if (vec_need > kVecPad || (long)a.M * std::max(a.ldo, a.ldh_out) + 4 > kVecPad * 64) return hipErrorInvalidValue;
+  const int esz = elem == ET_BF16 ? 2 : 4;
+  const long rows = (long)((a.M - 1) / a.row_group) * a.row_gstride + a.row_off + (a.M - 1) % a.row_group + 1;
+  const long a_bytes = rows * a.lda * esz;
+  const long w_bytes = (long)swizzled_bytes(a.N, a.K, elem);
+  const long ws_bytes = (long)gemm_ws_bytes(a);
+  if (a_bytes >= (1L << 31) || w_bytes >= (1L << 31) || ws_bytes >= (1L << 31)) return hipErrorInvalidValue;
+  a.a_bytes = (uint32_t)a_bytes; a.w_bytes = (uint32_t)w_bytes; a.ws_bytes = (uint32_t)ws_bytes;
   if (a.kind == GEMM_SKINNY) {
     if (a.M > 64) return hipErrorInvalidValue;
-    return elem == ET_BF16 ? launch_skinny_cfg<bf16>(a, s) : launch_skinny_cfg<float>(a, s);
+    return elem == ET_BF16 ? launch_skinny<bf16>(a, s) : launch_skinny<float>(a, s);
   }
   if (elem == ET_BF16) {
     switch (a.cfg) {

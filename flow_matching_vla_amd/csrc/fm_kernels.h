@@ -11,8 +11,10 @@ enum Act { ACT_NONE = 0, ACT_SILU = 1, ACT_GELU = 2 };
 enum NormKind { NORM_NONE = 0, NORM_RMS = 1, NORM_LN = 2 };
 
 // Columns per partial row-statistic slot written by the residual epilogue and the
-// in-projection, and read by the consumer GEMMs of the next modulated norm.
-constexpr int kStatCols = 16;
+// in-projection, and read by the consumer GEMMs of the next modulated norm. Statistics
+// are (mean, M2) float2 pairs laid out [row][slot]; hidden / kStatCols slots per row.
+constexpr int kStatCols = 32;
+constexpr int kMaxStatSlots = 64;   // hidden <= 2048
 
 // C[M x N] = A[M x K] * W^T, W stored fragment-major (see swizzle_weight).
 //
@@ -27,7 +29,8 @@ struct GemmArgs {
   const void* A; long lda;
   int row_group, row_gstride, row_off;
   // consumer side of a modulated norm (norm != NORM_NONE): per-row (mu, rinv) merged from
-  // stats [part][row] of the A rows; y = rinv (acc - mu d[n]) + c[n] (d only for LayerNorm)
+  // stats[row * stats_ld + slot] of the A rows (nparts slots of kStatCols columns);
+  // y = rinv (acc - mu d[n]) + c[n] (d only for LayerNorm)
   int norm;
   const float2* stats; int nparts; long stats_ld;
   const float* cvec; const float* dvec;
@@ -40,20 +43,30 @@ struct GemmArgs {
   // epilogue
   int epi;
   void* out; long ldo; const float* bias; int act; int out_f32;
-  // residual producer: h += gate * y; hs = T(h (1 + hscale)); stats of h per 64 columns
+  // residual producer: h += gate * y; hs = T(h (1 + hscale)); (mean, M2) of h per
+  // kStatCols columns at stats_out[row * stats_out_ld + n / kStatCols]
   float* h; long ldh_out; const float* gate; void* hs; const float* hscale; float2* stats_out; long stats_out_ld;
   int q_cols, kv_cols, tq, kv_off, rope, half_dh; const float2* rope_cs;
   void* kdst; long k_bs, k_rs; void* vdst; long v_bs, v_ds;
   float* x; float dt; float* vout;
   int vt_group; long vt_bs, vt_ds;
+  // Device buffers of at least kVecPad zeros / ones that the launcher substitutes for
+  // absent optional vectors (kernels never test pointers; an absent gate reads ones).
+  const float* zeros; const float* ones;
+  // byte extents of A, W and the split-K workspace, set by the launcher (each < 2^31: reads
+  // at or past them return zeros)
+  uint32_t a_bytes, w_bytes, ws_bytes;
   // launch shape chosen by the planner
   int kind;          // GEMM_SKINNY / GEMM_TILED
   int cfg;           // tile configuration of that kind
+  int cpw;           // skinny: k-chunks per wave
+  int kw;            // skinny: waves per workgroup (4 / 8)
 };
+constexpr long kVecPad = 1L << 18;   // floats in the zeros / ones buffers
 
 enum GemmKind { GEMM_SKINNY = 0, GEMM_TILED = 1 };
 enum GemmCfg { GEMM_64x64 = 0, GEMM_128x128 = 1, GEMM_32x64 = 2 };
-enum SkinnyCfg { SK_N16 = 0, SK_N32 = 1 };
+enum SkinnyCfg { SK_N16 = 0, SK_N32 = 1 };   // 16 * (cfg + 1) output columns per workgroup
 
 // Plan kernel, tile shape and split-K for an M x N x K problem.
 void gemm_plan(GemmArgs& a, int elem, int num_cus);
@@ -87,12 +100,13 @@ size_t swizzled_bytes(int N, int K, int elem);
 
 // h rows of the in-projection, with per-slot row statistics for the first norm.
 struct InProjArgs {
+  const float* zeros;                         // kVecPad zeros, read for absent tb / hscale / state_tok
   const float* x; int da;                     // x [B*Ha x da] fp32
   const void* w; const float* b;              // w [D x da] (T, row-major), bias fp32 [D]
   const float* tb;                            // per-step time bias fp32 [D] or null
   const float* state_tok;                     // [B*st x D] fp32 or null
   int B, Ha, st, D;                           // rows per request = st + Ha
-  float* h; float2* stats; long stats_ld;
+  float* h; float2* stats; long stats_ld;     // stats[row * stats_ld + slot], kStatCols columns per slot
   void* hs; const float* hscale;              // hs = T(h (1 + hscale)) (hscale may be null)
 };
 hipError_t inproj_launch(const InProjArgs& a, int elem, hipStream_t s);

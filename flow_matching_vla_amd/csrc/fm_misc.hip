@@ -6,10 +6,10 @@
 
 namespace fm {
 
-// Workgroup = 64 h rows x one 64-column statistic slot. The slot's weight rows and the
-// rows' inputs are staged in LDS with every global load issued up front; thread (row r,
-// 16-column group g) computes 16 outputs, stores them, and merges the slot's (mean, M2)
-// across the four lanes of its row.
+// Workgroup = 64 h rows x 64 columns. The columns' weight rows and the rows' inputs are
+// staged in LDS with every global load issued up front; thread (row r, 16-column group g)
+// computes 16 outputs, stores them, and merges (mean, M2) of each kStatCols-column slot
+// across the lanes of the row that share it.
 constexpr int kInMaxK = 64;
 template <typename T>
 __global__ void __launch_bounds__(256) k_inproj(InProjArgs a) {
@@ -49,9 +49,9 @@ __global__ void __launch_bounds__(256) k_inproj(InProjArgs a) {
     // unconditional loads; absent optional vectors read as zeros
     const int n = n0 + g * 16 + c;   // D is a multiple of 64: always in range
     const f32x4 bv = *(const f32x4*)(a.b + n);
-    const f32x4 tv = *(const f32x4*)(a.tb ? a.tb + n : g_zeros);
-    const f32x4 sv = *(const f32x4*)(a.hscale ? a.hscale + n : g_zeros);
-    const f32x4 stv = *(const f32x4*)(a.state_tok ? a.state_tok + (long)(b * a.st + tst) * a.D + n : g_zeros);
+    const f32x4 tv = *(const f32x4*)(a.tb + n);
+    const f32x4 sv = *(const f32x4*)(a.hscale + n);
+    const f32x4 stv = *(const f32x4*)(a.state_tok + (long)(b * a.st + tst) * a.D + n);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bias[c + j] = bv[j] + tv[j];
@@ -79,24 +79,38 @@ __global__ void __launch_bounds__(256) k_inproj(InProjArgs a) {
 #pragma unroll
       for (int c = 0; c < 16; ++c) hq[c] = from_f32<T>(y[c] * (1.f + hsc[c]));
     }
-    if (a.stats) {
-      // the thread's 16 columns are one statistic slot
-      float mean = 0.f;
+  }
+  if (a.stats) {   // uniform (kernel argument)
+    // (mean, M2) of the thread's 16 columns, merged with the other 16-column groups of the
+    // slot (adjacent lanes of the row); rows past the end still join the shuffles
+    static_assert(kStatCols % 16 == 0 && 64 % kStatCols == 0, "slot groups");
+    float mean = 0.f;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) mean += y[c];
-      mean *= (1.f / 16.f);
-      float m2 = 0.f;
+    for (int c = 0; c < 16; ++c) mean += y[c];
+    mean *= (1.f / 16.f);
+    float m2 = 0.f;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) m2 += (y[c] - mean) * (y[c] - mean);
-      a.stats[(long)((n0 + g * 16) / kStatCols) * a.stats_ld + hr] = make_float2(mean, m2);
+    for (int c = 0; c < 16; ++c) m2 += (y[c] - mean) * (y[c] - mean);
+#pragma unroll
+    for (int off = 1; off < kStatCols / 16; off <<= 1) {
+      const float mb = __shfl_xor(mean, off, 64), qb = __shfl_xor(m2, off, 64);
+      const float d = mb - mean;   // equal counts: merged mean is the average
+      m2 += qb + d * d * (float)(8 * off);
+      mean = 0.5f * (mean + mb);
     }
+    if (rok && (g % (kStatCols / 16)) == 0)
+      a.stats[(long)hr * a.stats_ld + (n0 + g * 16) / kStatCols] = make_float2(mean, m2);
   }
 }
 
-hipError_t inproj_launch(const InProjArgs& a, int elem, hipStream_t s) {
-  const int rows = a.B * (a.st + a.Ha);
+hipError_t inproj_launch(const InProjArgs& in, int elem, hipStream_t s) {
+  const int rows = in.B * (in.st + in.Ha);
   if (rows == 0) return hipSuccess;
-  if (a.da > kInMaxK || a.D % 64 != 0) return hipErrorInvalidValue;
+  if (in.da > kInMaxK || in.D % 64 != 0 || !in.zeros || (long)in.D + 4 > kVecPad) return hipErrorInvalidValue;
+  InProjArgs a = in;   // absent optional vectors read zeros
+  if (!a.tb) a.tb = a.zeros;
+  if (!a.hscale) a.hscale = a.zeros;
+  if (!a.state_tok) { a.state_tok = a.zeros; a.st = 0; }
   const dim3 grid(a.D / 64, (rows + 63) / 64);
   if (elem == ET_BF16) hipLaunchKernelGGL(k_inproj<bf16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_inproj<float>, grid, dim3(256), 0, s, a);
