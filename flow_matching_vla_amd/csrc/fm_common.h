@@ -82,11 +82,14 @@ template <> __device__ __forceinline__ V16 pack<bf16>(const float* in) {
 }
 __device__ __forceinline__ V16 vzero() { return V16{0u, 0u, 0u, 0u}; }
 
+// GELU, tanh form: 0.5 x (1 + tanh z) with z = sqrt(2/pi) (x + 0.044715 x^3), evaluated as
+// x / (1 + e^(-2z)) (the same function: 0.5 (1 + tanh z) = 1 / (1 + e^(-2z))), one
+// exponential and one division instead of a full tanh.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float c = 0.7978845608028654f;  // sqrt(2 / pi)
-  return 0.5f * x * (1.0f + tanhf(c * (x + 0.044715f * x * x * x)));
+  const float c2 = 1.5957691216057308f;  // 2 sqrt(2 / pi)
+  return x / (1.0f + __expf(-c2 * (x + 0.044715f * x * x * x)));
 }
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 // Sixteen zero bytes to read in place of an absent optional operand: kernels load from
 // (p ? p + i : g_zeros) unconditionally, because a load under a branch, even a uniform

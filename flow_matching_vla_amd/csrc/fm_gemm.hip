@@ -9,8 +9,10 @@
 
 #ifdef FM_PHASE_TIMING
 extern __device__ unsigned long long* g_phase;
-#define FM_PHASE(i) do { if (threadIdx.x == 0 && g_phase) g_phase[blockIdx.x * 8 + (i)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#define FM_PHASE_INIT unsigned long long* const fm_ph = g_phase
+#define FM_PHASE(i) do { if (threadIdx.x == 0 && fm_ph) fm_ph[blockIdx.x * 16 + (i)] = __builtin_amdgcn_s_memrealtime(); } while (0)
 #else
+#define FM_PHASE_INIT do { } while (0)
 #define FM_PHASE(i) do { } while (0)
 #endif
 
@@ -132,6 +134,19 @@ __device__ __forceinline__ f32x4 ld_dev(const Rsrc& r, uint32_t off) {
 // (bias, modulation vectors, residual, x, RoPE table) is loaded for all of the thread's
 // items before any is used.
 // ---------------------------------------------------------------------------------------
+// four / two consecutive outputs as one store (address aligned to its size)
+template <typename T> __device__ __forceinline__ void store4(T* o, const float* y);
+template <> __device__ __forceinline__ void store4<float>(float* o, const float* y) { *(f32x4*)o = f32x4{y[0], y[1], y[2], y[3]}; }
+template <> __device__ __forceinline__ void store4<bf16>(bf16* o, const float* y) {
+  *(bf16x4*)o = bf16x4{(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+}
+template <typename T> __device__ __forceinline__ void store2(T* o, float y0, float y1);
+template <> __device__ __forceinline__ void store2<float>(float* o, float y0, float y1) { *(float2*)o = make_float2(y0, y1); }
+template <> __device__ __forceinline__ void store2<bf16>(bf16* o, float y0, float y1) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  *(bf16x2*)o = bf16x2{(bf16)y0, (bf16)y1};
+}
+
 template <typename T, int BM, int BN, int NT, int EPI>
 struct Epilogue {
   static constexpr int C4 = BN / 4;
@@ -139,39 +154,49 @@ struct Epilogue {
   static constexpr int ITEMS = (TOT + NT - 1) / NT;
   static_assert(TOT % 64 == 0 && C4 % 4 == 0, "epilogue items");
   static_assert(EPI != EPI_RESID || BN % kStatCols == 0, "residual tiles cover whole statistic slots");
-  f32x4 pc[ITEMS], pd[ITEMS], p0[ITEMS], p1[ITEMS], p2[ITEMS];
+  static_assert(NT % C4 == 0, "every item of a thread is the same 4-column run");
+  // per-column inputs of the thread's column run (c, d, bias, gate, next scale) and the
+  // per-item row inputs (residual h, state x, RoPE cos/sin)
+  f32x4 pc, pd, pb, pg, ps;
+  f32x4 pr[ITEMS];
 
-  // the epilogue's global inputs for the thread's items (issued early by the caller)
-  __device__ __forceinline__ void prefetch(const GemmArgs& a, int m0, int n0) {
-  const int tid = threadIdx.x;
   // Loads use clamped indices and are unconditional (a divergent conditional load costs a
   // full memory round trip of its own); values outside the tile are never used. Per-column
-  // vectors (bias, c, d) are padded to a multiple of four floats by their owners, and the
-  // launcher has replaced every absent one by a zeros (gate: ones) buffer.
-  auto vec4 = [&](const float* p, long i) -> f32x4 { return *(const f32x4*)(p + i); };
-#pragma unroll
-  for (int q = 0; q < ITEMS; ++q) {
-    const int it = min(tid + q * NT, TOT - 1);
-    const int r = it / C4, c4 = it % C4;
-    const int mc = min(m0 + r, a.M - 1), n = min(n0 + c4 * 4, ((a.N - 1) / 4) * 4);
+  // vectors are padded to a multiple of four floats by their owners, and the launcher has
+  // replaced every absent one by a zeros (gate: ones) buffer.
+  static __device__ __forceinline__ f32x4 vec4(const float* p, long i) { return *(const f32x4*)(p + i); }
+
+  __device__ __forceinline__ void prefetch_cols(const GemmArgs& a, int n0) {
+    const int n = min(n0 + (int)(threadIdx.x % C4) * 4, ((a.N - 1) / 4) * 4);
     const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
-    pc[q] = z; pd[q] = z; p0[q] = z; p1[q] = z; p2[q] = z;
-    pc[q] = vec4(a.cvec, n);
-    pd[q] = vec4(a.dvec, n);
-    if constexpr (EPI == EPI_STORE || EPI == EPI_EULER) {
-      p0[q] = vec4(a.bias, n);
-      if constexpr (EPI == EPI_EULER) p1[q] = vec4(a.x, (long)mc * a.ldo + n);
-    } else if constexpr (EPI == EPI_RESID) {
-      p0[q] = vec4(a.h, (long)mc * a.ldh_out + n);
-      p1[q] = vec4(a.gate, n);
-      p2[q] = vec4(a.hscale, n);
-    } else if constexpr (EPI == EPI_QKV) {
-      const int nr = max(min(n, a.q_cols + a.kv_cols - 4), 0);
-      const int c = nr < a.q_cols ? nr : nr - a.q_cols;
-      const int jj = (c % max(2 * a.half_dh, 1)) / 2;   // even: pairs jj, jj + 1 are adjacent
-      p0[q] = vec4((const float*)a.rope_cs, 2L * ((long)(mc % a.tq) * a.half_dh + jj));
+    pc = vec4(a.cvec, n);
+    pd = vec4(a.dvec, n);
+    pb = z; pg = z; ps = z;
+    if constexpr (EPI == EPI_STORE || EPI == EPI_EULER) pb = vec4(a.bias, n);
+    if constexpr (EPI == EPI_RESID) { pg = vec4(a.gate, n); ps = vec4(a.hscale, n); }
+  }
+  __device__ __forceinline__ void prefetch_rows(const GemmArgs& a, int m0, int n0) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q) {
+      const int it = min(tid + q * NT, TOT - 1);
+      const int r = it / C4, c4 = it % C4;
+      const int mc = min(m0 + r, a.M - 1), n = min(n0 + c4 * 4, ((a.N - 1) / 4) * 4);
+      pr[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (EPI == EPI_EULER) pr[q] = vec4(a.x, (long)mc * a.ldo + n);
+      if constexpr (EPI == EPI_RESID) pr[q] = vec4(a.h, (long)mc * a.ldh_out + n);
+      if constexpr (EPI == EPI_QKV) {
+        const int nr = max(min(n, a.q_cols + a.kv_cols - 4), 0);
+        const int c = nr < a.q_cols ? nr : nr - a.q_cols;
+        const int jj = (c % max(2 * a.half_dh, 1)) / 2;   // even: pairs jj, jj + 1 are adjacent
+        pr[q] = vec4((const float*)a.rope_cs, 2L * ((long)(mc % a.tq) * a.half_dh + jj));
+      }
     }
   }
+  // the epilogue's global inputs for the thread's items (issued early by the caller)
+  __device__ __forceinline__ void prefetch(const GemmArgs& a, int m0, int n0) {
+    prefetch_cols(a, n0);
+    prefetch_rows(a, m0, n0);
   }
 
   // y from the fp32 tile C (row stride ldc), then the kind's transform and stores
@@ -189,16 +214,19 @@ struct Epilogue {
     f32x4 v = *(const f32x4*)(C + r * ldc + c4 * 4);
     if (consumer) {
       const float mu = s_mean[r], ri = s_rinv[r];
-      v = ri * (v - mu * pd[q]) + pc[q];   // absent c / d read as zeros
+      v = ri * (v - mu * pd) + pc;   // absent c / d read as zeros
     }
     if constexpr (EPI == EPI_STORE) {
       if (mok) {
         float y[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          y[j] = v[j] + p0[q][j];
-          if (a.act == ACT_SILU) y[j] = silu(y[j]);
-          else if (a.act == ACT_GELU) y[j] = gelu_tanh(y[j]);
+        for (int j = 0; j < 4; ++j) y[j] = v[j] + pb[j];
+        if (a.act == ACT_SILU) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = silu(y[j]);
+        } else if (a.act == ACT_GELU) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[j] = gelu_tanh(y[j]);
         }
         const long base = (long)m * a.ldo + n;
         if (a.out_f32) {
@@ -207,34 +235,36 @@ struct Epilogue {
           else for (int j = 0; j < 4; ++j) if (n + j < a.N) o[j] = y[j];
         } else {
           T* o = (T*)a.out + base;
-          for (int j = 0; j < 4; ++j) if (n + j < a.N) o[j] = from_f32<T>(y[j]);
+          if (n + 3 < a.N && (base & 3) == 0) store4<T>(o, y);
+          else for (int j = 0; j < 4; ++j) if (n + j < a.N) o[j] = from_f32<T>(y[j]);
         }
       }
     } else if constexpr (EPI == EPI_GELU_MUL) {
       // columns interleave (gate_f, up_f): outputs f = n / 2 and n / 2 + 1
       if (mok && n < a.N) {
         T* o = (T*)a.out + (long)m * a.ldo + n / 2;
-        o[0] = from_f32<T>(gelu_tanh(v[0]) * v[1]);
-        if (n + 2 < a.N) o[1] = from_f32<T>(gelu_tanh(v[2]) * v[3]);
+        const float g0 = gelu_tanh(v[0]) * v[1], g1 = gelu_tanh(v[2]) * v[3];
+        if (n + 2 < a.N && ((((long)m * a.ldo + n / 2) & 1) == 0)) store2<T>(o, g0, g1);
+        else {
+          o[0] = from_f32<T>(g0);
+          if (n + 2 < a.N) o[1] = from_f32<T>(g1);
+        }
       }
     } else if constexpr (EPI == EPI_QKV) {
       if (mok) {
         const int b = m / a.tq, i = m % a.tq;
         if (a.rope && n < a.q_cols + a.kv_cols) {
           const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
-          v[0] = x0 * p0[q][0] - x1 * p0[q][1];
-          v[1] = x1 * p0[q][0] + x0 * p0[q][1];
-          v[2] = x2 * p0[q][2] - x3 * p0[q][3];
-          v[3] = x3 * p0[q][2] + x2 * p0[q][3];
+          v[0] = x0 * pr[q][0] - x1 * pr[q][1];
+          v[1] = x1 * pr[q][0] + x0 * pr[q][1];
+          v[2] = x2 * pr[q][2] - x3 * pr[q][3];
+          v[3] = x3 * pr[q][2] + x2 * pr[q][3];
         }
+        const float y4[4] = {v[0], v[1], v[2], v[3]};
         if (n < a.q_cols) {
-          T* o = (T*)a.out + (long)m * a.ldo + n;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(v[j]);
+          store4<T>((T*)a.out + (long)m * a.ldo + n, y4);   // q_cols, ldo multiples of 4
         } else if (n < a.q_cols + a.kv_cols) {
-          T* o = (T*)a.kdst + (long)b * a.k_bs + (long)(a.kv_off + i) * a.k_rs + (n - a.q_cols);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(v[j]);
+          store4<T>((T*)a.kdst + (long)b * a.k_bs + (long)(a.kv_off + i) * a.k_rs + (n - a.q_cols), y4);
         } else if (n < a.N) {
           const int c = n - a.q_cols - a.kv_cols;
           T* o = (T*)a.vdst + (long)b * a.v_bs + vt_slot<T>(a.kv_off + i);
@@ -251,15 +281,13 @@ struct Epilogue {
     } else if constexpr (EPI == EPI_RESID) {
       // h += gate * y; hs = T(h (1 + next scale)); (mean, M2) of the kStatCols-column slot
       // (eight consecutive lanes of the row). N is a multiple of kStatCols here.
-      f32x4 hv = mok ? p0[q] + p1[q] * v : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 hv = mok ? pr[q] + pg * v : f32x4{0.f, 0.f, 0.f, 0.f};
       if (mok) {
         *(f32x4*)(a.h + (long)m * a.ldh_out + n) = hv;
         float hsv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hsv[j] = hv[j] * (1.f + p2[q][j]);
-        T* o = (T*)a.hs + (long)m * a.ldh_out + n;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = from_f32<T>(hsv[j]);
+        for (int j = 0; j < 4; ++j) hsv[j] = hv[j] * (1.f + ps[j]);
+        store4<T>((T*)a.hs + (long)m * a.ldh_out + n, hsv);   // ldh_out, n multiples of 4
       }
       // the slot's lanes hold four columns each: its mean is the mean of their sums, and
       // M2 the sum of their squared deviations from it (two reductions over the group)
@@ -274,10 +302,10 @@ struct Epilogue {
       if (mok) {
         for (int j = 0; j < 4; ++j) {
           if (n + j >= a.N) break;
-          const float vel = v[j] + p0[q][j];
+          const float vel = v[j] + pb[j];
           const long idx = (long)m * a.ldo + n + j;
           if (a.vout) a.vout[idx] = vel;
-          else a.x[idx] = p1[q][j] + a.dt * vel;
+          else a.x[idx] = pr[q][j] + a.dt * vel;
         }
       }
     }
@@ -470,6 +498,231 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Large-M kernel (bf16, K a multiple of 32): workgroup tile 256 x BN (BN = 128 or 256),
+// eight waves of (256 / WMW) x (BN / WNW), BK = 32 per stage. Both operand tiles are
+// copied global -> LDS by buffer-to-LDS DMA in fragment-major order (the weights are
+// stored that way; the activation fragments are gathered by the per-lane offsets of the
+// copy), as many stages deep as LDS holds (4 for BN 256, 6 for BN 128), so that the copies
+// of several stages cover the memory latency. Each stage's fragments are all read from
+// LDS before its MFMAs. Rows past M and columns past N read zeros. The epilogue runs in
+// 64-row slabs written straight from the accumulators; split-K (BN 128 only) exchanges the
+// whole tile as in the tiled kernel.
+// ---------------------------------------------------------------------------------------
+#define FM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+// Wait until at most EXTRA + pend * PER memory operations of this wave are in flight:
+// the operations issued after a stage's copies are EXTRA of its own plus PER for each of
+// the pend stages issued later (pend < NST <= 6).
+template <int PER, int EXTRA, int NST>
+__device__ __forceinline__ void wait_stages(int pend) {
+  static_assert(NST <= 6 && EXTRA + (NST - 1) * PER < 64, "vmcnt range");
+  switch (pend) {
+    case 5: if constexpr (NST > 5) { FM_WAIT_VM(EXTRA + 5 * PER); break; } [[fallthrough]];
+    case 4: if constexpr (NST > 4) { FM_WAIT_VM(EXTRA + 4 * PER); break; } [[fallthrough]];
+    case 3: if constexpr (NST > 3) { FM_WAIT_VM(EXTRA + 3 * PER); break; } [[fallthrough]];
+    case 2: if constexpr (NST > 2) { FM_WAIT_VM(EXTRA + 2 * PER); break; } [[fallthrough]];
+    case 1: FM_WAIT_VM(EXTRA + PER); break;
+    default: FM_WAIT_VM(EXTRA); break;
+  }
+}
+
+template <int BN, int WMW, int WNW, int EPI, bool NORM>
+__global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
+  typedef bf16 T;
+  typedef Mma<T> MT;
+  typedef typename MT::frag frag;
+  constexpr int NW = WMW * WNW, NT = NW * 64, VEC = MT::VEC, KC = MT::KC;
+  constexpr int BM = 256, BK = KC;
+  constexpr int RB = BM / 16, CB = BN / 16;
+  constexpr int FA = RB, FB = CB, FS = FA + FB;               // 1 KB fragments per stage
+  constexpr int LDS_BYTES = 144 * 1024;
+  constexpr int NST = LDS_BYTES / (FS * 1024) > 6 ? 6 : LDS_BYTES / (FS * 1024);
+  constexpr int FPW = FS / NW;
+  constexpr int WRB = RB / WMW, WCB = CB / WNW;               // wave tile in 16-blocks
+  constexpr int LDC = BN + 4;
+  constexpr bool WHOLE = BM * LDC * 4 <= NST * FS * 1024;     // whole fp32 tile fits in LDS
+  static_assert(FS % NW == 0 && RB % WMW == 0 && CB % WNW == 0 && NST >= 3, "layout");
+  static_assert(64 * LDC * 4 <= NST * FS * 1024, "slab fits");
+  __shared__ __attribute__((aligned(16))) V16 lds[NST * FS * 64];
+  __shared__ float s_mean[BM], s_rinv[BM];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WNW, wn = w % WNW;
+  const int ntn = (a.N + BN - 1) / BN, ntm = (a.M + BM - 1) / BM, tiles = ntn * ntm;
+  // The grid is padded to a multiple of 8, so each XCD (workgroup b runs on XCD b mod 8)
+  // takes a contiguous range of logical tiles; within a split, tiles are ordered in
+  // groups of 8 row tiles walked column by column, so the tiles an XCD runs together
+  // share a few weight column tiles and a few activation row tiles in its L2.
+  const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (bid >= tiles * a.splits) return;
+  const int split = bid / tiles, t = bid % tiles;
+  constexpr int GM = 8;
+  const int gfirst = (t / (GM * ntn)) * GM, gsz = min(ntm - gfirst, GM);
+  const int tm = gfirst + (t % (GM * ntn)) % gsz, tn = (t % (GM * ntn)) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KCt = a.K / KC;
+  const int kbeg = split * a.k_split;
+  const int kend = min(a.K, kbeg + a.k_split);
+  const int nks = (kend - kbeg) / BK;
+  FM_PHASE_INIT;
+  FM_PHASE(0);
+
+  // this wave's copies: fragments f = w FPW + i; f < FA: A row block f, else W column
+  // block f - FA. Per-copy lane offsets without the k part.
+  const V16 da = make_desc(a.A, a.a_bytes), dw = make_desc(a.W, a.w_bytes);
+  uint32_t coff[FPW];
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    const int f = w * FPW + i;
+    if (f < FA) {
+      const int r = m0 + f * 16 + (lane % 16);
+      coff[i] = r < a.M ? (uint32_t)(((long)a_row(a, r) * a.lda + (lane / 16) * VEC) * sizeof(T)) : kOob;
+    } else {
+      coff[i] = (uint32_t)((n0 / 16 + (f - FA)) * KCt * 1024 + lane * 16);
+    }
+  }
+  const uint32_t lds0 = lds_addr(lds) + (uint32_t)(w * FPW) * 1024u;
+  auto issue = [&](int k0, int st) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+      const int f = w * FPW + i;
+      const uint32_t dst = lds0 + (uint32_t)(st * FS + i) * 1024u;
+      if (f < FA) {   // uniform per wave
+        dma16_lds(da, dst, coff[i] == kOob ? kOob : coff[i] + (uint32_t)(k0 * sizeof(T)));
+      } else {
+        dma16_lds(dw, dst, coff[i] + (uint32_t)((k0 / KC) * 1024));
+      }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < nks) issue(kbeg + p * BK, p);
+  Epilogue<T, 64, BN, NT, EPI> ep0, ep1;   // slabs of 64 rows, row inputs double-buffered
+  ep0.prefetch_cols(a, n0);
+  if constexpr (NORM) {
+    // four 64-row slabs of (mu, rinv); waits here also complete the first stages
+    RowStats<64, NT> st;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      st.load(a, m0 + 64 * sl);
+      st.merge(a, m0 + 64 * sl, s_mean + 64 * sl, s_rinv + 64 * sl);
+    }
+  }
+
+  f32x4 acc[WRB][WCB];
+#pragma unroll
+  for (int i = 0; i < WRB; ++i)
+#pragma unroll
+    for (int j = 0; j < WCB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  FM_PHASE(1);
+
+  for (int ks = 0; ks < nks; ++ks) {
+    if (ks + NST - 1 < nks) issue(kbeg + (ks + NST - 1) * BK, (ks + NST - 1) % NST);
+    wait_stages<FPW, 0, NST>(min(NST - 1, nks - 1 - ks));   // stage ks has landed
+    __syncthreads();
+    if (ks < 8) FM_PHASE(2 + ks);
+    const V16* sA = lds + (ks % NST) * FS * 64;
+    const V16* sB = sA + FA * 64;
+    V16 af[WRB], bfr[WCB];
+#pragma unroll
+    for (int i = 0; i < WRB; ++i) af[i] = sA[(wm * WRB + i) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < WCB; ++j) bfr[j] = sB[(wn * WCB + j) * 64 + lane];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < WRB; ++i)
+#pragma unroll
+      for (int j = 0; j < WCB; ++j)
+        acc[i][j] = MT::mma(__builtin_bit_cast(frag, af[i]), __builtin_bit_cast(frag, bfr[j]), acc[i][j]);
+    __syncthreads();   // this stage is refilled by the next iteration's copies
+  }
+  FM_PHASE(10);
+  ep0.prefetch_rows(a, m0, n0);
+  ep1.pc = ep0.pc; ep1.pd = ep0.pd; ep1.pb = ep0.pb; ep1.pg = ep0.pg; ep1.ps = ep0.ps;
+  float* C = (float*)lds;
+
+  // accumulator rows of slab sl (4 row blocks) -> C rows [0, 64) (or the whole tile)
+  auto write_slab = [&](int sl, float* dst) {
+#pragma unroll
+    for (int i = 0; i < WRB; ++i) {
+      if ((wm * WRB + i) / 4 != sl) continue;   // uniform per wave
+      const int r0 = ((wm * WRB + i) % 4) * 16;
+#pragma unroll
+      for (int j = 0; j < WCB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dst[(r0 + 4 * (lane / 16) + e) * LDC + wn * WCB * 16 + j * 16 + (lane % 16)] = acc[i][j][e];
+    }
+  };
+
+  if constexpr (WHOLE) {
+    if (a.splits > 1) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) write_slab(sl, C + 64 * sl * LDC);
+      __syncthreads();
+      constexpr int Q4 = BM * BN / 4 / NT;
+      const Rsrc rws = make_rsrc(a.ws, a.ws_bytes);
+      const uint32_t tbase = (uint32_t)t * (uint32_t)a.splits * (BM * BN * 4);
+#pragma unroll 8
+      for (int q = 0; q < Q4; ++q) {
+        const int it = tid + q * NT;
+        const int r = it / (BN / 4), c4 = it % (BN / 4);
+        st_dev(rws, tbase + (uint32_t)split * (BM * BN * 4) + it * 16, *(const f32x4*)(C + r * LDC + c4 * 4));
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.splits - 1u;
+      __syncthreads();
+      if (!s_last) return;
+#pragma unroll 4
+      for (int q = 0; q < Q4; ++q) {
+        const int it = tid + q * NT;
+        const int r = it / (BN / 4), c4 = it % (BN / 4);
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = ld_dev(rws, u < a.splits ? tbase + (uint32_t)u * (BM * BN * 4) + it * 16 : kOob);
+        *(f32x4*)(C + r * LDC + c4 * 4) = (v[0] + v[1]) + (v[2] + v[3]);
+      }
+      if (tid == 0) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      FM_PHASE(12);
+#pragma unroll 1
+      for (int sl = 0; sl < 4; sl += 2) {
+        if (m0 + 64 * sl >= a.M) break;   // uniform
+        ep1.prefetch_rows(a, m0 + 64 * (sl + 1), n0);
+        ep0.apply(a, C + 64 * sl * LDC, LDC, m0 + 64 * sl, n0, s_mean + 64 * sl, s_rinv + 64 * sl);
+        if (m0 + 64 * (sl + 1) >= a.M) break;
+        if (sl + 2 < 4) ep0.prefetch_rows(a, m0 + 64 * (sl + 2), n0);
+        ep1.apply(a, C + 64 * (sl + 1) * LDC, LDC, m0 + 64 * (sl + 1), n0, s_mean + 64 * (sl + 1), s_rinv + 64 * (sl + 1));
+      }
+      FM_PHASE(11);
+      return;
+    }
+  }
+  // no split: slab by slab through one 64-row C buffer, the next slab's row inputs in flight
+  FM_PHASE(12);
+#pragma unroll 1
+  for (int sl = 0; sl < 4; sl += 2) {
+    if (m0 + 64 * sl >= a.M) break;   // uniform
+    write_slab(sl, C);
+    __syncthreads();
+    ep1.prefetch_rows(a, m0 + 64 * (sl + 1), n0);
+    ep0.apply(a, C, LDC, m0 + 64 * sl, n0, s_mean + 64 * sl, s_rinv + 64 * sl);
+    __syncthreads();
+    if (m0 + 64 * (sl + 1) >= a.M) break;
+    write_slab(sl + 1, C);
+    __syncthreads();
+    if (sl + 2 < 4) ep0.prefetch_rows(a, m0 + 64 * (sl + 2), n0);
+    ep1.apply(a, C, LDC, m0 + 64 * (sl + 1), n0, s_mean + 64 * (sl + 1), s_rinv + 64 * (sl + 1));
+    __syncthreads();
+  }
+  FM_PHASE(11);
+}
+
+// ---------------------------------------------------------------------------------------
 // Skinny kernel (M <= 64, the weight-streaming regime). A workgroup covers all rows and
 // 16*NB output columns over 1/splits of K; its KW waves split that range again into CPW
 // k-chunks each. Every wave issues all of its loads at once: the weight fragments
@@ -501,6 +754,7 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   const int KCt = a.K / KC;
   const int c_beg = (split * KW + w) * CPW;   // this wave's chunks: [c_beg, c_beg + CPW) within K
 
+  FM_PHASE_INIT;
   FM_PHASE(0);
   // activation fragments: lane l reads row 16 mb + l % 16, k run l / 16 of every chunk
   const Rsrc ra = make_rsrc(a.A, a.a_bytes);
@@ -632,6 +886,7 @@ static int skinny_bn(int cfg) { return cfg == SK_N32 ? 32 : 16; }
 
 int gemm_num_tiles(const GemmArgs& a) {
   if (a.kind == GEMM_SKINNY) return (a.N + skinny_bn(a.cfg) - 1) / skinny_bn(a.cfg);
+  if (a.kind == GEMM_BIG) return ((a.M + 255) / 256) * ((a.N + (a.cfg ? 255 : 127)) / (a.cfg ? 256 : 128));
   const CfgShape c = cfg_shape(a.cfg, ET_BF16);
   return ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
 }
@@ -678,6 +933,28 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
     a.k_split = bkw * bc * kq;
     return;
   }
+  if (elem == ET_BF16 && a.K % 32 == 0 && a.M >= 256) {
+    // 256 x 256 tiles (cfg 1) when they alone fill half the CUs; otherwise 256 x 128 tiles
+    // (cfg 0) with K split (up to 4 ways, at least 16 k-steps each) while the tiles fill
+    // less than three quarters of the CUs
+    a.kind = GEMM_BIG;
+    const int mt = (a.M + 255) / 256;
+    const int nks = a.K / 32;
+    if (mt * ((a.N + 255) / 256) * 2 >= num_cus) {
+      a.cfg = 1;
+      a.splits = 1;
+      a.k_split = a.K;
+      return;
+    }
+    a.cfg = 0;
+    const int tiles = mt * ((a.N + 127) / 128);
+    int splits = 1;
+    while (splits < 4 && tiles * splits * 4 < num_cus * 3 && nks / (2 * splits) >= 16) splits *= 2;
+    const int per = (nks + splits - 1) / splits;
+    a.splits = (nks + per - 1) / per;
+    a.k_split = per * 32;
+    return;
+  }
   a.kind = GEMM_TILED;
   if (elem == ET_BF16 && a.M >= 256 && a.N >= 512) a.cfg = GEMM_128x128;
   else a.cfg = GEMM_64x64;
@@ -700,6 +977,7 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
 
 size_t gemm_ws_bytes(const GemmArgs& a) {
   if (a.splits <= 1) return 0;
+  if (a.kind == GEMM_BIG) return (size_t)gemm_num_tiles(a) * a.splits * 256 * (a.cfg ? 256 : 128) * sizeof(float);
   if (a.kind == GEMM_SKINNY) return (size_t)gemm_num_tiles(a) * a.splits * 64 * skinny_bn(a.cfg) * sizeof(float);
   const CfgShape c = cfg_shape(a.cfg, ET_BF16);
   const int tiles = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
@@ -774,6 +1052,24 @@ static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   return a.cfg == SK_N32 ? launch_skinny_nb<T, 4, 2>(a, s) : launch_skinny_nb<T, 4, 1>(a, s);
 }
 
+template <int BN, int WMW, int WNW>
+static hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid((gemm_num_tiles(a) * a.splits + 7) / 8 * 8), block(WMW * WNW * 64);
+  const bool norm = a.norm != NORM_NONE;
+#define K_BIG(E, NRM) hipLaunchKernelGGL((k_gemm_big<BN, WMW, WNW, E, NRM>), grid, block, 0, s, a)
+  switch (a.epi) {
+    case EPI_STORE: if (norm) K_BIG(EPI_STORE, true); else K_BIG(EPI_STORE, false); break;
+    case EPI_GELU_MUL: if (norm) K_BIG(EPI_GELU_MUL, true); else K_BIG(EPI_GELU_MUL, false); break;
+    case EPI_QKV: if (norm) K_BIG(EPI_QKV, true); else K_BIG(EPI_QKV, false); break;
+    case EPI_EULER: if (norm) K_BIG(EPI_EULER, true); else K_BIG(EPI_EULER, false); break;
+    case EPI_RESID: if (norm) return hipErrorInvalidValue; K_BIG(EPI_RESID, false); break;
+    case EPI_VT: if (norm) return hipErrorInvalidValue; K_BIG(EPI_VT, false); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef K_BIG
+  return hipGetLastError();
+}
+
 hipError_t gemm_launch(const GemmArgs& in, int elem, hipStream_t s) {
   if (in.M <= 0 || in.N <= 0) return hipSuccess;
   // absent optional vectors read the zeros (gate: ones) buffers; descriptor extents
@@ -785,12 +1081,17 @@ hipError_t gemm_launch(const GemmArgs& in, int elem, hipStream_t s) {
   if (!a.hscale) a.hscale = a.zeros;
   if (!a.gate) a.gate = a.ones;
   if (!a.rope_cs) a.rope_cs = (const float2*)a.zeros;
-  if (!a.x) a.x = const_cast<float*>(a.zeros);
-  if (!a.h) a.h = const_cast<float*>(a.zeros);
+  // every vector index stays below N + 4; a substituted x / h is read over M rows
+  if ((long)a.N + 4 > kVecPad) return hipErrorInvalidValue;
+  if (!a.x) {
+    if (a.epi == EPI_EULER && (long)a.M * a.ldo + 4 > kVecPad) return hipErrorInvalidValue;
+    a.x = const_cast<float*>(a.zeros);
+  }
+  if (!a.h) {
+    if (a.epi == EPI_RESID) return hipErrorInvalidValue;
+    a.h = const_cast<float*>(a.zeros);
+  }
   if (!a.stats) a.stats = (const float2*)a.zeros;
-  // every vector index stays below N + 4 (matrices: M rows of ldo / ldh_out)
-  const long vec_need = (long)a.N + 4;
-  if (vec_need > kVecPad || (long)a.M * std::max(a.ldo, a.ldh_out) + 4 > kVecPad * 64) return hipErrorInvalidValue;
   const int esz = elem == ET_BF16 ? 2 : 4;
   const long rows = (long)((a.M - 1) / a.row_group) * a.row_gstride + a.row_off + (a.M - 1) % a.row_group + 1;
   const long a_bytes = rows * a.lda * esz;
@@ -801,6 +1102,10 @@ hipError_t gemm_launch(const GemmArgs& in, int elem, hipStream_t s) {
   if (a.kind == GEMM_SKINNY) {
     if (a.M > 64) return hipErrorInvalidValue;
     return elem == ET_BF16 ? launch_skinny<bf16>(a, s) : launch_skinny<float>(a, s);
+  }
+  if (a.kind == GEMM_BIG) {
+    if (elem != ET_BF16 || a.K % 32 != 0 || a.splits > 4 || (a.cfg == 1 && a.splits != 1)) return hipErrorInvalidValue;
+    return a.cfg == 1 ? launch_big<256, 2, 4>(a, s) : launch_big<128, 4, 2>(a, s);
   }
   if (elem == ET_BF16) {
     switch (a.cfg) {

@@ -64,7 +64,7 @@ struct GemmArgs {
 };
 constexpr long kVecPad = 1L << 18;   // floats in the zeros / ones buffers
 
-enum GemmKind { GEMM_SKINNY = 0, GEMM_TILED = 1 };
+enum GemmKind { GEMM_SKINNY = 0, GEMM_TILED = 1, GEMM_BIG = 2 };
 enum GemmCfg { GEMM_64x64 = 0, GEMM_128x128 = 1, GEMM_32x64 = 2 };
 enum SkinnyCfg { SK_N16 = 0, SK_N32 = 1 };   // 16 * (cfg + 1) output columns per workgroup
 
