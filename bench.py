@@ -3,14 +3,17 @@
 
 One bench step is one fm_denoise call: the whole T-step Euler loop of the action expert
 over one batch of seeded synthetic inputs already resident in HBM (weights, bound prefix
-K/V, x0), replayed as one hipGraph. The default workload is the pi0.5-shaped expert at
-batch 1, prefix 816, horizon 50, 10 Euler steps. Prints one JSON line.
+K/V, x0), run as one launch of the persistent loop kernel where it applies (batch x
+horizon <= 64 rows) or else replayed as one hipGraph of per-operation kernels. The default
+workload is the pi0.5-shaped expert at batch 1, prefix 816, horizon 50, 10 Euler steps.
+Prints one JSON line.
 
 Besides chunks/s it reports: a linear fit of latency over the step count T (the model
 latency P + T E of the vla.cpp paper, Sec. III-B Eq. (3)); the whole loop's algorithmic
-HBM rate; a roofline entry for the kernel role that takes the most time, timed with HIP
-events around each of its launches on the context stream; and the CPU oracle timed on the
-host cores on a bounded sample of the same workload.
+HBM rate; a roofline entry for the dominant kernel (the loop kernel's one launch, or the
+per-operation role that takes the most time), timed with HIP events around its launches on
+the context stream; and the CPU oracle timed on the host cores on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -209,8 +212,24 @@ def main():
         res["latency_fit"] = {"points_ms": [[int(t), round(l, 4)] for t, l in pts], "P_ms": round(float(P0), 4),
                               "E_us_per_step": round(float(E) * 1000, 2)}
         ctx.set_schedule(T, B)
-    # per-role kernel time inside the loop (eager launches with events on the context stream)
-    if not args.no_roles:
+    persistent, _ = ctx.loop_status()
+    res["loop_kernel"] = bool(persistent)
+    # kernel time inside the loop, with HIP events on the context stream: the loop kernel's
+    # single launch when it serves the workload, else each per-operation role (eager)
+    if not args.no_roles and persistent:
+        tot, nl = 0.0, 0
+        for _ in range(5):
+            m, n = fm.profile_loop(ctx, x0, T, "loop", out)
+            tot += m
+            nl += n
+        avg_s = tot / nl * 1e-3
+        nbytes, nflops = step_b * T, step_f * T
+        ach = nbytes / avg_s / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_loop",
+                           "alg_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2),
+                           "launches_per_chunk": 1, "mfma_TFLOPs": round(nflops / avg_s / 1e12, 2)}
+    if not args.no_roles and not persistent:
         roles = {}
         for r in ("inproj", "qkv", "attn", "oproj", "mlp_up", "mlp_down", "out"):
             ctx.denoise(x0, T, out)
@@ -223,6 +242,7 @@ def main():
             roles[r] = (tot / nl, nl // 3)
         res["roles_us_per_launch"] = {r: round(v[0] * 1000, 2) for r, v in roles.items()}
         dom = max(roles, key=lambda r: roles[r][0] * roles[r][1])
+        res["roofline_kernel_role"] = dom
         nbytes, nflops = role_bytes_flops(cfg, dom)
         avg_s = roles[dom][0] * 1e-3
         intensity = nflops / max(nbytes, 1)

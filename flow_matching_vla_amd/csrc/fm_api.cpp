@@ -13,6 +13,7 @@
 
 #include "../../include/fm.h"
 #include "fm_kernels.h"
+#include "fm_persist.h"
 
 using namespace fm;
 
@@ -176,6 +177,21 @@ struct fm_ctx {
   size_t ws_bytes = 0;
   unsigned* counters = nullptr;
   static constexpr int kCounters = 1 << 16;
+
+  // persistent loop kernel: per-step activation buffers (one set per step and layer, written
+  // once per launch), flag words, partial-result workspaces, per-step dt
+  int loop_mode = FM_LOOP_AUTO;
+  char* rot = nullptr;
+  size_t rot_bytes = 0;
+  uint32_t* pflags = nullptr;
+  float *pws_attn = nullptr, *pws_ml = nullptr, *pws_split = nullptr;
+  float* dts = nullptr;
+  uint32_t epoch = 0;
+  LoopArgs* loop_dev = nullptr;      // the loop description the kernel reads, and its host copy
+  LoopArgs loop_host;
+  bool loop_uploaded = false;
+  LayerW* lw_dev = nullptr;          // [n_layers] weight pointers
+  std::vector<LayerW> lw_host;
 
   // captured loop
   hipGraph_t graph = nullptr;
@@ -456,6 +472,129 @@ fm_status check_ready(fm_ctx* ctx) {
   return FM_OK;
 }
 
+// ---------------------------------------------------------------------------------------
+// Persistent loop kernel
+// ---------------------------------------------------------------------------------------
+LoopShape loop_shape(const fm_ctx* ctx) {
+  const fm_config& c = ctx->c;
+  LoopShape sh;
+  sh.dtype_bf16 = c.dtype == FM_BF16;
+  sh.B = ctx->bound_batch; sh.H = c.action_horizon; sh.M = sh.B * sh.H;
+  sh.D = c.hidden; sh.nq = c.n_heads; sh.dh = c.head_dim; sh.F = c.mlp_dim; sh.da = c.action_dim;
+  sh.L = c.n_layers; sh.P = ctx->prefix_len; sh.qd = c.n_heads * c.head_dim;
+  return sh;
+}
+
+// nullptr when the loop kernel serves the current weights / schedule / binding, else why not
+const char* loop_unsupported(const fm_ctx* ctx) {
+  const fm_config& c = ctx->c;
+  if (ctx->loop_mode != FM_LOOP_AUTO) return "loop mode is FM_LOOP_GRAPH";
+  if (c.arch != FM_ARCH_PREFIX_JOINT || !c.mlp_gated || c.n_kv_heads != 1) return "not a pi0.5-family expert";
+  if (!ctx->pflags) return "no loop-kernel workspace (bf16, head_dim 256 only)";
+  if (c.action_dim % 4 != 0) return "action_dim must be a multiple of 4";
+  if (ctx->steps < 1 || ctx->prefix_len < 0) return "no schedule or binding";
+  return loop_check(loop_shape(ctx), ctx->num_cus);
+}
+
+// byte layout of one (step, layer) set of activation buffers, each aligned to 4 KB so
+// that no cache line is shared by buffers written in different phases
+struct RotLayout { long o_hs, o_st, o_q, o_sk, o_svt, o_ao, o_hsu, o_stu, o_act, layer; int Hp; };
+RotLayout rot_layout(const fm_ctx* ctx) {
+  const fm_config& c = ctx->c;
+  const long M = (long)ctx->bound_batch * c.action_horizon, D = c.hidden, qd = (long)c.n_heads * c.head_dim;
+  const long dh = c.head_dim, F = c.mlp_dim, B = ctx->bound_batch;
+  RotLayout r;
+  r.Hp = (int)round_up(c.action_horizon, 32);
+  long off = 0;
+  auto put = [&](long bytes) { const long o = off; off += round_up(std::max(bytes, 1L), 4096); return o; };
+  r.o_hs = put(M * D * 2);
+  r.o_st = put(M * (D / 16) * 4);
+  r.o_q = put(M * qd * 2);
+  r.o_sk = put(B * r.Hp * dh * 2);
+  r.o_svt = put(B * dh * r.Hp * 2);
+  r.o_ao = put(M * qd * 2);
+  r.o_hsu = put(M * D * 2);
+  r.o_stu = put(M * (D / 16) * 4);
+  r.o_act = put(M * F * 2);
+  r.layer = off;
+  return r;
+}
+
+// the activation buffers for `steps` steps of the current binding
+fm_status loop_buffers(fm_ctx* ctx, int steps) {
+  const RotLayout r = rot_layout(ctx);
+  const size_t need = (size_t)steps * (ctx->c.n_layers + 1) * r.layer;
+  if (need <= ctx->rot_bytes) return FM_OK;
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  dfree(ctx, ctx->rot);
+  ctx->rot = nullptr;
+  ctx->rot_bytes = 0;
+  void* p;
+  fm_status s = dalloc(ctx, &p, need);
+  if (s != FM_OK) return s;
+  ctx->rot = (char*)p;
+  ctx->rot_bytes = need;
+  return FM_OK;
+}
+
+// one launch of the loop kernel: steps k0 .. k0 + nsteps - 1 on ctx->x (or, with vout, the
+// velocity of step k0 without the update)
+fm_status loop_run(fm_ctx* ctx, int k0, int nsteps, float* vout) {
+  const fm_config& c = ctx->c;
+  fm_status s = loop_buffers(ctx, ctx->steps);
+  if (s != FM_OK) return s;
+  const RotLayout r = rot_layout(ctx);
+  LoopArgs a;
+  memset(&a, 0, sizeof a);
+  a.B = ctx->bound_batch; a.H = c.action_horizon; a.M = a.B * a.H; a.D = c.hidden; a.nq = c.n_heads;
+  a.dh = c.head_dim; a.F = c.mlp_dim; a.da = c.action_dim; a.L = c.n_layers; a.P = ctx->prefix_len; a.cap = ctx->cap;
+  a.qd = a.nq * a.dh; a.nqkv = a.qd + 2 * a.dh; a.Hp = r.Hp; a.S = n_sites(c); a.csum = ctx->csum;
+  a.cq4 = (int)round_up(a.nqkv, 4); a.cg4 = (int)round_up(2 * a.F, 4); a.cout4 = (int)round_up(a.da, 4);
+  a.eps = c.norm_eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)a.dh));
+  a.rope = c.rope_base > 0.f;
+  a.RT = (a.nq * a.H + 63) / 64; a.TP = (a.P + 31) / 32; a.TS = (a.H + 31) / 32; a.SA = (a.TP + a.TS + 1) / 2;
+  a.max_steps = std::max(c.max_steps, 1); a.dts = ctx->dts;
+  a.w_in = ctx->w_in; a.b_in = ctx->b_in; a.w_out = ctx->w_out; a.b_out = ctx->b_out;
+  std::vector<LayerW> lw(c.n_layers);
+  for (int l = 0; l < c.n_layers; ++l) lw[l] = LayerW{ctx->L[l].qkv, ctx->L[l].o, ctx->L[l].gu, ctx->L[l].down};
+  a.lw = ctx->lw_dev;
+  a.wb_qkv = (uint32_t)swizzled_bytes(a.nqkv, a.D, ET_BF16);
+  a.wb_o = (uint32_t)swizzled_bytes(a.D, a.qd, ET_BF16);
+  a.wb_gu = (uint32_t)swizzled_bytes(2 * a.F, a.D, ET_BF16);
+  a.wb_down = (uint32_t)swizzled_bytes(a.D, a.F, ET_BF16);
+  a.wb_out = (uint32_t)swizzled_bytes(a.da, a.D, ET_BF16);
+  a.table = ctx->table; a.cbuf = ctx->cbuf; a.rope_cs = ctx->rope_cs;
+  a.x = ctx->x; a.h = ctx->h;
+  a.pool = (const __bf16*)ctx->pool; a.plane = (long)c.max_batch * ctx->cap * c.head_dim;
+  a.rot = ctx->rot; a.rot_layer = r.layer; a.rot_step = (long)(c.n_layers + 1) * r.layer;
+  a.o_hs = r.o_hs; a.o_st = r.o_st; a.o_q = r.o_q; a.o_sk = r.o_sk; a.o_svt = r.o_svt; a.o_ao = r.o_ao;
+  a.o_hsu = r.o_hsu; a.o_stu = r.o_stu; a.o_act = r.o_act;
+  a.ws_attn = ctx->pws_attn; a.ws_attn_ml = ctx->pws_ml; a.ws_split = ctx->pws_split;
+  a.flags = ctx->pflags;
+  // the description lives in device memory; it is uploaded again only when it changed
+  if (!ctx->loop_uploaded || memcmp(&a, &ctx->loop_host, sizeof a) != 0 || lw.size() != ctx->lw_host.size() ||
+      memcmp(lw.data(), ctx->lw_host.data(), lw.size() * sizeof(LayerW)) != 0) {
+    HIPCK(hipStreamSynchronize(ctx->stream));
+    ctx->loop_host = a;
+    ctx->lw_host = lw;
+    HIPCK(hipMemcpy(ctx->loop_dev, &ctx->loop_host, sizeof a, hipMemcpyHostToDevice));
+    HIPCK(hipMemcpy(ctx->lw_dev, ctx->lw_host.data(), lw.size() * sizeof(LayerW), hipMemcpyHostToDevice));
+    ctx->loop_uploaded = true;
+  }
+  LaunchArgs la;
+  la.k0 = k0; la.nsteps = nsteps; la.vout = vout;
+  const uint32_t nbar = (uint32_t)loop_barriers(c.n_layers, nsteps);
+  if (ctx->epoch > 0xf0000000u - nbar) {
+    // epochs only grow within a flag generation: start a new one
+    HIPCK(hipMemsetAsync(ctx->pflags, 0, kFlagWords * sizeof(uint32_t), ctx->stream));
+    ctx->epoch = 0;
+  }
+  la.e0 = ctx->epoch;
+  ctx->epoch += nbar;
+  HIPCK(loop_launch(ctx->loop_dev, la, ctx->num_cus, ctx->stream));
+  return FM_OK;
+}
+
 }  // namespace
 
 // =======================================================================================
@@ -576,6 +715,15 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
     ALLOC(dff, (size_t)c.n_layers * F * 4, float*);
   }
   ALLOC(counters, fm_ctx::kCounters * sizeof(unsigned), unsigned*);
+  if (c.arch == FM_ARCH_PREFIX_JOINT && c.dtype == FM_BF16 && c.head_dim == 256) {
+    ALLOC(pflags, kFlagWords * sizeof(uint32_t), uint32_t*);
+    ALLOC(pws_attn, (size_t)kMaxAttnItems * 64 * 256 * sizeof(float), float*);
+    ALLOC(pws_ml, (size_t)kMaxAttnItems * 64 * 2 * sizeof(float), float*);
+    ALLOC(pws_split, (size_t)kMaxSplitItems * 64 * 16 * sizeof(float), float*);
+    ALLOC(dts, (size_t)std::max(c.max_steps, 1) * sizeof(float), float*);
+    ALLOC(loop_dev, sizeof(LoopArgs), LoopArgs*);
+    ALLOC(lw_dev, (size_t)c.n_layers * sizeof(LayerW), LayerW*);
+  }
   if (c.arch == FM_ARCH_PREFIX_JOINT) {
     ctx->cap = pool_capacity(c);
     ALLOC(pool, (size_t)c.n_layers * 2 * B * ctx->cap * c.head_dim * esz, void*);
@@ -597,6 +745,7 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
   if (e == hipSuccess) e = hipMemsetAsync(ctx->zeros, 0, kVecPad * sizeof(float), ctx->stream);
   if (e == hipSuccess) e = fill_f32(ctx->ones, 1.f, kVecPad, ctx->stream);
   if (e == hipSuccess) e = hipMemsetAsync(ctx->stats, 0, ((D / kStatCols) * rows + 2 * kMaxStatSlots) * sizeof(float2), ctx->stream);
+  if (e == hipSuccess && ctx->pflags) e = hipMemsetAsync(ctx->pflags, 0, kFlagWords * sizeof(uint32_t), ctx->stream);
   if (e == hipSuccess && ctx->pool) e = hipMemsetAsync(ctx->pool, 0, (size_t)c.n_layers * 2 * B * ctx->cap * c.head_dim * esz, ctx->stream);
   if (e == hipSuccess && ctx->vtself) e = hipMemsetAsync(ctx->vtself, 0, B * D * ctx->tpad * esz, ctx->stream);
   if (e == hipSuccess && ctx->cross_vt) e = hipMemsetAsync(ctx->cross_vt, 0, ((c.n_layers + 1) / 2) * B * D * ctx->spad * esz, ctx->stream);
@@ -807,6 +956,11 @@ fm_status fm_set_schedule(fm_ctx* ctx, int32_t steps, int32_t batch, const float
   ctx->steps = steps;
   ctx->sched_batch = batch;
   if (steps == 0) return FM_OK;
+  if (ctx->dts) {
+    std::vector<float> dts(steps);
+    for (int k = 0; k < steps; ++k) dts[k] = tau[k + 1] - tau[k];
+    HIPCK(hipMemcpyAsync(ctx->dts, dts.data(), dts.size() * sizeof(float), hipMemcpyHostToDevice, ctx->stream));
+  }
   const int D = c.hidden, S = n_sites(c), T = steps;
   // sinusoidal time embedding of tau_0..tau_{T-1}, evaluated in double on the host:
   // [sin(2 pi tau / p_j)] ++ [cos(2 pi tau / p_j)], periods geometric from 4e-3 to 4
@@ -991,6 +1145,12 @@ fm_status fm_denoise(fm_ctx* ctx, const float* x0, int32_t steps, float* out) {
     if (out != x0) HIPCK(hipMemcpyAsync(out, x0, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
     return FM_OK;
   }
+  if (!loop_unsupported(ctx)) {
+    HIPCK(hipMemcpyAsync(ctx->x, x0, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+    if ((s = loop_run(ctx, 0, steps, nullptr)) != FM_OK) return s;
+    HIPCK(hipMemcpyAsync(out, ctx->x, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+    return FM_OK;
+  }
   if (!ctx->graph_valid && (s = capture_loop(ctx)) != FM_OK) return s;
   HIPCK(hipMemcpyAsync(ctx->x, x0, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
   HIPCK(hipGraphLaunch(ctx->gexec, ctx->stream));
@@ -1004,6 +1164,10 @@ static fm_status step_eager(fm_ctx* ctx, const float* xin, int32_t k, float* v, 
   if (!xin || !v) return fail(ctx, FM_ERR_INVALID_ARG, "x / v is NULL");
   if (k < 0 || k >= ctx->steps) return fail(ctx, FM_ERR_SCHEDULE, fmt("step %d outside the scheduled [0, %d)", k, ctx->steps));
   const size_t xbytes = (size_t)ctx->bound_batch * ctx->c.action_horizon * ctx->c.action_dim * sizeof(float);
+  if (!trace && !loop_unsupported(ctx)) {
+    HIPCK(hipMemcpyAsync(ctx->x, xin, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+    return loop_run(ctx, k, 1, v);
+  }
   std::vector<Op> ops = build_step(ctx, k, v, trace);
   if ((s = plan_ops(ctx, ops)) != FM_OK) return s;
   HIPCK(hipMemcpyAsync(ctx->x, xin, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
@@ -1026,11 +1190,32 @@ fm_status fm_profile_loop(fm_ctx* ctx, const float* x0, int32_t steps, float* ou
   if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
   fm_status s = check_ready(ctx);
   if (s != FM_OK) return s;
-  if (!x0 || !out || !ms || !launches || role < FM_OP_INPROJ || role > FM_OP_OUT)
+  if (!x0 || !out || !ms || !launches || role < FM_OP_INPROJ || role > FM_OP_LOOP)
     return fail(ctx, FM_ERR_INVALID_ARG, "fm_profile_loop: bad arguments");
   if (steps != ctx->steps || steps < 1)
     return fail(ctx, FM_ERR_SCHEDULE, fmt("steps %d differs from the scheduled %d", steps, ctx->steps));
   const size_t xbytes = (size_t)ctx->bound_batch * ctx->c.action_horizon * ctx->c.action_dim * sizeof(float);
+  if (role == FM_OP_LOOP) {
+    const char* why = loop_unsupported(ctx);
+    if (why) return fail(ctx, FM_ERR_UNSUPPORTED, fmt("the loop kernel does not serve this loop: %s", why));
+    hipEvent_t e0, e1;
+    HIPCK(hipEventCreate(&e0));
+    HIPCK(hipEventCreate(&e1));
+    HIPCK(hipMemcpyAsync(ctx->x, x0, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+    if ((s = loop_buffers(ctx, ctx->steps)) != FM_OK) return s;
+    HIPCK(hipEventRecord(e0, ctx->stream));
+    if ((s = loop_run(ctx, 0, steps, nullptr)) != FM_OK) return s;
+    HIPCK(hipEventRecord(e1, ctx->stream));
+    HIPCK(hipMemcpyAsync(out, ctx->x, xbytes, hipMemcpyDeviceToDevice, ctx->stream));
+    HIPCK(hipStreamSynchronize(ctx->stream));
+    float e = 0;
+    HIPCK(hipEventElapsedTime(&e, e0, e1));
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    *ms = e;
+    *launches = 1;
+    return FM_OK;
+  }
   std::vector<std::vector<Op>> all;
   size_t count = 0;
   for (int k = 0; k < steps; ++k) {
@@ -1061,6 +1246,29 @@ fm_status fm_profile_loop(fm_ctx* ctx, const float* x0, int32_t steps, float* ou
   for (auto& e : ev) (void)hipEventDestroy(e);
   *ms = (float)tot;
   *launches = (int32_t)count;
+  return FM_OK;
+}
+
+fm_status fm_set_loop_mode(fm_ctx* ctx, int32_t mode) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (mode != FM_LOOP_AUTO && mode != FM_LOOP_GRAPH) return fail(ctx, FM_ERR_INVALID_ARG, fmt("loop mode %d", mode));
+  ctx->loop_mode = mode;
+  return FM_OK;
+}
+
+fm_status fm_loop_status(fm_ctx* ctx, int32_t* persistent, uint32_t* fault) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  if (persistent) *persistent = (ctx->loaded && !loop_unsupported(ctx)) ? 1 : 0;
+  uint32_t f = 0;
+  if (ctx->pflags) HIPCK(hipMemcpy(&f, ctx->pflags + kFlagErr, sizeof f, hipMemcpyDeviceToHost));
+  if (fault) *fault = f;
+  if (f != 0) {
+    (void)hipMemset(ctx->pflags, 0, kFlagWords * sizeof(uint32_t));
+    ctx->epoch = 0;
+    return fail(ctx, FM_ERR_DEVICE, fmt("loop kernel: a grid-barrier wait expired (fault word %u)", f));
+  }
   return FM_OK;
 }
 

@@ -71,6 +71,8 @@ def lib():
         "fm_step_velocity": ([VP, VP, I32, VP], I32),
         "fm_step_trace": ([VP, VP, I32, VP, VP], I32),
         "fm_profile_loop": ([VP, VP, I32, VP, I32, P(C.c_float), P(I32)], I32),
+        "fm_set_loop_mode": ([VP, I32], I32),
+        "fm_loop_status": ([VP, P(I32), P(C.c_uint32)], I32),
         "fm_op_linear": ([I32, I32, I32, I32, VP, VP, VP, I32, VP, I32, VP], I32),
         "fm_op_attention": ([I32, I32, I32, I32, I32, I32, I32, VP, VP, VP, VP, VP], I32),
     }
@@ -225,6 +227,16 @@ class Context:
         _check(lib().fm_step_velocity(self.h, _ptr(x), k, _ptr(v)), self.h)
         return v
 
+    def set_loop_mode(self, mode: int):
+        """LOOP_AUTO: the persistent loop kernel where it applies; LOOP_GRAPH: per-op graph."""
+        _check(lib().fm_set_loop_mode(self.h, mode), self.h)
+
+    def loop_status(self):
+        """(persistent kernel serves the loop, fault word); raises FMError on a fault."""
+        p, f = C.c_int32(), C.c_uint32()
+        _check(lib().fm_loop_status(self.h, C.byref(p), C.byref(f)), self.h)
+        return bool(p.value), f.value
+
     def step_trace(self, x, k: int):
         torch = _torch()
         c = self.cfg
@@ -235,7 +247,8 @@ class Context:
         return v, tr
 
 
-OP_ROLES = {"inproj": 0, "qkv": 1, "attn": 2, "oproj": 3, "mlp_up": 4, "mlp_down": 5, "out": 6}
+OP_ROLES = {"inproj": 0, "qkv": 1, "attn": 2, "oproj": 3, "mlp_up": 4, "mlp_down": 5, "out": 6, "loop": 7}
+LOOP_AUTO, LOOP_GRAPH = 0, 1
 
 
 def profile_loop(ctx: "Context", x0, steps: int, role: str, out=None):

@@ -153,13 +153,18 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t prefix_len, cons
 /* Run the whole Euler loop: out_dev = X^T for X^0 = x0_dev. Both are DEVICE fp32 buffers
  * [batch, H, d_a] (the bound batch); out_dev may equal x0_dev. steps must equal the
  * scheduled step count (FM_ERR_SCHEDULE otherwise), and the scheduled batch must equal the
- * bound batch; steps == 0 copies x0 to out. The T steps replay as one captured hipGraph,
- * built on the first call after a schedule, bind or load changed the loop. */
+ * bound batch; steps == 0 copies x0 to out. Where the loop kernel applies (see
+ * fm_set_loop_mode) the T steps run inside ONE cooperative launch of one workgroup per CU;
+ * otherwise they replay as one captured hipGraph of per-operation kernels, built on the
+ * first call after a schedule, bind or load changed the loop. The first loop-kernel call
+ * after a schedule or bind allocates its per-step activation buffers. */
 fm_status fm_denoise(fm_ctx* ctx, const float* x0_dev, int32_t steps, float* out_dev);
 
 /* One step's velocity v(X, tau_k) without the Euler update (pi0.5 Design: the action
  * component returns the velocity), for teacher-forced checks: x_dev, v_dev DEVICE fp32
- * [batch, H, d_a]; 0 <= k < scheduled steps. Runs eagerly on the context stream. */
+ * [batch, H, d_a]; 0 <= k < scheduled steps. Runs on the context stream with the same
+ * implementation fm_denoise uses (one loop-kernel launch of one step, or the per-operation
+ * kernels launched eagerly). */
 fm_status fm_step_velocity(fm_ctx* ctx, const float* x_dev, int32_t k, float* v_dev);
 
 /* Like fm_step_velocity, and also copies the fp32 residual stream after the in-projection
@@ -176,13 +181,33 @@ enum {
   FM_OP_OPROJ = 3,    /* output projection + gated residual */
   FM_OP_MLP_UP = 4,   /* modulated norm + gate/up (or FF1) + GELU */
   FM_OP_MLP_DOWN = 5, /* down (or FF2) projection + residual */
-  FM_OP_OUT = 6       /* final modulated norm + velocity projection + Euler update */
+  FM_OP_OUT = 6,      /* final modulated norm + velocity projection + Euler update */
+  FM_OP_LOOP = 7      /* the single launch of the loop kernel (all roles of all steps) */
 };
+
+/* Implementation of fm_denoise / fm_step_velocity.
+ * FM_LOOP_AUTO: the persistent loop kernel wherever it applies - bf16 pi0.5-family expert
+ *   (PREFIX_JOINT, one K/V head, gated MLP) with head_dim 256, batch * H <= 64 action rows,
+ *   and every phase within two work items per CU - and the per-operation graph elsewhere.
+ * FM_LOOP_GRAPH: always the captured graph of per-operation kernels.
+ * Both compute the same function (reduction orders differ). Default FM_LOOP_AUTO.
+ * FM_ERR_INVALID_ARG for another mode. */
+enum { FM_LOOP_AUTO = 0, FM_LOOP_GRAPH = 1 };
+fm_status fm_set_loop_mode(fm_ctx* ctx, int32_t mode);
+
+/* Synchronize the context stream. *persistent = 1 when the loop kernel serves the current
+ * weights, schedule and binding (0 otherwise). *fault is the loop kernel's fault word: 0,
+ * or nonzero when one of its bounded grid-barrier waits expired since the last query (its
+ * results are then invalid; the context is poisoned and FM_ERR_DEVICE is returned). Either
+ * pointer may be NULL. */
+fm_status fm_loop_status(fm_ctx* ctx, int32_t* persistent, uint32_t* fault);
 
 /* Run the same loop as fm_denoise, eagerly, with a hipEvent pair on the context stream
  * around every launch of `role`; returns the summed duration in *ms (milliseconds) and
  * the number of those launches in *launches. Synchronizes the context stream. Arguments
- * and results as fm_denoise (steps must be the scheduled count, >= 1). For measurement. */
+ * and results as fm_denoise (steps must be the scheduled count, >= 1). For measurement.
+ * FM_OP_LOOP times the loop kernel's one launch (FM_ERR_UNSUPPORTED when it does not
+ * serve the current loop); the per-role values time the per-operation kernels. */
 fm_status fm_profile_loop(fm_ctx* ctx, const float* x0_dev, int32_t steps, float* out_dev, int32_t role, float* ms,
                           int32_t* launches);
 
