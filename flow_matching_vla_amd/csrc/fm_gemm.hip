@@ -617,10 +617,13 @@ __global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
     for (int j = 0; j < WCB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   FM_PHASE(1);
 
+  // One barrier per stage: it makes stage ks visible to every wave and also proves that
+  // every wave has finished reading stage ks - 1, whose buffer the copies issued right after
+  // it refill (with stage ks + NST - 1).
   for (int ks = 0; ks < nks; ++ks) {
-    if (ks + NST - 1 < nks) issue(kbeg + (ks + NST - 1) * BK, (ks + NST - 1) % NST);
-    wait_stages<FPW, 0, NST>(min(NST - 1, nks - 1 - ks));   // stage ks has landed
+    wait_stages<FPW, 0, NST>(min(NST - 2, nks - 1 - ks));   // stage ks has landed
     __syncthreads();
+    if (ks + NST - 1 < nks) issue(kbeg + (ks + NST - 1) * BK, (ks + NST - 1) % NST);
     if (ks < 8) FM_PHASE(2 + ks);
     const V16* sA = lds + (ks % NST) * FS * 64;
     const V16* sB = sA + FA * 64;
@@ -635,8 +638,8 @@ __global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < WCB; ++j)
         acc[i][j] = MT::mma(__builtin_bit_cast(frag, af[i]), __builtin_bit_cast(frag, bfr[j]), acc[i][j]);
-    __syncthreads();   // this stage is refilled by the next iteration's copies
   }
+  __syncthreads();   // every wave is done with the operand stages (the epilogue reuses LDS)
   FM_PHASE(10);
   ep0.prefetch_rows(a, m0, n0);
   ep1.pc = ep0.pc; ep1.pd = ep0.pd; ep1.pb = ep0.pb; ep1.pg = ep0.pg; ep1.ps = ep0.ps;
@@ -940,7 +943,20 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
     a.kind = GEMM_BIG;
     const int mt = (a.M + 255) / 256;
     const int nks = a.K / 32;
-    if (mt * ((a.N + 255) / 256) * 2 >= num_cus) {
+    const int tiles1 = mt * ((a.N + 255) / 256);
+    if (tiles1 * 2 >= num_cus) {
+      // 256 x 256 tiles, unless they leave most of their last round of CUs idle while
+      // 128 x 128 tiles (the tiled kernel, two workgroups per CU) fit in a single round:
+      // measured at M 3200, N 2560, K 1024, 47 us against 85 us
+      const int rounds1 = (tiles1 + num_cus - 1) / num_cus;
+      const int tiles_t = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+      if (tiles1 < 0.6 * rounds1 * num_cus && tiles_t <= 2 * num_cus) {
+        a.kind = GEMM_TILED;
+        a.cfg = GEMM_128x128;
+        a.splits = 1;
+        a.k_split = a.K;
+        return;
+      }
       a.cfg = 1;
       a.splits = 1;
       a.k_split = a.K;
