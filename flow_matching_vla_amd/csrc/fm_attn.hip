@@ -27,11 +27,11 @@ extern __device__ unsigned long long* g_phase;
 namespace fm {
 
 constexpr int kKeyTile = 32;
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 8;
 constexpr int kAttnRows = 16 * kAttnWaves;   // query rows per workgroup
 constexpr int kMaxAttnSplits = 16;
 
-constexpr int kAttnStages = 2;                 // LDS tile buffers (tiles in flight + 1); 64 KB: two workgroups per CU
+constexpr int kAttnStages = 4;                 // LDS tile buffers (tiles in flight + 1)
 
 // s_waitcnt with vmcnt <= n (n < 64) and the other counters left alone (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14])
