@@ -10,7 +10,7 @@
 #ifdef FM_PHASE_TIMING
 extern __device__ unsigned long long* g_phase;
 #define FM_PHASE_INIT unsigned long long* const fm_ph = g_phase
-#define FM_PHASE(i) do { if (threadIdx.x == 0 && fm_ph) fm_ph[blockIdx.x * 16 + (i)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#define FM_PHASE(i) do { if (threadIdx.x == 0 && fm_ph) ((__attribute__((address_space(1))) unsigned long long*)fm_ph)[blockIdx.x * 16 + (i)] = __builtin_amdgcn_s_memrealtime(); } while (0)
 #else
 #define FM_PHASE_INIT do { } while (0)
 #define FM_PHASE(i) do { } while (0)
@@ -147,6 +147,10 @@ template <> __device__ __forceinline__ void store2<bf16>(bf16* o, float y0, floa
   *(bf16x2*)o = bf16x2{(bf16)y0, (bf16)y1};
 }
 
+// Wait until at most n vector-memory operations of this wave are in flight. Issued through
+// the compiler's own intrinsic, so its wait tracking knows every older load has landed.
+#define FM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
 template <typename T, int BM, int BN, int NT, int EPI>
 struct Epilogue {
   static constexpr int C4 = BN / 4;
@@ -198,6 +202,12 @@ struct Epilogue {
     prefetch_cols(a, n0);
     prefetch_rows(a, m0, n0);
   }
+  // Land every prefetched input before the first store. On gfx9 one counter covers loads
+  // and stores, so a value loaded before a store can only be waited for together with that
+  // store; and the per-item branches keep the compiler from proving that an input has
+  // already landed, so without this it waits (stores included) before every item.
+  static constexpr bool ROWS = EPI == EPI_RESID || EPI == EPI_QKV || EPI == EPI_EULER;
+  static __device__ __forceinline__ void settle() { FM_WAIT_VM(0); }
 
   // y from the fp32 tile C (row stride ldc), then the kind's transform and stores
   __device__ __forceinline__ void apply(const GemmArgs& a, const float* C, int ldc, int m0, int n0,
@@ -494,21 +504,23 @@ __global__ void __launch_bounds__(WM* WN * 64) k_gemm(GemmArgs a) {
   }
   Epilogue<T, BM, BN, NT, EPI> ep;
   ep.prefetch(a, m0, n0);
+  ep.settle();
   ep.apply(a, C, LDC, m0, n0, s_mean, s_rinv);
 }
 
 // ---------------------------------------------------------------------------------------
-// Large-M kernel (bf16, K a multiple of 32): workgroup tile 256 x BN (BN = 128 or 256),
-// eight waves of (256 / WMW) x (BN / WNW), BK = 32 per stage. Both operand tiles are
+// Large-M kernel (bf16, K a multiple of 32): workgroup tile BM x BN (BM, BN = 128 or 256),
+// WMW x WNW waves of (BM / WMW) x (BN / WNW), BK = 32 per stage. Both operand tiles are
 // copied global -> LDS by buffer-to-LDS DMA in fragment-major order (the weights are
 // stored that way; the activation fragments are gathered by the per-lane offsets of the
-// copy), as many stages deep as LDS holds (4 for BN 256, 6 for BN 128), so that the copies
-// of several stages cover the memory latency. Each stage's fragments are all read from
-// LDS before its MFMAs. Rows past M and columns past N read zeros. The epilogue runs in
-// 64-row slabs written straight from the accumulators; split-K (BN 128 only) exchanges the
-// whole tile as in the tiled kernel.
+// copy), as many stages deep as the LDS budget holds (144 KB: one workgroup per CU; 64 KB
+// for 128 x 128 tiles: two workgroups per CU, so that one's epilogue overlaps the other's
+// main loop), so that the copies of several stages cover the memory latency. Each stage's
+// fragments are all read from LDS before its MFMAs. Rows past M and columns past N read
+// zeros. The epilogue runs in 64-row slabs written straight from the accumulators; split-K
+// (every shape whose fp32 tile fits in the LDS budget, i.e. all but 256 x 256) exchanges
+// the whole tile as in the tiled kernel.
 // ---------------------------------------------------------------------------------------
-#define FM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
 // Wait until at most EXTRA + pend * PER memory operations of this wave are in flight:
 // the operations issued after a stage's copies are EXTRA of its own plus PER for each of
@@ -526,24 +538,38 @@ __device__ __forceinline__ void wait_stages(int pend) {
   }
 }
 
-template <int BN, int WMW, int WNW, int EPI, bool NORM>
-__global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
+template <int BM, int BN>
+struct BigShape {
+  static constexpr bool PAIR = BM == 128 && BN == 128;        // two workgroups per CU
+  static constexpr int FS = BM / 16 + BN / 16;                // 1 KB fragments per stage
+  static constexpr int BUDGET = (PAIR ? 64 : 144) * 1024;
+  static constexpr int NST = BUDGET / (FS * 1024) > 6 ? 6 : BUDGET / (FS * 1024);
+  static constexpr int LDC = BN + 4;
+  static constexpr int OPS = NST * FS * 1024;                 // operand stages
+  static constexpr int TILE = BM * LDC * 4;                   // the whole fp32 tile
+  static constexpr bool WHOLE = TILE <= (PAIR ? 70 * 1024 : BUDGET);
+  static constexpr int BYTES = WHOLE && TILE > OPS ? TILE : OPS;
+};
+
+template <int BM, int BN, int WMW, int WNW, int EPI, bool NORM>
+__global__ void __launch_bounds__(WMW * WNW * 64, (BM == 128 && BN == 128) ? 2 : 1) k_gemm_big(GemmArgs a) {
   typedef bf16 T;
   typedef Mma<T> MT;
   typedef typename MT::frag frag;
+  typedef BigShape<BM, BN> SH;
   constexpr int NW = WMW * WNW, NT = NW * 64, VEC = MT::VEC, KC = MT::KC;
-  constexpr int BM = 256, BK = KC;
+  constexpr int BK = KC;
   constexpr int RB = BM / 16, CB = BN / 16;
   constexpr int FA = RB, FB = CB, FS = FA + FB;               // 1 KB fragments per stage
-  constexpr int LDS_BYTES = 144 * 1024;
-  constexpr int NST = LDS_BYTES / (FS * 1024) > 6 ? 6 : LDS_BYTES / (FS * 1024);
+  constexpr int NST = SH::NST;
   constexpr int FPW = FS / NW;
   constexpr int WRB = RB / WMW, WCB = CB / WNW;               // wave tile in 16-blocks
-  constexpr int LDC = BN + 4;
-  constexpr bool WHOLE = BM * LDC * 4 <= NST * FS * 1024;     // whole fp32 tile fits in LDS
+  constexpr int LDC = SH::LDC;
+  constexpr int NSL = BM / 64;                                // 64-row epilogue slabs
+  constexpr bool WHOLE = SH::WHOLE;                           // whole fp32 tile fits in LDS
   static_assert(FS % NW == 0 && RB % WMW == 0 && CB % WNW == 0 && NST >= 3, "layout");
-  static_assert(64 * LDC * 4 <= NST * FS * 1024, "slab fits");
-  __shared__ __attribute__((aligned(16))) V16 lds[NST * FS * 64];
+  static_assert(64 * LDC * 4 <= SH::BYTES && (NSL % 2) == 0, "slab fits");
+  __shared__ __attribute__((aligned(16))) V16 lds[SH::BYTES / 16];
   __shared__ float s_mean[BM], s_rinv[BM];
   __shared__ int s_last;
 
@@ -598,13 +624,13 @@ __global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
     if (p < nks) issue(kbeg + p * BK, p);
-  Epilogue<T, 64, BN, NT, EPI> ep0, ep1;   // slabs of 64 rows, row inputs double-buffered
+  Epilogue<T, 64, BN, NT, EPI> ep0;   // per-column inputs, loaded before the main loop
   ep0.prefetch_cols(a, n0);
   if constexpr (NORM) {
-    // four 64-row slabs of (mu, rinv); waits here also complete the first stages
+    // 64-row slabs of (mu, rinv); waits here also complete the first stages
     RowStats<64, NT> st;
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
+    for (int sl = 0; sl < NSL; ++sl) {
       st.load(a, m0 + 64 * sl);
       st.merge(a, m0 + 64 * sl, s_mean + 64 * sl, s_rinv + 64 * sl);
     }
@@ -619,7 +645,9 @@ __global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
 
   // One barrier per stage: it makes stage ks visible to every wave and also proves that
   // every wave has finished reading stage ks - 1, whose buffer the copies issued right after
-  // it refill (with stage ks + NST - 1).
+  // it refill (with stage ks + NST - 1). (Reading the next stage's fragments during this
+  // stage's MFMAs measured 2-7% slower: the stage time is set by the copies, not by the
+  // LDS reads.)
   for (int ks = 0; ks < nks; ++ks) {
     wait_stages<FPW, 0, NST>(min(NST - 2, nks - 1 - ks));   // stage ks has landed
     __syncthreads();
@@ -641,9 +669,23 @@ __global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
   }
   __syncthreads();   // every wave is done with the operand stages (the epilogue reuses LDS)
   FM_PHASE(10);
-  ep0.prefetch_rows(a, m0, n0);
-  ep1.pc = ep0.pc; ep1.pd = ep0.pd; ep1.pb = ep0.pb; ep1.pg = ep0.pg; ep1.ps = ep0.ps;
   float* C = (float*)lds;
+  typedef Epilogue<T, 64, BN, NT, EPI> EP;
+  // Row inputs (residual h, state x, RoPE cos/sin) of every slab are loaded before the
+  // first store when they fit in 16 VGPR quads per thread; otherwise slab by slab.
+  constexpr bool ALL = EP::ROWS && NSL * EP::ITEMS <= 16;
+  constexpr int NEP = ALL ? NSL : 1;
+  EP ep[NEP];
+  ep[0].pc = ep0.pc; ep[0].pd = ep0.pd; ep[0].pb = ep0.pb; ep[0].pg = ep0.pg; ep[0].ps = ep0.ps;
+#pragma unroll
+  for (int e = 1; e < NEP; ++e) {
+    ep[e].pc = ep0.pc; ep[e].pd = ep0.pd; ep[e].pb = ep0.pb; ep[e].pg = ep0.pg; ep[e].ps = ep0.ps;
+  }
+  if constexpr (ALL) {
+#pragma unroll
+    for (int e = 0; e < NEP; ++e) ep[e].prefetch_rows(a, m0 + 64 * e, n0);
+  }
+  EP::settle();   // no store of this workgroup is in flight yet
 
   // accumulator rows of slab sl (4 row blocks) -> C rows [0, 64) (or the whole tile)
   auto write_slab = [&](int sl, float* dst) {
@@ -658,11 +700,23 @@ __global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
           dst[(r0 + 4 * (lane / 16) + e) * LDC + wn * WCB * 16 + j * 16 + (lane % 16)] = acc[i][j][e];
     }
   };
+  // the epilogue of slab sl whose fp32 rows are at Cs
+  auto apply_slab = [&](int sl, const float* Cs) {
+    if constexpr (ALL) {
+      ep[sl].apply(a, Cs, LDC, m0 + 64 * sl, n0, s_mean + 64 * sl, s_rinv + 64 * sl);
+    } else {
+      if constexpr (EP::ROWS) {
+        ep[0].prefetch_rows(a, m0 + 64 * sl, n0);
+        EP::settle();   // also waits for the previous slab's stores
+      }
+      ep[0].apply(a, Cs, LDC, m0 + 64 * sl, n0, s_mean + 64 * sl, s_rinv + 64 * sl);
+    }
+  };
 
   if constexpr (WHOLE) {
     if (a.splits > 1) {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) write_slab(sl, C + 64 * sl * LDC);
+      for (int sl = 0; sl < NSL; ++sl) write_slab(sl, C + 64 * sl * LDC);
       __syncthreads();
       constexpr int Q4 = BM * BN / 4 / NT;
       const Rsrc rws = make_rsrc(a.ws, a.ws_bytes);
@@ -679,48 +733,39 @@ __global__ void __launch_bounds__(WMW * WNW * 64) k_gemm_big(GemmArgs a) {
         s_last = __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.splits - 1u;
       __syncthreads();
       if (!s_last) return;
-#pragma unroll 4
+#pragma unroll 2
       for (int q = 0; q < Q4; ++q) {
         const int it = tid + q * NT;
         const int r = it / (BN / 4), c4 = it % (BN / 4);
-        f32x4 v[4];
+        f32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
           v[u] = ld_dev(rws, u < a.splits ? tbase + (uint32_t)u * (BM * BN * 4) + it * 16 : kOob);
-        *(f32x4*)(C + r * LDC + c4 * 4) = (v[0] + v[1]) + (v[2] + v[3]);
+        *(f32x4*)(C + r * LDC + c4 * 4) = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
       }
       if (tid == 0) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       FM_PHASE(12);
-#pragma unroll 1
-      for (int sl = 0; sl < 4; sl += 2) {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
         if (m0 + 64 * sl >= a.M) break;   // uniform
-        ep1.prefetch_rows(a, m0 + 64 * (sl + 1), n0);
-        ep0.apply(a, C + 64 * sl * LDC, LDC, m0 + 64 * sl, n0, s_mean + 64 * sl, s_rinv + 64 * sl);
-        if (m0 + 64 * (sl + 1) >= a.M) break;
-        if (sl + 2 < 4) ep0.prefetch_rows(a, m0 + 64 * (sl + 2), n0);
-        ep1.apply(a, C + 64 * (sl + 1) * LDC, LDC, m0 + 64 * (sl + 1), n0, s_mean + 64 * (sl + 1), s_rinv + 64 * (sl + 1));
+        apply_slab(sl, C + 64 * sl * LDC);
       }
       FM_PHASE(11);
       return;
     }
   }
-  // no split: slab by slab through one 64-row C buffer, the next slab's row inputs in flight
+  // no split: slab by slab through one 64-row C buffer
   FM_PHASE(12);
-#pragma unroll 1
-  for (int sl = 0; sl < 4; sl += 2) {
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl) {
     if (m0 + 64 * sl >= a.M) break;   // uniform
     write_slab(sl, C);
     __syncthreads();
-    ep1.prefetch_rows(a, m0 + 64 * (sl + 1), n0);
-    ep0.apply(a, C, LDC, m0 + 64 * sl, n0, s_mean + 64 * sl, s_rinv + 64 * sl);
+    if (sl == 0) FM_PHASE(13);
+    apply_slab(sl, C);
     __syncthreads();
-    if (m0 + 64 * (sl + 1) >= a.M) break;
-    write_slab(sl + 1, C);
-    __syncthreads();
-    if (sl + 2 < 4) ep0.prefetch_rows(a, m0 + 64 * (sl + 2), n0);
-    ep1.apply(a, C, LDC, m0 + 64 * (sl + 1), n0, s_mean + 64 * (sl + 1), s_rinv + 64 * (sl + 1));
-    __syncthreads();
+    if (sl == 0) FM_PHASE(14);
   }
   FM_PHASE(11);
 }
@@ -869,6 +914,7 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     }
   }
   __syncthreads();
+  ep.settle();
   ep.apply(a, red, LDR, 0, n0, s_mean, s_rinv);
   FM_PHASE(5);
 }
@@ -887,9 +933,13 @@ static CfgShape cfg_shape(int cfg, int elem) {
 }
 static int skinny_bn(int cfg) { return cfg == SK_N32 ? 32 : 16; }
 
+// large-M tile shapes: cfg bit 0 selects BN 256 (else 128), bit 1 BM 128 (else 256)
+static int big_bm(int cfg) { return cfg & 2 ? 128 : 256; }
+static int big_bn(int cfg) { return cfg & 1 ? 256 : 128; }
+
 int gemm_num_tiles(const GemmArgs& a) {
   if (a.kind == GEMM_SKINNY) return (a.N + skinny_bn(a.cfg) - 1) / skinny_bn(a.cfg);
-  if (a.kind == GEMM_BIG) return ((a.M + 255) / 256) * ((a.N + (a.cfg ? 255 : 127)) / (a.cfg ? 256 : 128));
+  if (a.kind == GEMM_BIG) return ((a.M + big_bm(a.cfg) - 1) / big_bm(a.cfg)) * ((a.N + big_bn(a.cfg) - 1) / big_bn(a.cfg));
   const CfgShape c = cfg_shape(a.cfg, ET_BF16);
   return ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
 }
@@ -936,37 +986,45 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
     a.k_split = bkw * bc * kq;
     return;
   }
-  if (elem == ET_BF16 && a.K % 32 == 0 && a.M >= 256) {
-    // 256 x 256 tiles (cfg 1) when they alone fill half the CUs; otherwise 256 x 128 tiles
-    // (cfg 0) with K split (up to 4 ways, at least 16 k-steps each) while the tiles fill
-    // less than three quarters of the CUs
+  if (elem == ET_BF16 && a.K % 32 == 0) {
+    // Large-M kernel: the tile shape and K split with the lowest estimated time. Per
+    // workgroup: a fixed start (first copies, row statistics), k-stages of 32 at a
+    // per-shape cost, and the epilogue; rounds of workgroups over the CUs (two per CU for
+    // 128 x 128 tiles, whose stages then run slower); a split adds the last arriver's reads
+    // of every partial tile and the partial traffic through HBM. Constants measured on
+    // MI355X at M = 400 and 3200 (the pick is within 4% of the fastest measured choice at
+    // every expert GEMM shape).
     a.kind = GEMM_BIG;
-    const int mt = (a.M + 255) / 256;
     const int nks = a.K / 32;
-    const int tiles1 = mt * ((a.N + 255) / 256);
-    if (tiles1 * 2 >= num_cus) {
-      // 256 x 256 tiles, unless they leave most of their last round of CUs idle while
-      // 128 x 128 tiles (the tiled kernel, two workgroups per CU) fit in a single round:
-      // measured at M 3200, N 2560, K 1024, 47 us against 85 us
-      const int rounds1 = (tiles1 + num_cus - 1) / num_cus;
-      const int tiles_t = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-      if (tiles1 < 0.6 * rounds1 * num_cus && tiles_t <= 2 * num_cus) {
-        a.kind = GEMM_TILED;
-        a.cfg = GEMM_128x128;
-        a.splits = 1;
-        a.k_split = a.K;
-        return;
+    double best = 1e30;
+    int bc = 0, bs = 1;
+    for (int cfg = 0; cfg < 4; ++cfg) {
+      const int bm = big_bm(cfg), bn = big_bn(cfg);
+      const bool pair = cfg == 2;
+      const long tiles = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+      static const double kStage[4] = {0.57, 0.95, 0.41, 0.53};
+      static const double kStart[4] = {2.8, 2.6, 1.8, 2.4};
+      static const double kEpi[4] = {4.3, 9.8, 3.8, 4.0};
+      for (int sp = 1; sp <= 8; sp *= 2) {
+        if (sp > 1 && cfg == 1) break;           // the 256 x 256 fp32 tile does not fit in LDS
+        if (nks / sp < 4) break;
+        const int per = (nks + sp - 1) / sp;
+        const int splits = (nks + per - 1) / per;
+        if (splits != sp) continue;
+        const long items = tiles * splits;
+        const long slots = (long)num_cus * (pair ? 2 : 1);
+        const long rounds = (items + slots - 1) / slots;
+        const double st = pair && items > num_cus ? 0.60 : kStage[cfg];
+        double est = (double)rounds * (kStart[cfg] + per * st + kEpi[cfg]);
+        if (splits > 1) {
+          const double part = (double)bm * bn * 4;
+          est += 3.0 + 1.5 * splits * part / 65536.0 + (double)tiles * splits * part * 2.0 / 4.0e6;
+        }
+        if (est < best) { best = est; bc = cfg; bs = splits; }
       }
-      a.cfg = 1;
-      a.splits = 1;
-      a.k_split = a.K;
-      return;
     }
-    a.cfg = 0;
-    const int tiles = mt * ((a.N + 127) / 128);
-    int splits = 1;
-    while (splits < 4 && tiles * splits * 4 < num_cus * 3 && nks / (2 * splits) >= 16) splits *= 2;
-    const int per = (nks + splits - 1) / splits;
+    a.cfg = bc;
+    const int per = (nks + bs - 1) / bs;
     a.splits = (nks + per - 1) / per;
     a.k_split = per * 32;
     return;
@@ -993,7 +1051,7 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
 
 size_t gemm_ws_bytes(const GemmArgs& a) {
   if (a.splits <= 1) return 0;
-  if (a.kind == GEMM_BIG) return (size_t)gemm_num_tiles(a) * a.splits * 256 * (a.cfg ? 256 : 128) * sizeof(float);
+  if (a.kind == GEMM_BIG) return (size_t)gemm_num_tiles(a) * a.splits * big_bm(a.cfg) * big_bn(a.cfg) * sizeof(float);
   if (a.kind == GEMM_SKINNY) return (size_t)gemm_num_tiles(a) * a.splits * 64 * skinny_bn(a.cfg) * sizeof(float);
   const CfgShape c = cfg_shape(a.cfg, ET_BF16);
   const int tiles = ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
@@ -1068,11 +1126,12 @@ static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   return a.cfg == SK_N32 ? launch_skinny_nb<T, 4, 2>(a, s) : launch_skinny_nb<T, 4, 1>(a, s);
 }
 
-template <int BN, int WMW, int WNW>
+template <int BM, int BN, int WMW, int WNW>
 static hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
+  if (a.splits > 1 && !BigShape<BM, BN>::WHOLE) return hipErrorInvalidValue;
   const dim3 grid((gemm_num_tiles(a) * a.splits + 7) / 8 * 8), block(WMW * WNW * 64);
   const bool norm = a.norm != NORM_NONE;
-#define K_BIG(E, NRM) hipLaunchKernelGGL((k_gemm_big<BN, WMW, WNW, E, NRM>), grid, block, 0, s, a)
+#define K_BIG(E, NRM) hipLaunchKernelGGL((k_gemm_big<BM, BN, WMW, WNW, E, NRM>), grid, block, 0, s, a)
   switch (a.epi) {
     case EPI_STORE: if (norm) K_BIG(EPI_STORE, true); else K_BIG(EPI_STORE, false); break;
     case EPI_GELU_MUL: if (norm) K_BIG(EPI_GELU_MUL, true); else K_BIG(EPI_GELU_MUL, false); break;
@@ -1120,8 +1179,14 @@ hipError_t gemm_launch(const GemmArgs& in, int elem, hipStream_t s) {
     return elem == ET_BF16 ? launch_skinny<bf16>(a, s) : launch_skinny<float>(a, s);
   }
   if (a.kind == GEMM_BIG) {
-    if (elem != ET_BF16 || a.K % 32 != 0 || a.splits > 4 || (a.cfg == 1 && a.splits != 1)) return hipErrorInvalidValue;
-    return a.cfg == 1 ? launch_big<256, 2, 4>(a, s) : launch_big<128, 4, 2>(a, s);
+    if (elem != ET_BF16 || a.K % 32 != 0 || a.splits > 8 || a.k_split % 32 != 0) return hipErrorInvalidValue;
+    switch (a.cfg) {
+      case 0: return launch_big<256, 128, 4, 2>(a, s);
+      case 1: return launch_big<256, 256, 2, 4>(a, s);
+      case 2: return launch_big<128, 128, 2, 2>(a, s);
+      case 3: return launch_big<128, 256, 2, 4>(a, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   if (elem == ET_BF16) {
     switch (a.cfg) {
