@@ -209,11 +209,52 @@ struct Epilogue {
   static constexpr bool ROWS = EPI == EPI_RESID || EPI == EPI_QKV || EPI == EPI_EULER;
   static __device__ __forceinline__ void settle() { FM_WAIT_VM(0); }
 
+  // A tile of V columns only, stored transposed ([d][key] planes). Its items walk the rows
+  // (lane = row of the 64-row slab), so each store instruction writes 64 keys of one
+  // transposed row instead of 64 scattered keys. An item's four columns are then the same
+  // for the whole wave, so its norm vectors are scalar loads (waited on the scalar counter:
+  // no store of this call is waited for).
+  __device__ __forceinline__ void apply_vt(const GemmArgs& a, const float* C, int ldc, int m0, int n0,
+                                           const float* s_mean, const float* s_rinv) {
+    typedef const __attribute__((address_space(4))) f32x4 CF4;
+    const int tid = threadIdx.x;
+    const bool consumer = a.norm != NORM_NONE;
+#pragma unroll
+    for (int q = 0; q < ITEMS; ++q) {
+      const int it = tid + q * NT;
+      if (it >= TOT) continue;   // uniform per wave
+      const int r = it % 64, c4 = it / 64;
+      const int m = m0 + r, n = n0 + c4 * 4;
+      f32x4 v = *(const f32x4*)(C + r * ldc + c4 * 4);
+      if (consumer) {
+        const int nu = __builtin_amdgcn_readfirstlane(min(n, ((a.N - 1) / 4) * 4));
+        const f32x4 cc = *(CF4*)(a.cvec + nu), dd = *(CF4*)(a.dvec + nu);
+        v = s_rinv[r] * (v - s_mean[r] * dd) + cc;
+      }
+      if (m < a.M && n < a.N) {
+        const int b = m / a.tq, i = m % a.tq;
+        const int c = n - a.q_cols - a.kv_cols;
+        T* o = (T*)a.vdst + (long)b * a.v_bs + vt_slot<T>(a.kv_off + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[(long)(c + j) * a.v_ds] = from_f32<T>(v[j]);
+      }
+    }
+  }
+
   // y from the fp32 tile C (row stride ldc), then the kind's transform and stores
   __device__ __forceinline__ void apply(const GemmArgs& a, const float* C, int ldc, int m0, int n0,
                                         const float* s_mean, const float* s_rinv) {
   const int tid = threadIdx.x;
   const bool consumer = a.norm != NORM_NONE;
+  // A tile of V columns only is stored transposed ([d][key] planes): its items walk the
+  // rows (lane = row of a 64-row slab), so that each store instruction writes 64 keys of
+  // one transposed row instead of 64 scattered keys.
+  if constexpr (EPI == EPI_QKV && BM == 64) {
+    if (n0 >= a.q_cols + a.kv_cols) {   // uniform: a tile of V columns only
+      apply_vt(a, C, ldc, m0, n0, s_mean, s_rinv);
+      return;
+    }
+  }
 #pragma unroll
   for (int q = 0; q < ITEMS; ++q) {
     const int it = tid + q * NT;
@@ -673,7 +714,7 @@ __global__ void __launch_bounds__(WMW * WNW * 64, (BM == 128 && BN == 128) ? 2 :
   typedef Epilogue<T, 64, BN, NT, EPI> EP;
   // Row inputs (residual h, state x, RoPE cos/sin) of every slab are loaded before the
   // first store when they fit in 16 VGPR quads per thread; otherwise slab by slab.
-  constexpr bool ALL = EP::ROWS && NSL * EP::ITEMS <= 16;
+  constexpr bool ALL = EP::ROWS && NSL * EP::ITEMS <= (EPI == EPI_QKV ? 8 : 16);
   constexpr int NEP = ALL ? NSL : 1;
   EP ep[NEP];
   ep[0].pc = ep0.pc; ep[0].pd = ep0.pd; ep[0].pb = ep0.pb; ep[0].pg = ep0.pg; ep[0].ps = ep0.ps;
@@ -999,6 +1040,7 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
     double best = 1e30;
     int bc = 0, bs = 1;
     for (int cfg = 0; cfg < 4; ++cfg) {
+      if (cfg == 1 && a.epi == EPI_QKV) continue;   // its registers spill with that epilogue
       const int bm = big_bm(cfg), bn = big_bn(cfg);
       const bool pair = cfg == 2;
       const long tiles = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
