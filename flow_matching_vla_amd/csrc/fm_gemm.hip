@@ -127,6 +127,24 @@ __device__ __forceinline__ void st_dev(const Rsrc& r, uint32_t off, f32x4 v) {
 __device__ __forceinline__ f32x4 ld_dev(const Rsrc& r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1));
 }
+// XCD-local exchange (all parties on one XCD, which has one L2): plain stores (the vector
+// L1 writes through to L2), an arrival counter updated by atomics that execute in L2, and
+// plain loads after the reader has invalidated its own L1.
+__device__ __forceinline__ void st_l2(const Rsrc& r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V16, v), r, off, 0, 0);
+}
+__device__ __forceinline__ f32x4 ld_l2(const Rsrc& r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t l2_fetch_add(unsigned* p, uint32_t v) {
+  uint32_t old;
+  asm volatile("global_atomic_add %0, %1, %2, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(old) : "v"(p), "v"(v) : "memory");
+  return old;
+}
+__device__ __forceinline__ void l2_put(unsigned* p, uint32_t v) {
+  __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void inv_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------
 // Epilogue over a BM x BN fp32 tile held in LDS (row stride ldc). Items are 4-column runs;
@@ -617,13 +635,14 @@ __global__ void __launch_bounds__(WMW * WNW * 64, (BM == 128 && BN == 128) ? 2 :
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / WNW, wn = w % WNW;
   const int ntn = (a.N + BN - 1) / BN, ntm = (a.M + BM - 1) / BM, tiles = ntn * ntm;
-  // The grid is padded to a multiple of 8, so each XCD (workgroup b runs on XCD b mod 8)
-  // takes a contiguous range of logical tiles; within a split, tiles are ordered in
-  // groups of 8 row tiles walked column by column, so the tiles an XCD runs together
-  // share a few weight column tiles and a few activation row tiles in its L2.
+  // The grid is padded to a multiple of 8 x splits, so each XCD (workgroup b runs on XCD
+  // b mod 8) takes a contiguous range of logical items made of whole tiles: the splits of a
+  // tile are consecutive items, so they run on one XCD and exchange partial tiles through
+  // its L2. Tiles are ordered in groups of 8 row tiles walked column by column, so the tiles
+  // an XCD runs together share a few weight column tiles and activation row tiles in its L2.
   const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
   if (bid >= tiles * a.splits) return;
-  const int split = bid / tiles, t = bid % tiles;
+  const int split = bid % a.splits, t = bid / a.splits;
   constexpr int GM = 8;
   const int gfirst = (t / (GM * ntn)) * GM, gsz = min(ntm - gfirst, GM);
   const int tm = gfirst + (t % (GM * ntn)) % gsz, tn = (t % (GM * ntn)) / gsz;
@@ -766,14 +785,14 @@ __global__ void __launch_bounds__(WMW * WNW * 64, (BM == 128 && BN == 128) ? 2 :
       for (int q = 0; q < Q4; ++q) {
         const int it = tid + q * NT;
         const int r = it / (BN / 4), c4 = it % (BN / 4);
-        st_dev(rws, tbase + (uint32_t)split * (BM * BN * 4) + it * 16, *(const f32x4*)(C + r * LDC + c4 * 4));
+        st_l2(rws, tbase + (uint32_t)split * (BM * BN * 4) + it * 16, *(const f32x4*)(C + r * LDC + c4 * 4));
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_waitcnt(0);   // this workgroup's partial is in L2
       __syncthreads();
-      if (tid == 0)
-        s_last = __hip_atomic_fetch_add(a.counters + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.splits - 1u;
+      if (tid == 0) s_last = l2_fetch_add(a.counters + t, 1u) == (unsigned)a.splits - 1u;
       __syncthreads();
       if (!s_last) return;
+      inv_l1();
 #pragma unroll 2
       for (int q = 0; q < Q4; ++q) {
         const int it = tid + q * NT;
@@ -781,10 +800,10 @@ __global__ void __launch_bounds__(WMW * WNW * 64, (BM == 128 && BN == 128) ? 2 :
         f32x4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          v[u] = ld_dev(rws, u < a.splits ? tbase + (uint32_t)u * (BM * BN * 4) + it * 16 : kOob);
+          v[u] = ld_l2(rws, u < a.splits ? tbase + (uint32_t)u * (BM * BN * 4) + it * 16 : kOob);
         *(f32x4*)(C + r * LDC + c4 * 4) = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
       }
-      if (tid == 0) __hip_atomic_store(a.counters + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) l2_put(a.counters + t, 0u);
       __syncthreads();
       FM_PHASE(12);
 #pragma unroll
@@ -1031,10 +1050,10 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
     // Large-M kernel: the tile shape and K split with the lowest estimated time. Per
     // workgroup: a fixed start (first copies, row statistics), k-stages of 32 at a
     // per-shape cost, and the epilogue; rounds of workgroups over the CUs (two per CU for
-    // 128 x 128 tiles, whose stages then run slower); a split adds the last arriver's reads
-    // of every partial tile and the partial traffic through HBM. Constants measured on
-    // MI355X at M = 400 and 3200 (the pick is within 4% of the fastest measured choice at
-    // every expert GEMM shape).
+    // 128 x 128 tiles, whose stages then run slower); a split adds the partial exchange
+    // (store, arrival, the last arriver's reads) and, past what the L2s hold, HBM traffic.
+    // Constants measured on MI355X at M = 400 and 3200 (the pick is the fastest measured
+    // choice at every expert GEMM shape).
     a.kind = GEMM_BIG;
     const int nks = a.K / 32;
     double best = 1e30;
@@ -1059,8 +1078,11 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
         const double st = pair && items > num_cus ? 0.60 : kStage[cfg];
         double est = (double)rounds * (kStart[cfg] + per * st + kEpi[cfg]);
         if (splits > 1) {
+          // partial tiles go through the XCD's L2; past half of its 4 MB they spill to HBM
           const double part = (double)bm * bn * 4;
-          est += 3.0 + 1.5 * splits * part / 65536.0 + (double)tiles * splits * part * 2.0 / 4.0e6;
+          est += 1.5 + 3.5 * part / 65536.0 + 0.8 * splits;
+          const double per_xcd = (double)tiles * splits * part / 8.0;
+          if (per_xcd > 2.0 * (1 << 20)) est += (per_xcd - 2.0 * (1 << 20)) * 8.0 * 2.0 / 4.0e6;
         }
         if (est < best) { best = est; bc = cfg; bs = splits; }
       }
@@ -1171,7 +1193,8 @@ static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 template <int BM, int BN, int WMW, int WNW>
 static hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   if (a.splits > 1 && !BigShape<BM, BN>::WHOLE) return hipErrorInvalidValue;
-  const dim3 grid((gemm_num_tiles(a) * a.splits + 7) / 8 * 8), block(WMW * WNW * 64);
+  const int per_round = 8 * a.splits;   // whole tiles per XCD range
+  const dim3 grid((gemm_num_tiles(a) * a.splits + per_round - 1) / per_round * per_round), block(WMW * WNW * 64);
   const bool norm = a.norm != NORM_NONE;
 #define K_BIG(E, NRM) hipLaunchKernelGGL((k_gemm_big<BM, BN, WMW, WNW, E, NRM>), grid, block, 0, s, a)
   switch (a.epi) {
