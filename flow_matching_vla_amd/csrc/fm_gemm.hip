@@ -856,8 +856,12 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntn = (a.N + BN - 1) / BN;
+  // The grid is padded to a multiple of 8 x splits and the splits of a column tile are
+  // consecutive logical items, so they run on one XCD (workgroup b runs on XCD b mod 8) and
+  // exchange partial tiles through its L2.
   const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int tile = bid % ntn, split = bid / ntn;
+  if (bid >= ntn * a.splits) return;
+  const int tile = bid / a.splits, split = bid % a.splits;
   const int n0 = tile * BN;
   const int KCt = a.K / KC;
   const int c_beg = (split * KW + w) * CPW;   // this wave's chunks: [c_beg, c_beg + CPW) within K
@@ -938,14 +942,14 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < Q4; ++q) {
       const int i = tid + q * NT;
-      if (i < BM * BN / 4) st_dev(rws, tbase + (uint32_t)split * (BM * BN * 4) + i * 16, part[q]);
+      if (i < BM * BN / 4) st_l2(rws, tbase + (uint32_t)split * (BM * BN * 4) + i * 16, part[q]);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0);   // this workgroup's partial is in L2
     __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.splits - 1u;
+    if (tid == 0) s_last = l2_fetch_add(a.counters + tile, 1u) == (unsigned)a.splits - 1u;
     __syncthreads();
     if (!s_last) return;
+    inv_l1();
 #pragma unroll
     for (int q = 0; q < Q4; ++q) {
       const int i = tid + q * NT;
@@ -955,13 +959,13 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
         f32x4 v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          v[u] = ld_dev(rws, s0 + u < a.splits ? tbase + (uint32_t)(s0 + u) * (BM * BN * 4) + i * 16 : kOob);
+          v[u] = ld_l2(rws, s0 + u < a.splits ? tbase + (uint32_t)(s0 + u) * (BM * BN * 4) + i * 16 : kOob);
 #pragma unroll
         for (int u = 0; u < 8; ++u) sum += v[u];
       }
       part[q] = sum;
     }
-    if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) l2_put(a.counters + tile, 0u);
   }
   FM_PHASE(4);
   __syncthreads();
@@ -1146,7 +1150,9 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
 // Skinny instantiations: the residual epilogue never consumes a norm; the others can.
 template <typename T, int KW, int NB, int CPW>
 static hipError_t launch_skinny_cpw(const GemmArgs& a, hipStream_t s) {
-  const dim3 grid(((a.N + 16 * NB - 1) / (16 * NB)) * a.splits), block(KW * 64);
+  const int per_round = 8 * a.splits;   // whole column tiles per XCD range
+  const int items = ((a.N + 16 * NB - 1) / (16 * NB)) * a.splits;
+  const dim3 grid((items + per_round - 1) / per_round * per_round), block(KW * 64);
   const bool norm = a.norm != NORM_NONE;
 #define K_SK(E, NRM) hipLaunchKernelGGL((k_gemm_skinny<T, KW, NB, CPW, E, NRM>), grid, block, 0, s, a)
   switch (a.epi) {
