@@ -424,6 +424,11 @@ __device__ __forceinline__ AttnItem attn_item(LA& a) {
   return it;
 }
 
+// Key tile `which` (0/1) of split sp: tiles sp and sp + SA, so that this step's suffix tiles
+// (the last ones, written by the QKV phase just before and loaded only after its barrier)
+// fall to different splits instead of doubling one split's loads.
+__device__ __forceinline__ int attn_tile(LA& a, const AttnItem& it, int which) { return it.sp + which * a.SA; }
+
 // Issue the copies of key tile `which` (0/1) of the item into LDS: prefix tiles only when
 // suffix == false, suffix tiles only when suffix == true.
 __device__ __forceinline__ void attn_issue(LA& a, const AttnItem& it, int l, const char* rot_l, int which,
@@ -432,7 +437,7 @@ __device__ __forceinline__ void attn_issue(LA& a, const AttnItem& it, int l, con
   // prefix tiles: the copy waves, each its own and wave w - 4's fragments; suffix tiles:
   // every wave its own
   if (!suffix && wave < 4) return;
-  const int ti = it.sp * 2 + which;
+  const int ti = attn_tile(a, it, which);
   if (!it.valid || ti >= a.TP + a.TS) return;
   const bool is_suf = ti >= a.TP;
   if (is_suf != suffix) return;
@@ -496,7 +501,7 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
   wait_all();
   __syncthreads();
 
-  const int ti = it.sp * 2 + half;
+  const int ti = attn_tile(a, it, half);
   const bool has = it.valid && ti < a.TP + a.TS;
   f32x4 o[kDB];
 #pragma unroll
