@@ -46,7 +46,10 @@ __device__ __forceinline__ void wait_tiles(int pend) {
   else FM_WAIT_VMCNT(0);
 }
 
-template <typename T, int DH, int WAVES>
+// WAVES waves of QB query blocks (16 rows each): ROWS = 16 WAVES QB rows per workgroup.
+// Every K and V^T fragment a wave reads from LDS feeds QB MFMAs, so QB = 2 halves the LDS
+// reads per MFMA (one wave per SIMD then holds twice the accumulators).
+template <typename T, int DH, int WAVES, int QB>
 __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   using MT = Mma<T>;
   typedef typename MT::frag frag;
@@ -58,7 +61,8 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   constexpr int FK = KB * DCH, FV = DB * KCH;  // 1 KB fragments per K / V^T tile
   constexpr int FT = FK + FV;
   constexpr int FPW = FT / WAVES;
-  constexpr int ROWS = 16 * WAVES;
+  constexpr int ROWS = 16 * WAVES * QB;
+  static_assert(ROWS == kAttnRows, "row tile shared with the planner and the merge");
   static_assert(FT % WAVES == 0 && FPW <= 15, "tile fragments per wave");
   static_assert(KB == 2 * KCH || KB == KCH, "P fragment packing");
   constexpr int NST = kAttnStages;
@@ -114,15 +118,17 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   };
   if (ntile > 0) issue(key_beg, 0);   // tile 0 first, the other prefetched tiles after Q
 
-  // Q^T fragments (B operand of S^T): lane l carries query row l % 16 of this wave, d
-  // run l / 16 of every d-chunk. Rows past R read row R-1; their outputs are not stored.
-  frag qf[DCH];
-  {
-    const int r = min(rt * ROWS + wave * 16 + (lane % 16), R - 1);
+  // Q^T fragments (B operand of S^T): lane l carries query row l % 16 of query block
+  // wave QB + qb, d run l / 16 of every d-chunk. Rows past R read row R-1; their outputs
+  // are not stored.
+  frag qf[QB][DCH];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = min(rt * ROWS + (wave * QB + qb) * 16 + (lane % 16), R - 1);
     const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
     const T* qp = (const T*)a.q + (long)b * a.q_bs + (long)t * a.q_rs + (long)n * a.dh + (lane / 16) * VEC;
 #pragma unroll
-    for (int c = 0; c < DCH; ++c) qf[c] = __builtin_bit_cast(frag, *(const V16*)(qp + c * KC));
+    for (int c = 0; c < DCH; ++c) qf[qb][c] = __builtin_bit_cast(frag, *(const V16*)(qp + c * KC));
   }
   // Q and the first tile's copies complete here; the loop below then waits only on the
   // copies it issues itself (the compiler cannot see those: they are inline asm)
@@ -132,10 +138,14 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
     if (p < ntile) issue(key_beg + p * BK, p);
   FM_PHASE(1);
 
-  f32x4 o[DB];   // O^T: lane l, element e holds d = 16 db + 4 (l / 16) + e of query l % 16
+  f32x4 o[QB][DB];   // O^T: lane l, element e holds d = 16 db + 4 (l / 16) + e of query l % 16
 #pragma unroll
-  for (int i = 0; i < DB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;   // of this lane's query, base-2 logits
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int i = 0; i < DB; ++i) o[qb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[QB], l_run[QB];   // of this lane's queries, base-2 logits
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
 
   for (int t = 0; t < ntile; ++t) {
     const int kt = key_beg + t * BK;
@@ -147,73 +157,78 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
     const V16* sK = sbuf[t % NST];
     const V16* sV = sK + FK * 64;
 
-    // S^T = K Q^T: 16 keys x 16 queries per kb, two partial chains per kb. A key block's
-    // fragments are all read from LDS before its MFMAs, so the reads overlap each other
-    // instead of each MFMA waiting on its own read.
-    f32x4 s[KB];
+    // S^T = K Q^T: 16 keys x 16 queries per (kb, qb), two partial chains each. A key
+    // block's fragments are all read from LDS before its MFMAs, so the reads overlap each
+    // other instead of each MFMA waiting on its own read.
+    f32x4 s[QB][KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       V16 kf[DCH];
 #pragma unroll
       for (int c = 0; c < DCH; ++c) kf[c] = sK[(kb * DCH + c) * 64 + lane];
       __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the MFMAs
-      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-      for (int c = 0; c < DCH; c += 2) {
-        s0 = MT::mma(__builtin_bit_cast(frag, kf[c]), qf[c], s0);
-        if (c + 1 < DCH) s1 = MT::mma(__builtin_bit_cast(frag, kf[c + 1]), qf[c + 1], s1);
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+        for (int c = 0; c < DCH; c += 2) {
+          s0 = MT::mma(__builtin_bit_cast(frag, kf[c]), qf[qb][c], s0);
+          if (c + 1 < DCH) s1 = MT::mma(__builtin_bit_cast(frag, kf[c + 1]), qf[qb][c + 1], s1);
+        }
+        s[qb][kb] = s0 + s1;
       }
-      s[kb] = s0 + s1;
     }
     // V^T fragments read now; their LDS latency hides behind the softmax
     V16 vf[FV];
 #pragma unroll
     for (int f = 0; f < FV; ++f) vf[f] = sV[f * 64 + lane];
     __builtin_amdgcn_sched_barrier(0);
-    // online softmax of this lane's query over keys kt + 16 kb + 4 (l / 16) + e
+    // online softmax of this lane's queries over keys kt + 16 kb + 4 (l / 16) + e
     const int kl = kt + 4 * (lane / 16);
-    float mt = -INFINITY;
+    frag pf[QB][KCH];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mt = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = (kl + 16 * kb + e < key_end) ? s[kb][e] * a.scale_log2 : -INFINITY;
-        s[kb][e] = v;
-        mt = fmaxf(mt, v);
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = (kl + 16 * kb + e < key_end) ? s[qb][kb][e] * a.scale_log2 : -INFINITY;
+          s[qb][kb][e] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = group4_max(mt);
+      // The reference max moves only when a score exceeds it by more than 2^8: until then
+      // p = 2^(s - m_run) <= 256 stays exact in fp32 / bf16 and O, l need no rescale. The
+      // final O / l is the same for any reference, so this changes no result.
+      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + 8.f)) {   // wave-uniform
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float alpha = exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[qb][i] *= alpha;
       }
-    mt = group4_max(mt);
-    // The reference max moves only when a score exceeds it by more than 2^8: until then
-    // p = 2^(s - m_run) <= 256 stays exact in fp32 / bf16 and O, l need no rescale. The
-    // final O / l is the same for any reference, so this changes no result.
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + 8.f)) {   // wave-uniform
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+      float ls = 0.f;
 #pragma unroll
-      for (int i = 0; i < DB; ++i) o[i] *= alpha;
-    }
-    float ls = 0.f;
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+        for (int e = 0; e < 4; ++e) {
+          const float p = exp2f(s[qb][kb][e] - m_run[qb]);
+          s[qb][kb][e] = p;
+          ls += p;
+        }
+      ls = group4_sum(ls);
+      l_run[qb] += ls;
+      // P^T fragments: keys 16 h + 4 (l / 16) + r of chunk kc, h over the chunk's key blocks
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = exp2f(s[kb][e] - m_run);
-        s[kb][e] = p;
-        ls += p;
-      }
-    ls = group4_sum(ls);
-    l_run += ls;
-
-    // P^T fragments: keys 16 h + 4 (l / 16) + r of chunk kc, h over the chunk's key blocks
-    frag pf[KCH];
-#pragma unroll
-    for (int kc = 0; kc < KCH; ++kc) {
-      if constexpr (sizeof(T) == 2) {
-        const f32x4 p0 = s[2 * kc], p1 = s[2 * kc + 1];
-        pf[kc] = frag{(bf16)p0[0], (bf16)p0[1], (bf16)p0[2], (bf16)p0[3], (bf16)p1[0], (bf16)p1[1], (bf16)p1[2], (bf16)p1[3]};
-      } else {
-        pf[kc] = __builtin_bit_cast(frag, s[kc]);
+      for (int kc = 0; kc < KCH; ++kc) {
+        if constexpr (sizeof(T) == 2) {
+          const f32x4 p0 = s[qb][2 * kc], p1 = s[qb][2 * kc + 1];
+          pf[qb][kc] = frag{(bf16)p0[0], (bf16)p0[1], (bf16)p0[2], (bf16)p0[3], (bf16)p1[0], (bf16)p1[1], (bf16)p1[2], (bf16)p1[3]};
+        } else {
+          pf[qb][kc] = __builtin_bit_cast(frag, s[qb][kc]);
+        }
       }
     }
     // O^T += V^T P^T
@@ -221,37 +236,42 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
     for (int kc = 0; kc < KCH; ++kc)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        o[db] = MT::mma(__builtin_bit_cast(frag, vf[db * KCH + kc]), pf[kc], o[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][db] = MT::mma(__builtin_bit_cast(frag, vf[db * KCH + kc]), pf[qb][kc], o[qb][db]);
     __syncthreads();   // this buffer is refilled by the next iteration's copies
   }
   FM_PHASE(3);
 
-  const int rq = rt * ROWS + wave * 16 + (lane % 16);   // this lane's query row
-  if (a.splits == 1) {
-    if (rq < R) {
-      const int n = g * a.heads_per_kv + rq / a.Tq, t = rq % a.Tq;
-      T* op = (T*)a.o + (long)b * a.o_bs + (long)t * a.o_rs + (long)n * a.dh + 4 * (lane / 16);
-      const float inv = 1.f / l_run;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        if constexpr (sizeof(T) == 2) {
-          *(bf16x4*)(op + db * 16) = bf16x4{(bf16)(o[db][0] * inv), (bf16)(o[db][1] * inv), (bf16)(o[db][2] * inv), (bf16)(o[db][3] * inv)};
-        } else {
-          *(f32x4*)(op + db * 16) = o[db] * inv;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int blk = wave * QB + qb;                      // 16-row block of the row tile
+    const int rq = rt * ROWS + blk * 16 + (lane % 16);   // this lane's query row
+    if (a.splits == 1) {
+      if (rq < R) {
+        const int n = g * a.heads_per_kv + rq / a.Tq, t = rq % a.Tq;
+        T* op = (T*)a.o + (long)b * a.o_bs + (long)t * a.o_rs + (long)n * a.dh + 4 * (lane / 16);
+        const float inv = 1.f / l_run[qb];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          if constexpr (sizeof(T) == 2) {
+            *(bf16x4*)(op + db * 16) = bf16x4{(bf16)(o[qb][db][0] * inv), (bf16)(o[qb][db][1] * inv), (bf16)(o[qb][db][2] * inv), (bf16)(o[qb][db][3] * inv)};
+          } else {
+            *(f32x4*)(op + db * 16) = o[qb][db] * inv;
+          }
         }
       }
+      continue;
     }
-    return;
-  }
-
-  // split keys: unnormalised O^T in the MFMA output layout ([wave][db][lane][e], one
-  // 16-byte store per lane and d-block) and (m, l) of each query row
-  float* wo = a.ws + ((long)tile_id * a.splits + sp) * (ROWS * DH);
+    // split keys: unnormalised O^T in the MFMA output layout ([block][db][lane][e], one
+    // 16-byte store per lane and d-block) and (m, l) of each query row
+    float* wo = a.ws + ((long)tile_id * a.splits + sp) * (ROWS * DH);
 #pragma unroll
-  for (int db = 0; db < DB; ++db) *(f32x4*)(wo + ((wave * DB + db) * 64 + lane) * 4) = o[db];
-  if (lane < 16) {
-    float2* wml = (float2*)(a.ws + (long)a.B * groups * rtiles * a.splits * (ROWS * DH)) + ((long)tile_id * a.splits + sp) * ROWS;
-    wml[wave * 16 + lane] = make_float2(m_run, l_run);
+    for (int db = 0; db < DB; ++db) *(f32x4*)(wo + ((blk * DB + db) * 64 + lane) * 4) = o[qb][db];
+    if (lane < 16) {
+      float2* wml = (float2*)(a.ws + (long)a.B * groups * rtiles * a.splits * (ROWS * DH)) + ((long)tile_id * a.splits + sp) * ROWS;
+      wml[blk * 16 + lane] = make_float2(m_run[qb], l_run[qb]);
+    }
   }
   FM_PHASE(4);
 }
@@ -344,7 +364,10 @@ static void launch_attn(const AttnArgs& a, hipStream_t s) {
   const int rtiles = (R + kAttnRows - 1) / kAttnRows;
   const int units = a.B * (a.n_heads / a.heads_per_kv) * a.splits;
   const dim3 grid(8 * ((units + 7) / 8) * rtiles);
-  hipLaunchKernelGGL((k_attn<T, DH, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, s, a);
+  // one query block per wave: two blocks per wave (four waves, one per SIMD) halve the LDS
+  // reads per MFMA but measured slower (pi05_b64: 73 against 62 us per layer), the single
+  // wave per SIMD leaving LDS and softmax latencies uncovered
+  hipLaunchKernelGGL((k_attn<T, DH, kAttnWaves, 1>), grid, dim3(64 * kAttnWaves), 0, s, a);
   if (a.splits > 1) {
     const long threads = (long)attn_num_items(a) * kAttnRows * DH / 4;
     const dim3 cgrid((unsigned)((threads + 255) / 256));

@@ -597,9 +597,12 @@ __device__ __forceinline__ void wait_stages(int pend) {
   }
 }
 
-template <int BM, int BN>
+// 128 x 128 tiles of four waves run two workgroups per CU
+constexpr bool big_pair(int bm, int bn, int nw) { return bm == 128 && bn == 128 && nw == 4; }
+
+template <int BM, int BN, int NW>
 struct BigShape {
-  static constexpr bool PAIR = BM == 128 && BN == 128;        // two workgroups per CU
+  static constexpr bool PAIR = big_pair(BM, BN, NW);
   static constexpr int FS = BM / 16 + BN / 16;                // 1 KB fragments per stage
   static constexpr int BUDGET = (PAIR ? 64 : 144) * 1024;
   static constexpr int NST = BUDGET / (FS * 1024) > 6 ? 6 : BUDGET / (FS * 1024);
@@ -611,11 +614,11 @@ struct BigShape {
 };
 
 template <int BM, int BN, int WMW, int WNW, int EPI, bool NORM>
-__global__ void __launch_bounds__(WMW * WNW * 64, (BM == 128 && BN == 128) ? 2 : 1) k_gemm_big(GemmArgs a) {
+__global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 2 : 1) k_gemm_big(GemmArgs a) {
   typedef bf16 T;
   typedef Mma<T> MT;
   typedef typename MT::frag frag;
-  typedef BigShape<BM, BN> SH;
+  typedef BigShape<BM, BN, WMW * WNW> SH;
   constexpr int NW = WMW * WNW, NT = NW * 64, VEC = MT::VEC, KC = MT::KC;
   constexpr int BK = KC;
   constexpr int RB = BM / 16, CB = BN / 16;
@@ -997,9 +1000,11 @@ static CfgShape cfg_shape(int cfg, int elem) {
 }
 static int skinny_bn(int cfg) { return cfg == SK_N32 ? 32 : 16; }
 
-// large-M tile shapes: cfg bit 0 selects BN 256 (else 128), bit 1 BM 128 (else 256)
-static int big_bm(int cfg) { return cfg & 2 ? 128 : 256; }
-static int big_bn(int cfg) { return cfg & 1 ? 256 : 128; }
+// large-M tile shapes: cfg 0..3: bit 0 selects BN 256 (else 128), bit 1 BM 128 (else 256);
+// 128 x 128 tiles run four waves, two workgroups per CU (cfg 2), or eight waves, one
+// workgroup per CU (cfg 4: faster while the tiles fit in one round)
+static int big_bm(int cfg) { return cfg == 4 || (cfg & 2) ? 128 : 256; }
+static int big_bn(int cfg) { return cfg != 4 && (cfg & 1) ? 256 : 128; }
 
 int gemm_num_tiles(const GemmArgs& a) {
   if (a.kind == GEMM_SKINNY) return (a.N + skinny_bn(a.cfg) - 1) / skinny_bn(a.cfg);
@@ -1062,14 +1067,14 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
     const int nks = a.K / 32;
     double best = 1e30;
     int bc = 0, bs = 1;
-    for (int cfg = 0; cfg < 4; ++cfg) {
+    for (int cfg = 0; cfg < 5; ++cfg) {
       if (cfg == 1 && a.epi == EPI_QKV) continue;   // its registers spill with that epilogue
       const int bm = big_bm(cfg), bn = big_bn(cfg);
       const bool pair = cfg == 2;
       const long tiles = (long)((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
-      static const double kStage[4] = {0.57, 0.95, 0.41, 0.53};
-      static const double kStart[4] = {2.8, 2.6, 1.8, 2.4};
-      static const double kEpi[4] = {4.3, 9.8, 3.8, 4.0};
+      static const double kStage[5] = {0.57, 0.95, 0.41, 0.53, 0.375};
+      static const double kStart[5] = {2.8, 2.6, 1.8, 2.4, 1.8};
+      static const double kEpi[5] = {4.3, 9.8, 3.8, 4.0, 3.5};
       for (int sp = 1; sp <= 8; sp *= 2) {
         if (sp > 1 && cfg == 1) break;           // the 256 x 256 fp32 tile does not fit in LDS
         if (nks / sp < 4) break;
@@ -1198,7 +1203,7 @@ static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 
 template <int BM, int BN, int WMW, int WNW>
 static hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
-  if (a.splits > 1 && !BigShape<BM, BN>::WHOLE) return hipErrorInvalidValue;
+  if (a.splits > 1 && !BigShape<BM, BN, WMW * WNW>::WHOLE) return hipErrorInvalidValue;
   const int per_round = 8 * a.splits;   // whole tiles per XCD range
   const dim3 grid((gemm_num_tiles(a) * a.splits + per_round - 1) / per_round * per_round), block(WMW * WNW * 64);
   const bool norm = a.norm != NORM_NONE;
@@ -1256,6 +1261,7 @@ hipError_t gemm_launch(const GemmArgs& in, int elem, hipStream_t s) {
       case 1: return launch_big<256, 256, 2, 4>(a, s);
       case 2: return launch_big<128, 128, 2, 2>(a, s);
       case 3: return launch_big<128, 256, 2, 4>(a, s);
+      case 4: return launch_big<128, 128, 2, 4>(a, s);
       default: return hipErrorInvalidValue;
     }
   }
