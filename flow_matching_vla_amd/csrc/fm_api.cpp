@@ -507,15 +507,16 @@ RotLayout rot_layout(const fm_ctx* ctx) {
   r.Hp = (int)round_up(c.action_horizon, 32);
   long off = 0;
   auto put = [&](long bytes) { const long o = off; off += round_up(std::max(bytes, 1L), 4096); return o; };
-  r.o_hs = put(M * D * 2);
+  const long Mp = round_up(M, 16);   // the GEMM operands hs, ao, hsu, act: whole 16-row blocks
+  r.o_hs = put(Mp * D * 2);
   r.o_st = put(M * (D / 16) * 4);
   r.o_q = put(M * qd * 2);
   r.o_sk = put(B * r.Hp * dh * 2);
   r.o_svt = put(B * dh * r.Hp * 2);
-  r.o_ao = put(M * qd * 2);
-  r.o_hsu = put(M * D * 2);
+  r.o_ao = put(Mp * qd * 2);
+  r.o_hsu = put(Mp * D * 2);
   r.o_stu = put(M * (D / 16) * 4);
-  r.o_act = put(M * F * 2);
+  r.o_act = put(Mp * F * 2);
   r.layer = off;
   return r;
 }

@@ -234,6 +234,17 @@ __device__ __forceinline__ void read_w(const Smem& sm, V16 (&wr)[2][kPCh], int n
 }
 
 // A fragments of this workgroup's K range: lane l holds row 16 mb + l % 16, k run l / 16.
+// Activation operands (the GEMM A inputs hs, attention output, GELU.up output) are stored
+// fragment-major: 16 x 32 blocks (row block r / 16, k-chunk k / 32) of 1 KB, row-block
+// major, lane (r % 16) + 16 ((k % 32) / 8) holding 8 consecutive k. A fragment load is then
+// one contiguous kilobyte (8 whole cache lines) instead of 16 rows x 64 bytes. Byte offset
+// of element (r, k) of a K-wide operand:
+__device__ __forceinline__ uint32_t act_off(int r, int k, int K) {
+  return (uint32_t)(((((r >> 4) * (K >> 5) + (k >> 5)) * 64 + (r & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7)) * 2);
+}
+// bytes of a K-wide operand of M rows (whole row blocks)
+__device__ __forceinline__ uint32_t act_bytes(int M, int K) { return (uint32_t)(((M + 15) & ~15) * K * 2); }
+
 __device__ __forceinline__ void load_a(const GemmIn& g, int M, V16 (&ra)[kPCh][4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const Rsrc rA = make_rsrc(g.A, g.abytes);
@@ -245,7 +256,7 @@ __device__ __forceinline__ void load_a(const GemmIn& g, int M, V16 (&ra)[kPCh][4
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int row = 16 * mb + (lane & 15);
-      ra[j][mb] = ld16<0>(rA, (row < M && c < kct) ? (uint32_t)((row * g.lda + c * 32 + (lane >> 4) * 8) * 2) : kOob);
+      ra[j][mb] = ld16<0>(rA, (row < M && c < kct) ? (uint32_t)(((mb * kct + c) * 64 + lane) * 16) : kOob);
     }
   }
 }
@@ -383,8 +394,8 @@ __device__ __forceinline__ void epi_resid(LA& a, f32x4 v, const ResidIn& in, int
   if (ok) {
     const Rsrc rh = make_rsrc(a.h, (uint32_t)(a.M * a.D * 4));
     st16(rh, (uint32_t)((r * a.D + n) * 4), as_v(hv));
-    const Rsrc rs = make_rsrc(hs_out, (uint32_t)(a.M * a.D * 2));
-    st8(rs, (uint32_t)((r * a.D + n) * 2),
+    const Rsrc rs = make_rsrc(hs_out, act_bytes(a.M, a.D));
+    st8(rs, act_off(r, n, a.D),
         u32x2{pack_bf2(hv[0] * (1.f + sc[0]), hv[1] * (1.f + sc[1])), pack_bf2(hv[2] * (1.f + sc[2]), hv[3] * (1.f + sc[3]))});
     if ((threadIdx.x & 3) == 0) {
       const Rsrc rt = make_rsrc(st_out, (uint32_t)(a.M * (a.D / 16) * 4));
@@ -636,7 +647,7 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
   constexpr int PER_TILE = 64 * kDH / 4;
   const int per = (PER_TILE + SA - 1) / SA;
   const int beg = it.sp * per, end = min(PER_TILE, beg + per);
-  const Rsrc rao = make_rsrc(rot_l + a.o_ao, (uint32_t)(a.M * a.qd * 2));
+  const Rsrc rao = make_rsrc(rot_l + a.o_ao, act_bytes(a.M, a.qd));
   const int R = a.nq * a.H;
   for (int w0 = beg + (int)threadIdx.x; w0 < end; w0 += 512) {
     V16 ov[2][kMaxSA];
@@ -661,7 +672,7 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
       const int r = it.rt * 64 + rl;
       if (r < R) {
         const int n = r / a.H, t = r % a.H;
-        const uint32_t off = (uint32_t)((((it.b * a.H + t) * a.qd) + n * kDH + db * 16 + 4 * (ln >> 4)) * 2);
+        const uint32_t off = act_off(it.b * a.H + t, n * kDH + db * 16 + 4 * (ln >> 4), a.qd);
         st8(rao, off, u32x2{pack_bf2(num[0], num[1]), pack_bf2(num[2], num[3])});
       }
     }
@@ -696,35 +707,35 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = W; g.wbytes = a.wb_qkv; g.N = a.nqkv; g.K = D; g.nks = (D + kPKS - 1) / kPKS;
-    g.ntiles = (a.nqkv + 15) / 16; g.A = rl + a.o_hs; g.lda = D; g.abytes = M * D * 2; g.xbase = 0;
+    g.ntiles = (a.nqkv + 15) / 16; g.A = rl + a.o_hs; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0;
     return g;
   };
   auto gin_o = [&](LA& a, const void* W, char* rl) {
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = W; g.wbytes = a.wb_o; g.N = D; g.K = a.qd; g.nks = (a.qd + kPKS - 1) / kPKS;
-    g.ntiles = D / 16; g.A = rl + a.o_ao; g.lda = a.qd; g.abytes = M * a.qd * 2; g.xbase = 0;
+    g.ntiles = D / 16; g.A = rl + a.o_ao; g.lda = a.qd; g.abytes = act_bytes(M, a.qd); g.xbase = 0;
     return g;
   };
   auto gin_up = [&](LA& a, const void* W, char* rl) {
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = W; g.wbytes = a.wb_gu; g.N = 2 * a.F; g.K = D; g.nks = (D + kPKS - 1) / kPKS;
-    g.ntiles = 2 * a.F / 16; g.A = rl + a.o_hsu; g.lda = D; g.abytes = M * D * 2; g.xbase = 0;
+    g.ntiles = 2 * a.F / 16; g.A = rl + a.o_hsu; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0;
     return g;
   };
   auto gin_down = [&](LA& a, const void* W, char* rl) {
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = W; g.wbytes = a.wb_down; g.N = D; g.K = a.F; g.nks = (a.F + kPKS - 1) / kPKS;
-    g.ntiles = D / 16; g.A = rl + a.o_act; g.lda = a.F; g.abytes = M * a.F * 2; g.xbase = kMaxSplitItems / 2;
+    g.ntiles = D / 16; g.A = rl + a.o_act; g.lda = a.F; g.abytes = act_bytes(M, a.F); g.xbase = kMaxSplitItems / 2;
     return g;
   };
   auto gin_out = [&](LA& a, char* rf) {
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = a.w_out; g.wbytes = a.wb_out; g.N = a.da; g.K = D; g.nks = (D + kPKS - 1) / kPKS;
-    g.ntiles = (a.da + 15) / 16; g.A = rf + a.o_hs; g.lda = D; g.abytes = M * D * 2; g.xbase = 0;
+    g.ntiles = (a.da + 15) / 16; g.A = rf + a.o_hs; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0;
     return g;
   };
   // the table row of site s at step k: [scale | shift | gate], D each
@@ -780,8 +791,8 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         if (ok) {
           const Rsrc rh = make_rsrc(a.h, (uint32_t)(M * D * 4));
           st16(rh, (uint32_t)((r * D + n) * 4), as_v(h));
-          const Rsrc rs = make_rsrc(r0 + a.o_hs, (uint32_t)(M * D * 2));
-          st8(rs, (uint32_t)((r * D + n) * 2),
+          const Rsrc rs = make_rsrc(r0 + a.o_hs, act_bytes(M, D));
+          st8(rs, act_off(r, n, D),
               u32x2{pack_bf2(h[0] * (1.f + s4[0]), h[1] * (1.f + s4[1])), pack_bf2(h[2] * (1.f + s4[2]), h[3] * (1.f + s4[3]))});
           if ((t & 3) == 0) {
             const Rsrc rt = make_rsrc(r0 + a.o_st, (uint32_t)(M * (D / 16) * 4));
@@ -902,13 +913,13 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         if (nslot) gemm_core(wr, ra, sm, nslot, v);
         __syncthreads();
         prefetch_w(gin_down(a, lw.down, rl), sm);
-        const Rsrc ra2 = make_rsrc(rl + a.o_act, (uint32_t)(M * a.F * 2));
+        const Rsrc ra2 = make_rsrc(rl + a.o_act, act_bytes(M, a.F));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int n = ((int)blockIdx.x + s2 * G) * 16 + 4 * eq;
           if (t < 256 && s2 < nslot && er < M) {
             const f32x4 y = sm.rinv[er] * v[s2] + as_f4(cv[s2]);
-            st4(ra2, (uint32_t)((er * a.F + n / 2) * 2), pack_bf2(gelu_tanh(y[0]) * y[1], gelu_tanh(y[2]) * y[3]));
+            st4(ra2, act_off(er, n / 2, a.F), pack_bf2(gelu_tanh(y[0]) * y[1], gelu_tanh(y[2]) * y[3]));
           }
         }
         grid_sync(a.flags, ++e);
