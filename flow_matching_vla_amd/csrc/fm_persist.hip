@@ -597,6 +597,10 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
   // the splits of the row tile meet: publish this one, wait for all of them
   if (!copy_wave()) wait_all();
   __syncthreads();
+  // O projection weights for the next phase (copy waves; no load of theirs follows): issued
+  // before the wait for the other splits, so they arrive during it instead of competing
+  // with the merge's loads
+  prefetch_w(gin_o_next, sm);
   uint32_t* fl = a.flags + kFlagAttn + rb * kMaxSA;
   if (threadIdx.x == 0 && it.valid) l2_set(fl + it.sp, e_attn);
   if (threadIdx.x < 64 && it.valid) {
@@ -608,8 +612,6 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
     }
   }
   __syncthreads();
-  // O projection weights for the next phase (copy waves; no load of theirs follows)
-  prefetch_w(gin_o_next, sm);
   const int SA = a.SA;
   const bool merger = it.valid && threadIdx.x < 256;
   // per row of the tile, the split weights exp2(m_s - max) / sum_s exp2(m_s - max) l_s:
