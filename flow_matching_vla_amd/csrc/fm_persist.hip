@@ -643,28 +643,24 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
     for (int u = 0; u < kMaxSA / 4; ++u) sm.aw[rl][q + 4 * u] = wv[u] * inv;
   }
   __syncthreads();
-  if (!merger) return;
+  if (!it.valid) return;
   // merge this split's share of the row tile: thread = 4 consecutive head dims of one row,
-  // two such items per thread with all their loads issued together
+  // every wave taking items (all of an item's loads issued together)
   constexpr int PER_TILE = 64 * kDH / 4;
   const int per = (PER_TILE + SA - 1) / SA;
   const int beg = it.sp * per, end = min(PER_TILE, beg + per);
   const Rsrc rao = make_rsrc(rot_l + a.o_ao, act_bytes(a.M, a.qd));
   const int R = a.nq * a.H;
+  if (copy_wave()) asm volatile("buffer_inv sc0" ::: "memory");   // as the mergers above
   for (int w0 = beg + (int)threadIdx.x; w0 < end; w0 += 512) {
-    V16 ov[2][kMaxSA];
+    V16 ov[1][kMaxSA];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int w = w0 + 256 * h2;
-#pragma unroll
-      for (int sp = 0; sp < kMaxSA; ++sp)
-        ov[h2][sp] = ld16<0>(rw, (sp < SA && w < end) ? (uint32_t)(((rb * SA + sp) * 64 * kDH + w * 4) * 4) : kOob);
-    }
+    for (int sp = 0; sp < kMaxSA; ++sp)
+      ov[0][sp] = ld16<0>(rw, sp < SA ? (uint32_t)(((rb * SA + sp) * 64 * kDH + w0 * 4) * 4) : kOob);
     __builtin_amdgcn_sched_barrier(0);   // every load in flight before the first use
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int w = w0 + 256 * h2;
-      if (w >= end) break;
+    for (int h2 = 0; h2 < 1; ++h2) {
+      const int w = w0;
       const int ln = w & 63, db = (w >> 6) % kDB, ww = w / (64 * kDB);
       const int rl = 16 * ww + (ln & 15);
       f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -679,6 +675,10 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
       }
     }
   }
+  // the copy waves stored merge results too: they complete before this workgroup arrives at
+  // the barrier (grid_sync waits only for the store waves' memory operations); their O
+  // weight copies, issued before the wait for the splits, are waited for with them
+  if (copy_wave()) wait_all();
 }
 
 // ---------------------------------------------------------------------------------------
