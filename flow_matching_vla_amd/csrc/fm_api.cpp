@@ -510,7 +510,7 @@ RotLayout rot_layout(const fm_ctx* ctx) {
   const long Mp = round_up(M, 16);   // the GEMM operands hs, ao, hsu, act: whole 16-row blocks
   r.o_hs = put(Mp * D * 2);
   r.o_st = put(M * (D / 16) * 4);
-  r.o_q = put(M * qd * 2);
+  r.o_q = put(B * round_up((long)c.n_heads * c.action_horizon, 16) * dh * 2);   // folded rows
   r.o_sk = put(B * r.Hp * dh * 2);
   r.o_svt = put(B * dh * r.Hp * 2);
   r.o_ao = put(Mp * qd * 2);

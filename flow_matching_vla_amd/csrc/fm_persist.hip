@@ -242,6 +242,11 @@ __device__ __forceinline__ void read_w(const Smem& sm, V16 (&wr)[2][kPCh], int n
 __device__ __forceinline__ uint32_t act_off(int r, int k, int K) {
   return (uint32_t)(((((r >> 4) * (K >> 5) + (k >> 5)) * 64 + (r & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7)) * 2);
 }
+// Folded attention row of query head n, token i of request b: requests hold nq H rows
+// (head-major), padded to whole 16-row blocks.
+__device__ __forceinline__ int q_row(LA& a, int b, int n, int i) {
+  return b * ((a.nq * a.H + 15) & ~15) + n * a.H + i;
+}
 // bytes of a K-wide operand of M rows (whole row blocks)
 __device__ __forceinline__ uint32_t act_bytes(int M, int K) { return (uint32_t)(((M + 15) & ~15) * K * 2); }
 
@@ -497,13 +502,15 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
   const int w4 = wave & 3, half = wave >> 2;
   frag qf[kDCH];
   {
-    const int R = a.nq * a.H;
-    const int r = min(it.rt * 64 + 16 * w4 + (lane & 15), R - 1);
-    const int n = r / a.H, t = r % a.H;
-    const Rsrc rq = make_rsrc(rot_l + a.o_q, (uint32_t)(a.M * a.qd * 2));
-    const uint32_t base = (uint32_t)((((it.b * a.H + t) * a.qd) + n * kDH + (lane >> 4) * 8) * 2);
+    // q is stored fragment-major over the folded rows of each request (q_row): the 16 rows
+    // of this wave are one contiguous kilobyte per 32-wide d chunk
+    const int R = a.nq * a.H, Rp = (R + 15) & ~15;
+    const int rloc = it.rt * 64 + 16 * w4 + (lane & 15);
+    const int blk = (it.b * Rp + it.rt * 64 + 16 * w4) >> 4;
+    const Rsrc rq = make_rsrc(rot_l + a.o_q, (uint32_t)(a.B * Rp * kDH * 2));
 #pragma unroll
-    for (int c = 0; c < kDCH; ++c) qf[c] = __builtin_bit_cast(frag, ld16<0>(rq, it.valid ? base + c * 64 : kOob));
+    for (int c = 0; c < kDCH; ++c)
+      qf[c] = __builtin_bit_cast(frag, ld16<0>(rq, (it.valid && rloc < R) ? (uint32_t)(((blk * kDCH + c) * 64 + lane) * 16) : kOob));
   }
   // the suffix tiles are this phase's inputs: copy them now (prefix tiles were issued
   // before the barrier)
@@ -853,8 +860,9 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
               y[3] = x3 * cs[2] + x2 * cs[3];
             }
             if (n < a.qd) {
-              const Rsrc rq = make_rsrc(rl + a.o_q, (uint32_t)(M * a.qd * 2));
-              st8(rq, (uint32_t)((er * a.qd + n) * 2), u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])});
+              const int Rp = (a.nq * a.H + 15) & ~15;
+              const Rsrc rq = make_rsrc(rl + a.o_q, (uint32_t)(a.B * Rp * kDH * 2));
+              st8(rq, act_off(q_row(a, b, n / kDH, i), n % kDH, kDH), u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])});
             } else if (n < a.qd + kDH) {
               const Rsrc rk = make_rsrc(rl + a.o_sk, (uint32_t)(a.B * a.Hp * kDH * 2));
               st8(rk, (uint32_t)(((b * a.Hp + i) * kDH + (n - a.qd)) * 2), u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])});
