@@ -533,6 +533,9 @@ fm_status loop_buffers(fm_ctx* ctx, int steps) {
   void* p;
   fm_status s = dalloc(ctx, &p, need);
   if (s != FM_OK) return s;
+  // zeroed once: key slots past the horizon in the last suffix K / V^T tile are never
+  // written, and their zero softmax weight must not meet a stale NaN or Inf
+  HIPCK(hipMemsetAsync(p, 0, need, ctx->stream));
   ctx->rot = (char*)p;
   ctx->rot_bytes = need;
   return FM_OK;

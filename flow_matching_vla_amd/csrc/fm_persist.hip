@@ -479,7 +479,15 @@ __device__ __forceinline__ void attn_issue(LA& a, const AttnItem& it, int l, con
   for (int i = 0; i < kFPW; ++i) {
     const int f = (suffix ? wave : wave - 4 + 4 * sec) * kFPW + i;
     uint32_t off;
-    if (f < kFK) {
+    if (is_suf) {   // this step's K and V^T are fragment-major: contiguous kilobytes
+      if (f < kFK) {
+        const int kb = f / kDCH, c = f % kDCH;
+        off = (uint32_t)(((((kt >> 4) + kb) * kDCH + c) * 64 + lane) * 16);
+      } else {
+        const int db = f - kFK;
+        off = (uint32_t)(((db * (vds >> 5) + (kt >> 5)) * 64 + lane) * 16);
+      }
+    } else if (f < kFK) {
       const int kb = f / kDCH, c = f % kDCH;
       off = (uint32_t)(((kt + 16 * kb + (lane & 15)) * kDH + c * 32 + (lane >> 4) * 8) * 2);
     } else {
@@ -864,15 +872,16 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
               const Rsrc rq = make_rsrc(rl + a.o_q, (uint32_t)(a.B * Rp * kDH * 2));
               st8(rq, act_off(q_row(a, b, n / kDH, i), n % kDH, kDH), u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])});
             } else if (n < a.qd + kDH) {
+              // this step's K ([b][Hp keys][dh]) and V^T ([b][dh][Hp key slots]) fragment-major
               const Rsrc rk = make_rsrc(rl + a.o_sk, (uint32_t)(a.B * a.Hp * kDH * 2));
-              st8(rk, (uint32_t)(((b * a.Hp + i) * kDH + (n - a.qd)) * 2), u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])});
+              st8(rk, act_off(b * a.Hp + i, n - a.qd, kDH), u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])});
             } else {
               const Rsrc rv = make_rsrc(rl + a.o_svt, (uint32_t)(a.B * kDH * a.Hp * 2));
               const int d0 = n - a.qd - kDH;
               const int slot = vt_slot<bf16>(i);
 #pragma unroll
               for (int j = 0; j < 4; ++j)
-                st2(rv, (uint32_t)(((b * kDH + d0 + j) * a.Hp + slot) * 2), __builtin_bit_cast(uint16_t, (bf16)y[j]));
+                st2(rv, act_off(b * kDH + d0 + j, slot, a.Hp), __builtin_bit_cast(uint16_t, (bf16)y[j]));
             }
           }
         }
