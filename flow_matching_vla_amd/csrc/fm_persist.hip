@@ -850,10 +850,6 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         f32x4 v[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         if (nslot) gemm_core(wr, ra, sm, nslot, v);
         __syncthreads();   // rinv visible; every read of the wave partial tiles is done
-        // prefix tiles of this layer's attention item, into the buffer the partial tiles
-        // used; in flight across the barrier
-        attn_issue(a, ait, l, rl, 0, false, sm);
-        attn_issue(a, ait, l, rl, 1, false, sm);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int n = ((int)blockIdx.x + s2 * G) * 16 + 4 * eq;
@@ -885,6 +881,12 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
             }
           }
         }
+        // prefix tiles of this layer's attention item, into the buffer the partial tiles
+        // used; in flight across the barrier. Issued after the stores above, which the
+        // barrier waits for and which would otherwise queue behind these copies.
+        __syncthreads();
+        attn_issue(a, ait, l, rl, 0, false, sm);
+        attn_issue(a, ait, l, rl, 1, false, sm);
         grid_sync(a.flags, ++e);
       }
       // ---- attention: key-split partials, merged per row tile on its XCD ---------------
