@@ -332,6 +332,50 @@ def run(cfg, weights, inputs, steps=None, tau=None, dtype=np.float64, return_tra
                    return_trace=return_trace, dtype=dtype)
 
 
+# ----------------------------------------------------------------------------- after the path
+# The chunk leaves the loop in normalized model space; the step after maps it back to robot
+# units with the action statistics (q01, q99 per dimension) and keeps the robot's share.
+UNNORM_QUANTILE_EPS = 0    # pi0.5 (openpi quantile normalization, epsilon included)
+UNNORM_QUANTILE_CLIP = 1   # GR00T (clip to [-1, 1], no epsilon)
+QUANTILE_EPS = 1e-6
+
+
+def quantile_normalize(x, q01, q99, kind):
+    """Normalization of robot values into [-1, 1]-ish model space, written to pin its inverse.
+    pi0.5 Design, "Embodiment adapters": (x - q01) / (q99 - q01 + 1e-6) * 2 - 1.
+    GR00T N1.7, "Policy contract": 2 (x - q01) / (q99 - q01) - 1 clipped to [-1, 1], a group
+    whose q99 equals its q01 mapping to zero instead of dividing by its range."""
+    x = np.asarray(x, np.float64)
+    q01 = np.asarray(q01, np.float64)
+    q99 = np.asarray(q99, np.float64)
+    if kind == UNNORM_QUANTILE_EPS:
+        return (x - q01) / (q99 - q01 + QUANTILE_EPS) * 2.0 - 1.0
+    span = q99 - q01
+    safe = np.where(span == 0, 1.0, span)
+    y = np.clip(2.0 * (x - q01) / safe - 1.0, -1.0, 1.0)
+    return np.where(span == 0, 0.0, y)
+
+
+def quantile_unnormalize(x, q01, q99, kind, robot_horizon=None, robot_dim=None):
+    """Model-space chunk [B, H, d_a] -> robot units [B, robot_horizon, robot_dim].
+    pi0.5 Design, "Embodiment adapters": the openpi normalization above inverted,
+    (x + 1) / 2 * (q99 - q01 + 1e-6) + q01, then the chunk sliced to the robot's width.
+    GR00T N1.7, "Policy contract": (clip(x, -1, 1) + 1) / 2 * (q99 - q01) + q01 with no
+    guard, the policy keeping its own horizon (shorter than the model's) and width.
+    q01 / q99 hold robot_dim values (the first robot_dim model dimensions)."""
+    x = np.asarray(x, np.float64)
+    B, H, da = x.shape
+    hr = H if robot_horizon is None else robot_horizon
+    dr = da if robot_dim is None else robot_dim
+    assert 0 < hr <= H and 0 < dr <= da
+    q01 = np.asarray(q01, np.float64).reshape(dr)
+    q99 = np.asarray(q99, np.float64).reshape(dr)
+    xs = x[:, :hr, :dr]
+    if kind == UNNORM_QUANTILE_EPS:
+        return (xs + 1.0) / 2.0 * (q99 - q01 + QUANTILE_EPS) + q01
+    return (np.clip(xs, -1.0, 1.0) + 1.0) / 2.0 * (q99 - q01) + q01
+
+
 # ----------------------------------------------------------------------------- metrics
 def e_inf(a, ref):
     """Maximum absolute error (vla.cpp Sec. III-E, Eq. (5))."""

@@ -463,3 +463,65 @@ def test_scalar_brute_force_dit_micro():
     Wl = {k: np.asarray(a).tolist() for k, a in W.items()}
     ref = _brute_velocity_dit(cfg, Wl, I, x[0].tolist(), table[0].tolist(), tb[0].tolist())
     np.testing.assert_allclose(v[0], np.array(ref), rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- after the path
+def test_quantile_unnormalize_inverts_openpi_normalization():
+    # pi0.5 Design, "Embodiment adapters": the normalization with its epsilon, inverted
+    rng = np.random.default_rng(7)
+    q01 = rng.normal(size=7) - 1.0
+    q99 = q01 + rng.uniform(0.1, 3.0, size=7)
+    x = rng.uniform(q01 - 0.5, q99 + 0.5, size=(2, 5, 7))
+    y = oracle.quantile_normalize(x, q01, q99, oracle.UNNORM_QUANTILE_EPS)
+    pad = np.concatenate([y, rng.normal(size=(2, 5, 25))], axis=2)   # model width 32
+    back = oracle.quantile_unnormalize(pad, q01, q99, oracle.UNNORM_QUANTILE_EPS, robot_dim=7)
+    np.testing.assert_allclose(back, x, rtol=0, atol=1e-12)
+    # the ends of the model range: -1 -> q01, +1 -> q99 + 1e-6 (the epsilon is part of the formula)
+    ends = np.stack([-np.ones(7), np.ones(7)])[None]
+    u = oracle.quantile_unnormalize(ends, q01, q99, oracle.UNNORM_QUANTILE_EPS)
+    np.testing.assert_array_equal(u[0, 0], q01)
+    np.testing.assert_allclose(u[0, 1], q99 + 1e-6, rtol=0, atol=1e-15)
+
+
+def test_quantile_unnormalize_gr00t_clip_and_slice():
+    # GR00T N1.7, "Policy contract": clip to [-1, 1], no epsilon, no guard; the policy keeps
+    # a horizon shorter than the model's 40 and the robot's width
+    q01 = np.array([-2.0, 0.0, 1.0, 5.0, -1.0, 0.5, 0.0])
+    q99 = np.array([2.0, 1.0, 3.0, 5.0, 1.0, 0.5, 4.0])   # dims 3 and 5 degenerate
+    x = np.zeros((1, 40, 32))
+    x[0, 0, :7] = [-1.0, 1.0, 0.0, 0.3, 7.0, -9.0, 0.5]
+    x[0, 1, :7] = [3.0, -3.0, 1.0, 1.0, -1.0, 1.0, -0.5]
+    x[0, 20, :] = 99.0                                     # past the kept horizon
+    u = oracle.quantile_unnormalize(x, q01, q99, oracle.UNNORM_QUANTILE_CLIP, robot_horizon=16, robot_dim=7)
+    assert u.shape == (1, 16, 7)
+    np.testing.assert_allclose(u[0, 0], [-2.0, 1.0, 2.0, 5.0, 1.0, 0.5, 3.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(u[0, 1], [2.0, 0.0, 3.0, 5.0, -1.0, 0.5, 1.0], rtol=0, atol=1e-15)
+    # x = 0 -> midpoint of (q01, q99) for every kept step without a planted value
+    np.testing.assert_allclose(u[0, 2:], np.broadcast_to((q01 + q99) / 2, (14, 7)), rtol=0, atol=1e-15)
+    # normalization maps a degenerate group to zero and clips the rest
+    y = oracle.quantile_normalize(np.array([5.0, 9.0]), np.array([5.0, 0.0]), np.array([5.0, 4.0]),
+                                  oracle.UNNORM_QUANTILE_CLIP)
+    np.testing.assert_array_equal(y, [0.0, 1.0])
+    # round trip inside the bounds (non-degenerate groups)
+    rng = np.random.default_rng(3)
+    lo = rng.normal(size=4); hi = lo + rng.uniform(0.5, 2.0, size=4)
+    v = rng.uniform(lo, hi, size=(3, 6, 4))
+    back = oracle.quantile_unnormalize(oracle.quantile_normalize(v, lo, hi, oracle.UNNORM_QUANTILE_CLIP),
+                                       lo, hi, oracle.UNNORM_QUANTILE_CLIP)
+    np.testing.assert_allclose(back, v, rtol=0, atol=1e-12)
+
+
+def test_increasing_schedule_constant_field():
+    # GR00T integrates tau 0 -> 1 (vla.cpp Eq. (1) with the schedule reversed): the direction
+    # is the tau array alone; with a constant field x_T = x_0 + (tau_T - tau_0) c
+    T = 4
+    tau = np.arange(T + 1) / T
+    sched = oracle.schedule(T, tau)
+    np.testing.assert_allclose(np.diff(sched), 1.0 / T)
+    cfg = _tiny()
+    w, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+    c = np.linspace(-1.0, 1.0, cfg["action_dim"]).astype(np.float32)
+    w["action_out.w"] = np.zeros_like(w["action_out.w"])
+    w["action_out.b"] = c
+    xT = oracle.run(cfg, w, I, steps=T, tau=tau)
+    np.testing.assert_allclose(xT, I["x0"].astype(np.float64) + c.astype(np.float64), rtol=0, atol=1e-12)
