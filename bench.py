@@ -298,9 +298,37 @@ def main():
                                "frac": round(ach / peak, 4), "traffic": None, "kernel_role": dom,
                                "alg_flops_per_launch": int(nflops), "avg_launch_us": round(avg_s * 1e6, 2),
                                "launches_per_chunk": roles[dom][1]}
+    # the step after the path: the chunk back to robot units (LIBERO width 7; GR00T's policy
+    # keeps 16 of the model's 40 steps), timed with HIP events on the context stream
+    post_kind = fm.UNNORM_QUANTILE_EPS if cfg["arch"] == 0 else fm.UNNORM_QUANTILE_CLIP
+    post_h = cfg["action_horizon"] if cfg["arch"] == 0 else min(16, cfg["action_horizon"])
+    post_d = min(7, cfg["action_dim"])
+    q01 = -np.linspace(1.0, 2.0, post_d, dtype=np.float32)
+    q99 = np.linspace(1.0, 3.0, post_d, dtype=np.float32)
+    ctx.set_action_stats(post_kind, post_h, post_d, q01, q99)
+    ctx.denoise(x0, T, out)
+    robot = ctx.unnormalize(out, post_h, post_d)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(200):
+        ctx.unnormalize(out, post_h, post_d, robot)
+    b.record(stream)
+    torch.cuda.synchronize()
+    post_us = a.elapsed_time(b) / 200 * 1000
+    post_bytes = 2 * B * post_h * post_d * 4 + 2 * post_d * 4
+    res["post"] = {"kernel": "k_unnormalize", "kind": "quantile+eps (pi0.5)" if post_kind == 0 else "quantile clip (GR00T)",
+                   "robot_horizon": post_h, "robot_dim": post_d, "us_per_chunk": round(post_us, 2),
+                   "alg_bytes": int(post_bytes), "achieved_GBps": round(post_bytes / (post_us * 1e-6) / 1e9, 2)}
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, W, I)
+        import oracle
+        chunk = out.cpu().numpy()
+        t1 = time.perf_counter()
+        for _ in range(100):
+            oracle.quantile_unnormalize(chunk, q01, q99, post_kind, post_h, post_d)
+        res["post"]["oracle_us"] = round((time.perf_counter() - t1) / 100 * 1e6, 2)
     ctx.close()
     print(json.dumps(res), flush=True)
 

@@ -193,6 +193,10 @@ struct fm_ctx {
   LayerW* lw_dev = nullptr;          // [n_layers] weight pointers
   std::vector<LayerW> lw_host;
 
+  // the step after the path: action statistics of the robot's share of the chunk
+  int unnorm_kind = -1, robot_h = 0, robot_d = 0;
+  float *q01 = nullptr, *q99 = nullptr;   // [action_dim] each
+
   // captured loop
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
@@ -1181,6 +1185,43 @@ static fm_status step_eager(fm_ctx* ctx, const float* xin, int32_t k, float* v, 
 fm_status fm_step_velocity(fm_ctx* ctx, const float* x, int32_t k, float* v) {
   if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
   return step_eager(ctx, x, k, v, nullptr);
+}
+
+fm_status fm_set_action_stats(fm_ctx* ctx, int32_t kind, int32_t robot_horizon, int32_t robot_dim,
+                              const float* q01_host, const float* q99_host) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  const fm_config& c = ctx->c;
+  if ((kind != FM_UNNORM_QUANTILE_EPS && kind != FM_UNNORM_QUANTILE_CLIP) || robot_horizon < 1 ||
+      robot_horizon > c.action_horizon || robot_dim < 1 || robot_dim > c.action_dim || !q01_host || !q99_host)
+    return fail(ctx, FM_ERR_INVALID_ARG,
+                fmt("fm_set_action_stats: kind %d, robot horizon %d (1..%d), robot dim %d (1..%d), q01/q99 %s", kind,
+                    robot_horizon, c.action_horizon, robot_dim, c.action_dim, q01_host && q99_host ? "given" : "missing"));
+  if (!ctx->q01) {
+    void* p;
+    fm_status s = dalloc(ctx, &p, 2 * (size_t)c.action_dim * sizeof(float));
+    if (s != FM_OK) return s;
+    ctx->q01 = (float*)p;
+    ctx->q99 = ctx->q01 + c.action_dim;
+  }
+  HIPCK(hipMemcpyAsync(ctx->q01, q01_host, (size_t)robot_dim * sizeof(float), hipMemcpyHostToDevice, ctx->stream));
+  HIPCK(hipMemcpyAsync(ctx->q99, q99_host, (size_t)robot_dim * sizeof(float), hipMemcpyHostToDevice, ctx->stream));
+  // the host arrays may be reused once this returns
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  ctx->unnorm_kind = kind; ctx->robot_h = robot_horizon; ctx->robot_d = robot_dim;
+  return FM_OK;
+}
+
+fm_status fm_unnormalize(fm_ctx* ctx, const float* x, float* out) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  if (!x || !out) return fail(ctx, FM_ERR_INVALID_ARG, "fm_unnormalize: x or out is NULL");
+  if (ctx->unnorm_kind < 0) return fail(ctx, FM_ERR_STATE, "fm_unnormalize before fm_set_action_stats");
+  if (ctx->bound_batch < 1) return fail(ctx, FM_ERR_STATE, "fm_unnormalize before a binding");
+  const fm_config& c = ctx->c;
+  HIPCK(unnormalize_launch(x, out, ctx->q01, ctx->q99, ctx->bound_batch, c.action_horizon, c.action_dim, ctx->robot_h,
+                           ctx->robot_d, ctx->unnorm_kind, ctx->stream));
+  return FM_OK;
 }
 
 fm_status fm_step_trace(fm_ctx* ctx, const float* x, int32_t k, float* v, float* trace) {

@@ -120,6 +120,9 @@ hipError_t prefix_k_copy(void* pool, long pool_bs, const void* src, int B, int P
 hipError_t prefix_v_copy_t(void* pool, long pool_bs, int cap, const void* src, int B, int P, int dh,
                            int elem, hipStream_t s);
 hipError_t fill_f32(float* dst, float v, long n, hipStream_t s);
+// model-space chunk -> robot units, first hr steps and dr dims (kind 0 / 1 as fm.h)
+hipError_t unnormalize_launch(const float* x, float* out, const float* q01, const float* q99, int B, int H, int da,
+                              int hr, int dr, int kind, hipStream_t s);
 // dst[r*dld + c] = T(src[r*sld + c] + add) for r < rows, c < cols.
 hipError_t rows_from_f32(void* dst, long dld, const float* src, long sld, int rows, int cols, float add, int elem,
                          hipStream_t s);

@@ -163,6 +163,38 @@ hipError_t rows_from_f32(void* dst, long dld, const float* src, long sld, int ro
     hipLaunchKernelGGL(k_rows_from_f32<float>, dim3(grid_for(n)), dim3(256), 0, s, (float*)dst, dld, src, sld, rows, cols, add);
   return hipGetLastError();
 }
+
+// The step after the path: a model-space chunk [B][H][da] back to robot units
+// [B][hr][dr] with per-dimension (q01, q99), and cut to the first hr steps and dr dims.
+// kind 0 (pi0.5 Design, "Embodiment adapters": openpi's quantile normalization inverted,
+// epsilon included): (x + 1) / 2 * (q99 - q01 + 1e-6) + q01. kind 1 (GR00T N1.7, "Policy
+// contract"): (clip(x, -1, 1) + 1) / 2 * (q99 - q01) + q01. One thread per output element.
+__global__ void k_unnormalize(const float* __restrict__ x, float* __restrict__ out, const float* __restrict__ q01,
+                              const float* __restrict__ q99, int B, int H, int da, int hr, int dr, int kind) {
+  const long n = (long)B * hr * dr;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const int j = (int)(i % dr);
+    const long bt = i / dr;
+    const int t = (int)(bt % hr), b = (int)(bt / hr);
+    float v = x[((long)b * H + t) * da + j];
+    const float lo = q01[j], hi = q99[j];
+    if (kind == 0) {
+      out[i] = (v + 1.f) * 0.5f * (hi - lo + 1e-6f) + lo;
+    } else {
+      v = fminf(fmaxf(v, -1.f), 1.f);
+      out[i] = (v + 1.f) * 0.5f * (hi - lo) + lo;
+    }
+  }
+}
+
+hipError_t unnormalize_launch(const float* x, float* out, const float* q01, const float* q99, int B, int H, int da,
+                              int hr, int dr, int kind, hipStream_t s) {
+  const long n = (long)B * hr * dr;
+  if (n <= 0) return hipSuccess;
+  const int grid = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+  hipLaunchKernelGGL(k_unnormalize, dim3(grid), dim3(256), 0, s, x, out, q01, q99, B, H, da, hr, dr, kind);
+  return hipGetLastError();
+}
 hipError_t fill_f32(float* dst, float v, long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill, dim3(grid_for(n)), dim3(256), 0, s, dst, v, n);

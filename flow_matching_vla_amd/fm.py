@@ -73,6 +73,8 @@ def lib():
         "fm_profile_loop": ([VP, VP, I32, VP, I32, P(C.c_float), P(I32)], I32),
         "fm_set_loop_mode": ([VP, I32], I32),
         "fm_loop_status": ([VP, P(I32), P(C.c_uint32)], I32),
+        "fm_set_action_stats": ([VP, I32, I32, I32, P(C.c_float), P(C.c_float)], I32),
+        "fm_unnormalize": ([VP, VP, VP], I32),
         "fm_op_linear": ([I32, I32, I32, I32, VP, VP, VP, I32, VP, I32, VP], I32),
         "fm_op_attention": ([I32, I32, I32, I32, I32, I32, I32, VP, VP, VP, VP, VP], I32),
     }
@@ -231,6 +233,25 @@ class Context:
         """LOOP_AUTO: the persistent loop kernel where it applies; LOOP_GRAPH: per-op graph."""
         _check(lib().fm_set_loop_mode(self.h, mode), self.h)
 
+    def set_action_stats(self, kind: int, robot_horizon: int, robot_dim: int, q01, q99):
+        """Action statistics of the step after the path (kind UNNORM_QUANTILE_EPS / _CLIP)."""
+        import numpy as np
+        lo = np.ascontiguousarray(q01, np.float32).ravel()
+        hi = np.ascontiguousarray(q99, np.float32).ravel()
+        if lo.size != robot_dim or hi.size != robot_dim:
+            raise ValueError(f"q01 / q99 need {robot_dim} values each")
+        fp = C.POINTER(C.c_float)
+        _check(lib().fm_set_action_stats(self.h, kind, robot_horizon, robot_dim, lo.ctypes.data_as(fp),
+                                         hi.ctypes.data_as(fp)), self.h)
+
+    def unnormalize(self, x, robot_horizon: int, robot_dim: int, out=None):
+        """Model-space chunk (device fp32 [B, H, d_a]) -> robot units [B, robot_horizon, robot_dim]."""
+        torch = _torch()
+        if out is None:
+            out = torch.empty((x.shape[0], robot_horizon, robot_dim), dtype=torch.float32, device=x.device)
+        _check(lib().fm_unnormalize(self.h, _ptr(x), _ptr(out)), self.h)
+        return out
+
     def loop_status(self):
         """(persistent kernel serves the loop, fault word); raises FMError on a fault."""
         p, f = C.c_int32(), C.c_uint32()
@@ -249,6 +270,7 @@ class Context:
 
 OP_ROLES = {"inproj": 0, "qkv": 1, "attn": 2, "oproj": 3, "mlp_up": 4, "mlp_down": 5, "out": 6, "loop": 7}
 LOOP_AUTO, LOOP_GRAPH = 0, 1
+UNNORM_QUANTILE_EPS, UNNORM_QUANTILE_CLIP = 0, 1
 
 
 def profile_loop(ctx: "Context", x0, steps: int, role: str, out=None):

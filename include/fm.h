@@ -167,6 +167,28 @@ fm_status fm_denoise(fm_ctx* ctx, const float* x0_dev, int32_t steps, float* out
  * kernels launched eagerly). */
 fm_status fm_step_velocity(fm_ctx* ctx, const float* x_dev, int32_t k, float* v_dev);
 
+/* The step after the path: the chunk leaves fm_denoise in normalized model space, and is
+ * mapped back to robot units with per-dimension action statistics and cut to the robot's
+ * share of it.
+ *   FM_UNNORM_QUANTILE_EPS (pi0.5): the inverse of openpi's quantile normalization with its
+ *     epsilon, y = (x + 1) / 2 * (q99 - q01 + 1e-6) + q01 (pi0.5 Design, "Embodiment
+ *     adapters": quantile normalization follows openpi exactly, epsilon included, inverted
+ *     on the way out; the chunk is unnormalized and sliced to the robot's width).
+ *   FM_UNNORM_QUANTILE_CLIP (GR00T): y = (clip(x, -1, 1) + 1) / 2 * (q99 - q01) + q01, no
+ *     guard for a degenerate group (GR00T N1.7, "Policy contract"; the policy keeps an
+ *     action horizon shorter than the model's).
+ * fm_set_action_stats: q01_host, q99_host HOST fp32 [robot_dim], copied; 1 <= robot_horizon
+ * <= action_horizon, 1 <= robot_dim <= action_dim (FM_ERR_INVALID_ARG otherwise). The
+ * statistics are kept until replaced.
+ * fm_unnormalize: x_dev DEVICE fp32 [batch, action_horizon, action_dim] (e.g. the output of
+ * fm_denoise), out_dev DEVICE fp32 [batch, robot_horizon, robot_dim] holding steps
+ * [0, robot_horizon) and dimensions [0, robot_dim); batch is the bound batch.
+ * FM_ERR_STATE before fm_set_action_stats or a binding. Enqueued on the context stream. */
+enum { FM_UNNORM_QUANTILE_EPS = 0, FM_UNNORM_QUANTILE_CLIP = 1 };
+fm_status fm_set_action_stats(fm_ctx* ctx, int32_t kind, int32_t robot_horizon, int32_t robot_dim,
+                              const float* q01_host, const float* q99_host);
+fm_status fm_unnormalize(fm_ctx* ctx, const float* x_dev, float* out_dev);
+
 /* Like fm_step_velocity, and also copies the fp32 residual stream after the in-projection
  * and after every layer into h_trace_dev: DEVICE fp32 [n_layers + 1, rows, hidden], rows =
  * batch * (state_tokens + H). Intermediate tensors localize a discrepancy (vla.cpp
