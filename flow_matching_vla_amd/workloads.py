@@ -174,3 +174,36 @@ def make_inputs(cfg) -> dict:
 
 def param_count(cfg) -> int:
     return int(sum(int(np.prod(s)) for s in weight_shapes(cfg).values()))
+
+
+def make_visibility(cfg, seed: int = 0) -> dict:
+    """Seeded per-request key visibility for a mixed-request batch (no arithmetic of the
+    method: lengths and booleans only).
+
+    PREFIX_JOINT -> {"prefix_lens": int32 [B]}: request 0 keeps the whole bound prefix, the
+    others a uniform draw in [P/2, P]: compact prefixes of different lengths sharing one
+    binding.
+    DIT_CROSS -> {"text_mask", "image_mask": bool [B, S]}: every context token is an image
+    token (probability 3/4) or a text token, interleaved at random (the masks are arbitrary
+    booleans, not spans); a uniform number in [0, S/4] of trailing tokens per request is
+    padding, hidden from both. A request left with no visible token in a mask sees token 0
+    in it."""
+    rng = np.random.default_rng(7919 * (cfg["index"] + 1) + seed)
+    B = cfg["batch"]
+    if cfg["arch"] == ARCH_PREFIX_JOINT:
+        P = cfg["prefix_len"]
+        lens = rng.integers(P // 2, P + 1, size=B).astype(np.int32)
+        lens[0] = P
+        return {"prefix_lens": lens}
+    S = cfg["ctx_len"]
+    image = rng.random((B, S)) < 0.75
+    valid = np.ones((B, S), dtype=bool)
+    for b in range(B):
+        pad = int(rng.integers(0, S // 4 + 1))
+        if pad:
+            valid[b, S - pad:] = False
+    text_mask = valid & ~image
+    image_mask = valid & image
+    for m in (text_mask, image_mask):   # an empty mask shows token 0 (masks may overlap)
+        m[~m.any(axis=1), 0] = True
+    return {"text_mask": text_mask, "image_mask": image_mask}

@@ -122,16 +122,22 @@ def rope(x, positions, base):
 
 
 # ----------------------------------------------------------------------------- attention
-def attention(q, k, v):
-    """softmax(Q K^T / sqrt(d_k)) V with no mask (vla.cpp Eq. (2), M = 0), softmax over keys.
+def attention(q, k, v, visible=None):
+    """softmax(Q K^T / sqrt(d_k) + M) V (vla.cpp Eq. (2)), softmax over keys. The additive mask
+    M is 0 where `visible` is true and -inf where it is false; visible=None is M = 0.
 
     q: [B, n_q, Tq, d]; k, v: [B, n_kv, Tk, d] with n_kv == 1 (the single K/V head shared by
-    every query head, pi0.5 Design "Attention and the K/V pool") or n_kv == n_q."""
+    every query head, pi0.5 Design "Attention and the K/V pool") or n_kv == n_q; visible:
+    booleans broadcastable to [B, n_q, Tq, Tk]. A query row with no visible key has no
+    defined result (0 / 0); it comes out NaN here."""
     d = q.shape[-1]
     s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(d)
-    s = s - np.max(s, axis=-1, keepdims=True)
-    p = np.exp(s)
-    p = p / np.sum(p, axis=-1, keepdims=True)
+    if visible is not None:
+        s = s + np.where(visible, 0.0, -np.inf).astype(s.dtype)
+    with np.errstate(invalid="ignore"):
+        s = s - np.max(s, axis=-1, keepdims=True)
+        p = np.exp(s)
+        p = p / np.sum(p, axis=-1, keepdims=True)
     return p @ v
 
 
@@ -182,14 +188,25 @@ def bind(cfg, w, inputs, dtype=np.float64):
     Sec. III-B, observation reuse; GR00T N1.7 "Who runs what", vl_backbone row).
 
     pi0.5: the per-layer prefix K/V [B, P, 1, d_h] as given (already rotated by the
-    prefix tower). DiT: cross K/V of each even block, K_c = Z W_K^T, V_c = Z W_V^T, and
-    the state token W_s s + b_s. Arrays are returned read-only: the loop never writes them."""
+    prefix tower), and each request's compact prefix length P_b <= P ("prefix_lens", int
+    [B]; default P for all): request b attends to its first P_b prefix keys and its chunk
+    sits at positions P_b + i (pi0.5 Design, "Component contract": the filled length after
+    the append is per request, and the prefix is compact). DiT: cross K/V of each even
+    block, K_c = Z W_K^T, V_c = Z W_V^T, the state token W_s s + b_s, and the text and image
+    masks over the context ("text_mask", "image_mask", bool [B, S]; default all visible;
+    GR00T N1.7 section "action"). Arrays are returned read-only: the loop never writes them."""
     out = {}
     if cfg["arch"] == ARCH_PREFIX_JOINT:
         L = cfg["n_layers"]
         out["k"] = [np.asarray(inputs[f"prefix.k.{l}"], dtype=dtype)[:, :, 0, :][:, None] for l in range(L)]
         out["v"] = [np.asarray(inputs[f"prefix.v.{l}"], dtype=dtype)[:, :, 0, :][:, None] for l in range(L)]
         out["prefix_len"] = out["k"][0].shape[2] if L else 0
+        B = out["k"][0].shape[0] if L else cfg["batch"]
+        lens = inputs.get("prefix_lens")
+        lens = np.full(B, out["prefix_len"], dtype=np.int64) if lens is None else np.asarray(lens, dtype=np.int64)
+        if lens.shape != (B,) or np.any(lens < 0) or np.any(lens > out["prefix_len"]):
+            raise ValueError("prefix_lens must be [B] within [0, prefix_len]")
+        out["prefix_lens"] = lens
     else:
         nh, dh = cfg["n_heads"], cfg["head_dim"]
         z = np.asarray(inputs["context"], dtype=dtype)
@@ -202,6 +219,11 @@ def bind(cfg, w, inputs, dtype=np.float64):
             out["v"][i] = vc.reshape(B, S, nh, dh).transpose(0, 2, 1, 3)
         s = np.asarray(inputs["state"], dtype=dtype)
         out["state_token"] = linear(s, w["state_in.w"].astype(dtype), w["state_in.b"].astype(dtype))
+        for name in ("text_mask", "image_mask"):
+            m = inputs.get(name)
+            out[name] = np.ones((B, S), dtype=bool) if m is None else np.asarray(m, dtype=bool)
+            if out[name].shape != (B, S):
+                raise ValueError(f"{name} must be [B, S]")
     for key in ("k", "v"):
         vals = out[key].values() if isinstance(out[key], dict) else out[key]
         for a in vals:
@@ -218,8 +240,7 @@ def velocity_prefix_joint(cfg, w, bound, x, row, trace=None):
     D, L = cfg["hidden"], cfg["n_layers"]
     nq, dh, eps = cfg["n_heads"], cfg["head_dim"], cfg["norm_eps"]
     B, H, _ = x.shape
-    P = bound["prefix_len"]
-    pos = P + np.arange(H)  # suffix positions continue after the compact prefix
+    lens = bound["prefix_lens"]
     h = linear(x, w["action_in.w"], w["action_in.b"])
     if trace is not None:
         trace.append(h)
@@ -230,12 +251,18 @@ def velocity_prefix_joint(cfg, w, bound, x, row, trace=None):
         q = linear(u, w[p + "q.w"]).reshape(B, H, nq, dh).transpose(0, 2, 1, 3)
         k = linear(u, w[p + "k.w"]).reshape(B, H, 1, dh).transpose(0, 2, 1, 3)
         v = linear(u, w[p + "v.w"]).reshape(B, H, 1, dh).transpose(0, 2, 1, 3)
-        if cfg["rope_base"] > 0:
-            q = rope(q, pos, cfg["rope_base"])
-            k = rope(k, pos, cfg["rope_base"])
-        K = np.concatenate([bound["k"][l], k], axis=2)   # suffix appended after the prefix
-        V = np.concatenate([bound["v"][l], v], axis=2)
-        o = attention(q, K, V).transpose(0, 2, 1, 3).reshape(B, H, nq * dh)
+        o = np.empty((B, nq, H, dh), dtype=h.dtype)
+        for b in range(B):   # each request: its compact prefix, then its own chunk
+            P = lens[b]
+            pos = P + np.arange(H)   # suffix positions continue after the compact prefix
+            qb, kb = q[b:b + 1], k[b:b + 1]
+            if cfg["rope_base"] > 0:
+                qb = rope(qb, pos, cfg["rope_base"])
+                kb = rope(kb, pos, cfg["rope_base"])
+            K = np.concatenate([bound["k"][l][b:b + 1, :, :P], kb], axis=2)   # suffix after the prefix
+            V = np.concatenate([bound["v"][l][b:b + 1, :, :P], v[b:b + 1]], axis=2)
+            o[b] = attention(qb, K, V)[0]
+        o = o.transpose(0, 2, 1, 3).reshape(B, H, nq * dh)
         h = h + gate * linear(o, w[p + "o.w"])
         scale, shift, gate = split_site(row[2 * l + 1], D)
         u = modulate(rms_norm(h, eps), scale, shift)
@@ -256,7 +283,9 @@ def velocity_dit_cross(cfg, w, bound, x, row, time_bias, trace=None):
     prepended to the action tokens; 0-based even blocks cross-attend into the bound context
     K/V, odd blocks self-attend over state + action tokens; AdaLN-modulated LayerNorm with a
     gated attention residual, plain LayerNorm + GELU feed-forward; the output norm uses the
-    last site and only action tokens are projected to the velocity."""
+    last site and only action tokens are projected to the velocity. A cross block reads the
+    text mask when its index is a multiple of 4 and the image mask otherwise (one cross block
+    in two reads text)."""
     D, L = cfg["hidden"], cfg["n_layers"]
     nh, dh, eps = cfg["n_heads"], cfg["head_dim"], cfg["norm_eps"]
     B, H, _ = x.shape
@@ -271,11 +300,15 @@ def velocity_dit_cross(cfg, w, bound, x, row, time_bias, trace=None):
         u = modulate(layer_norm(h, eps), scale, shift)
         q = linear(u, w[p + "q.w"]).reshape(B, T, nh, dh).transpose(0, 2, 1, 3)
         if i % 2 == 0:
+            # cross block: the text mask when i % 4 == 0, else the image mask
             K, V = bound["k"][i], bound["v"][i]
+            mask = bound["text_mask"] if i % 4 == 0 else bound["image_mask"]
+            vis = mask[:, None, None, :]
         else:
             K = linear(u, w[p + "k.w"]).reshape(B, T, nh, dh).transpose(0, 2, 1, 3)
             V = linear(u, w[p + "v.w"]).reshape(B, T, nh, dh).transpose(0, 2, 1, 3)
-        o = attention(q, K, V).transpose(0, 2, 1, 3).reshape(B, T, D)
+            vis = None
+        o = attention(q, K, V, vis).transpose(0, 2, 1, 3).reshape(B, T, D)
         h = h + gate * linear(o, w[p + "o.w"])
         h = h + linear(gelu_tanh(linear(layer_norm(h, eps), w[p + "ff1.w"])), w[p + "ff2.w"])
         if trace is not None:

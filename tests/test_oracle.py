@@ -400,7 +400,9 @@ def test_scalar_brute_force_pi05_micro():
     np.testing.assert_allclose(v[0], np.array(ref), rtol=1e-10, atol=1e-12)
 
 
-def _brute_velocity_dit(cfg, W, I, x, row, tb):
+def _brute_velocity_dit(cfg, W, I, x, row, tb, text=None, image=None):
+    """text / image: visible context indices of the request for the cross blocks that read
+    each mask (block i reads text when i % 4 == 0, else image); None = all visible."""
     D, L, nh, dh, F_, eps = cfg["hidden"], cfg["n_layers"], cfg["n_heads"], cfg["head_dim"], cfg["mlp_dim"], cfg["norm_eps"]
     H, da = cfg["action_horizon"], cfg["action_dim"]
     ctx = I["context"][0].astype(np.float64).tolist()
@@ -426,6 +428,10 @@ def _brute_velocity_dit(cfg, W, I, x, row, tb):
         u = [[n * (1 + row[i][c]) + row[i][D + c] for c, n in enumerate(ln(h[t]))] for t in range(T)]
         q = [mv(W[p + "q.w"], u[t]) for t in range(T)]
         src = ctx if i % 2 == 0 else u
+        if i % 2 == 0:
+            keep = text if i % 4 == 0 else image
+            if keep is not None:
+                src = [ctx[j] for j in keep]
         ks = [mv(W[p + "k.w"], s) for s in src]
         vs = [mv(W[p + "v.w"], s) for s in src]
         o = [[0.0] * D for _ in range(T)]
@@ -463,6 +469,136 @@ def test_scalar_brute_force_dit_micro():
     Wl = {k: np.asarray(a).tolist() for k, a in W.items()}
     ref = _brute_velocity_dit(cfg, Wl, I, x[0].tolist(), table[0].tolist(), tb[0].tolist())
     np.testing.assert_allclose(v[0], np.array(ref), rtol=1e-10, atol=1e-12)
+
+
+def test_scalar_brute_force_dit_micro_masked():
+    # four blocks: cross block 0 reads the text mask, cross block 2 the image mask; the
+    # brute force drops the hidden keys instead of adding -inf to their scores
+    cfg = wl.workload("dit_b1", n_layers=4, hidden=8, n_heads=2, head_dim=4, n_kv_heads=2, mlp_dim=12,
+                      action_horizon=3, action_dim=2, state_dim=3, ctx_len=7, ctx_dim=6, weight_std=0.5)
+    W, I = oracle.cast_weights(wl.make_weights(cfg)), dict(wl.make_inputs(cfg))
+    text, image = [0, 3, 4], [1, 2, 4, 6]
+    I["text_mask"] = np.isin(np.arange(7), text)[None]
+    I["image_mask"] = np.isin(np.arange(7), image)[None]
+    bound = oracle.bind(cfg, W, I)
+    tau = oracle.schedule(2)
+    table, tb = oracle.modulation_table(cfg, W, tau)
+    x = I["x0"].astype(np.float64)
+    v = oracle.velocity(cfg, W, bound, x, table, tb, 1)
+    Wl = {k: np.asarray(a).tolist() for k, a in W.items()}
+    ref = _brute_velocity_dit(cfg, Wl, I, x[0].tolist(), table[1].tolist(), tb[1].tolist(), text, image)
+    np.testing.assert_allclose(v[0], np.array(ref), rtol=1e-10, atol=1e-12)
+    # the masks swapped give another result: each block reads its own mask
+    ref_sw = _brute_velocity_dit(cfg, Wl, I, x[0].tolist(), table[1].tolist(), tb[1].tolist(), image, text)
+    assert np.max(np.abs(v[0] - np.array(ref_sw))) > 1e-6
+
+
+# ----------------------------------------------------------------------------- masks and ragged prefixes
+def test_masked_attention_is_attention_over_visible_keys():
+    # vla.cpp Eq. (2): M = -inf on a key removes it from the softmax
+    B, nq, Tq, Tk, d = 3, 2, 4, 11, 5
+    q = RNG.standard_normal((B, nq, Tq, d))
+    k, v = RNG.standard_normal((B, 1, Tk, d)), RNG.standard_normal((B, 1, Tk, d))
+    vis = RNG.random((B, 1, Tq, Tk)) < 0.6
+    vis[..., 0] = True
+    vis[1, 0, 2] = False
+    vis[1, 0, 2, 7] = True          # a row with one visible key
+    out = oracle.attention(q, k, v, vis)
+    for b in range(B):
+        for i in range(Tq):
+            j = np.flatnonzero(vis[b, 0, i])
+            ref = oracle.attention(q[b:b + 1, :, i:i + 1], k[b:b + 1, :, j], v[b:b + 1, :, j])
+            np.testing.assert_allclose(out[b:b + 1, :, i:i + 1], ref, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(out[1, :, 2], np.broadcast_to(v[1, 0, 7], (nq, d)), rtol=1e-14)
+    # torch's boolean-mask attention (True takes part), K/V replicated over the query heads
+    ref = F.scaled_dot_product_attention(t64(q), t64(k).expand(B, nq, Tk, d), t64(v).expand(B, nq, Tk, d),
+                                         attn_mask=torch.from_numpy(vis)).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+    # all visible is M = 0; no visible key has no defined result
+    np.testing.assert_array_equal(oracle.attention(q, k, v, np.ones((B, 1, 1, Tk), bool)), oracle.attention(q, k, v))
+    assert np.all(np.isnan(oracle.attention(q, k, v, np.zeros((B, 1, 1, Tk), bool))))
+
+
+def test_ragged_prefix_equals_compact_single_request():
+    # pi0.5 Design, "Component contract": request b's filled length is P_b + H with its chunk
+    # just past its own prefix, so a ragged batch equals each request run alone on its
+    # compact prefix (positions P_b + i); prefix rows past P_b are never read
+    cfg = _tiny(batch=3, n_layers=2)
+    W, I = wl.make_weights(cfg), dict(wl.make_inputs(cfg))
+    P = cfg["prefix_len"]
+    lens = np.array([P, 37, 0])
+    Ir = dict(I, prefix_lens=lens)
+    xr = oracle.run(cfg, W, Ir, steps=3)
+    Ig = dict(Ir)
+    for l in range(cfg["n_layers"]):
+        for nm in (f"prefix.k.{l}", f"prefix.v.{l}"):
+            g = I[nm].copy()
+            for b in range(3):
+                g[b, lens[b]:] = 1e3 * RNG.standard_normal(g[b, lens[b]:].shape)
+            Ig[nm] = g
+    np.testing.assert_array_equal(oracle.run(cfg, W, Ig, steps=3), xr)
+    for b in range(3):
+        Ib = {nm: a[b:b + 1, :lens[b]] if nm.startswith("prefix.") else a[b:b + 1] for nm, a in I.items()}
+        xb = oracle.run(dict(cfg, batch=1, prefix_len=int(lens[b])), W, Ib, steps=3)
+        np.testing.assert_allclose(xr[b:b + 1], xb, rtol=1e-12, atol=1e-13)
+    # the positions follow P_b: the same rows at the full length differ
+    assert np.max(np.abs(xr[1] - oracle.run(cfg, W, I, steps=3)[1])) > 1e-6
+    with pytest.raises(ValueError):
+        oracle.bind(cfg, oracle.cast_weights(W), dict(I, prefix_lens=np.array([P + 1, 0, 0])))
+
+
+def test_dit_mask_reaches_only_its_blocks():
+    # GR00T N1.7, section "action": cross block i reads the text mask when i % 4 == 0 and the
+    # image mask otherwise. Context rows hidden from the text mask cannot move the residual
+    # after block 0; rows the image mask shows move it after block 2; rows hidden from both
+    # cannot move the velocity.
+    cfg = wl.workload("dit_b1", n_layers=4, hidden=64, n_heads=2, head_dim=32, n_kv_heads=2, mlp_dim=128,
+                      action_horizon=6, action_dim=5, state_dim=4, ctx_len=24, ctx_dim=16, weight_std=0.2)
+    W, I = wl.make_weights(cfg), dict(wl.make_inputs(cfg))
+    S = cfg["ctx_len"]
+    text = np.zeros((1, S), bool); text[0, :10] = True
+    image = np.zeros((1, S), bool); image[0, 6:18] = True
+    I.update(text_mask=text, image_mask=image)
+    W64 = oracle.cast_weights(W)
+    table, tb = oracle.modulation_table(cfg, W64, oracle.schedule(2))
+    x0 = I["x0"].astype(np.float64)
+
+    def step(inputs):
+        tr = []   # residual after the in-projection, then after every block
+        v = oracle.velocity(cfg, W64, oracle.bind(cfg, W64, inputs), x0, table, tb, 0, tr)
+        return v, tr
+
+    base, tr0 = step(I)
+
+    def moved(rows):
+        z = I["context"].copy()
+        z[0, rows] += 3.0 * RNG.standard_normal((len(rows), z.shape[2]))
+        v, tr = step(dict(I, context=z))
+        return v, [float(np.max(np.abs(a - b))) for a, b in zip(tr, tr0)]
+
+    v, d = moved([12, 15])          # shown by the image mask only
+    assert d[1] == 0.0 and d[2] == 0.0 and d[3] > 1e-6
+    v, d = moved([2, 5])            # shown by the text mask only
+    assert d[1] > 1e-6
+    v, d = moved([19, 23])          # hidden from both
+    np.testing.assert_array_equal(v, base)
+
+
+def test_dit_shared_mask_equals_compacted_context():
+    # masking keys == dropping them: with one mask for every cross block, a request equals
+    # its run on the compacted context
+    cfg = wl.workload("dit_b1", batch=2, n_layers=2, hidden=64, n_heads=2, head_dim=32, n_kv_heads=2, mlp_dim=128,
+                      action_horizon=5, action_dim=4, state_dim=3, ctx_len=20, ctx_dim=12, weight_std=0.2)
+    W, I = wl.make_weights(cfg), dict(wl.make_inputs(cfg))
+    m = RNG.random((2, 20)) < 0.5
+    m[:, 0] = True
+    xr = oracle.run(cfg, W, dict(I, text_mask=m, image_mask=m), steps=2)
+    for b in range(2):
+        j = np.flatnonzero(m[b])
+        Ib = {nm: a[b:b + 1] for nm, a in I.items()}
+        Ib["context"] = I["context"][b:b + 1, j]
+        xb = oracle.run(dict(cfg, batch=1, ctx_len=len(j)), W, Ib, steps=2)
+        np.testing.assert_allclose(xr[b:b + 1], xb, rtol=1e-12, atol=1e-13)
 
 
 # ----------------------------------------------------------------------------- after the path
