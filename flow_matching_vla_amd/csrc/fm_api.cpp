@@ -163,7 +163,12 @@ struct fm_ctx {
   void* cross_k = nullptr;    // DIT: [ceil(L/2)][Bmax][ctx_max][D]
   void* cross_vt = nullptr;   // DIT: [ceil(L/2)][Bmax][D][spad]
   float* state_tok = nullptr; // DIT: [Bmax*st][D]
-  float2* rope_cs = nullptr;  // [H][dh/2]
+  float2* rope_cs = nullptr;  // [Bmax][H][dh/2]: cos/sin at each request's chunk positions P_b + i
+  std::vector<float2> rope_pos;   // host [max_prefix_len + H][dh/2]: cos/sin of every position
+  // per-request visibility: PREFIX_JOINT compact prefix lengths, DIT text / image masks
+  int* plens = nullptr;       // [Bmax]
+  uint32_t* kmask = nullptr;  // [2][Bmax][ctx_words]: bit j % 32 of word j / 32 = key j visible
+  int ctx_words = 0;
 
   // activations
   float *h = nullptr, *x = nullptr;
@@ -336,6 +341,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       at.k_len = at.v_len = (long)c.max_batch * ctx->cap * dh;
       at.o = ctx->obuf; at.o_bs = (long)H * qd; at.o_rs = qd;
       at.B = B; at.Tq = H; at.n_heads = nq; at.heads_per_kv = nq; at.n_keys = ctx->prefix_len + H; at.dh = dh;
+      at.seg_len = ctx->plens; at.seg_end = ctx->prefix_len;   // request b: its first P_b prefix keys, then its chunk
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
       memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.role = FM_OP_ATTN; op.at = at; ops.push_back(op);
       // O projection + gated residual
@@ -378,6 +384,8 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
         at.v_bs = (long)D * ctx->spad; at.v_hs = (long)dh * ctx->spad; at.v_ds = ctx->spad;
         at.k_len = (long)c.max_batch * c.ctx_len_max * D; at.v_len = (long)c.max_batch * D * ctx->spad;
         at.n_keys = ctx->prefix_len;
+        // the text mask on cross blocks whose index is a multiple of 4, the image mask on the others
+        at.kmask = ctx->kmask + (size_t)(l % 4 == 0 ? 0 : 1) * c.max_batch * ctx->ctx_words; at.km_bs = ctx->ctx_words;
       } else {
         g = gemm_base(Mh, 3 * D, D, W.qkv);
         set_consumer(ctx, g, NORM_LN, k, l, nullptr, Mh);
@@ -571,7 +579,7 @@ fm_status loop_run(fm_ctx* ctx, int k0, int nsteps, float* vout) {
   a.wb_gu = (uint32_t)swizzled_bytes(2 * a.F, a.D, ET_BF16);
   a.wb_down = (uint32_t)swizzled_bytes(a.D, a.F, ET_BF16);
   a.wb_out = (uint32_t)swizzled_bytes(a.da, a.D, ET_BF16);
-  a.table = ctx->table; a.cbuf = ctx->cbuf; a.rope_cs = ctx->rope_cs;
+  a.table = ctx->table; a.cbuf = ctx->cbuf; a.rope_cs = ctx->rope_cs; a.plens = ctx->plens;
   a.x = ctx->x; a.h = ctx->h;
   a.pool = (const __bf16*)ctx->pool; a.plane = (long)c.max_batch * ctx->cap * c.head_dim;
   a.rot = ctx->rot; a.rot_layer = r.layer; a.rot_step = (long)(c.n_layers + 1) * r.layer;
@@ -735,7 +743,8 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
   if (c.arch == FM_ARCH_PREFIX_JOINT) {
     ctx->cap = pool_capacity(c);
     ALLOC(pool, (size_t)c.n_layers * 2 * B * ctx->cap * c.head_dim * esz, void*);
-    ALLOC(rope_cs, H * (c.head_dim / 2) * sizeof(float2), float2*);
+    ALLOC(rope_cs, B * H * (c.head_dim / 2) * sizeof(float2), float2*);
+    ALLOC(plens, B * sizeof(int), int*);
   } else {
     const size_t nc = (c.n_layers + 1) / 2;
     // transposed V planes hold whole key tiles (and the permuted slots of each)
@@ -747,8 +756,21 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
     ALLOC(vtself, B * D * ctx->tpad * esz, void*);
     ALLOC(tbias, (size_t)c.max_steps * D * 4, float*);
     if (st > 0) ALLOC(state_tok, B * st * D * 4, float*);
+    ctx->ctx_words = (int)((c.ctx_len_max + 31) / 32);
+    ALLOC(kmask, 2 * B * ctx->ctx_words * sizeof(uint32_t), uint32_t*);
   }
 #undef ALLOC
+  if (c.arch == FM_ARCH_PREFIX_JOINT) {
+    // cos/sin of positions 0 .. max_prefix_len + H - 1 (rotate_half pairs j, j + dh/2), in
+    // double; a request's chunk rows take positions P_b .. P_b + H - 1 of it
+    const int dh = c.head_dim, np = c.max_prefix_len + H;
+    ctx->rope_pos.resize((size_t)np * (dh / 2));
+    for (int j = 0; j < dh / 2; ++j) {
+      const double th = c.rope_base > 0.f ? std::pow((double)c.rope_base, -2.0 * j / dh) : 0.0;
+      for (int p = 0; p < np; ++p)
+        ctx->rope_pos[(size_t)p * (dh / 2) + j] = make_float2((float)std::cos(p * th), (float)std::sin(p * th));
+    }
+  }
   e = hipMemsetAsync(ctx->counters, 0, fm_ctx::kCounters * sizeof(unsigned), ctx->stream);
   if (e == hipSuccess) e = hipMemsetAsync(ctx->zeros, 0, kVecPad * sizeof(float), ctx->stream);
   if (e == hipSuccess) e = fill_f32(ctx->ones, 1.f, kVecPad, ctx->stream);
@@ -1033,6 +1055,44 @@ fm_status fm_set_schedule(fm_ctx* ctx, int32_t steps, int32_t batch, const float
   return FM_OK;
 }
 
+// Per-request compact prefix lengths and the cos/sin rows of each request's chunk positions
+// P_b + i. Device copies on the context stream (ordered after any loop still running on it),
+// then a wait, so the host vectors may go.
+static fm_status upload_lengths(fm_ctx* ctx, const std::vector<int>& lens) {
+  const int H = ctx->c.action_horizon, hd = ctx->c.head_dim / 2, B = (int)lens.size();
+  std::vector<float2> cs((size_t)B * H * hd);
+  for (int b = 0; b < B; ++b)
+    memcpy(&cs[(size_t)b * H * hd], &ctx->rope_pos[(size_t)lens[b] * hd], (size_t)H * hd * sizeof(float2));
+  HIPCK(hipMemcpyAsync(ctx->rope_cs, cs.data(), cs.size() * sizeof(float2), hipMemcpyHostToDevice, ctx->stream));
+  HIPCK(hipMemcpyAsync(ctx->plens, lens.data(), (size_t)B * sizeof(int), hipMemcpyHostToDevice, ctx->stream));
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  return FM_OK;
+}
+
+// Text and image masks of the DiT cross blocks, bit-packed per request (NULL: every token of
+// the bound context visible). A mask that some cross block reads must show each request at
+// least one token: softmax over no visible key has no value.
+static fm_status upload_masks(fm_ctx* ctx, int batch, int S, const uint8_t* text, const uint8_t* image) {
+  const fm_config& c = ctx->c;
+  const int W = ctx->ctx_words;
+  std::vector<uint32_t> bits((size_t)2 * c.max_batch * W, 0u);
+  const uint8_t* src[2] = {text, image};
+  const bool read[2] = {c.n_layers >= 1, c.n_layers >= 3};   // block 0 reads text, block 2 image
+  const char* name[2] = {"text", "image"};
+  for (int m = 0; m < 2; ++m)
+    for (int b = 0; b < batch; ++b) {
+      uint32_t* w = &bits[((size_t)m * c.max_batch + b) * W];
+      int seen = 0;
+      for (int j = 0; j < S; ++j)
+        if (!src[m] || src[m][(size_t)b * S + j]) { w[j / 32] |= 1u << (j % 32); ++seen; }
+      if (read[m] && seen == 0)
+        return fail(ctx, FM_ERR_INVALID_ARG, fmt("the %s mask shows request %d no context token", name[m], b));
+    }
+  HIPCK(hipMemcpyAsync(ctx->kmask, bits.data(), bits.size() * sizeof(uint32_t), hipMemcpyHostToDevice, ctx->stream));
+  HIPCK(hipStreamSynchronize(ctx->stream));
+  return FM_OK;
+}
+
 fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void* const* k_dev,
                             const void* const* v_dev, const void* ctx_dev, const void* state_dev) {
   if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
@@ -1040,7 +1100,7 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void
   if (!ctx->loaded) return fail(ctx, FM_ERR_STATE, "weights are not loaded");
   const fm_config& c = ctx->c;
   if (batch < 1 || batch > c.max_batch) return fail(ctx, FM_ERR_INVALID_ARG, fmt("batch %d outside [1, %d]", batch, c.max_batch));
-  const int D = c.hidden, H = c.action_horizon;
+  const int D = c.hidden;
   if (c.arch == FM_ARCH_PREFIX_JOINT) {
     if (plen < 0 || plen > c.max_prefix_len) return fail(ctx, FM_ERR_INVALID_ARG, fmt("prefix_len %d outside [0, %d]", plen, c.max_prefix_len));
     if (ctx_dev || state_dev) return fail(ctx, FM_ERR_INVALID_ARG, "ctx_dev / state_dev must be NULL for the prefix-joint expert");
@@ -1055,16 +1115,10 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void
       HIPCK(prefix_k_copy((char*)ctx->pool + 2 * l * plane, (long)ctx->cap * dh, k_dev[l], batch, plen, dh, c.rope_base > 0.f, ctx->elem, ctx->stream));
       HIPCK(prefix_v_copy_t((char*)ctx->pool + (2 * l + 1) * plane, (long)dh * ctx->cap, ctx->cap, v_dev[l], batch, plen, dh, ctx->elem, ctx->stream));
     }
-    // cos/sin of the chunk positions plen + i (rotate_half pairs j, j + dh/2), in double
-    std::vector<float2> cs((size_t)H * (dh / 2));
-    for (int i = 0; i < H; ++i)
-      for (int j = 0; j < dh / 2; ++j) {
-        const double th = c.rope_base > 0.f ? std::pow((double)c.rope_base, -2.0 * j / dh) : 0.0;
-        const double ang = (double)(plen + i) * th;
-        cs[(size_t)i * (dh / 2) + j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
-      }
-    HIPCK(hipMemcpyAsync(ctx->rope_cs, cs.data(), cs.size() * sizeof(float2), hipMemcpyHostToDevice, ctx->stream));
-    HIPCK(hipStreamSynchronize(ctx->stream));
+    // every request sees the whole bound prefix until fm_bind_prefix_lengths says otherwise
+    std::vector<int> lens(batch, plen);
+    fm_status s = upload_lengths(ctx, lens);
+    if (s != FM_OK) return s;
   } else {
     if (plen < 1 || plen > c.ctx_len_max) return fail(ctx, FM_ERR_INVALID_ARG, fmt("context length %d outside [1, %d]", plen, c.ctx_len_max));
     if (k_dev || v_dev) return fail(ctx, FM_ERR_INVALID_ARG, "k_dev / v_dev must be NULL for the DiT head");
@@ -1110,11 +1164,34 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void
     fm_status s = plan_ops(ctx, ops);
     if (s != FM_OK) return s;
     if ((s = enqueue_ops(ctx, ops, ctx->stream, nullptr)) != FM_OK) return s;
-    HIPCK(hipStreamSynchronize(ctx->stream));
+    // every context token visible until fm_bind_context_masks says otherwise
+    if ((s = upload_masks(ctx, batch, plen, nullptr, nullptr)) != FM_OK) return s;
   }
   ctx->bound_batch = batch;
   ctx->prefix_len = plen;
   return FM_OK;
+}
+
+fm_status fm_bind_prefix_lengths(fm_ctx* ctx, const int32_t* lens_host) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  if (ctx->c.arch != FM_ARCH_PREFIX_JOINT) return fail(ctx, FM_ERR_UNSUPPORTED, "per-request prefix lengths belong to the prefix-joint expert");
+  if (ctx->prefix_len < 0) return fail(ctx, FM_ERR_STATE, "nothing bound: call fm_bind_prefix_kv first");
+  std::vector<int> lens(ctx->bound_batch, ctx->prefix_len);
+  for (int b = 0; lens_host && b < ctx->bound_batch; ++b) {
+    if (lens_host[b] < 0 || lens_host[b] > ctx->prefix_len)
+      return fail(ctx, FM_ERR_INVALID_ARG, fmt("prefix length %d of request %d outside [0, %d]", lens_host[b], b, ctx->prefix_len));
+    lens[b] = lens_host[b];
+  }
+  return upload_lengths(ctx, lens);
+}
+
+fm_status fm_bind_context_masks(fm_ctx* ctx, const uint8_t* text_host, const uint8_t* image_host) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  if (ctx->c.arch != FM_ARCH_DIT_CROSS) return fail(ctx, FM_ERR_UNSUPPORTED, "context masks belong to the DiT head");
+  if (ctx->prefix_len < 0) return fail(ctx, FM_ERR_STATE, "nothing bound: call fm_bind_prefix_kv first");
+  return upload_masks(ctx, ctx->bound_batch, ctx->prefix_len, text_host, image_host);
 }
 
 static fm_status capture_loop(fm_ctx* ctx) {

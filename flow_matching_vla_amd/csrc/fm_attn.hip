@@ -88,7 +88,21 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   const int tile_id = (b * groups + g) * rtiles + rt;
   const int key_beg = sp * a.keys_per_split;
   const int key_end = min(a.n_keys, key_beg + a.keys_per_split);
-  const int ntile = (key_end - key_beg + BK - 1) / BK;
+  // Key tiles of this split that hold a visible key: n1 tiles from key_beg, then (with a
+  // leading segment of this request's own length pb) the tiles from s2 on; the tiles in
+  // between hold only keys the request does not see and are neither copied nor computed.
+  typedef const __attribute__((address_space(4))) int CI;
+  typedef const __attribute__((address_space(4))) uint32_t CU;
+  int pb = 0x3fffffff, n1 = (key_end - key_beg + BK - 1) / BK, s2 = key_end, n2 = 0;
+  if (a.seg_len) {
+    pb = *(CI*)(a.seg_len + __builtin_amdgcn_readfirstlane(b));
+    const int e1 = max(key_beg, min(key_end, (pb + BK - 1) / BK * BK));
+    n1 = (e1 - key_beg + BK - 1) / BK;
+    s2 = max(key_beg + n1 * BK, a.seg_end / BK * BK);
+    n2 = key_end > s2 ? (key_end - s2 + BK - 1) / BK : 0;
+  }
+  const int ntile = n1 + n2;
+  auto tile_start = [&](int t) { return t < n1 ? key_beg + t * BK : s2 + (t - n1) * BK; };
 
   FM_PHASE(0);
   // K / V^T tile copies: fragment f of a tile is 64 lanes x 16 bytes. K fragment (kb, c):
@@ -116,7 +130,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
       }
     }
   };
-  if (ntile > 0) issue(key_beg, 0);   // tile 0 first, the other prefetched tiles after Q
+  if (ntile > 0) issue(tile_start(0), 0);   // tile 0 first, the other prefetched tiles after Q
 
   // Q^T fragments (B operand of S^T): lane l carries query row l % 16 of query block
   // wave QB + qb, d run l / 16 of every d-chunk. Rows past R read row R-1; their outputs
@@ -135,7 +149,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   FM_WAIT_VMCNT(0);
 #pragma unroll
   for (int p = 1; p < NST - 1; ++p)
-    if (p < ntile) issue(key_beg + p * BK, p);
+    if (p < ntile) issue(tile_start(p), p);
   FM_PHASE(1);
 
   f32x4 o[QB][DB];   // O^T: lane l, element e holds d = 16 db + 4 (l / 16) + e of query l % 16
@@ -143,13 +157,19 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int i = 0; i < DB; ++i) o[qb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[QB], l_run[QB];   // of this lane's queries, base-2 logits
+  // of this lane's queries, base-2 logits. The reference starts finite (below any score),
+  // so a tile whose keys this query cannot see gives weights exp2(-inf - m) = 0, and a split
+  // with none leaves (O, l) = 0 and a reference the merge weighs by exp2(-1e30 - m) = 0.
+  float m_run[QB], l_run[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; }
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -1e30f; l_run[qb] = 0.f; }
 
   for (int t = 0; t < ntile; ++t) {
-    const int kt = key_beg + t * BK;
-    if (t + NST - 1 < ntile) issue(kt + (NST - 1) * BK, (t + NST - 1) % NST);
+    const int kt = tile_start(t);
+    if (t + NST - 1 < ntile) issue(tile_start(t + NST - 1), (t + NST - 1) % NST);
+    // visibility bits of the tile's 32 keys (a scalar load: its wait does not count the
+    // tile copies)
+    const uint32_t mw = a.kmask ? *(CU*)(a.kmask + __builtin_amdgcn_readfirstlane((int)(b * a.km_bs) + (kt >> 5))) : 0xffffffffu;
     // tile t's copies are done once at most the tiles issued after it are in flight
     wait_tiles<FPW, NST>(min(NST - 1, ntile - 1 - t));
     __syncthreads();
@@ -193,7 +213,9 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = (kl + 16 * kb + e < key_end) ? s[qb][kb][e] * a.scale_log2 : -INFINITY;
+          const int j = kl + 16 * kb + e;
+          const bool vis = j < key_end && (j < pb || j >= a.seg_end) && ((mw >> (j - kt)) & 1u);
+          const float v = vis ? s[qb][kb][e] * a.scale_log2 : -INFINITY;
           s[qb][kb][e] = v;
           mt = fmaxf(mt, v);
         }

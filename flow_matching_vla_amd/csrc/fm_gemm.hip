@@ -211,7 +211,7 @@ struct Epilogue {
         const int nr = max(min(n, a.q_cols + a.kv_cols - 4), 0);
         const int c = nr < a.q_cols ? nr : nr - a.q_cols;
         const int jj = (c % max(2 * a.half_dh, 1)) / 2;   // even: pairs jj, jj + 1 are adjacent
-        pr[q] = vec4((const float*)a.rope_cs, 2L * ((long)(mc % a.tq) * a.half_dh + jj));
+        pr[q] = vec4((const float*)a.rope_cs, 2L * ((long)mc * a.half_dh + jj));   // [row][half_dh]
       }
     }
   }

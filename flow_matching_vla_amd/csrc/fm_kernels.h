@@ -46,7 +46,7 @@ struct GemmArgs {
   // residual producer: h += gate * y; hs = T(h (1 + hscale)); (mean, M2) of h per
   // kStatCols columns at stats_out[row * stats_out_ld + n / kStatCols]
   float* h; long ldh_out; const float* gate; void* hs; const float* hscale; float2* stats_out; long stats_out_ld;
-  int q_cols, kv_cols, tq, kv_off, rope, half_dh; const float2* rope_cs;
+  int q_cols, kv_cols, tq, kv_off, rope, half_dh; const float2* rope_cs;   // rope_cs [M rows][half_dh]: each row's position
   void* kdst; long k_bs, k_rs; void* vdst; long v_bs, v_ds;
   float* x; float dt; float* vout;
   int vt_group; long vt_bs, vt_ds;
@@ -82,6 +82,12 @@ struct AttnArgs {
   long k_len, v_len;                          // elements readable from k / vt (reads past them give 0)
   void* o; long o_bs, o_rs;                   // o[b*o_bs + t*o_rs + n*dh + d]
   int B, Tq, n_heads, heads_per_kv, n_keys, dh;
+  // Per-request key visibility (the additive mask of Eq. (2): 0 or -inf), null = every key:
+  //  seg_len: request b sees keys [0, seg_len[b]) of its leading segment and every key in
+  //    [seg_end, n_keys) (a compact prefix of its own length, then its chunk's keys);
+  //  kmask: request b sees key j when bit j % 32 of kmask[b * km_bs + j / 32] is set.
+  const int* seg_len; int seg_end;
+  const uint32_t* kmask; long km_bs;
   float scale_log2;                            // log2(e) / sqrt(dh)
   int splits, keys_per_split;
   float* ws;                                   // split partials (attn_ws_bytes), merged by a second kernel

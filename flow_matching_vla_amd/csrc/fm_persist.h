@@ -44,7 +44,8 @@ struct LoopArgs {
   uint32_t wb_qkv, wb_o, wb_gu, wb_down, wb_out;
   const float* table;            // [steps][S][3D]
   const float* cbuf;             // [steps][csum]
-  const float2* rope_cs;         // [H][dh / 2]
+  const float2* rope_cs;         // [B][H][dh / 2]: cos / sin at each request's positions P_b + i
+  const int* plens;              // [B] compact prefix length P_b <= P of each request
   float* x; float* h;
   const __bf16* pool; long plane;   // elements per pool plane
   char* rot; long rot_step, rot_layer;

@@ -423,7 +423,7 @@ constexpr int kFT = kFK + kFV;
 constexpr int kFPW = kFT / kPW;                 // fragments per wave per tile
 static_assert(kFT % kPW == 0, "tile fragments per wave");
 
-struct AttnItem { int valid, b, rt, sp; };
+struct AttnItem { int valid, b, rt, sp, pb; };   // pb: the request's compact prefix length
 
 // All key splits of one row tile run on one XCD (workgroup b runs on XCD b % 8): their
 // partial results stay in that XCD's L2, which every CU of the XCD sees coherently, and
@@ -437,6 +437,8 @@ __device__ __forceinline__ AttnItem attn_item(LA& a) {
   it.b = rb / a.RT;
   it.rt = rb % a.RT;
   it.valid = rb < a.B * a.RT;
+  typedef const __attribute__((address_space(4))) int CI;
+  it.pb = it.valid ? *(CI*)(a.plens + __builtin_amdgcn_readfirstlane(it.b)) : 0;
   return it;
 }
 
@@ -457,6 +459,7 @@ __device__ __forceinline__ void attn_issue(LA& a, const AttnItem& it, int l, con
   if (!it.valid || ti >= a.TP + a.TS) return;
   const bool is_suf = ti >= a.TP;
   if (is_suf != suffix) return;
+  if (!is_suf && 32 * ti >= it.pb) return;   // past the request's own prefix: nothing it sees
   V16 dk, dv;
   int kt, vds;
   if (!is_suf) {
@@ -528,17 +531,21 @@ __device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem
   __syncthreads();
 
   const int ti = attn_tile(a, it, half);
-  const bool has = it.valid && ti < a.TP + a.TS;
+  // a tile with a key the request sees: a suffix tile, or a prefix tile that starts inside
+  // the request's compact prefix
+  const bool has = it.valid && ti < a.TP + a.TS && (ti >= a.TP || 32 * ti < it.pb);
   f32x4 o[kDB];
 #pragma unroll
   for (int i = 0; i < kDB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  // a half without such a tile keeps (O, l) = 0 and a finite reference below any score, which
+  // the merges below weigh by exp2(-1e30 - m) = 0
+  float m = -1e30f, lsum = 0.f;
   if (has) {
     const V16* sK = &sm.att[half][0];
     const V16* sV = sK + kFK * 64;
     const bool is_suf = ti >= a.TP;
     const int kbase = is_suf ? 32 * (ti - a.TP) : 32 * ti;
-    const int klim = is_suf ? a.H : a.P;
+    const int klim = is_suf ? a.H : it.pb;
     f32x4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -837,14 +844,14 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         StatLoad st;
         st.issue(rl + a.o_st, M, D);
         const int b = er / a.H, i = er % a.H;
-        const Rsrc rc = make_rsrc(a.rope_cs, (uint32_t)(a.H * (kDH / 2) * 8));
+        const Rsrc rc = make_rsrc(a.rope_cs, (uint32_t)(a.B * a.H * (kDH / 2) * 8));
         V16 cv[2], csv[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int n = ((int)blockIdx.x + s2 * G) * 16 + 4 * eq;
           const bool use = t < 256 && s2 < nslot && er < M;
           cv[s2] = col4(cvec(a, k, 2 * l), min(n, a.cq4 - 4), a.cq4, use);
-          csv[s2] = ld16<0>(rc, (use && a.rope && n < a.qd + kDH) ? (uint32_t)((i * (kDH / 2) + (n % kDH) / 2) * 8) : kOob);
+          csv[s2] = ld16<0>(rc, (use && a.rope && n < a.qd + kDH) ? (uint32_t)((er * (kDH / 2) + (n % kDH) / 2) * 8) : kOob);
         }
         st.finish(D, a.eps, sm);
         f32x4 v[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};

@@ -67,6 +67,8 @@ def lib():
         "fm_load_weights": ([VP, P(fm_tensor), I32], I32),
         "fm_set_schedule": ([VP, I32, I32, P(C.c_float)], I32),
         "fm_bind_prefix_kv": ([VP, I32, I32, P(VP), P(VP), VP, VP], I32),
+        "fm_bind_prefix_lengths": ([VP, P(I32)], I32),
+        "fm_bind_context_masks": ([VP, P(C.c_uint8), P(C.c_uint8)], I32),
         "fm_denoise": ([VP, VP, I32, VP], I32),
         "fm_step_velocity": ([VP, VP, I32, VP], I32),
         "fm_step_trace": ([VP, VP, I32, VP, VP], I32),
@@ -165,6 +167,7 @@ class Context:
         _check(lib().fm_create(C.byref(self._c), C.c_void_p(stream.cuda_stream), C.byref(h)))
         self.h = h
         self._keep = []
+        self._bound = (0, 0)   # (batch, prefix or context length) of the binding
 
     def close(self):
         if self.h:
@@ -214,6 +217,35 @@ class Context:
             kp = (C.c_void_p * len(k))(*[t.data_ptr() for t in k])
             vp = (C.c_void_p * len(v))(*[t.data_ptr() for t in v])
         _check(lib().fm_bind_prefix_kv(self.h, batch, prefix_len, kp, vp, _ptr(context), _ptr(state)), self.h)
+        self._bound = (batch, prefix_len)
+
+    def bind_prefix_lengths(self, lens=None):
+        """Compact prefix length P_b of each bound request (host ints [batch]); None: the whole
+        bound prefix for every request."""
+        import numpy as np
+        arr = p = None
+        if lens is not None:
+            arr = np.ascontiguousarray(lens, dtype=np.int32).ravel()
+            if arr.size != self._bound[0]:
+                raise ValueError(f"{arr.size} lengths for a bound batch of {self._bound[0]}")
+            p = arr.ctypes.data_as(C.POINTER(C.c_int32))
+        _check(lib().fm_bind_prefix_lengths(self.h, p), self.h)
+
+    def bind_context_masks(self, text=None, image=None):
+        """DiT text / image masks over the bound context (host booleans [batch, ctx_len],
+        true = visible); None: every token visible."""
+        import numpy as np
+        keep, ptrs = [], []
+        for m in (text, image):
+            if m is None:
+                ptrs.append(None)
+                continue
+            a = np.ascontiguousarray(m, dtype=np.uint8)
+            if a.shape != self._bound:
+                raise ValueError(f"mask shape {a.shape}, bound (batch, context length) {self._bound}")
+            keep.append(a)
+            ptrs.append(a.ctypes.data_as(C.POINTER(C.c_uint8)))
+        _check(lib().fm_bind_context_masks(self.h, ptrs[0], ptrs[1]), self.h)
 
     def denoise(self, x0, steps: int, out=None):
         torch = _torch()

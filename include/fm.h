@@ -146,9 +146,34 @@ fm_status fm_set_schedule(fm_ctx* ctx, int32_t steps, int32_t batch, const float
  *   VL context, projected here to the cross-attention K/V of every even block; state_dev is
  *   a DEVICE fp32 buffer [batch, state_tokens, state_dim], embedded here to the state
  *   token(s). k_dev / v_dev must be NULL. 1 <= prefix_len <= ctx_len_max.
- * 1 <= batch <= max_batch. Requires loaded weights. */
+ * 1 <= batch <= max_batch. Requires loaded weights. Every request sees the whole binding
+ * (all prefix_len prefix keys, every context token) until one of the two calls below
+ * narrows it. */
 fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t prefix_len, const void* const* k_dev,
                             const void* const* v_dev, const void* ctx_dev, const void* state_dev);
+
+/* Per-request key visibility of the bound batch: the additive mask M of Eq. (2) (vla.cpp
+ * Sec. III-B: 0 for a visible key, -inf for a hidden one). Both calls copy what they are
+ * given into library memory and synchronize the context stream before returning (the host
+ * arrays may then be reused); loops already enqueued run with the previous visibility. They
+ * may be called any number of times per binding; captured loops stay valid. FM_ERR_STATE
+ * before a binding; FM_ERR_UNSUPPORTED on the other architecture.
+ *
+ * fm_bind_prefix_lengths (PREFIX_JOINT): lens_host HOST int32 [batch], request b's compact
+ *   prefix length 0 <= P_b <= prefix_len (FM_ERR_INVALID_ARG otherwise), or NULL for
+ *   prefix_len everywhere. Request b attends to its first P_b prefix keys and to its chunk's
+ *   own keys, and its chunk takes RoPE positions P_b .. P_b + H - 1: its filled length after
+ *   the append is P_b + H (pi0.5 Design, "Component contract": attention_sequence_lengths;
+ *   the prefix is compact, so a shorter observation is a shorter prefix). Pool rows
+ *   [P_b, prefix_len) of the request are kept but not read.
+ * fm_bind_context_masks (DIT_CROSS): text_host, image_host HOST bytes [batch, prefix_len]
+ *   (the bound context length), nonzero = the context token is visible, or NULL for all
+ *   visible. Cross block i (even) reads the text mask when i % 4 == 0 and the image mask
+ *   otherwise (GR00T N1.7, section "action": the masks are arbitrary booleans over the
+ *   context). FM_ERR_INVALID_ARG when a mask that some cross block reads shows a request no
+ *   token (softmax over no key has no value); nothing is changed then. */
+fm_status fm_bind_prefix_lengths(fm_ctx* ctx, const int32_t* lens_host);
+fm_status fm_bind_context_masks(fm_ctx* ctx, const uint8_t* text_host, const uint8_t* image_host);
 
 /* Run the whole Euler loop: out_dev = X^T for X^0 = x0_dev. Both are DEVICE fp32 buffers
  * [batch, H, d_a] (the bound batch); out_dev may equal x0_dev. steps must equal the

@@ -16,7 +16,7 @@ def say(*a):
 class Case:
     """One workload: host weights/inputs, the oracle's bound state, and a GPU context."""
 
-    def __init__(self, cfg, W=None, I=None, steps=None, tau=None):
+    def __init__(self, cfg, W=None, I=None, steps=None, tau=None, vis=None):
         import torch
         from flow_matching_vla_amd import fm
 
@@ -45,9 +45,20 @@ class Case:
         self.x0 = torch.from_numpy(self.I["x0"]).cuda()
         # oracle state (float64)
         self.w64 = oracle.cast_weights(self.W)
-        self.bound = oracle.bind(cfg, self.w64, self.I)
+        self.set_visibility(vis)
         self.tau64 = oracle.schedule(self.steps, tau)
         self.table, self.tb = oracle.modulation_table(cfg, self.w64, self.tau64) if self.steps else (None, None)
+
+    def set_visibility(self, vis):
+        """Per-request visibility on both sides: {"prefix_lens"} or {"text_mask", "image_mask"}
+        (None: the whole binding)."""
+        vis = vis or {}
+        if self.cfg["arch"] == wl.ARCH_PREFIX_JOINT:
+            self.ctx.bind_prefix_lengths(vis.get("prefix_lens"))
+        else:
+            self.ctx.bind_context_masks(vis.get("text_mask"), vis.get("image_mask"))
+        self.vis = vis
+        self.bound = oracle.bind(self.cfg, self.w64, dict(self.I, **vis))
 
     def oracle_velocity(self, x, k, trace=None, requests=None):
         if requests is None:
@@ -80,3 +91,38 @@ class Case:
 
     def close(self):
         self.ctx.close()
+
+
+def teacher_forced(case, tol_v, requests=None, layers_trace=False):
+    """GPU velocity at the GPU's own trajectory x_k vs the oracle velocity at the same x_k."""
+    x = case.I["x0"].astype(np.float32)
+    worst = 0.0
+    for k in range(case.steps):
+        v_gpu = case.gpu_velocity(x, k)
+        v_ref = case.oracle_velocity(x, k, requests=requests)
+        vg = v_gpu if requests is None else v_gpu[requests]
+        e = oracle.e_rel(vg, v_ref)
+        say(f"  step {k}: velocity e_rel {e:.3e} e_inf {oracle.e_inf(vg, v_ref):.3e}")
+        worst = max(worst, e)
+        x = (x + np.float32(case.tau64[k + 1] - case.tau64[k]) * v_gpu).astype(np.float32)
+    assert worst <= tol_v, worst
+    return worst
+
+
+def chunk(case, tol_x, requests=None):
+    x_gpu = case.gpu_denoise()
+    I = case.I
+    if requests is not None:
+        x_ref = oracle.denoise(dict(case.cfg, batch=len(requests)), case.w64,
+                               {k: ([a[requests] for a in v] if isinstance(v, list) else
+                                    ({i: a[requests] for i, a in v.items()} if isinstance(v, dict) else
+                                     (v[requests] if isinstance(v, np.ndarray) else v)))
+                                for k, v in case.bound.items()},
+                               I["x0"][requests], case.steps, tau=case.tau)
+        x_gpu = x_gpu[requests]
+    else:
+        x_ref = oracle.denoise(case.cfg, case.w64, case.bound, I["x0"], case.steps, tau=case.tau)
+    e = oracle.e_rel(x_gpu, x_ref)
+    say(f"  chunk e_rel {e:.3e} e_inf {oracle.e_inf(x_gpu, x_ref):.3e}")
+    assert e <= tol_x, e
+    return x_gpu

@@ -7,44 +7,9 @@ import pytest
 
 import oracle
 from flow_matching_vla_amd import workloads as wl
-from gpu_util import Case, say
+from gpu_util import Case, say, teacher_forced as _teacher_forced, chunk as _chunk
 
 pytestmark = pytest.mark.gpu
-
-
-def _teacher_forced(case, tol_v, requests=None, layers_trace=False):
-    """GPU velocity at the GPU's own trajectory x_k vs the oracle velocity at the same x_k."""
-    x = case.I["x0"].astype(np.float32)
-    worst = 0.0
-    for k in range(case.steps):
-        v_gpu = case.gpu_velocity(x, k)
-        v_ref = case.oracle_velocity(x, k, requests=requests)
-        vg = v_gpu if requests is None else v_gpu[requests]
-        e = oracle.e_rel(vg, v_ref)
-        say(f"  step {k}: velocity e_rel {e:.3e} e_inf {oracle.e_inf(vg, v_ref):.3e}")
-        worst = max(worst, e)
-        x = (x + np.float32(case.tau64[k + 1] - case.tau64[k]) * v_gpu).astype(np.float32)
-    assert worst <= tol_v, worst
-    return worst
-
-
-def _chunk(case, tol_x, requests=None):
-    x_gpu = case.gpu_denoise()
-    I = case.I
-    if requests is not None:
-        x_ref = oracle.denoise(dict(case.cfg, batch=len(requests)), case.w64,
-                               {k: ([a[requests] for a in v] if isinstance(v, list) else
-                                    ({i: a[requests] for i, a in v.items()} if isinstance(v, dict) else
-                                     (v[requests] if isinstance(v, np.ndarray) else v)))
-                                for k, v in case.bound.items()},
-                               I["x0"][requests], case.steps, tau=case.tau)
-        x_gpu = x_gpu[requests]
-    else:
-        x_ref = oracle.denoise(case.cfg, case.w64, case.bound, I["x0"], case.steps, tau=case.tau)
-    e = oracle.e_rel(x_gpu, x_ref)
-    say(f"  chunk e_rel {e:.3e} e_inf {oracle.e_inf(x_gpu, x_ref):.3e}")
-    assert e <= tol_x, e
-    return x_gpu
 
 
 # ----------------------------------------------------------------------------- fp32 tiny expert
