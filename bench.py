@@ -145,6 +145,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fit", action="store_true")
     ap.add_argument("--no-roles", action="store_true")
+    ap.add_argument("--no-visibility", action="store_true")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc runs: a plain 512 MiB device copy (3x, the counter scale) "
                          "then 3 chunk calls; prints no JSON")
@@ -298,6 +299,33 @@ def main():
                                "frac": round(ach / peak, 4), "traffic": None, "kernel_role": dom,
                                "alg_flops_per_launch": int(nflops), "avg_launch_us": round(avg_s * 1e6, 2),
                                "launches_per_chunk": roles[dom][1]}
+    # per-request visibility: the workload's seeded mixed batch (ragged compact prefixes for
+    # pi0.5, text / image masks for DiT), same binding, timed like the main loop
+    vis = None if args.no_visibility else wl.make_visibility(cfg)
+    if vis is not None and (cfg["arch"] != 0 or bool(np.any(vis["prefix_lens"] < cfg["prefix_len"]))):
+        if cfg["arch"] == 0:
+            ctx.bind_prefix_lengths(vis["prefix_lens"])
+            desc = {"prefix_lens_mean": round(float(vis["prefix_lens"].mean()), 1), "prefix_len": cfg["prefix_len"]}
+        else:
+            ctx.bind_context_masks(vis["text_mask"], vis["image_mask"])
+            desc = {"text_visible_mean": round(float(vis["text_mask"].sum(1).mean()), 1),
+                    "image_visible_mean": round(float(vis["image_mask"].sum(1).mean()), 1), "ctx_len": cfg["ctx_len"]}
+        for _ in range(3):
+            ctx.denoise(x0, T, out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(20):
+            ctx.denoise(x0, T, out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        vms = a.elapsed_time(b) / 20
+        res["visibility"] = dict(desc, ms_per_chunk=round(vms, 4), chunks_per_s=round(B / (vms * 1e-3), 2),
+                                 ms_per_chunk_whole_binding=round(ms, 4))
+        if cfg["arch"] == 0:
+            ctx.bind_prefix_lengths(None)
+        else:
+            ctx.bind_context_masks(None, None)
     # the step after the path: the chunk back to robot units (LIBERO width 7; GR00T's policy
     # keeps 16 of the model's 40 steps), timed with HIP events on the context stream
     post_kind = fm.UNNORM_QUANTILE_EPS if cfg["arch"] == 0 else fm.UNNORM_QUANTILE_CLIP

@@ -169,6 +169,9 @@ struct fm_ctx {
   int* plens = nullptr;       // [Bmax]
   uint32_t* kmask = nullptr;  // [2][Bmax][ctx_words]: bit j % 32 of word j / 32 = key j visible
   int ctx_words = 0;
+  // whether a request sees less than the whole binding (some P_b < P; a text / image mask
+  // with a hidden token): the attention then runs its visibility variant
+  bool ragged = false, masked[2] = {false, false};
 
   // activations
   float *h = nullptr, *x = nullptr;
@@ -341,7 +344,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       at.k_len = at.v_len = (long)c.max_batch * ctx->cap * dh;
       at.o = ctx->obuf; at.o_bs = (long)H * qd; at.o_rs = qd;
       at.B = B; at.Tq = H; at.n_heads = nq; at.heads_per_kv = nq; at.n_keys = ctx->prefix_len + H; at.dh = dh;
-      at.seg_len = ctx->plens; at.seg_end = ctx->prefix_len;   // request b: its first P_b prefix keys, then its chunk
+      if (ctx->ragged) { at.seg_len = ctx->plens; at.seg_end = ctx->prefix_len; }   // request b: its first P_b prefix keys, then its chunk
       at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
       memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.role = FM_OP_ATTN; op.at = at; ops.push_back(op);
       // O projection + gated residual
@@ -385,7 +388,8 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
         at.k_len = (long)c.max_batch * c.ctx_len_max * D; at.v_len = (long)c.max_batch * D * ctx->spad;
         at.n_keys = ctx->prefix_len;
         // the text mask on cross blocks whose index is a multiple of 4, the image mask on the others
-        at.kmask = ctx->kmask + (size_t)(l % 4 == 0 ? 0 : 1) * c.max_batch * ctx->ctx_words; at.km_bs = ctx->ctx_words;
+        const int mi = l % 4 == 0 ? 0 : 1;
+        if (ctx->masked[mi]) { at.kmask = ctx->kmask + (size_t)mi * c.max_batch * ctx->ctx_words; at.km_bs = ctx->ctx_words; }
       } else {
         g = gemm_base(Mh, 3 * D, D, W.qkv);
         set_consumer(ctx, g, NORM_LN, k, l, nullptr, Mh);
@@ -1058,7 +1062,7 @@ fm_status fm_set_schedule(fm_ctx* ctx, int32_t steps, int32_t batch, const float
 // Per-request compact prefix lengths and the cos/sin rows of each request's chunk positions
 // P_b + i. Device copies on the context stream (ordered after any loop still running on it),
 // then a wait, so the host vectors may go.
-static fm_status upload_lengths(fm_ctx* ctx, const std::vector<int>& lens) {
+static fm_status upload_lengths(fm_ctx* ctx, const std::vector<int>& lens, int P) {
   const int H = ctx->c.action_horizon, hd = ctx->c.head_dim / 2, B = (int)lens.size();
   std::vector<float2> cs((size_t)B * H * hd);
   for (int b = 0; b < B; ++b)
@@ -1066,6 +1070,9 @@ static fm_status upload_lengths(fm_ctx* ctx, const std::vector<int>& lens) {
   HIPCK(hipMemcpyAsync(ctx->rope_cs, cs.data(), cs.size() * sizeof(float2), hipMemcpyHostToDevice, ctx->stream));
   HIPCK(hipMemcpyAsync(ctx->plens, lens.data(), (size_t)B * sizeof(int), hipMemcpyHostToDevice, ctx->stream));
   HIPCK(hipStreamSynchronize(ctx->stream));
+  bool ragged = false;
+  for (int b = 0; b < B; ++b) ragged |= lens[b] != P;
+  if (ragged != ctx->ragged) { ctx->ragged = ragged; invalidate_graph(ctx); }   // the attention variant changes
   return FM_OK;
 }
 
@@ -1079,6 +1086,7 @@ static fm_status upload_masks(fm_ctx* ctx, int batch, int S, const uint8_t* text
   const uint8_t* src[2] = {text, image};
   const bool read[2] = {c.n_layers >= 1, c.n_layers >= 3};   // block 0 reads text, block 2 image
   const char* name[2] = {"text", "image"};
+  bool hidden[2] = {false, false};
   for (int m = 0; m < 2; ++m)
     for (int b = 0; b < batch; ++b) {
       uint32_t* w = &bits[((size_t)m * c.max_batch + b) * W];
@@ -1087,9 +1095,14 @@ static fm_status upload_masks(fm_ctx* ctx, int batch, int S, const uint8_t* text
         if (!src[m] || src[m][(size_t)b * S + j]) { w[j / 32] |= 1u << (j % 32); ++seen; }
       if (read[m] && seen == 0)
         return fail(ctx, FM_ERR_INVALID_ARG, fmt("the %s mask shows request %d no context token", name[m], b));
+      hidden[m] |= seen < S;
     }
   HIPCK(hipMemcpyAsync(ctx->kmask, bits.data(), bits.size() * sizeof(uint32_t), hipMemcpyHostToDevice, ctx->stream));
   HIPCK(hipStreamSynchronize(ctx->stream));
+  if (hidden[0] != ctx->masked[0] || hidden[1] != ctx->masked[1]) {   // the attention variant changes
+    ctx->masked[0] = hidden[0]; ctx->masked[1] = hidden[1];
+    invalidate_graph(ctx);
+  }
   return FM_OK;
 }
 
@@ -1117,7 +1130,7 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void
     }
     // every request sees the whole bound prefix until fm_bind_prefix_lengths says otherwise
     std::vector<int> lens(batch, plen);
-    fm_status s = upload_lengths(ctx, lens);
+    fm_status s = upload_lengths(ctx, lens, plen);
     if (s != FM_OK) return s;
   } else {
     if (plen < 1 || plen > c.ctx_len_max) return fail(ctx, FM_ERR_INVALID_ARG, fmt("context length %d outside [1, %d]", plen, c.ctx_len_max));
@@ -1183,7 +1196,7 @@ fm_status fm_bind_prefix_lengths(fm_ctx* ctx, const int32_t* lens_host) {
       return fail(ctx, FM_ERR_INVALID_ARG, fmt("prefix length %d of request %d outside [0, %d]", lens_host[b], b, ctx->prefix_len));
     lens[b] = lens_host[b];
   }
-  return upload_lengths(ctx, lens);
+  return upload_lengths(ctx, lens, ctx->prefix_len);
 }
 
 fm_status fm_bind_context_masks(fm_ctx* ctx, const uint8_t* text_host, const uint8_t* image_host) {

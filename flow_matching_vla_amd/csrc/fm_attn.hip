@@ -46,10 +46,18 @@ __device__ __forceinline__ void wait_tiles(int pend) {
   else FM_WAIT_VMCNT(0);
 }
 
+// 32-bit word with bits [0, n) set (n clamped to [0, 32])
+__device__ __forceinline__ uint32_t bits_below(int n) {
+  return n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : (1u << n) - 1u);
+}
+
 // WAVES waves of QB query blocks (16 rows each): ROWS = 16 WAVES QB rows per workgroup.
 // Every K and V^T fragment a wave reads from LDS feeds QB MFMAs, so QB = 2 halves the LDS
-// reads per MFMA (one wave per SIMD then holds twice the accumulators).
-template <typename T, int DH, int WAVES, int QB>
+// reads per MFMA (one wave per SIMD then holds twice the accumulators). VIS: the per-request
+// visibility (seg_len / kmask) is applied; without it every key below n_keys is visible and
+// the kernel carries none of that code (measured: the visibility code, even unused, cost
+// ~10% at 64 requests).
+template <typename T, int DH, int WAVES, int QB, bool VIS>
 __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   using MT = Mma<T>;
   typedef typename MT::frag frag;
@@ -94,7 +102,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   typedef const __attribute__((address_space(4))) int CI;
   typedef const __attribute__((address_space(4))) uint32_t CU;
   int pb = 0x3fffffff, n1 = (key_end - key_beg + BK - 1) / BK, s2 = key_end, n2 = 0;
-  if (a.seg_len) {
+  if (VIS && a.seg_len) {
     pb = *(CI*)(a.seg_len + __builtin_amdgcn_readfirstlane(b));
     const int e1 = max(key_beg, min(key_end, (pb + BK - 1) / BK * BK));
     n1 = (e1 - key_beg + BK - 1) / BK;
@@ -102,7 +110,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
     n2 = key_end > s2 ? (key_end - s2 + BK - 1) / BK : 0;
   }
   const int ntile = n1 + n2;
-  auto tile_start = [&](int t) { return t < n1 ? key_beg + t * BK : s2 + (t - n1) * BK; };
+  auto tile_start = [&](int t) { return (!VIS || t < n1) ? key_beg + t * BK : s2 + (t - n1) * BK; };
 
   FM_PHASE(0);
   // K / V^T tile copies: fragment f of a tile is 64 lanes x 16 bytes. K fragment (kb, c):
@@ -162,14 +170,20 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   // with none leaves (O, l) = 0 and a reference the merge weighs by exp2(-1e30 - m) = 0.
   float m_run[QB], l_run[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -1e30f; l_run[qb] = 0.f; }
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = VIS ? -1e30f : -INFINITY; l_run[qb] = 0.f; }
 
   for (int t = 0; t < ntile; ++t) {
     const int kt = tile_start(t);
     if (t + NST - 1 < ntile) issue(tile_start(t + NST - 1), (t + NST - 1) % NST);
     // visibility bits of the tile's 32 keys (a scalar load: its wait does not count the
     // tile copies)
-    const uint32_t mw = a.kmask ? *(CU*)(a.kmask + __builtin_amdgcn_readfirstlane((int)(b * a.km_bs) + (kt >> 5))) : 0xffffffffu;
+    uint32_t vis = 0xffffffffu;
+    if constexpr (VIS) {
+      if (a.kmask) vis = *(CU*)(a.kmask + __builtin_amdgcn_readfirstlane((int)(b * a.km_bs) + (kt >> 5)));
+      // bit i of vis: key kt + i is visible (uniform: scalar arithmetic)
+      vis &= bits_below(key_end - kt);
+      vis &= ~(bits_below(a.seg_end - kt) & ~bits_below(pb - kt));   // the keys in [pb, seg_end)
+    }
     // tile t's copies are done once at most the tiles issued after it are in flight
     wait_tiles<FPW, NST>(min(NST - 1, ntile - 1 - t));
     __syncthreads();
@@ -203,22 +217,41 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
 #pragma unroll
     for (int f = 0; f < FV; ++f) vf[f] = sV[f * 64 + lane];
     __builtin_amdgcn_sched_barrier(0);
-    // online softmax of this lane's queries over keys kt + 16 kb + 4 (l / 16) + e
-    const int kl = kt + 4 * (lane / 16);
+    // online softmax of this lane's queries over keys kt + 16 kb + 4 (l / 16) + e; a tile
+    // whose keys are all visible (the common case) skips the per-key test
+    const uint32_t lvis = vis >> (4 * (lane / 16));
     frag pf[QB][KCH];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mt = -INFINITY;
+      if constexpr (!VIS) {
+        const int kl = kt + 4 * (lane / 16);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = kl + 16 * kb + e;
-          const bool vis = j < key_end && (j < pb || j >= a.seg_end) && ((mw >> (j - kt)) & 1u);
-          const float v = vis ? s[qb][kb][e] * a.scale_log2 : -INFINITY;
-          s[qb][kb][e] = v;
-          mt = fmaxf(mt, v);
-        }
+          for (int e = 0; e < 4; ++e) {
+            const float v = (kl + 16 * kb + e < key_end) ? s[qb][kb][e] * a.scale_log2 : -INFINITY;
+            s[qb][kb][e] = v;
+            mt = fmaxf(mt, v);
+          }
+      } else if (vis == 0xffffffffu) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[qb][kb][e] *= a.scale_log2;
+            mt = fmaxf(mt, s[qb][kb][e]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = ((lvis >> (16 * kb + e)) & 1u) ? s[qb][kb][e] * a.scale_log2 : -INFINITY;
+            s[qb][kb][e] = v;
+            mt = fmaxf(mt, v);
+          }
+      }
       mt = group4_max(mt);
       // The reference max moves only when a score exceeds it by more than 2^8: until then
       // p = 2^(s - m_run) <= 256 stays exact in fp32 / bf16 and O, l need no rescale. The
@@ -389,7 +422,8 @@ static void launch_attn(const AttnArgs& a, hipStream_t s) {
   // one query block per wave: two blocks per wave (four waves, one per SIMD) halve the LDS
   // reads per MFMA but measured slower (pi05_b64: 73 against 62 us per layer), the single
   // wave per SIMD leaving LDS and softmax latencies uncovered
-  hipLaunchKernelGGL((k_attn<T, DH, kAttnWaves, 1>), grid, dim3(64 * kAttnWaves), 0, s, a);
+  if (a.seg_len || a.kmask) hipLaunchKernelGGL((k_attn<T, DH, kAttnWaves, 1, true>), grid, dim3(64 * kAttnWaves), 0, s, a);
+  else hipLaunchKernelGGL((k_attn<T, DH, kAttnWaves, 1, false>), grid, dim3(64 * kAttnWaves), 0, s, a);
   if (a.splits > 1) {
     const long threads = (long)attn_num_items(a) * kAttnRows * DH / 4;
     const dim3 cgrid((unsigned)((threads + 255) / 256));

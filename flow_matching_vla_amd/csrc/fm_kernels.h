@@ -82,16 +82,18 @@ struct AttnArgs {
   long k_len, v_len;                          // elements readable from k / vt (reads past them give 0)
   void* o; long o_bs, o_rs;                   // o[b*o_bs + t*o_rs + n*dh + d]
   int B, Tq, n_heads, heads_per_kv, n_keys, dh;
-  // Per-request key visibility (the additive mask of Eq. (2): 0 or -inf), null = every key:
-  //  seg_len: request b sees keys [0, seg_len[b]) of its leading segment and every key in
-  //    [seg_end, n_keys) (a compact prefix of its own length, then its chunk's keys);
-  //  kmask: request b sees key j when bit j % 32 of kmask[b * km_bs + j / 32] is set.
-  const int* seg_len; int seg_end;
-  const uint32_t* kmask; long km_bs;
   float scale_log2;                            // log2(e) / sqrt(dh)
   int splits, keys_per_split;
   float* ws;                                   // split partials (attn_ws_bytes), merged by a second kernel
   int cfg;
+  // Per-request key visibility (the additive mask of Eq. (2): 0 or -inf), null = every key:
+  //  seg_len: request b sees keys [0, seg_len[b]) of its leading segment and every key in
+  //    [seg_end, n_keys) (a compact prefix of its own length, then its chunk's keys);
+  //  kmask: request b sees key j when bit j % 32 of kmask[b * km_bs + j / 32] is set.
+  // Kept last: placed between the fields above they moved those fields' offsets, and the
+  // attention kernel's argument loads then ran measurably slower (62 -> 66 us at 64 requests).
+  const int* seg_len; int seg_end;
+  const uint32_t* kmask; long km_bs;
 };
 void attn_plan(AttnArgs& a, int elem, int num_cus);
 size_t attn_ws_bytes(const AttnArgs& a);

@@ -156,8 +156,10 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t prefix_len, cons
  * Sec. III-B: 0 for a visible key, -inf for a hidden one). Both calls copy what they are
  * given into library memory and synchronize the context stream before returning (the host
  * arrays may then be reused); loops already enqueued run with the previous visibility. They
- * may be called any number of times per binding; captured loops stay valid. FM_ERR_STATE
- * before a binding; FM_ERR_UNSUPPORTED on the other architecture.
+ * may be called any number of times per binding. A batch that sees the whole binding runs
+ * attention without the visibility test; a change between the two re-captures the loop's
+ * graph on the next fm_denoise. FM_ERR_STATE before a binding; FM_ERR_UNSUPPORTED on the
+ * other architecture.
  *
  * fm_bind_prefix_lengths (PREFIX_JOINT): lens_host HOST int32 [batch], request b's compact
  *   prefix length 0 <= P_b <= prefix_len (FM_ERR_INVALID_ARG otherwise), or NULL for
