@@ -174,11 +174,16 @@ def main():
         L = cfg["n_layers"]
         kk = [fm.to_device(I[f"prefix.k.{l}"], dt) for l in range(L)]
         vv = [fm.to_device(I[f"prefix.v.{l}"], dt) for l in range(L)]
-        ctx.bind_prefix_kv(B, cfg["prefix_len"], kk, vv)
-        torch.cuda.synchronize()
-        del kk, vv
+
+        def bind():
+            ctx.bind_prefix_kv(B, cfg["prefix_len"], kk, vv)
     else:
-        ctx.bind_prefix_kv(B, cfg["ctx_len"], context=fm.to_device(I["context"], dt), state=fm.to_device(I["state"], fm.F32))
+        zc, st = fm.to_device(I["context"], dt), fm.to_device(I["state"], fm.F32)
+
+        def bind():
+            ctx.bind_prefix_kv(B, cfg["ctx_len"], context=zc, state=st)
+    bind()
+    torch.cuda.synchronize()
     ctx.set_schedule(T, B)
     x0 = torch.from_numpy(I["x0"]).cuda()
     out = torch.empty_like(x0)
@@ -348,6 +353,19 @@ def main():
     res["post"] = {"kernel": "k_unnormalize", "kind": "quantile+eps (pi0.5)" if post_kind == 0 else "quantile clip (GR00T)",
                    "robot_horizon": post_h, "robot_dim": post_d, "us_per_chunk": round(post_us, 2),
                    "alg_bytes": int(post_bytes), "achieved_GBps": round(post_bytes / (post_us * 1e-6) / 1e9, 2)}
+    # off the step path: the per-observation binding (prefix K/V copy into the pool, or the
+    # DiT context projected to every cross block's K / V) and the per-schedule table; each
+    # call synchronizes the stream before returning
+    def per_call_ms(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return round((time.perf_counter() - t0) / n * 1e3, 3)
+    res["bind_ms"] = per_call_ms(bind, 5)
+    res["schedule_ms"] = per_call_ms(lambda: ctx.set_schedule(T, B), 3)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, W, I)

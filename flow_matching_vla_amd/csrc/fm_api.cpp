@@ -160,8 +160,11 @@ struct fm_ctx {
   int bound_batch = 0, prefix_len = -1;
   int cap = 0, spad = 0, tpad = 0;
   void* pool = nullptr;       // PREFIX_JOINT: [L][2][Bmax][cap][dh]; K plane RoPE-interleaved, V plane transposed
-  void* cross_k = nullptr;    // DIT: [ceil(L/2)][Bmax][ctx_max][D]
-  void* cross_vt = nullptr;   // DIT: [ceil(L/2)][Bmax][D][spad]
+  // DIT: cross block ci's K plane holds [batch][ctx_len][D] packed (the bound length), its V
+  // plane [Bmax][D][spad] transposed; both written at bind by one GEMM over all cross blocks
+  void* cross_k = nullptr;    // [ceil(L/2)][Bmax * ctx_max * D]
+  void* cross_vt = nullptr;   // [ceil(L/2)][Bmax][D][spad]
+  void *wkx_all = nullptr, *wvx_all = nullptr;   // DIT: every cross block's W_K (W_V), stacked
   float* state_tok = nullptr; // DIT: [Bmax*st][D]
   float2* rope_cs = nullptr;  // [Bmax][H][dh/2]: cos/sin at each request's chunk positions P_b + i
   std::vector<float2> rope_pos;   // host [max_prefix_len + H][dh/2]: cos/sin of every position
@@ -382,7 +385,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
         g.epi = EPI_STORE; g.out = ctx->qbuf; g.ldo = D;
         memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_QKV; op.g = g; ops.push_back(op);
         at.k = (char*)ctx->cross_k + (size_t)ci * c.max_batch * c.ctx_len_max * D * ctx->esz;
-        at.k_bs = (long)c.ctx_len_max * D; at.k_rs = D; at.k_hs = dh;
+        at.k_bs = (long)ctx->prefix_len * D; at.k_rs = D; at.k_hs = dh;   // packed at the bound length
         at.vt = (char*)ctx->cross_vt + (size_t)ci * c.max_batch * D * ctx->spad * ctx->esz;
         at.v_bs = (long)D * ctx->spad; at.v_hs = (long)dh * ctx->spad; at.v_ds = ctx->spad;
         at.k_len = (long)c.max_batch * c.ctx_len_max * D; at.v_len = (long)c.max_batch * D * ctx->spad;
@@ -836,7 +839,8 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
   invalidate_graph(ctx);
   // drop previous weights
   auto drop = [&](void*& p) { dfree(ctx, p); p = nullptr; };
-  for (auto& l : ctx->L) { drop(l.qkv); drop(l.q); drop(l.kx); drop(l.vx); drop(l.o); drop(l.gu); drop(l.down); }
+  for (auto& l : ctx->L) { drop(l.qkv); drop(l.q); l.kx = l.vx = nullptr; drop(l.o); drop(l.gu); drop(l.down); }
+  drop(ctx->wkx_all); drop(ctx->wvx_all);   // kx / vx point into these
   drop(ctx->w_tin); drop(ctx->w_tout); drop(ctx->w_mod); drop(ctx->w_tb); drop(ctx->w_in); drop(ctx->w_out); drop(ctx->w_state);
   { void* bp[] = {ctx->b_tin, ctx->b_tout, ctx->b_mod, ctx->b_tb, ctx->b_in, ctx->b_out, ctx->b_state}; for (void* q : bp) dfree(ctx, q); }
   ctx->b_tin = ctx->b_tout = ctx->b_mod = ctx->b_tb = ctx->b_in = ctx->b_out = ctx->b_state = nullptr;
@@ -929,13 +933,21 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
     if ((s = bias(&ctx->b_tb, data("time_bias.b"), D)) != FM_OK) return s;
     if ((s = plain(&ctx->w_state, data("state_in.w"), (size_t)D * c.state_dim * esz)) != FM_OK) return s;
     if ((s = bias(&ctx->b_state, data("state_in.b"), D)) != FM_OK) return s;
+    // the cross blocks' K and V weights stacked: the fragment-major [nc D, ctx_dim] matrix is
+    // the blocks' [D, ctx_dim] matrices one after another (D is a multiple of 16)
+    const size_t xb = swizzled_bytes(D, c.ctx_dim, elem);
+    const int nc = (c.n_layers + 1) / 2;
+    if ((s = dalloc(ctx, &ctx->wkx_all, nc * xb)) != FM_OK) return s;
+    if ((s = dalloc(ctx, &ctx->wvx_all, nc * xb)) != FM_OK) return s;
     for (int i = 0; i < c.n_layers; ++i) {
       const std::string p = "blocks." + std::to_string(i) + ".";
       auto& W = ctx->L[i];
       if (i % 2 == 0) {
         if ((s = swz(&W.q, data((p + "q.w").c_str()), nullptr, D, D)) != FM_OK) return s;
-        if ((s = swz(&W.kx, data((p + "k.w").c_str()), nullptr, D, c.ctx_dim)) != FM_OK) return s;
-        if ((s = swz(&W.vx, data((p + "v.w").c_str()), nullptr, D, c.ctx_dim)) != FM_OK) return s;
+        W.kx = (char*)ctx->wkx_all + (size_t)(i / 2) * xb;
+        W.vx = (char*)ctx->wvx_all + (size_t)(i / 2) * xb;
+        HIPCK(swizzle_weight(W.kx, data((p + "k.w").c_str()), nullptr, D, c.ctx_dim, c.ctx_dim, elem, ctx->stream));
+        HIPCK(swizzle_weight(W.vx, data((p + "v.w").c_str()), nullptr, D, c.ctx_dim, c.ctx_dim, elem, ctx->stream));
       } else {
         HIPCK(hipMemcpyAsync(stage, data((p + "q.w").c_str()), (size_t)D * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
         HIPCK(hipMemcpyAsync((char*)stage + (size_t)D * D * esz, data((p + "k.w").c_str()), (size_t)D * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
@@ -1141,30 +1153,21 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void
     invalidate_graph(ctx);
     std::vector<Op> ops;
     Op op;
-    for (int i = 0; i < c.n_layers; i += 2) {
-      const int ci = i / 2;
-      GemmArgs g = gemm_base(batch * plen, D, c.ctx_dim, ctx->L[i].kx);
+    // K_c = Z W_K^T and V_c = Z W_V^T of every cross block as two GEMMs over the stacked
+    // weights (GR00T N1.7, "vl_backbone": projected once per observation), each output column
+    // block of width D going to its cross block's plane
+    const int nc = (c.n_layers + 1) / 2;
+    if (nc > 0) {
+      GemmArgs g = gemm_base(batch * plen, nc * D, c.ctx_dim, ctx->wkx_all);
       g.A = ctx_dev; g.lda = c.ctx_dim;
-      g.epi = EPI_STORE; g.out = (char*)ctx->cross_k + (size_t)ci * c.max_batch * c.ctx_len_max * D * ctx->esz;
-      g.ldo = D;
-      // rows b*plen + s -> b*ctx_len_max + s
-      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g;
-      if (plen != c.ctx_len_max) {
-        // one launch per request keeps the [b][ctx_len_max][D] layout
-        for (int b = 0; b < batch; ++b) {
-          Op o2 = op;
-          o2.g.M = plen;
-          o2.g.A = (const char*)ctx_dev + (size_t)b * plen * c.ctx_dim * ctx->esz;
-          o2.g.out = (char*)g.out + (size_t)b * c.ctx_len_max * D * ctx->esz;
-          ops.push_back(o2);
-        }
-      } else {
-        ops.push_back(op);
-      }
-      g = gemm_base(batch * plen, D, c.ctx_dim, ctx->L[i].vx);
+      g.epi = EPI_STORE; g.out = ctx->cross_k; g.ldo = D;   // rows b*plen + s: packed per request
+      g.col_group = D; g.col_gstride = (long)c.max_batch * c.ctx_len_max * D;
+      memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
+      g = gemm_base(batch * plen, nc * D, c.ctx_dim, ctx->wvx_all);
       g.A = ctx_dev; g.lda = c.ctx_dim;
-      g.epi = EPI_VT; g.out = (char*)ctx->cross_vt + (size_t)ci * c.max_batch * D * ctx->spad * ctx->esz;
+      g.epi = EPI_VT; g.out = ctx->cross_vt;
       g.vt_group = plen; g.vt_bs = (long)D * ctx->spad; g.vt_ds = ctx->spad;
+      g.col_group = D; g.col_gstride = (long)c.max_batch * D * ctx->spad;
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.g = g; ops.push_back(op);
     }
     if (c.state_tokens > 0) {
@@ -1180,6 +1183,37 @@ fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t plen, const void
     // every context token visible until fm_bind_context_masks says otherwise
     if ((s = upload_masks(ctx, batch, plen, nullptr, nullptr)) != FM_OK) return s;
   }
+  ctx->bound_batch = batch;
+  ctx->prefix_len = plen;
+  return FM_OK;
+}
+
+fm_status fm_prefix_kv_slot(fm_ctx* ctx, int32_t layer, void** k_dev, void** v_dev) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  const fm_config& c = ctx->c;
+  if (c.arch != FM_ARCH_PREFIX_JOINT) return fail(ctx, FM_ERR_UNSUPPORTED, "the prefix K/V pool belongs to the prefix-joint expert");
+  if (layer < 0 || layer >= c.n_layers || !k_dev || !v_dev)
+    return fail(ctx, FM_ERR_INVALID_ARG, fmt("fm_prefix_kv_slot: layer %d outside [0, %d) or a NULL output", layer, c.n_layers));
+  const size_t plane = (size_t)c.max_batch * ctx->cap * c.head_dim * ctx->esz;
+  *k_dev = (char*)ctx->pool + (size_t)(2 * layer) * plane;
+  *v_dev = (char*)ctx->pool + (size_t)(2 * layer + 1) * plane;
+  return FM_OK;
+}
+
+fm_status fm_bind_prefix_inplace(fm_ctx* ctx, int32_t batch, int32_t plen) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  if (!ctx->loaded) return fail(ctx, FM_ERR_STATE, "weights are not loaded");
+  const fm_config& c = ctx->c;
+  if (c.arch != FM_ARCH_PREFIX_JOINT) return fail(ctx, FM_ERR_UNSUPPORTED, "an in-place binding belongs to the prefix-joint expert");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, FM_ERR_INVALID_ARG, fmt("batch %d outside [1, %d]", batch, c.max_batch));
+  if (plen < 0 || plen > c.max_prefix_len) return fail(ctx, FM_ERR_INVALID_ARG, fmt("prefix_len %d outside [0, %d]", plen, c.max_prefix_len));
+  HIPCK(hipStreamSynchronize(ctx->stream));   // the producer's writes on this stream are done
+  invalidate_graph(ctx);
+  std::vector<int> lens(batch, plen);
+  fm_status s = upload_lengths(ctx, lens, plen);
+  if (s != FM_OK) return s;
   ctx->bound_batch = batch;
   ctx->prefix_len = plen;
   return FM_OK;

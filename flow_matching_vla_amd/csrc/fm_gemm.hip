@@ -297,7 +297,8 @@ struct Epilogue {
 #pragma unroll
           for (int j = 0; j < 4; ++j) y[j] = gelu_tanh(y[j]);
         }
-        const long base = (long)m * a.ldo + n;
+        long base = (long)m * a.ldo + n;
+        if (a.col_group) base = (long)(n / a.col_group) * a.col_gstride + (long)m * a.ldo + n % a.col_group;
         if (a.out_f32) {
           float* o = (float*)a.out + base;
           if (n + 3 < a.N && (base & 3) == 0) *(f32x4*)o = f32x4{y[0], y[1], y[2], y[3]};
@@ -344,8 +345,12 @@ struct Epilogue {
     } else if constexpr (EPI == EPI_VT) {
       if (mok) {
         const int b = m / a.vt_group, sidx = m % a.vt_group;
-        for (int j = 0; j < 4; ++j)
-          if (n + j < a.N) ((T*)a.out)[(long)b * a.vt_bs + (long)(n + j) * a.vt_ds + vt_slot<T>(sidx)] = from_f32<T>(v[j]);
+        for (int j = 0; j < 4; ++j) {
+          const int nn = n + j;
+          const long col = a.col_group ? (long)(nn / a.col_group) * a.col_gstride + (long)(nn % a.col_group) * a.vt_ds
+                                       : (long)nn * a.vt_ds;
+          if (nn < a.N) ((T*)a.out)[(long)b * a.vt_bs + col + vt_slot<T>(sidx)] = from_f32<T>(v[j]);
+        }
       }
     } else if constexpr (EPI == EPI_RESID) {
       // h += gate * y; hs = T(h (1 + next scale)); (mean, M2) of the kStatCols-column slot

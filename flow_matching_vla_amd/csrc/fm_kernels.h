@@ -61,6 +61,10 @@ struct GemmArgs {
   int cfg;           // tile configuration of that kind
   int cpw;           // skinny: k-chunks per wave
   int kw;            // skinny: waves per workgroup (4 / 8)
+  // EPI_STORE / EPI_VT column planes: output column n is column n % col_group of plane
+  // n / col_group, the planes col_gstride elements apart (col_group 0: one plane). Kept last,
+  // so that the fields above keep their offsets in the kernel arguments.
+  int col_group; long col_gstride;
 };
 constexpr long kVecPad = 1L << 18;   // floats in the zeros / ones buffers
 

@@ -45,13 +45,13 @@ struct LoopArgs {
   const float* table;            // [steps][S][3D]
   const float* cbuf;             // [steps][csum]
   const float2* rope_cs;         // [B][H][dh / 2]: cos / sin at each request's positions P_b + i
-  const int* plens;              // [B] compact prefix length P_b <= P of each request
   float* x; float* h;
   const __bf16* pool; long plane;   // elements per pool plane
   char* rot; long rot_step, rot_layer;
   long o_hs, o_st, o_q, o_sk, o_svt, o_ao, o_hsu, o_stu, o_act;
   float* ws_attn; float* ws_attn_ml; float* ws_split;
   uint32_t* flags;
+  const int* plens;              // [B] compact prefix length P_b <= P of each request (kept last)
 };
 
 // Per-launch arguments: first step, step count, first barrier epoch, and the velocity

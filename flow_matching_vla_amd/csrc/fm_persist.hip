@@ -429,7 +429,8 @@ struct AttnItem { int valid, b, rt, sp, pb; };   // pb: the request's compact pr
 // partial results stay in that XCD's L2, which every CU of the XCD sees coherently, and
 // the splits synchronize among themselves through L2 atomics. Row tile rb of the B * RT
 // goes to XCD rb % 8, split sp to slot (rb / 8) * SA + sp of that XCD.
-__device__ __forceinline__ AttnItem attn_item(LA& a) {
+// pb: the item's compact prefix length (attn_item_pb, loaded once per launch)
+__device__ __forceinline__ AttnItem attn_item(LA& a, int pb) {
   AttnItem it;
   const int x = blockIdx.x % 8, j = blockIdx.x / 8;
   const int rb = (j / a.SA) * 8 + x;
@@ -437,9 +438,13 @@ __device__ __forceinline__ AttnItem attn_item(LA& a) {
   it.b = rb / a.RT;
   it.rt = rb % a.RT;
   it.valid = rb < a.B * a.RT;
-  typedef const __attribute__((address_space(4))) int CI;
-  it.pb = it.valid ? *(CI*)(a.plens + __builtin_amdgcn_readfirstlane(it.b)) : 0;
+  it.pb = pb;
   return it;
+}
+__device__ __forceinline__ int attn_item_pb(LA& a) {
+  const AttnItem it = attn_item(a, 0);
+  typedef const __attribute__((address_space(4))) int CI;
+  return it.valid ? *(CI*)(a.plens + __builtin_amdgcn_readfirstlane(it.b)) : 0;
 }
 
 // Key tile `which` (0/1) of split sp: tiles sp and sp + SA, so that this step's suffix tiles
@@ -504,11 +509,11 @@ __device__ __forceinline__ void attn_issue(LA& a, const AttnItem& it, int l, con
   }
 }
 
-__device__ __forceinline__ void attn_phase(LA& a, int l, const char* rot_l, Smem& sm, uint32_t e_attn,
+__device__ __forceinline__ void attn_phase(LA& a, int pb, int l, const char* rot_l, Smem& sm, uint32_t e_attn,
                                            const GemmIn& gin_o_next) {
   typedef Mma<bf16> MT;
   typedef MT::frag frag;
-  const AttnItem it = attn_item(a);
+  const AttnItem it = attn_item(a, pb);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int w4 = wave & 3, half = wave >> 2;
   frag qf[kDCH];
@@ -769,9 +774,11 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
     return a.cbuf + (size_t)k * a.csum + off;
   };
 
+  int pb;   // this workgroup's attention item: its request's compact prefix length
   {
     LA& a = launder(pa);
     prefetch_w(gin_qkv(a, layer_w(a, 0).qkv, rot(a, 0, 0)), sm);
+    pb = attn_item_pb(a);
   }
   for (int kk = 0; kk < la.nsteps; ++kk) {
     LA& a = launder(pa);
@@ -832,7 +839,7 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
       const int D = a.D, M = a.M;
       char* rl = rot(a, kk, l);
       const LayerW lw = layer_w(a, l);
-      const AttnItem ait = attn_item(a);
+      const AttnItem ait = attn_item(a, pb);
       // ---- QKV + RoPE: q to the q buffer, k / v to this step's suffix K / V^T ---------
       {
         const GemmIn g = gin_qkv(a, lw.qkv, rl);
@@ -897,7 +904,7 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         grid_sync(a.flags, ++e);
       }
       // ---- attention: key-split partials, merged per row tile on its XCD ---------------
-      attn_phase(a, l, rl, sm, e + 1, gin_o(a, lw.o, rl));
+      attn_phase(a, pb, l, rl, sm, e + 1, gin_o(a, lw.o, rl));
       grid_sync(a.flags, ++e);
       // ---- O projection + gated residual -------------------------------------------------
       {

@@ -68,6 +68,8 @@ def lib():
         "fm_set_schedule": ([VP, I32, I32, P(C.c_float)], I32),
         "fm_bind_prefix_kv": ([VP, I32, I32, P(VP), P(VP), VP, VP], I32),
         "fm_bind_prefix_lengths": ([VP, P(I32)], I32),
+        "fm_prefix_kv_slot": ([VP, I32, P(VP), P(VP)], I32),
+        "fm_bind_prefix_inplace": ([VP, I32, I32], I32),
         "fm_bind_context_masks": ([VP, P(C.c_uint8), P(C.c_uint8)], I32),
         "fm_denoise": ([VP, VP, I32, VP], I32),
         "fm_step_velocity": ([VP, VP, I32, VP], I32),
@@ -85,6 +87,22 @@ def lib():
         f.argtypes, f.restype = args, res
     _lib = L
     return L
+
+
+def pool_k_col(d, head_dim: int, rope: bool):
+    """Pool column of head-dim index d of a prefix key (the header's fm_pool_k_col)."""
+    d = np.asarray(d)
+    if not rope:
+        return d
+    return np.where(d < head_dim // 2, 2 * d, 2 * (d - head_dim // 2) + 1)
+
+
+def pool_v_slot(j, dtype: int):
+    """Slot of key j in a transposed V row (the header's fm_pool_v_slot)."""
+    j = np.asarray(j)
+    if dtype != BF16:
+        return j
+    return (j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3)
 
 
 def header_symbols():
@@ -217,6 +235,38 @@ class Context:
             kp = (C.c_void_p * len(k))(*[t.data_ptr() for t in k])
             vp = (C.c_void_p * len(v))(*[t.data_ptr() for t in v])
         _check(lib().fm_bind_prefix_kv(self.h, batch, prefix_len, kp, vp, _ptr(context), _ptr(state)), self.h)
+        self._bound = (batch, prefix_len)
+
+    def prefix_kv_slot(self, layer: int):
+        """Device addresses of layer `layer`'s K and V pool planes (see pool_k_col / pool_v_slot
+        for where a prefix key goes)."""
+        k, v = C.c_void_p(), C.c_void_p()
+        _check(lib().fm_prefix_kv_slot(self.h, layer, C.byref(k), C.byref(v)), self.h)
+        return k.value, v.value
+
+    def prefix_pool_views(self, layer: int):
+        """The K plane [max_batch, cap, dh] and transposed V plane [max_batch, dh, cap] of layer
+        `layer` as torch tensors over the pool's own memory (no copy), for a producer that
+        writes the prefix in place."""
+        torch = _torch()
+        cap = query(self.cfg)["pool_capacity"]
+        B, dh = self._c.max_batch, self._c.head_dim
+        bf16 = self.dtype == BF16
+        k, v = self.prefix_kv_slot(layer)
+
+        class _Dev:
+            def __init__(self, ptr, shape):
+                self.__cuda_array_interface__ = {"shape": shape, "typestr": "<i2" if bf16 else "<f4",
+                                                 "data": (ptr, False), "version": 2}
+        kt = torch.as_tensor(_Dev(k, (B, cap, dh)), device="cuda")
+        vt = torch.as_tensor(_Dev(v, (B, dh, cap)), device="cuda")
+        if bf16:
+            kt, vt = kt.view(torch.bfloat16), vt.view(torch.bfloat16)
+        return kt, vt
+
+    def bind_prefix_inplace(self, batch: int, prefix_len: int):
+        """Bind what the pool holds (written through prefix_kv_slot / prefix_pool_views)."""
+        _check(lib().fm_bind_prefix_inplace(self.h, batch, prefix_len), self.h)
         self._bound = (batch, prefix_len)
 
     def bind_prefix_lengths(self, lens=None):

@@ -152,6 +152,39 @@ fm_status fm_set_schedule(fm_ctx* ctx, int32_t steps, int32_t batch, const float
 fm_status fm_bind_prefix_kv(fm_ctx* ctx, int32_t batch, int32_t prefix_len, const void* const* k_dev,
                             const void* const* v_dev, const void* ctx_dev, const void* state_dev);
 
+/* The step before the path without a copy: a prefix producer (the prefix tower's last
+ * projection) writes each layer's K and V straight into the library's pool, and the binding
+ * then only records the batch and length (pi0.5 Design, "Attention and the K/V pool": the
+ * tower writes its output into the pool instead of having it repacked; here the pool keeps
+ * the layout its kernels read, given below).
+ *
+ * fm_prefix_kv_slot (PREFIX_JOINT): *k_dev, *v_dev = DEVICE addresses of layer `layer`'s K
+ *   and V planes; stable for the context's lifetime. With cap = fm_plan_info.pool_capacity,
+ *   dh = head_dim and elements of the config dtype, prefix key j of request b goes to
+ *     K: k_dev[(b * cap + j) * dh + fm_pool_k_col(d, dh, rope_base > 0)] = k[b, j, d]
+ *     V: v_dev[(b * dh + d) * cap + fm_pool_v_slot(j, dtype)]            = v[b, j, d]
+ *   for j < prefix_len (the rows and slots past it belong to the chunk; do not write them).
+ *   Keys are taken as already rotated, as for fm_bind_prefix_kv. FM_ERR_INVALID_ARG for a
+ *   layer out of range or a NULL output.
+ * fm_bind_prefix_inplace (PREFIX_JOINT): binds what the pool holds for requests
+ *   [0, batch) and keys [0, prefix_len), with the bounds of fm_bind_prefix_kv. It synchronizes
+ *   the context stream first: writes enqueued there are complete; writes on another stream
+ *   must be complete before the call. Every request sees the whole prefix (see
+ *   fm_bind_prefix_lengths). The loop never writes pool rows [0, prefix_len), so a binding
+ *   stays valid until the producer writes again. */
+fm_status fm_prefix_kv_slot(fm_ctx* ctx, int32_t layer, void** k_dev, void** v_dev);
+fm_status fm_bind_prefix_inplace(fm_ctx* ctx, int32_t batch, int32_t prefix_len);
+/* Pool column of head-dim index d of a key: RoPE pairs (d, d + dh/2) side by side when the
+ * config uses RoPE, else d. */
+static inline int32_t fm_pool_k_col(int32_t d, int32_t head_dim, int32_t rope) {
+  return !rope ? d : (d < head_dim / 2 ? 2 * d : 2 * (d - head_dim / 2) + 1);
+}
+/* Slot of key j in a transposed V row: bf16 permutes each 32-key tile so that a lane's
+ * MFMA operand is contiguous; fp32 keeps the order. */
+static inline int32_t fm_pool_v_slot(int32_t j, int32_t dtype) {
+  return dtype != FM_BF16 ? j : ((j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3));
+}
+
 /* Per-request key visibility of the bound batch: the additive mask M of Eq. (2) (vla.cpp
  * Sec. III-B: 0 for a visible key, -inf for a hidden one). Both calls copy what they are
  * given into library memory and synchronize the context stream before returning (the host

@@ -4,6 +4,7 @@ the weight tensors the seeded workloads draw. No compute calls: these run withou
 import ctypes as C
 import os
 
+import numpy as np
 import pytest
 
 from flow_matching_vla_amd import fm, workloads as wl
@@ -86,3 +87,18 @@ def test_binding_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fm, "_lib", None)
     with pytest.raises(RuntimeError):
         fm.lib()
+
+
+def test_pool_layout_helpers_are_permutations():
+    # where a prefix producer writes key dims and key slots (fm_pool_k_col / fm_pool_v_slot):
+    # each a permutation, RoPE pairs (d, d + dh/2) side by side, slots permuted within 32-key tiles
+    for dh in (64, 128, 256):
+        cols = fm.pool_k_col(np.arange(dh), dh, True)
+        assert sorted(cols.tolist()) == list(range(dh))
+        assert np.all(cols[dh // 2:] == cols[:dh // 2] + 1)
+        assert np.array_equal(fm.pool_k_col(np.arange(dh), dh, False), np.arange(dh))
+    j = np.arange(1280)
+    s = fm.pool_v_slot(j, fm.BF16)
+    assert sorted(s.tolist()) == j.tolist()
+    assert np.array_equal(s // 32, j // 32)
+    assert np.array_equal(fm.pool_v_slot(j, fm.F32), j)
