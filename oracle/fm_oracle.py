@@ -365,6 +365,77 @@ def run(cfg, weights, inputs, steps=None, tau=None, dtype=np.float64, return_tra
                    return_trace=return_trace, dtype=dtype)
 
 
+# ----------------------------------------------------------------------------- low-bit weights
+# Weight streaming at half the bytes (vla.cpp Sec. IV-D, Table V: quantized GR00T weights; pi0.5
+# Design: FP8 named as an option for the expert): each row of a per-layer matrix (one output
+# feature) is stored as FP8 E4M3 codes times one power-of-two scale. The codes follow the OCP
+# E4M3 ("fn") format: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, subnormals below 2^-6,
+# largest value 448, no infinity. The expert then computes with the dequantized weights.
+FP8_E4M3_MAX = 448.0
+FP8_LAYER_WEIGHTS = ("q.w", "k.w", "v.w", "o.w", "gate.w", "up.w", "down.w")
+
+
+def fp8_e4m3_value(code):
+    """Value of E4M3 code bytes (the format's definition; 0x7F / 0xFF are NaN)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, c & 7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+def fp8_e4m3_encode(x):
+    """Round to the nearest E4M3 value, ties to an even mantissa, for |x| <= 448; returns the
+    code bytes. The quantum is 2^(E - 3) in binade [2^E, 2^(E+1)) for E >= -6, and 2^-9 below
+    2^-6 (subnormals); x / quantum is exact, so the rounding is a half-to-even integer round."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > FP8_E4M3_MAX):
+        raise ValueError("outside the E4M3 range")
+    a = np.abs(x)
+    _, ex = np.frexp(a)                       # a = f 2^ex, f in [0.5, 1)
+    E = np.maximum(ex - 1, -6)                # binade exponent, subnormals share -6
+    q = np.ldexp(1.0, E - 3)
+    n = np.round(a / q)                       # half to even
+    v = n * q                                 # may step up to the next binade: still exact
+    _, ev = np.frexp(np.where(v > 0, v, 1.0))
+    Ev = ev - 1
+    normal = v >= 2.0 ** -6
+    e_field = np.where(normal, Ev + 7, 0)
+    m_field = np.where(normal, np.round(v / np.ldexp(1.0, Ev - 3)) - 8, np.round(v / 2.0 ** -9)).astype(np.int64)
+    code = (e_field.astype(np.int64) << 3) | m_field
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)   # the sign kept on a zero too
+
+
+def fp8_row_exponents(w):
+    """Per row, the smallest e with max |w_row| <= 448 2^e (exact: with max = f 2^x, f in
+    [0.5, 1), e = x - 9 + [f > 0.875], as 448 = 0.875 2^9); 0 for an all-zero row."""
+    amax = np.max(np.abs(np.asarray(w, dtype=np.float64)), axis=-1)
+    f, x = np.frexp(amax)
+    return np.where(amax > 0, x - 9 + (f > 0.875), 0).astype(np.int64)
+
+
+def quantize_fp8_rows(w):
+    """w [N, K] -> (codes uint8 [N, K], exponents int [N], dequantized float64 [N, K]) with
+    w_row ~ value(codes_row) 2^e_row."""
+    w = np.asarray(w, dtype=np.float64)
+    e = fp8_row_exponents(w)
+    codes = fp8_e4m3_encode(np.ldexp(w, -e[:, None]))
+    return codes, e, np.ldexp(fp8_e4m3_value(codes), e[:, None])
+
+
+def fp8_weights(cfg, w):
+    """The expert's per-layer matrices replaced by their FP8-dequantized values (pi0.5-shaped
+    expert); everything else unchanged."""
+    out = dict(w)
+    for l in range(cfg["n_layers"]):
+        for nm in FP8_LAYER_WEIGHTS:
+            key = f"layers.{l}.{nm}"
+            if key in out:
+                out[key] = quantize_fp8_rows(out[key])[2].astype(np.asarray(w[key]).dtype)
+    return out
+
+
 # ----------------------------------------------------------------------------- after the path
 # The chunk leaves the loop in normalized model space; the step after maps it back to robot
 # units with the action statistics (q01, q99 per dimension) and keeps the robot's share.

@@ -601,6 +601,67 @@ def test_dit_shared_mask_equals_compacted_context():
         np.testing.assert_allclose(xr[b:b + 1], xb, rtol=1e-12, atol=1e-13)
 
 
+# ----------------------------------------------------------------------------- low-bit weights
+def test_fp8_e4m3_codes_match_torch_and_brute_force():
+    # the format's 256 codes: 254 values and two NaN; encoding picks the nearest value, ties to
+    # an even mantissa (brute force over every code), and agrees with torch's float8_e4m3fn
+    vals = oracle.fp8_e4m3_value(np.arange(256))
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF]) and np.sum(np.isnan(vals)) == 2
+    assert np.nanmax(vals) == 448.0 and vals[1] == 2.0 ** -9 and vals[8] == 2.0 ** -6
+    finite = np.array([c for c in range(256) if not np.isnan(vals[c])])
+    x = np.concatenate([RNG.standard_normal(3000) * 40, RNG.standard_normal(3000) * 3e-3,
+                        (vals[finite][:, None] + np.array([0.0])).ravel(),
+                        0.5 * (np.sort(vals[finite])[1:] + np.sort(vals[finite])[:-1])])   # every midpoint
+    x = np.clip(x, -448, 448)
+    codes = oracle.fp8_e4m3_encode(x)
+    got = oracle.fp8_e4m3_value(codes)
+    d = np.abs(vals[finite][None, :] - x[:, None])
+    best = d.min(axis=1)
+    assert np.all(np.abs(got - x) == best)                      # nearest
+    tie = (d == best[:, None]).sum(axis=1) > 1
+    assert tie.sum() > 200
+    assert np.all((codes[tie] & 1) == 0)                        # ties: even mantissa
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes, ref)
+    with pytest.raises(ValueError):
+        oracle.fp8_e4m3_encode(np.array([449.0]))
+
+
+def test_fp8_row_scales_and_error_bound():
+    # per row the smallest power of two that brings max |w| within 448; the dequantized
+    # weight is within half a quantum of w (relative 2^-4 for normal values)
+    w = np.stack([RNG.standard_normal(256) * s for s in (1e-3, 0.02, 1.0, 300.0)] + [np.zeros(256)])
+    w[1, 7] = 448 * 2.0 ** -8   # a row max exactly 448 2^e: e = -8, not -7
+    codes, e, deq = oracle.quantize_fp8_rows(w)
+    amax = np.abs(w).max(axis=1)
+    for r in range(4):
+        assert amax[r] <= 448 * 2.0 ** e[r] and amax[r] > 448 * 2.0 ** (e[r] - 1)
+        q = np.ldexp(w[r], -e[r])
+        assert np.all(np.abs(q) <= 448)
+        quantum = np.ldexp(1.0, np.maximum(np.frexp(np.abs(q))[1] - 1, -6) - 3)
+        assert np.all(np.abs(np.ldexp(deq[r], -e[r]) - q) <= quantum / 2)
+    assert e[4] == 0 and np.all(deq[4] == 0)
+    # dequantized values are exact in bf16 (at most 4 significant bits times a power of two)
+    np.testing.assert_array_equal(wl.round_bf16(deq[:4].astype(np.float32)), deq[:4].astype(np.float32))
+    # the result is a function of the row alone: scaling a row by 2^k scales e by k
+    c2, e2, d2 = oracle.quantize_fp8_rows(np.ldexp(w[:4], 5))
+    np.testing.assert_array_equal(c2, codes[:4])
+    np.testing.assert_array_equal(e2, e[:4] + 5)
+
+
+def test_fp8_weights_replace_only_layer_matrices():
+    cfg = _tiny()
+    W = wl.make_weights(cfg)
+    Q = oracle.fp8_weights(cfg, W)
+    for k in W:
+        if any(k.endswith(nm) for nm in oracle.FP8_LAYER_WEIGHTS) and k.startswith("layers."):
+            assert not np.array_equal(Q[k], W[k])
+            e = oracle.fp8_row_exponents(W[k])[:, None]   # half a quantum: relative 2^-4, or 2^(e-10) for subnormals
+            assert np.all(np.abs(Q[k] - W[k]) <= np.maximum(np.abs(W[k]) / 16, np.ldexp(1.0, e - 10)))
+        else:
+            np.testing.assert_array_equal(Q[k], W[k])
+
+
 # ----------------------------------------------------------------------------- after the path
 def test_quantile_unnormalize_inverts_openpi_normalization():
     # pi0.5 Design, "Embodiment adapters": the normalization with its epsilon, inverted
