@@ -43,6 +43,7 @@ def role_bytes_flops(cfg, role):
     kernels are not counted (they can stay on chip)."""
     e = 2 if cfg["dtype"] == 1 else 4
     D, F, L = cfg["hidden"], cfg["mlp_dim"], cfg["n_layers"]
+    w8 = cfg.get("w8", False)   # FP8 per-layer matrices: 1 byte per weight + a 4-byte scale per row
     B, H, da = cfg["batch"], cfg["action_horizon"], cfg["action_dim"]
     nq, dh = cfg["n_heads"], cfg["head_dim"]
     st = cfg.get("state_tokens", 0)
@@ -50,15 +51,17 @@ def role_bytes_flops(cfg, role):
     if cfg["arch"] == 0:
         qd = nq * dh
         keys = cfg["prefix_len"] + H
-        shapes = {
-            "qkv": ((qd + 2 * dh) * D, 2 * D), "oproj": (D * qd, D), "mlp_up": (2 * F * D if cfg["mlp_gated"] else F * D, 2 * D),
-            "mlp_down": (D * F, D), "out": (da * D, 2 * D), "inproj": (D * da, 0),
+        nup = 2 * F if cfg["mlp_gated"] else F
+        shapes = {   # (weights, modulation floats, weight rows)
+            "qkv": ((qd + 2 * dh) * D, 2 * D, qd + 2 * dh), "oproj": (D * qd, D, D), "mlp_up": (nup * D, 2 * D, nup),
+            "mlp_down": (D * F, D, D), "out": (da * D, 2 * D, 0), "inproj": (D * da, 0, 0),
         }
         if role == "attn":
             return B * keys * dh * 2 * e, B * 4 * nq * H * keys * dh
-        w, mod = shapes[role]
+        w, mod, rows = shapes[role]
         Mr = B * H
-        return w * e + mod * 4, 2 * w * Mr
+        wb = w + 4 * rows if (w8 and rows) else w * e
+        return wb + mod * 4, 2 * w * Mr
     # DiT: per-role averages over the two block kinds
     S = cfg["ctx_len"]
     if role == "qkv":
@@ -146,6 +149,8 @@ def main():
     ap.add_argument("--no-fit", action="store_true")
     ap.add_argument("--no-roles", action="store_true")
     ap.add_argument("--no-visibility", action="store_true")
+    ap.add_argument("--weights", choices=("as-given", "fp8"), default="as-given",
+                    help="fp8: the expert's per-layer matrices as FP8 E4M3 codes with per-row scales")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for rocprofv3 --pmc runs: a plain 512 MiB device copy (3x, the counter scale) "
                          "then 3 chunk calls; prints no JSON")
@@ -161,12 +166,16 @@ def main():
     from flow_matching_vla_amd import fm, workloads as wl
 
     cfg = wl.workload(args.workload)
+    if args.weights == "fp8":
+        cfg["w8"] = True
     T, B = cfg["steps"], cfg["batch"]
     dt = cfg["dtype"]
     print(f"[bench] {cfg['name']}: generating seeded inputs", file=sys.stderr, flush=True)
     W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
     torch.cuda.set_device(0)
     ctx = fm.Context(cfg)
+    if args.weights == "fp8":
+        ctx.set_weight_format(fm.WEIGHTS_FP8_E4M3)
     wt = {n: fm.to_device(a, dt) for n, a in W.items()}
     ctx.load_weights(wt)
     del wt
@@ -227,7 +236,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if dt == 1 else "f32", "data": "synthetic (seeded, random-init)",
         "config": {"workload": f"{cfg['name']}: {DESCRIPTIONS[cfg['name']]}", "batch": B, "euler_steps": T,
                    "prefix_len": cfg["prefix_len"], "action_horizon": cfg["action_horizon"],
-                   "action_dim": cfg["action_dim"], "parallelism": "none (1 GPU)"},
+                   "action_dim": cfg["action_dim"], "parallelism": "none (1 GPU)",
+                   "weights": "fp8-e4m3, per-row power-of-two scale" if args.weights == "fp8" else "as given"},
         "per_euler_step_us": round(1000 * ms / T, 2),
         "loop": {"alg_bytes_per_euler_step": int(step_b), "alg_flops_per_euler_step": int(step_f),
                  "achieved_GBps": round(step_b * T / (ms * 1e-3) / 1e9, 1),
@@ -270,7 +280,7 @@ def main():
         nbytes, nflops = step_b * T, step_f * T
         ach = nbytes / avg_s / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": loop_traffic(cfg["name"]), "kernel": "k_loop",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": loop_traffic(cfg["name"] + ("_fp8" if args.weights == "fp8" else "")), "kernel": "k_loop",
                            "alg_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2),
                            "launches_per_chunk": 1, "mfma_TFLOPs": round(nflops / avg_s / 1e12, 2)}
     if not args.no_roles and not persistent:

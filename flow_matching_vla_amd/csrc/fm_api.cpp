@@ -140,7 +140,13 @@ struct fm_ctx {
   // device memory owned by the context
   std::vector<void*> allocs;
   bool loaded = false;
-  struct Layer { void *qkv = nullptr, *q = nullptr, *kx = nullptr, *vx = nullptr, *o = nullptr, *gu = nullptr, *down = nullptr; };
+  struct Layer {
+    void *qkv = nullptr, *q = nullptr, *kx = nullptr, *vx = nullptr, *o = nullptr, *gu = nullptr, *down = nullptr;
+    // FP8 weights (FM_WEIGHTS_FP8_E4M3): codes fragment-major and per-row scales of the same
+    // four matrices, streamed by the loop kernel; qkv .. down then hold the dequantized bf16
+    void *qkv8 = nullptr, *o8 = nullptr, *gu8 = nullptr, *down8 = nullptr;
+    float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sdown = nullptr;
+  };
   std::vector<Layer> L;
   void *w_tin = nullptr, *w_tout = nullptr, *w_mod = nullptr, *w_tb = nullptr, *w_in = nullptr, *w_out = nullptr, *w_state = nullptr;
   float *b_tin = nullptr, *b_tout = nullptr, *b_mod = nullptr, *b_tb = nullptr, *b_in = nullptr, *b_out = nullptr, *b_state = nullptr;
@@ -201,6 +207,8 @@ struct fm_ctx {
   LoopArgs* loop_dev = nullptr;      // the loop description the kernel reads, and its host copy
   LoopArgs loop_host;
   bool loop_uploaded = false;
+  int wformat = FM_WEIGHTS_AS_GIVEN;   // for the next fm_load_weights
+  bool w8 = false;                     // the loaded per-layer weights have FP8 copies
   LayerW* lw_dev = nullptr;          // [n_layers] weight pointers
   std::vector<LayerW> lw_host;
 
@@ -579,12 +587,17 @@ fm_status loop_run(fm_ctx* ctx, int k0, int nsteps, float* vout) {
   a.max_steps = std::max(c.max_steps, 1); a.dts = ctx->dts;
   a.w_in = ctx->w_in; a.b_in = ctx->b_in; a.w_out = ctx->w_out; a.b_out = ctx->b_out;
   std::vector<LayerW> lw(c.n_layers);
-  for (int l = 0; l < c.n_layers; ++l) lw[l] = LayerW{ctx->L[l].qkv, ctx->L[l].o, ctx->L[l].gu, ctx->L[l].down};
+  for (int l = 0; l < c.n_layers; ++l) {
+    const auto& W = ctx->L[l];
+    lw[l] = ctx->w8 ? LayerW{W.qkv8, W.o8, W.gu8, W.down8, W.sqkv, W.so, W.sgu, W.sdown}
+                    : LayerW{W.qkv, W.o, W.gu, W.down, nullptr, nullptr, nullptr, nullptr};
+  }
   a.lw = ctx->lw_dev;
-  a.wb_qkv = (uint32_t)swizzled_bytes(a.nqkv, a.D, ET_BF16);
-  a.wb_o = (uint32_t)swizzled_bytes(a.D, a.qd, ET_BF16);
-  a.wb_gu = (uint32_t)swizzled_bytes(2 * a.F, a.D, ET_BF16);
-  a.wb_down = (uint32_t)swizzled_bytes(a.D, a.F, ET_BF16);
+  auto wbytes = [&](int N, int K) { return (uint32_t)(ctx->w8 ? swizzled_fp8_bytes(N, K) : swizzled_bytes(N, K, ET_BF16)); };
+  a.wb_qkv = wbytes(a.nqkv, a.D);
+  a.wb_o = wbytes(a.D, a.qd);
+  a.wb_gu = wbytes(2 * a.F, a.D);
+  a.wb_down = wbytes(a.D, a.F);
   a.wb_out = (uint32_t)swizzled_bytes(a.da, a.D, ET_BF16);
   a.table = ctx->table; a.cbuf = ctx->cbuf; a.rope_cs = ctx->rope_cs; a.plens = ctx->plens;
   a.x = ctx->x; a.h = ctx->h;
@@ -614,7 +627,7 @@ fm_status loop_run(fm_ctx* ctx, int k0, int nsteps, float* vout) {
   }
   la.e0 = ctx->epoch;
   ctx->epoch += nbar;
-  HIPCK(loop_launch(ctx->loop_dev, la, ctx->num_cus, ctx->stream));
+  HIPCK(loop_launch(ctx->loop_dev, la, ctx->num_cus, ctx->w8, ctx->stream));
   return FM_OK;
 }
 
@@ -839,7 +852,13 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
   invalidate_graph(ctx);
   // drop previous weights
   auto drop = [&](void*& p) { dfree(ctx, p); p = nullptr; };
-  for (auto& l : ctx->L) { drop(l.qkv); drop(l.q); l.kx = l.vx = nullptr; drop(l.o); drop(l.gu); drop(l.down); }
+  for (auto& l : ctx->L) {
+    drop(l.qkv); drop(l.q); l.kx = l.vx = nullptr; drop(l.o); drop(l.gu); drop(l.down);
+    drop(l.qkv8); drop(l.o8); drop(l.gu8); drop(l.down8);
+    { void* sp[] = {l.sqkv, l.so, l.sgu, l.sdown}; for (void* q : sp) dfree(ctx, q); }
+    l.sqkv = l.so = l.sgu = l.sdown = nullptr;
+  }
+  ctx->w8 = false;
   drop(ctx->wkx_all); drop(ctx->wvx_all);   // kx / vx point into these
   drop(ctx->w_tin); drop(ctx->w_tout); drop(ctx->w_mod); drop(ctx->w_tb); drop(ctx->w_in); drop(ctx->w_out); drop(ctx->w_state);
   { void* bp[] = {ctx->b_tin, ctx->b_tout, ctx->b_mod, ctx->b_tb, ctx->b_in, ctx->b_out, ctx->b_state}; for (void* q : bp) dfree(ctx, q); }
@@ -892,6 +911,29 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
   int* rowidx = nullptr;
   std::vector<int> rows;
   if ((s = dalloc(ctx, &stage, stage_rows * D * esz)) != FM_OK) return s;
+  // FP8 weights: the matrix quantized row by row (codes, row scales, dequantized bf16), then
+  // the dequantized matrix laid out for the per-operation kernels and the schedule, and the
+  // codes and scales for the loop kernel, all in the same output-row order (rows)
+  const bool w8 = c.arch == FM_ARCH_PREFIX_JOINT && ctx->wformat == FM_WEIGHTS_FP8_E4M3;
+  void *st8 = nullptr, *stsc = nullptr, *stdq = nullptr;
+  if (w8) {
+    if ((s = dalloc(ctx, &st8, stage_rows * D)) != FM_OK) return s;
+    if ((s = dalloc(ctx, &stsc, stage_rows * 4)) != FM_OK) return s;
+    if ((s = dalloc(ctx, &stdq, stage_rows * D * esz)) != FM_OK) return s;
+  }
+  auto q8 = [&](void** dbf, void** d8, float** dsc, const void* src, const int* rws, int N, int K) -> fm_status {
+    HIPCK(quantize_fp8_rows(src, K, N, K, (uint8_t*)st8, (float*)stsc, stdq, ctx->stream));
+    fm_status st2 = swz(dbf, stdq, rws, N, K);
+    if (st2 != FM_OK) return st2;
+    if ((st2 = dalloc(ctx, d8, swizzled_fp8_bytes(N, K))) != FM_OK) return st2;
+    HIPCK(swizzle_fp8(*d8, (const uint8_t*)st8, rws, N, K, ctx->stream));
+    const int Np = (int)round_up(N, 4);
+    void* p;
+    if ((st2 = dalloc(ctx, &p, (size_t)Np * 4)) != FM_OK) return st2;
+    *dsc = (float*)p;
+    HIPCK(gather_f32(*dsc, (const float*)stsc, rws, N, Np, ctx->stream));
+    return FM_OK;
+  };
 
   if (c.arch == FM_ARCH_PREFIX_JOINT) {
     const int nq = c.n_heads, dh = c.head_dim, qd = nq * dh, N = qd + 2 * dh;
@@ -917,15 +959,18 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
       HIPCK(hipMemcpyAsync(stage, data((p + "q.w").c_str()), (size_t)qd * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
       HIPCK(hipMemcpyAsync((char*)stage + (size_t)qd * D * esz, data((p + "k.w").c_str()), (size_t)dh * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
       HIPCK(hipMemcpyAsync((char*)stage + (size_t)(qd + dh) * D * esz, data((p + "v.w").c_str()), (size_t)dh * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
-      if ((s = swz(&W.qkv, stage, rowidx, N, D)) != FM_OK) return s;
-      if ((s = swz(&W.o, data((p + "o.w").c_str()), nullptr, D, qd)) != FM_OK) return s;
-      if ((s = swz(&W.down, data((p + "down.w").c_str()), nullptr, D, F)) != FM_OK) return s;
+      if ((s = w8 ? q8(&W.qkv, &W.qkv8, &W.sqkv, stage, rowidx, N, D) : swz(&W.qkv, stage, rowidx, N, D)) != FM_OK) return s;
+      const void* ow = data((p + "o.w").c_str());
+      if ((s = w8 ? q8(&W.o, &W.o8, &W.so, ow, nullptr, D, qd) : swz(&W.o, ow, nullptr, D, qd)) != FM_OK) return s;
+      const void* dw = data((p + "down.w").c_str());
+      if ((s = w8 ? q8(&W.down, &W.down8, &W.sdown, dw, nullptr, D, F) : swz(&W.down, dw, nullptr, D, F)) != FM_OK) return s;
       if (c.mlp_gated) {
         HIPCK(hipMemcpyAsync(stage, data((p + "gate.w").c_str()), (size_t)F * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
         HIPCK(hipMemcpyAsync((char*)stage + (size_t)F * D * esz, data((p + "up.w").c_str()), (size_t)F * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
-        if ((s = swz(&W.gu, stage, rowidx + N, 2 * F, D)) != FM_OK) return s;
+        if ((s = w8 ? q8(&W.gu, &W.gu8, &W.sgu, stage, rowidx + N, 2 * F, D) : swz(&W.gu, stage, rowidx + N, 2 * F, D)) != FM_OK) return s;
       } else {
-        if ((s = swz(&W.gu, data((p + "gate.w").c_str()), nullptr, F, D)) != FM_OK) return s;
+        const void* gw = data((p + "gate.w").c_str());
+        if ((s = w8 ? q8(&W.gu, &W.gu8, &W.sgu, gw, nullptr, F, D) : swz(&W.gu, gw, nullptr, F, D)) != FM_OK) return s;
       }
     }
   } else {
@@ -979,8 +1024,31 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
   HIPCK(hipStreamSynchronize(ctx->stream));
   dfree(ctx, stage);
   dfree(ctx, rowidx);
+  dfree(ctx, st8); dfree(ctx, stsc); dfree(ctx, stdq);
+  ctx->w8 = w8;
   ctx->loaded = true;
   ctx->prefix_len = -1;  // a binding may depend on the previous weights (DiT projections)
+  return FM_OK;
+}
+
+fm_status fm_set_weight_format(fm_ctx* ctx, int32_t format) {
+  if (!ctx) { g_err = "ctx is NULL"; return FM_ERR_INVALID_ARG; }
+  if (ctx->poisoned) return FM_ERR_DEVICE;
+  const fm_config& c = ctx->c;
+  if (format != FM_WEIGHTS_AS_GIVEN && format != FM_WEIGHTS_FP8_E4M3)
+    return fail(ctx, FM_ERR_INVALID_ARG, fmt("weight format %d", format));
+  if (format == FM_WEIGHTS_FP8_E4M3 && (c.arch != FM_ARCH_PREFIX_JOINT || c.dtype != FM_BF16 || c.mlp_dim % 64 != 0))
+    return fail(ctx, FM_ERR_UNSUPPORTED, "FP8 weights need the prefix-joint expert in bf16 with mlp_dim a multiple of 64");
+  ctx->wformat = format;
+  return FM_OK;
+}
+
+fm_status fm_op_quantize_fp8(int32_t N, int32_t K, const void* src, void* codes, float* scale, void* deq, void* hip_stream) {
+  if (N < 0 || K < 2 || K % 2 || !src || !codes || !scale || !deq) { g_err = "fm_op_quantize_fp8: bad arguments"; return FM_ERR_INVALID_ARG; }
+  hipStream_t st = (hipStream_t)hip_stream;
+  hipError_t e = quantize_fp8_rows(src, K, N, K, (uint8_t*)codes, scale, deq, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) { g_err = fmt("fm_op_quantize_fp8: %s", hipGetErrorString(e)); return FM_ERR_DEVICE; }
   return FM_OK;
 }
 

@@ -132,6 +132,14 @@ hipError_t prefix_k_copy(void* pool, long pool_bs, const void* src, int B, int P
 hipError_t prefix_v_copy_t(void* pool, long pool_bs, int cap, const void* src, int B, int P, int dh,
                            int elem, hipStream_t s);
 hipError_t fill_f32(float* dst, float v, long n, hipStream_t s);
+// FP8 E4M3 weights, one power-of-two scale per row: codes [N x K] bytes, scale [N], and the
+// dequantized bf16 matrix deq [N x K] (exact). src bf16 rows of stride ld; K even.
+hipError_t quantize_fp8_rows(const void* src, long ld, int N, int K, uint8_t* codes, float* scale, void* deq, hipStream_t s);
+// FP8 codes fragment-major (16 rows x 64 k per 1 KB fragment; K a multiple of 64), rows as swizzle_weight.
+hipError_t swizzle_fp8(void* dst, const uint8_t* codes, const int* rows, int N, int K, hipStream_t s);
+size_t swizzled_fp8_bytes(int N, int K);
+// dst[i] = src[rows[i]] (or src[i]) for i < N, 0 for N <= i < Npad
+hipError_t gather_f32(float* dst, const float* src, const int* rows, int N, int Npad, hipStream_t s);
 // model-space chunk -> robot units, first hr steps and dr dims (kind 0 / 1 as fm.h)
 hipError_t unnormalize_launch(const float* x, float* out, const float* q01, const float* q99, int B, int H, int da,
                               int hr, int dr, int kind, hipStream_t s);

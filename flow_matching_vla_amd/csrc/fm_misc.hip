@@ -195,6 +195,90 @@ hipError_t unnormalize_launch(const float* x, float* out, const float* q01, cons
   hipLaunchKernelGGL(k_unnormalize, dim3(grid), dim3(256), 0, s, x, out, q01, q99, B, H, da, hr, dr, kind);
   return hipGetLastError();
 }
+// FP8 weights: each row of src [N x K] (bf16) as E4M3 codes times 2^e_row, e_row the smallest
+// exponent with max |row| <= 448 2^e (max = f 2^x, f in [0.5, 1): e = x - 9 + [f > 0.875]).
+// One workgroup per row. Codes come from the hardware conversion (round to nearest even;
+// |x 2^-e| <= 448 cannot overflow); deq = code 2^e in bf16, exact (a code has at most four
+// significant bits).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__global__ void __launch_bounds__(256) k_quant_fp8(const bf16* __restrict__ src, long ld, int K, uint8_t* __restrict__ codes,
+                                                   float* __restrict__ scale, bf16* __restrict__ deq) {
+  __shared__ float red[256];
+  const long r = blockIdx.x;
+  const bf16* row = src + r * ld;
+  float m = 0.f;
+  for (int k = threadIdx.x; k < K; k += 256) m = fmaxf(m, fabsf((float)row[k]));
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const float amax = red[0];
+  int x = 0;
+  const float f = frexpf(amax, &x);
+  const int e = amax > 0.f ? x - 9 + (f > 0.875f ? 1 : 0) : 0;
+  const float sc = ldexpf(1.f, e);
+  if (threadIdx.x == 0) scale[r] = sc;
+  for (int k = 2 * (int)threadIdx.x; k < K; k += 512) {   // K even: pairs
+    const float q0 = ldexpf((float)row[k], -e), q1 = ldexpf((float)row[k + 1], -e);
+    const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);   // codes in bits [15:0]
+    *(uint16_t*)(codes + r * K + k) = (uint16_t)(w & 0xFFFFu);
+    *(bf16x2*)(deq + r * K + k) = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, false);
+  }
+}
+
+// FP8 weights fragment-major: fragment (nb, kp) = rows 16 nb .. 16 nb + 15 x k 64 kp .. 64 kp
+// + 63, 1 KB; lane l holds row 16 nb + l % 16: bytes 0-7 the codes of k = 64 kp + 8 (l / 16)
+// + 0..7, bytes 8-15 those of k + 32 (two 32-wide MFMA k-chunks). rows: source row of each
+// output row (null = identity). Rows past N are zeros.
+__global__ void k_swizzle_fp8(uint8_t* __restrict__ dst, const uint8_t* __restrict__ codes, const int* __restrict__ rows,
+                              int N, int K) {
+  const int KP = K / 64;
+  const long nfrag = (long)((N + 15) / 16) * KP;
+  for (long c = blockIdx.x * (long)blockDim.x + threadIdx.x; c < nfrag * 64; c += (long)gridDim.x * blockDim.x) {
+    const long fidx = c / 64;
+    const int l = (int)(c % 64);
+    const int nb = (int)(fidx / KP), kp = (int)(fidx % KP);
+    const int n = nb * 16 + (l % 16);
+    const int k = kp * 64 + (l / 16) * 8;
+    uint2 lo = make_uint2(0u, 0u), hi = lo;
+    if (n < N) {
+      const int sr = rows ? rows[n] : n;
+      lo = *(const uint2*)(codes + (long)sr * K + k);
+      hi = *(const uint2*)(codes + (long)sr * K + k + 32);
+    }
+    *(uint4*)(dst + c * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+__global__ void k_gather_f32(float* __restrict__ dst, const float* __restrict__ src, const int* __restrict__ rows, int N, int Npad) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < Npad) dst[i] = i < N ? src[rows ? rows[i] : i] : 0.f;
+}
+
+hipError_t quantize_fp8_rows(const void* src, long ld, int N, int K, uint8_t* codes, float* scale, void* deq, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (K % 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_quant_fp8, dim3(N), dim3(256), 0, s, (const bf16*)src, ld, K, codes, scale, (bf16*)deq);
+  return hipGetLastError();
+}
+
+size_t swizzled_fp8_bytes(int N, int K) { return (size_t)((N + 15) / 16) * 16 * K; }
+
+hipError_t swizzle_fp8(void* dst, const uint8_t* codes, const int* rows, int N, int K, hipStream_t s) {
+  if (K % 64) return hipErrorInvalidValue;
+  const long n = (long)((N + 15) / 16) * (K / 64) * 64;
+  hipLaunchKernelGGL(k_swizzle_fp8, dim3(grid_for(n)), dim3(256), 0, s, (uint8_t*)dst, codes, rows, N, K);
+  return hipGetLastError();
+}
+
+hipError_t gather_f32(float* dst, const float* src, const int* rows, int N, int Npad, hipStream_t s) {
+  if (Npad <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather_f32, dim3((Npad + 255) / 256), dim3(256), 0, s, dst, src, rows, N, Npad);
+  return hipGetLastError();
+}
+
 hipError_t fill_f32(float* dst, float v, long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill, dim3(grid_for(n)), dim3(256), 0, s, dst, v, n);

@@ -20,7 +20,12 @@ constexpr int kFlagAttn = kFlagSplit + kMaxSplitItems;
 constexpr int kFlagWords = kFlagAttn + kMaxRowTiles * kMaxSA;
 
 // Fragment-major weights of one layer.
-struct LayerW { const void* qkv; const void* o; const void* gu; const void* down; };
+// With FP8 weights the four matrices hold codes and s* their per-row scales (padded to 4
+// floats); with bf16 weights the s* are null.
+struct LayerW {
+  const void* qkv; const void* o; const void* gu; const void* down;
+  const float* sqkv; const float* so; const float* sgu; const float* sdown;
+};
 
 // Shapes that decide whether the loop kernel applies.
 struct LoopShape {
@@ -67,6 +72,7 @@ const char* loop_check(const LoopShape& s, int num_cus);
 // grid barriers one launch of `steps` Euler steps performs
 int loop_barriers(int L, int steps);
 // a: the loop description in DEVICE memory (read by the kernel through a pointer)
-hipError_t loop_launch(const LoopArgs* a_dev, const LaunchArgs& la, int grid, hipStream_t s);
+// w8: the LayerW matrices are FP8 codes (k_loop<true>)
+hipError_t loop_launch(const LoopArgs* a_dev, const LaunchArgs& la, int grid, bool w8, hipStream_t s);
 
 }  // namespace fm

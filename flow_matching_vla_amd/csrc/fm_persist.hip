@@ -170,6 +170,7 @@ struct GemmIn {
   int N, K, nks, ntiles;
   const void* A; uint32_t lda, abytes;        // A [M x lda] bf16
   int xbase;                                  // split-K: first partial / flag slot of this GEMM
+  bool w8;                                    // W holds FP8 codes (16 rows x 64 k per 1 KB fragment)
 };
 
 // Work item in slot s (0, 1) of this workgroup. Without split-K, items are column tiles
@@ -218,6 +219,12 @@ __device__ __forceinline__ void prefetch_w(const GemmIn& g, Smem& sm) {
 #pragma unroll
       for (int j = 0; j < kPCh; ++j) {
         const int c = ks * (kPKS / 32) + ws * kPCh + j;
+        if (g.w8) {   // one 16-byte copy carries the FP8 codes of chunks c, c + 1 (j even)
+          if (j & 1) continue;
+          const uint32_t off = (ok && c < kct) ? (uint32_t)(((tile * (kct / 2) + c / 2) * 64 + lane) * 16) : kOob;
+          dma16_lds(dw, lds_addr(&sm.wbuf[s][ws][j / 2][0]), off);
+          continue;
+        }
         const uint32_t off = (ok && c < kct) ? (uint32_t)(((tile * kct + c) * 64 + lane) * 16) : kOob;
         dma16_lds(dw, lds_addr(&sm.wbuf[s][ws][j][0]), off);
       }
@@ -225,8 +232,28 @@ __device__ __forceinline__ void prefetch_w(const GemmIn& g, Smem& sm) {
   }
 }
 // This wave's weight fragments from wbuf (the copies completed at the last barrier).
-__device__ __forceinline__ void read_w(const Smem& sm, V16 (&wr)[2][kPCh], int nslot) {
+// Eight FP8 codes (two words, k order) to the bf16 MFMA operand, exactly (unscaled: the row
+// scale is applied in the epilogue).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ V16 fp8x8_bf16(uint32_t w0, uint32_t w1) {
+  return V16{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+}
+__device__ __forceinline__ void read_w(const Smem& sm, V16 (&wr)[2][kPCh], int nslot, bool w8) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (w8) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < kPCh; j += 2) {
+        const V16 x = s < nslot ? sm.wbuf[s][wave][j / 2][lane] : vzero();
+        wr[s][j] = fp8x8_bf16(x[0], x[1]);
+        wr[s][j + 1] = fp8x8_bf16(x[2], x[3]);
+      }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -378,10 +405,12 @@ __device__ __forceinline__ bool split_reduce(LA& a, const GemmIn& g, uint32_t e,
 
 // Residual epilogue inputs of thread (row r, columns n..n+3): gate, next scale, h (sc1).
 struct ResidIn {
-  V16 g, sc, h;
-  __device__ __forceinline__ void issue(LA& a, int r, int n, const float* gate, const float* scale_next, bool use) {
+  V16 g, sc, h, ws;   // ws: FP8 row scales of the weight (ones for bf16 weights)
+  __device__ __forceinline__ void issue(LA& a, int r, int n, const float* gate, const float* scale_next, bool use,
+                                        const float* wscale) {
     g = col4(gate, n, a.D, use);
     sc = col4(scale_next, n, a.D, use);
+    ws = wscale ? col4(wscale, n, a.D, use) : as_v(f32x4{1.f, 1.f, 1.f, 1.f});
     const Rsrc rh = make_rsrc(a.h, (uint32_t)(a.M * a.D * 4));
     h = ld16<kCpSc1>(rh, (use && r < a.M) ? (uint32_t)((r * a.D + n) * 4) : kOob);
   }
@@ -392,7 +421,7 @@ struct ResidIn {
 __device__ __forceinline__ void epi_resid(LA& a, f32x4 v, const ResidIn& in, int r, int n, int tile,
                                           char* hs_out, float* st_out) {
   const bool ok = r < a.M;
-  const f32x4 hv = as_f4(in.h) + as_f4(in.g) * v;
+  const f32x4 hv = as_f4(in.h) + as_f4(in.g) * (as_f4(in.ws) * v);
   const f32x4 sc = as_f4(in.sc);
   float ss = hv[0] * hv[0] + hv[1] * hv[1] + hv[2] * hv[2] + hv[3] * hv[3];
   ss = group_sum<4>(ss);
@@ -721,9 +750,11 @@ __device__ __forceinline__ LA& launder(const LoopArgs* p) {
 }
 __device__ __forceinline__ LayerW layer_w(LA& a, int l) {
   CLayerW* p = (CLayerW*)a.lw + l;
-  return LayerW{p->qkv, p->o, p->gu, p->down};
+  return LayerW{p->qkv, p->o, p->gu, p->down, p->sqkv, p->so, p->sgu, p->sdown};
 }
 
+// W8: the per-layer weights are FP8 codes with per-row scales (see read_w)
+template <bool W8>
 __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa, LaunchArgs la) {
   __shared__ Smem sm;
   const int t = threadIdx.x, G = gridDim.x;
@@ -736,35 +767,35 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = W; g.wbytes = a.wb_qkv; g.N = a.nqkv; g.K = D; g.nks = (D + kPKS - 1) / kPKS;
-    g.ntiles = (a.nqkv + 15) / 16; g.A = rl + a.o_hs; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0;
+    g.ntiles = (a.nqkv + 15) / 16; g.A = rl + a.o_hs; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0; g.w8 = W8;
     return g;
   };
   auto gin_o = [&](LA& a, const void* W, char* rl) {
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = W; g.wbytes = a.wb_o; g.N = D; g.K = a.qd; g.nks = (a.qd + kPKS - 1) / kPKS;
-    g.ntiles = D / 16; g.A = rl + a.o_ao; g.lda = a.qd; g.abytes = act_bytes(M, a.qd); g.xbase = 0;
+    g.ntiles = D / 16; g.A = rl + a.o_ao; g.lda = a.qd; g.abytes = act_bytes(M, a.qd); g.xbase = 0; g.w8 = W8;
     return g;
   };
   auto gin_up = [&](LA& a, const void* W, char* rl) {
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = W; g.wbytes = a.wb_gu; g.N = 2 * a.F; g.K = D; g.nks = (D + kPKS - 1) / kPKS;
-    g.ntiles = 2 * a.F / 16; g.A = rl + a.o_hsu; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0;
+    g.ntiles = 2 * a.F / 16; g.A = rl + a.o_hsu; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0; g.w8 = W8;
     return g;
   };
   auto gin_down = [&](LA& a, const void* W, char* rl) {
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = W; g.wbytes = a.wb_down; g.N = D; g.K = a.F; g.nks = (a.F + kPKS - 1) / kPKS;
-    g.ntiles = D / 16; g.A = rl + a.o_act; g.lda = a.F; g.abytes = act_bytes(M, a.F); g.xbase = kMaxSplitItems / 2;
+    g.ntiles = D / 16; g.A = rl + a.o_act; g.lda = a.F; g.abytes = act_bytes(M, a.F); g.xbase = kMaxSplitItems / 2; g.w8 = W8;
     return g;
   };
   auto gin_out = [&](LA& a, char* rf) {
     const int D = a.D, M = a.M;
     GemmIn g;
     g.W = a.w_out; g.wbytes = a.wb_out; g.N = a.da; g.K = D; g.nks = (D + kPKS - 1) / kPKS;
-    g.ntiles = (a.da + 15) / 16; g.A = rf + a.o_hs; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0;
+    g.ntiles = (a.da + 15) / 16; g.A = rf + a.o_hs; g.lda = D; g.abytes = act_bytes(M, D); g.xbase = 0; g.w8 = false;
     return g;
   };
   // the table row of site s at step k: [scale | shift | gate], D each
@@ -845,19 +876,20 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         const GemmIn g = gin_qkv(a, lw.qkv, rl);
         const int nslot = gemm_slots(g);
         V16 wr[2][kPCh];
-        read_w(sm, wr, nslot);
+        read_w(sm, wr, nslot, g.w8);
         V16 ra[kPCh][4];
         load_a(g, M, ra);
         StatLoad st;
         st.issue(rl + a.o_st, M, D);
         const int b = er / a.H, i = er % a.H;
         const Rsrc rc = make_rsrc(a.rope_cs, (uint32_t)(a.B * a.H * (kDH / 2) * 8));
-        V16 cv[2], csv[2];
+        V16 cv[2], csv[2], wsv[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int n = ((int)blockIdx.x + s2 * G) * 16 + 4 * eq;
           const bool use = t < 256 && s2 < nslot && er < M;
           cv[s2] = col4(cvec(a, k, 2 * l), min(n, a.cq4 - 4), a.cq4, use);
+          wsv[s2] = W8 ? col4(lw.sqkv, min(n, a.cq4 - 4), a.cq4, use) : as_v(f32x4{1.f, 1.f, 1.f, 1.f});
           csv[s2] = ld16<0>(rc, (use && a.rope && n < a.qd + kDH) ? (uint32_t)((er * (kDH / 2) + (n % kDH) / 2) * 8) : kOob);
         }
         st.finish(D, a.eps, sm);
@@ -868,7 +900,7 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         for (int s2 = 0; s2 < 2; ++s2) {
           const int n = ((int)blockIdx.x + s2 * G) * 16 + 4 * eq;
           if (t < 256 && s2 < nslot && er < M && n < a.nqkv) {
-            f32x4 y = sm.rinv[er] * v[s2] + as_f4(cv[s2]);
+            f32x4 y = sm.rinv[er] * (as_f4(wsv[s2]) * v[s2]) + as_f4(cv[s2]);
             if (a.rope && n < a.qd + kDH) {
               const f32x4 cs = as_f4(csv[s2]);
               const float x0 = y[0], x1 = y[1], x2 = y[2], x3 = y[3];
@@ -912,13 +944,13 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         const GItem gi = gemm_item(g, 0);
         const bool has = gi.valid;
         V16 wr[2][kPCh];
-        read_w(sm, wr, has ? 1 : 0);
+        read_w(sm, wr, has ? 1 : 0, g.w8);
         V16 ra[kPCh][4];
         load_a(g, M, ra);
         const int tile = gi.tile;
         const int n = tile * 16 + 4 * eq;
         ResidIn rin;
-        rin.issue(a, er, n, site(a, k, 2 * l, 2), site(a, k, 2 * l + 1, 0), has && gi.ks == 0 && t < 256);
+        rin.issue(a, er, n, site(a, k, 2 * l, 2), site(a, k, 2 * l + 1, 0), has && gi.ks == 0 && t < 256, W8 ? lw.so : nullptr);
         f32x4 v[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         if (has) gemm_core(wr, ra, sm, 1, v);
         else __syncthreads();   // as in gemm_core: every wave's read of wbuf is done
@@ -932,16 +964,18 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         const GemmIn g = gin_up(a, lw.gu, rl);
         const int nslot = gemm_slots(g);
         V16 wr[2][kPCh];
-        read_w(sm, wr, nslot);
+        read_w(sm, wr, nslot, g.w8);
         V16 ra[kPCh][4];
         load_a(g, M, ra);
         StatLoad st;
         st.issue(rl + a.o_stu, M, D);
-        V16 cv[2];
+        V16 cv[2], wsv[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int n = ((int)blockIdx.x + s2 * G) * 16 + 4 * eq;   // interleaved (gate_f, up_f) pairs
-          cv[s2] = col4(cvec(a, k, 2 * l + 1), min(n, a.cg4 - 4), a.cg4, t < 256 && s2 < nslot && er < M);
+          const bool use = t < 256 && s2 < nslot && er < M;
+          cv[s2] = col4(cvec(a, k, 2 * l + 1), min(n, a.cg4 - 4), a.cg4, use);
+          wsv[s2] = W8 ? col4(lw.sgu, min(n, a.cg4 - 4), a.cg4, use) : as_v(f32x4{1.f, 1.f, 1.f, 1.f});
         }
         st.finish(D, a.eps, sm);
         f32x4 v[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -953,7 +987,7 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         for (int s2 = 0; s2 < 2; ++s2) {
           const int n = ((int)blockIdx.x + s2 * G) * 16 + 4 * eq;
           if (t < 256 && s2 < nslot && er < M) {
-            const f32x4 y = sm.rinv[er] * v[s2] + as_f4(cv[s2]);
+            const f32x4 y = sm.rinv[er] * (as_f4(wsv[s2]) * v[s2]) + as_f4(cv[s2]);
             st4(ra2, act_off(er, n / 2, a.F), pack_bf2(gelu_tanh(y[0]) * y[1], gelu_tanh(y[2]) * y[3]));
           }
         }
@@ -966,13 +1000,13 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
         const bool has = gi.valid;
         char* rnext = rot(a, kk, l + 1);
         V16 wr[2][kPCh];
-        read_w(sm, wr, has ? 1 : 0);
+        read_w(sm, wr, has ? 1 : 0, g.w8);
         V16 ra[kPCh][4];
         load_a(g, M, ra);
         const int tile = gi.tile;
         const int n = tile * 16 + 4 * eq;
         ResidIn rin;
-        rin.issue(a, er, n, site(a, k, 2 * l + 1, 2), site(a, k, 2 * l + 2, 0), has && gi.ks == 0 && t < 256);
+        rin.issue(a, er, n, site(a, k, 2 * l + 1, 2), site(a, k, 2 * l + 2, 0), has && gi.ks == 0 && t < 256, W8 ? lw.sdown : nullptr);
         f32x4 v[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         if (has) gemm_core(wr, ra, sm, 1, v);
         else __syncthreads();
@@ -989,7 +1023,7 @@ __global__ void __launch_bounds__(kPT, 1) k_loop(const LoopArgs* __restrict__ pa
       const GemmIn g = gin_out(a, rf);
       const bool has = gemm_item(g, 0).valid;
       V16 wr[2][kPCh];
-      read_w(sm, wr, has ? 1 : 0);
+      read_w(sm, wr, has ? 1 : 0, g.w8);
       V16 ra[kPCh][4];
       load_a(g, M, ra);
       StatLoad st;
@@ -1062,11 +1096,12 @@ const char* loop_check(const LoopShape& s, int num_cus) {
   return nullptr;
 }
 
-hipError_t loop_launch(const LoopArgs* a_dev, const LaunchArgs& la, int grid, hipStream_t s) {
+hipError_t loop_launch(const LoopArgs* a_dev, const LaunchArgs& la, int grid, bool w8, hipStream_t s) {
   const LoopArgs* p = a_dev;
   LaunchArgs l2 = la;
   void* args[] = {&p, &l2};
-  return hipLaunchCooperativeKernel((const void*)k_loop, dim3(grid), dim3(kPT), args, 0, s);
+  if (w8) return hipLaunchCooperativeKernel((const void*)k_loop<true>, dim3(grid), dim3(kPT), args, 0, s);
+  return hipLaunchCooperativeKernel((const void*)k_loop<false>, dim3(grid), dim3(kPT), args, 0, s);
 }
 
 }  // namespace fm

@@ -81,12 +81,30 @@ def lib():
         "fm_unnormalize": ([VP, VP, VP], I32),
         "fm_op_linear": ([I32, I32, I32, I32, VP, VP, VP, I32, VP, I32, VP], I32),
         "fm_op_attention": ([I32, I32, I32, I32, I32, I32, I32, VP, VP, VP, VP, VP], I32),
+        "fm_op_quantize_fp8": ([I32, I32, VP, VP, VP, VP, VP], I32),
+        "fm_set_weight_format": ([VP, I32], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
         f.argtypes, f.restype = args, res
     _lib = L
     return L
+
+
+WEIGHTS_AS_GIVEN, WEIGHTS_FP8_E4M3 = 0, 1
+
+
+def quantize_fp8(w):
+    """The library's FP8 weight quantizer on a device bf16 [N, K] tensor: (codes uint8 [N, K],
+    per-row scales fp32 [N], dequantized bf16 [N, K]), all device tensors."""
+    torch = _torch()
+    N, K = w.shape
+    codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((N,), dtype=torch.float32, device=w.device)
+    deq = torch.empty_like(w)
+    st = torch.cuda.current_stream()
+    _check(lib().fm_op_quantize_fp8(N, K, _ptr(w), _ptr(codes), _ptr(scale), _ptr(deq), C.c_void_p(st.cuda_stream)))
+    return codes, scale, deq
 
 
 def pool_k_col(d, head_dim: int, rope: bool):
@@ -268,6 +286,10 @@ class Context:
         """Bind what the pool holds (written through prefix_kv_slot / prefix_pool_views)."""
         _check(lib().fm_bind_prefix_inplace(self.h, batch, prefix_len), self.h)
         self._bound = (batch, prefix_len)
+
+    def set_weight_format(self, fmt: int):
+        """WEIGHTS_AS_GIVEN or WEIGHTS_FP8_E4M3; applied by the next load_weights."""
+        _check(lib().fm_set_weight_format(self.h, fmt), self.h)
 
     def bind_prefix_lengths(self, lens=None):
         """Compact prefix length P_b of each bound request (host ints [batch]); None: the whole

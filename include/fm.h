@@ -185,6 +185,20 @@ static inline int32_t fm_pool_v_slot(int32_t j, int32_t dtype) {
   return dtype != FM_BF16 ? j : ((j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3));
 }
 
+/* Storage of the expert's per-layer matrices (q, k, v, o, gate, up, down), applied by the next
+ * fm_load_weights (vla.cpp Sec. IV-D, Table V: quantized action-head weights; pi0.5 Design
+ * names FP8 for the expert).
+ *   FM_WEIGHTS_AS_GIVEN  the config dtype (default).
+ *   FM_WEIGHTS_FP8_E4M3  each row (output feature) becomes OCP FP8 E4M3 codes times one
+ *     power-of-two scale 2^e, e the smallest exponent with max |row| <= 448 2^e; codes round
+ *     to nearest, ties to even. The loop kernel streams the codes (half the bytes) and turns
+ *     them into bf16 exactly; the per-operation kernels use the dequantized bf16 weights. Both
+ *     therefore compute the same function of the dequantized weights, which is the model.
+ *     PREFIX_JOINT in FM_BF16 with mlp_dim a multiple of 64 (FM_ERR_UNSUPPORTED otherwise).
+ * FM_ERR_INVALID_ARG for another format. */
+enum { FM_WEIGHTS_AS_GIVEN = 0, FM_WEIGHTS_FP8_E4M3 = 1 };
+fm_status fm_set_weight_format(fm_ctx* ctx, int32_t format);
+
 /* Per-request key visibility of the bound batch: the additive mask M of Eq. (2) (vla.cpp
  * Sec. III-B: 0 for a visible key, -inf for a hidden one). Both calls copy what they are
  * given into library memory and synchronize the context stream before returning (the host
@@ -306,6 +320,12 @@ fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const voi
                        const float* bias, int32_t act, void* out, int32_t out_f32, void* hip_stream);
 fm_status fm_op_attention(int32_t dtype, int32_t B, int32_t Tq, int32_t n_heads, int32_t n_kv, int32_t n_keys,
                           int32_t dh, const void* q, const void* k, const void* v, void* o, void* hip_stream);
+/* fm_op_quantize_fp8: the FP8 weight quantizer alone (see fm_set_weight_format), for parity.
+ *   src DEVICE bf16 [N, K] row-major (K even); codes DEVICE bytes [N, K]; scale DEVICE fp32 [N]
+ *   (2^e of each row); deq DEVICE bf16 [N, K] = code value x 2^e (exact). Synchronizes
+ *   hip_stream. FM_ERR_INVALID_ARG for a NULL buffer or an odd K. */
+fm_status fm_op_quantize_fp8(int32_t N, int32_t K, const void* src, void* codes, float* scale, void* deq,
+                             void* hip_stream);
 
 #ifdef __cplusplus
 }
