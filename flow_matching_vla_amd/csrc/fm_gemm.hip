@@ -840,17 +840,20 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
 
 // ---------------------------------------------------------------------------------------
 // Skinny kernel (M <= 64, the weight-streaming regime). A workgroup covers all rows and
-// 16*NB output columns over 1/splits of K; its KW waves split that range again into CPW
-// k-chunks each. Every wave issues all of its loads at once: the weight fragments
-// (contiguous 1 KB runs) and the matching activation fragments, through buffer
-// descriptors with 32-bit offsets (rows past M and chunks past the wave's range read zeros
-// through out-of-range offsets, so nothing is clamped or selected). The wave partials are
+// 16*NB output columns over 1/splits of K (k_split), in stages of KW x CPW k-chunks: each
+// wave takes CPW chunks of a stage and issues all of their loads at once, the weight
+// fragments (contiguous 1 KB runs) and the matching activation fragments, through buffer
+// descriptors with 32-bit offsets (rows past M and chunks past the range read zeros
+// through out-of-range offsets, so nothing is clamped or selected). Two stages are in
+// flight at a time. The wave partials are
 // summed in LDS in wave order; with splits > 1 the workgroup partials are exchanged through
 // device-scope stores and the last-arriving workgroup of the column tile sums them in split
 // order before the shared epilogue. NORM: the A operand is a modulated-norm input whose row
 // statistics are loaded with the operands and merged before the epilogue.
 // ---------------------------------------------------------------------------------------
-template <typename T, int KW, int NB, int CPW, int EPI, bool NORM>
+// ST: the range can hold more than one stage (a second register set, double buffering);
+// without it the range is exactly one stage and the kernel keeps half the registers.
+template <typename T, int KW, int NB, int CPW, int EPI, bool NORM, bool ST>
 __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   typedef Mma<T> MT;
   typedef typename MT::frag frag;
@@ -872,7 +875,13 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   const int tile = bid / a.splits, split = bid % a.splits;
   const int n0 = tile * BN;
   const int KCt = a.K / KC;
-  const int c_beg = (split * KW + w) * CPW;   // this wave's chunks: [c_beg, c_beg + CPW) within K
+  // this workgroup's K range: chunks [c_lo, c_hi), walked in stages of KW x CPW chunks (wave w
+  // takes CPW consecutive chunks of each stage); the next stage's loads are in flight while
+  // this stage's MFMAs run
+  constexpr int SPC = KW * CPW;
+  const int span = a.k_split / KC;
+  const int c_lo = split * span, c_hi = min(KCt, c_lo + span);
+  const int nst = (c_hi - c_lo + SPC - 1) / SPC;
 
   FM_PHASE_INIT;
   FM_PHASE(0);
@@ -888,20 +897,26 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   const Rsrc rw = make_rsrc(a.W, a.w_bytes);
   const uint32_t wbase = (uint32_t)((n0 / 16) * KCt * 1024 + lane * 16);
 
-  V16 ra_[CPW][MB], rb_[CPW][NB];
+  V16 ra0[CPW][MB], rb0[CPW][NB], ra1[CPW][MB], rb1[CPW][NB];
+  auto issue = [&](int stg, V16 (&xa)[CPW][MB], V16 (&xb)[CPW][NB]) {
 #pragma unroll
-  for (int c = 0; c < CPW; ++c) {
-    const int cc = c_beg + c;
-    const bool cok = cc < KCt;   // uniform per wave
+    for (int c = 0; c < CPW; ++c) {
+      const int cc = c_lo + stg * SPC + w * CPW + c;
+      const bool cok = cc < c_hi;   // uniform per wave
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) ra_[c][mb] = bload16(ra, aoff[mb] + (uint32_t)(cc * KC * sizeof(T)));
+      for (int mb = 0; mb < MB; ++mb) xa[c][mb] = bload16(ra, cok ? aoff[mb] + (uint32_t)(cc * KC * sizeof(T)) : kOob);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) rb_[c][nb] = bload16(rw, cok ? wbase + (uint32_t)((nb * KCt + cc) * 1024) : kOob);
-  }
+      for (int nb = 0; nb < NB; ++nb) xb[c][nb] = bload16(rw, cok ? wbase + (uint32_t)((nb * KCt + cc) * 1024) : kOob);
+    }
+  };
+  issue(0, ra0, rb0);
   RowStats<BM, NT> st;
   if constexpr (NORM) st.load(a, 0);
   Epilogue<T, BM, BN, NT, EPI> ep;
   ep.prefetch(a, 0, n0);
+  if constexpr (ST) {
+    if (nst > 1) issue(1, ra1, rb1);
+  }
   // all loads are in flight before the first MFMA waits on one (the scheduler would
   // otherwise interleave them with the MFMAs and keep only a few outstanding)
   __builtin_amdgcn_sched_barrier(0);
@@ -912,13 +927,35 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const V16 (&xa)[CPW][MB], const V16 (&xb)[CPW][NB]) {
 #pragma unroll
-  for (int c = 0; c < CPW; ++c)
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = MT::mma(__builtin_bit_cast(frag, ra_[c][mb]), __builtin_bit_cast(frag, rb_[c][nb]), acc[mb][nb]);
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = MT::mma(__builtin_bit_cast(frag, xa[c][mb]), __builtin_bit_cast(frag, xb[c][nb]), acc[mb][nb]);
+  };
+  if constexpr (!ST) {
+    mma(ra0, rb0);
+  } else {
+    // stages alternate between the two register sets; a set is refilled (two stages ahead)
+    // right after its MFMAs have read it
+    for (int stg = 0; stg < nst; stg += 2) {
+      mma(ra0, rb0);
+      if (stg + 2 < nst) {
+        issue(stg + 2, ra0, rb0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (stg + 1 < nst) {
+        mma(ra1, rb1);
+        if (stg + 3 < nst) {
+          issue(stg + 3, ra1, rb1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
   if constexpr (NORM) st.merge(a, 0, s_mean, s_rinv);
   FM_PHASE(2);
 
@@ -1021,6 +1058,28 @@ int gemm_num_tiles(const GemmArgs& a) {
 void gemm_plan(GemmArgs& a, int elem, int num_cus) {
   const int kq = elem == ET_BF16 ? 32 : 16;
   const int esz = elem == ET_BF16 ? 2 : 4;
+  if (a.M <= 64 && elem == ET_BF16 && a.K % 32 == 0) {
+    // Weight streaming in bf16: eight waves, two chunks per wave and stage (double-buffered
+    // stages), 32-column tiles (the activation fragments then feed two weight columns each),
+    // and a K split that brings the workgroups to about one per CU, at least 8 chunks each.
+    // Measured on MI355X at 41 rows (the DiT head), against the one-stage cost model below:
+    // 6144 x 1536 8.1 us (11.7), 1536 x 6144 10.1 us (13.5), 4608 x 1536 8.1 us (8.8),
+    // 1536 x 1536 6.6 us (6.8); every other shape of the sweep was slower with 16 columns.
+    a.kind = GEMM_SKINNY;
+    a.kw = 8;
+    a.cpw = 2;
+    const int nb = (a.epi == EPI_RESID || a.N > 16) ? 2 : 1;
+    a.cfg = nb == 2 ? SK_N32 : SK_N16;
+    const int kct = a.K / kq, tiles = (a.N + 16 * nb - 1) / (16 * nb);
+    int splits = num_cus / tiles;
+    if (splits > kct / 8) splits = kct / 8;
+    if (splits > 16) splits = 16;
+    if (splits < 1) splits = 1;
+    const int span = (kct + splits - 1) / splits;
+    a.splits = (kct + span - 1) / span;
+    a.k_split = span * kq;
+    return;
+  }
   if (a.M <= 64) {
     // Weight streaming: pick the waves per workgroup (4 / 8), the column width (16 / 32),
     // the chunks per wave (2 / 4 / 8, all loaded at once) and the k-split over workgroups
@@ -1158,13 +1217,13 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
 }
 
 // Skinny instantiations: the residual epilogue never consumes a norm; the others can.
-template <typename T, int KW, int NB, int CPW>
-static hipError_t launch_skinny_cpw(const GemmArgs& a, hipStream_t s) {
+template <typename T, int KW, int NB, int CPW, bool ST>
+static hipError_t launch_skinny_st(const GemmArgs& a, hipStream_t s) {
   const int per_round = 8 * a.splits;   // whole column tiles per XCD range
   const int items = ((a.N + 16 * NB - 1) / (16 * NB)) * a.splits;
   const dim3 grid((items + per_round - 1) / per_round * per_round), block(KW * 64);
   const bool norm = a.norm != NORM_NONE;
-#define K_SK(E, NRM) hipLaunchKernelGGL((k_gemm_skinny<T, KW, NB, CPW, E, NRM>), grid, block, 0, s, a)
+#define K_SK(E, NRM) hipLaunchKernelGGL((k_gemm_skinny<T, KW, NB, CPW, E, NRM, ST>), grid, block, 0, s, a)
   switch (a.epi) {
     case EPI_STORE: if (norm) K_SK(EPI_STORE, true); else K_SK(EPI_STORE, false); break;
     case EPI_GELU_MUL: if (norm) K_SK(EPI_GELU_MUL, true); else K_SK(EPI_GELU_MUL, false); break;
@@ -1183,6 +1242,15 @@ static hipError_t launch_skinny_cpw(const GemmArgs& a, hipStream_t s) {
   }
 #undef K_SK
   return hipGetLastError();
+}
+
+// a range of more than one stage needs the double-buffered kernel (CPW 2 only: registers)
+template <typename T, int KW, int NB, int CPW>
+static hipError_t launch_skinny_cpw(const GemmArgs& a, hipStream_t s) {
+  const int kc = sizeof(T) == 2 ? 32 : 16;
+  if (a.k_split <= KW * CPW * kc) return launch_skinny_st<T, KW, NB, CPW, false>(a, s);
+  if constexpr (CPW == 2) return launch_skinny_st<T, KW, NB, CPW, true>(a, s);
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int KW, int NB>
