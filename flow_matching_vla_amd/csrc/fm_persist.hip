@@ -1073,7 +1073,9 @@ const char* loop_check(const LoopShape& s, int num_cus) {
   if (s.L < 1 || s.L > kMaxLayers) return "too many layers";
   if (s.D % 16 != 0 || s.D / 16 > num_cus) return "hidden must be a multiple of 16 and at most 16 x CUs";
   if (s.qd % 32 != 0 || s.D % 32 != 0 || s.F % 32 != 0) return "GEMM K dims must be multiples of 32";
-  if (s.D % 512 != 0 || s.D > 2048) return "hidden must be a multiple of 512 and at most 2048";
+  // the QKV, gate / up and output phases run unsplit over K = hidden (no split-K reduction):
+  // one GEMM item covers at most kPKS of K
+  if (s.D % 512 != 0 || s.D > kPKS) return "hidden must be a multiple of 512 and at most 1024";
   if (s.da % 4 != 0 || s.da > kMaxDa) return "action_dim must be a multiple of 4 and at most 32";
   const int G = num_cus;
   auto items = [&](int N, int K) { return ((N + 15) / 16) * ((K + kPKS - 1) / kPKS); };

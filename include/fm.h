@@ -283,8 +283,9 @@ enum {
 
 /* Implementation of fm_denoise / fm_step_velocity.
  * FM_LOOP_AUTO: the persistent loop kernel wherever it applies - bf16 pi0.5-family expert
- *   (PREFIX_JOINT, one K/V head, gated MLP) with head_dim 256, batch * H <= 64 action rows,
- *   and every phase within two work items per CU - and the per-operation graph elsewhere.
+ *   (PREFIX_JOINT, one K/V head, gated MLP) with head_dim 256, hidden a multiple of 512 up to
+ *   1024, action_dim a multiple of 4 up to 32, batch * H <= 64 action rows, and every phase
+ *   within two work items per CU - and the per-operation graph elsewhere.
  * FM_LOOP_GRAPH: always the captured graph of per-operation kernels.
  * Both compute the same function (reduction orders differ). Default FM_LOOP_AUTO.
  * FM_ERR_INVALID_ARG for another mode. */

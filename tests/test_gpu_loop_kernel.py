@@ -43,6 +43,23 @@ def test_loop_kernel_shapes(B, H, P):
     c.close()
 
 
+def test_hidden_beyond_one_k_range_uses_the_graph():
+    # hidden 2048: the QKV, gate/up and output GEMMs would need a K split that the loop
+    # kernel's phases do not reduce, so the loop takes the per-operation graph (and stays
+    # correct); a randomized shape sweep found the wrong results this guards against
+    cfg = wl.workload("pi05_b1", n_layers=1, hidden=2048, n_heads=2, mlp_dim=1024, action_horizon=50,
+                      action_dim=4, prefix_len=300, steps=2)
+    c = Case(cfg)
+    persistent, _ = c.ctx.loop_status()
+    assert not persistent
+    wv = _velocities(c, 2)
+    x_gpu = c.gpu_denoise()
+    ex = oracle.e_rel(x_gpu, oracle.denoise(cfg, c.w64, c.bound, c.I["x0"], c.steps, tau=c.tau))
+    say(f"  hidden 2048: worst velocity e_rel {wv:.3e}, chunk e_rel {ex:.3e}")
+    assert wv <= 1e-2 and ex <= 2e-2
+    c.close()
+
+
 def test_loop_kernel_matches_graph_path_pi05_b1():
     c = Case(wl.workload("pi05_b1"))
     persistent, _ = c.ctx.loop_status()
