@@ -149,6 +149,7 @@ def main():
     ap.add_argument("--no-fit", action="store_true")
     ap.add_argument("--no-roles", action="store_true")
     ap.add_argument("--no-visibility", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weights line of pi0.5 workloads")
     ap.add_argument("--weights", choices=("as-given", "fp8"), default="as-given",
                     help="fp8: the expert's per-layer matrices as FP8 E4M3 codes with per-row scales")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -341,6 +342,35 @@ def main():
             ctx.bind_prefix_lengths(None)
         else:
             ctx.bind_context_masks(None, None)
+    # the same workload with the expert's per-layer matrices as FP8 codes (a separate model:
+    # reported beside the bf16 line, never as its value)
+    if cfg["arch"] == 0 and args.weights == "as-given" and not args.no_fp8:
+        c8 = fm.Context(cfg)
+        c8.set_weight_format(fm.WEIGHTS_FP8_E4M3)
+        c8.load_weights({n: fm.to_device(a, dt) for n, a in W.items()})
+        L = cfg["n_layers"]
+        c8.bind_prefix_kv(B, cfg["prefix_len"], [fm.to_device(I[f"prefix.k.{l}"], dt) for l in range(L)],
+                          [fm.to_device(I[f"prefix.v.{l}"], dt) for l in range(L)])
+        c8.set_schedule(T, B)
+        o8 = torch.empty_like(x0)
+        for _ in range(5):
+            c8.denoise(x0, T, o8)
+        torch.cuda.synchronize()
+        a8, b8 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a8.record(c8.stream)
+        for _ in range(args.steps):
+            c8.denoise(x0, T, o8)
+        b8.record(c8.stream)
+        torch.cuda.synchronize()
+        ms8 = a8.elapsed_time(b8) / args.steps
+        ctx.denoise(x0, T, out)   # the bf16 model's chunk on the whole binding
+        torch.cuda.synchronize()
+        b8y, _ = step_bytes_flops(dict(cfg, w8=True))
+        res["fp8_weights"] = {"chunks_per_s": round(B / (ms8 * 1e-3), 2), "per_euler_step_us": round(1000 * ms8 / T, 2),
+                              "alg_bytes_per_euler_step": int(b8y), "loop_kernel": bool(c8.loop_status()[0]),
+                              "traffic": loop_traffic(cfg["name"] + "_fp8"),
+                              "chunk_e_rel_vs_bf16_weights": round(float(torch.linalg.vector_norm(o8 - out) / torch.linalg.vector_norm(out)), 5)}
+        c8.close()
     # the step after the path: the chunk back to robot units (LIBERO width 7; GR00T's policy
     # keeps 16 of the model's 40 steps), timed with HIP events on the context stream
     post_kind = fm.UNNORM_QUANTILE_EPS if cfg["arch"] == 0 else fm.UNNORM_QUANTILE_CLIP
