@@ -387,15 +387,17 @@ int attn_num_items(const AttnArgs& a) {
 }
 
 void attn_plan(AttnArgs& a, int elem, int num_cus) {
-  // Split the keys only when the row tiles alone leave most of the chip idle. The merge
-  // reads every split's partial O (4 bytes per row and head dim), so splits keep at least
-  // two key tiles and the launch stays near half of the CUs (measured: at 8 requests of
-  // 400 folded rows and 866 keys, 26 us per layer against 34 us at a quarter).
+  // Split the keys when the row tiles alone leave part of the chip idle. The merge reads
+  // every split's partial O (4 bytes per row and head dim), so splits keep at least two key
+  // tiles, and the launch aims at one workgroup per CU (measured at 8 requests of 400 folded
+  // rows and 866 keys: 34 us per layer at a quarter of the CUs, 26 at half, 25.8 at all;
+  // never splitting short key ranges was much slower: 48 us there, 14 against 10.6 us for
+  // the DiT head's 600-key cross attention).
   a.cfg = 0;
   const int items = attn_num_items(a);
   const int ktiles = (a.n_keys + kKeyTile - 1) / kKeyTile;
   int splits = 1;
-  const int target = num_cus / 2 > 0 ? num_cus / 2 : 1;
+  const int target = num_cus > 0 ? num_cus : 1;
   if (items < target) {
     splits = (target + items - 1) / items;
     const int max_splits = ktiles / 2 > 1 ? ktiles / 2 : 1;
