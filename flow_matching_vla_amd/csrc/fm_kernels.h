@@ -78,7 +78,8 @@ size_t gemm_ws_bytes(const GemmArgs& a);        // split-K partial workspace byt
 int gemm_num_tiles(const GemmArgs& a);
 hipError_t gemm_launch(const GemmArgs& a, int elem, hipStream_t s);
 
-// Attention (vla.cpp Eq. (2), no mask) over groups of query rows sharing one K/V head.
+// Attention (vla.cpp Eq. (2); its additive mask as the visibility fields below) over groups of
+// query rows sharing one K/V head.
 struct AttnArgs {
   const void* q; long q_bs, q_rs;             // q[b*q_bs + t*q_rs + n*dh + d]
   const void* k; long k_bs, k_rs, k_hs;       // k[b*k_bs + g*k_hs + j*k_rs + d]
