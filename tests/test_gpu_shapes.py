@@ -18,8 +18,6 @@ import oracle
 from flow_matching_vla_amd import workloads as wl
 from gpu_util import Case, say
 
-pytestmark = pytest.mark.gpu
-
 N_CASES = 16
 
 
@@ -73,6 +71,7 @@ def test_draws_cover_the_families():
     assert any(c["batch"] > 1 for c, _ in cases)
 
 
+@pytest.mark.gpu
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape(i):
     cfg, vis = draw(i)
