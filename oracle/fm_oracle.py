@@ -105,6 +105,18 @@ def split_site(row, D):
     return row[..., :D], row[..., D:2 * D], row[..., 2 * D:3 * D]
 
 
+# ----------------------------------------------------------------------------- bf16 operands
+def round_bf16(x):
+    """x held in float32 (round to nearest, ties to even), then rounded to bfloat16 (1 sign,
+    8 exponent, 7 stored mantissa bits), ties to even, as float64 (vla.cpp Sec. III-E: the
+    reduced-precision model rounds to nearest even). bfloat16 is the upper half of a float32:
+    adding 0x7FFF plus the lowest kept bit and clearing the lower 16 bits rounds to the
+    nearest half, a tie going to the even one."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 # ----------------------------------------------------------------------------- RoPE
 def rope(x, positions, base):
     """Rotary embedding, rotate_half convention (LoongForge blog Sec. 3.3): for j < d/2,
@@ -154,26 +166,30 @@ def sinusoidal_embedding(tau, width, min_period=SINUSOID_MIN_PERIOD, max_period=
     return np.concatenate([np.sin(arg), np.cos(arg)], axis=-1).astype(tau.dtype)
 
 
-def time_conditioning(w, tau_steps):
-    """c_k = SiLU(W_out SiLU(W_in e(tau_k) + b_in) + b_out) for each evaluated tau_k."""
+def time_conditioning(w, tau_steps, round_acts=False):
+    """c_k = SiLU(W_out SiLU(W_in e(tau_k) + b_in) + b_out) for each evaluated tau_k.
+    round_acts: the bf16 model's reading, where the embedding and both activations are bf16
+    tensors (each rounded where formed)."""
+    rnd = round_bf16 if round_acts else (lambda a: a)
     D = w["time_in.w"].shape[0]
-    e = sinusoidal_embedding(tau_steps, D)
-    c = silu(linear(e, w["time_in.w"], w["time_in.b"]))
-    return silu(linear(c, w["time_out.w"], w["time_out.b"]))
+    e = rnd(sinusoidal_embedding(tau_steps, D))
+    c = rnd(silu(linear(e, w["time_in.w"], w["time_in.b"])))
+    return rnd(silu(linear(c, w["time_out.w"], w["time_out.b"])))
 
 
-def modulation_table(cfg, w, tau):
+def modulation_table(cfg, w, tau, round_acts=False):
     """Per-step modulation rows, evaluated once per (steps, batch) off the step path
     (pi0.5 Design: the optional cond component, evaluated again only on a new step count or
     batch; GR00T N1.7 "Build-time constants"). Returns (table [T, S, 3D], time_bias [T, D] or None).
 
     table[k, s] = W_s c_k + b_s. The pages' tensor repeats each step's row once per
     request ([steps * batch, S, 3D]); every request shares tau_k, so the rows are equal
-    across requests and one per step is kept here."""
+    across requests and one per step is kept here. round_acts: time_conditioning's reading
+    (the rows themselves stay exact functions of the rounded c_k)."""
     T = len(tau) - 1
     if T == 0:
         return None, None
-    c = time_conditioning(w, tau[:T])                      # [T, D]
+    c = time_conditioning(w, tau[:T], round_acts)          # [T, D]
     S, O, D = w["mod.w"].shape
     table = (w["mod.w"].reshape(S * O, D) @ c.T).T.reshape(T, S, O) + w["mod.b"][None]
     tb = None
@@ -232,11 +248,29 @@ def bind(cfg, w, inputs, dtype=np.float64):
 
 
 # ----------------------------------------------------------------------------- velocity
-def velocity_prefix_joint(cfg, w, bound, x, row, trace=None):
+def velocity_prefix_joint(cfg, w, bound, x, row, trace=None, round_acts=False):
     """One step of the pi0.5-shaped action expert: x [B, H, d_a] -> v [B, H, d_a].
 
     row: this step's modulation row [2L+1, 3D]; site 2l is layer l's input norm, 2l+1 its
-    post-attention norm, the last site the final norm (pi0.5 Design, "Component contract")."""
+    post-attention norm, the last site the final norm (pi0.5 Design, "Component contract").
+
+    round_acts: a reading of the bf16 model rather than of the exact one, to tell rounding from
+    bugs. Every activation that the bf16 model holds as a bf16 tensor is rounded to bfloat16
+    (round_bf16) where it is formed, everything else stays exact:
+      - the operand of each modulated norm's consumer: u = rinv * bf16(h (1 + scale)) +
+        bf16(shift), rinv = 1 / sqrt(mean(h^2) + eps) of the unrounded h (the same u as
+        n(h)(1 + scale) + shift, with the scaled input and the shift held in bf16);
+      - the chunk's queries and keys after RoPE, its values, and the attention output;
+      - the gated-GELU activation GELU(u W_gate^T) * (u W_up^T).
+    The residual stream, the attention's scores and probabilities, x and v stay exact."""
+    rnd = round_bf16 if round_acts else (lambda a: a)
+
+    def norm_mod(h, site):
+        scale, shift, _ = split_site(row[site], D)
+        if not round_acts:
+            return modulate(rms_norm(h, eps), scale, shift)
+        rinv = 1.0 / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+        return (round_bf16(h * (1.0 + scale)) * rinv + round_bf16(shift)).astype(h.dtype)
     D, L = cfg["hidden"], cfg["n_layers"]
     nq, dh, eps = cfg["n_heads"], cfg["head_dim"], cfg["norm_eps"]
     B, H, _ = x.shape
@@ -246,11 +280,11 @@ def velocity_prefix_joint(cfg, w, bound, x, row, trace=None):
         trace.append(h)
     for l in range(L):
         p = f"layers.{l}."
-        scale, shift, gate = split_site(row[2 * l], D)
-        u = modulate(rms_norm(h, eps), scale, shift)
+        gate = split_site(row[2 * l], D)[2]
+        u = norm_mod(h, 2 * l)
         q = linear(u, w[p + "q.w"]).reshape(B, H, nq, dh).transpose(0, 2, 1, 3)
         k = linear(u, w[p + "k.w"]).reshape(B, H, 1, dh).transpose(0, 2, 1, 3)
-        v = linear(u, w[p + "v.w"]).reshape(B, H, 1, dh).transpose(0, 2, 1, 3)
+        v = rnd(linear(u, w[p + "v.w"]).reshape(B, H, 1, dh).transpose(0, 2, 1, 3)).astype(h.dtype)
         o = np.empty((B, nq, H, dh), dtype=h.dtype)
         for b in range(B):   # each request: its compact prefix, then its own chunk
             P = lens[b]
@@ -259,22 +293,23 @@ def velocity_prefix_joint(cfg, w, bound, x, row, trace=None):
             if cfg["rope_base"] > 0:
                 qb = rope(qb, pos, cfg["rope_base"])
                 kb = rope(kb, pos, cfg["rope_base"])
+            qb, kb = rnd(qb).astype(h.dtype), rnd(kb).astype(h.dtype)
             K = np.concatenate([bound["k"][l][b:b + 1, :, :P], kb], axis=2)   # suffix after the prefix
             V = np.concatenate([bound["v"][l][b:b + 1, :, :P], v[b:b + 1]], axis=2)
             o[b] = attention(qb, K, V)[0]
-        o = o.transpose(0, 2, 1, 3).reshape(B, H, nq * dh)
+        o = rnd(o.transpose(0, 2, 1, 3).reshape(B, H, nq * dh)).astype(h.dtype)
         h = h + gate * linear(o, w[p + "o.w"])
-        scale, shift, gate = split_site(row[2 * l + 1], D)
-        u = modulate(rms_norm(h, eps), scale, shift)
+        gate = split_site(row[2 * l + 1], D)[2]
+        u = norm_mod(h, 2 * l + 1)
         if cfg["mlp_gated"]:
             a = gelu_tanh(linear(u, w[p + "gate.w"])) * linear(u, w[p + "up.w"])
         else:
             a = gelu_tanh(linear(u, w[p + "gate.w"]))
+        a = rnd(a).astype(h.dtype)
         h = h + gate * linear(a, w[p + "down.w"])
         if trace is not None:
             trace.append(h)
-    scale, shift, _ = split_site(row[2 * L], D)
-    u = modulate(rms_norm(h, eps), scale, shift)
+    u = norm_mod(h, 2 * L)
     return linear(u, w["action_out.w"], w["action_out.b"])
 
 
@@ -318,12 +353,15 @@ def velocity_dit_cross(cfg, w, bound, x, row, time_bias, trace=None):
     return linear(u, w["action_out.w"], w["action_out.b"])
 
 
-def velocity(cfg, w, bound, x, table, time_bias, k, trace=None):
+def velocity(cfg, w, bound, x, table, time_bias, k, trace=None, round_acts=False):
     """v_theta(X^k, tau_k, C) of vla.cpp Eq. (1), for step k of the scheduled table.
     trace: optional list that receives the residual stream after the in-projection and
-    after every layer (vla.cpp Sec. III-E: intermediate tensors localize discrepancies)."""
+    after every layer (vla.cpp Sec. III-E: intermediate tensors localize discrepancies).
+    round_acts: the bf16-operand reading of velocity_prefix_joint (pi0.5-shaped expert only)."""
     if cfg["arch"] == ARCH_PREFIX_JOINT:
-        return velocity_prefix_joint(cfg, w, bound, x, table[k], trace)
+        return velocity_prefix_joint(cfg, w, bound, x, table[k], trace, round_acts)
+    if round_acts:
+        raise ValueError("round_acts is a reading of the pi0.5-shaped expert only")
     return velocity_dit_cross(cfg, w, bound, x, table[k], time_bias[k], trace)
 
 

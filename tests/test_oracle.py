@@ -330,8 +330,13 @@ def test_metrics():
 
 
 # ----------------------------------------------------------------------------- scalar brute force
-def _brute_velocity_pi05(cfg, W, I, x, row):
-    """Scalar-loop re-statement of one expert step on micro shapes (pure Python floats)."""
+def _brute_velocity_pi05(cfg, W, I, x, row, rq=None):
+    """Scalar-loop re-statement of one expert step on micro shapes (pure Python floats).
+    rq: optional rounding of a list of values (the bf16 reading): applied to the norm's scaled
+    input h (1 + scale) and shift, the chunk's queries and keys after RoPE, its values, the
+    attention output and the gated-GELU activation."""
+    rounding = rq is not None
+    rq = rq or (lambda vec: vec)
     D, L, nq, dh, F_, eps = cfg["hidden"], cfg["n_layers"], cfg["n_heads"], cfg["head_dim"], cfg["mlp_dim"], cfg["norm_eps"]
     H, da, P, base = cfg["action_horizon"], cfg["action_dim"], cfg["prefix_len"], cfg["rope_base"]
 
@@ -349,6 +354,10 @@ def _brute_velocity_pi05(cfg, W, I, x, row):
 
     def nm(vec, site):
         r = math.sqrt(sum(t * t for t in vec) / D + eps)
+        if rounding:
+            hs = rq([vec[i] * (1 + row[site][i]) for i in range(D)])
+            sh = rq([row[site][D + i] for i in range(D)])
+            return [hs[i] / r + sh[i] for i in range(D)]
         return [vec[i] / r * (1 + row[site][i]) + row[site][D + i] for i in range(D)]
 
     h = [[sum(W["action_in.w"][o][i] * x[t][i] for i in range(da)) + W["action_in.b"][o] for o in range(D)] for t in range(H)]
@@ -356,27 +365,28 @@ def _brute_velocity_pi05(cfg, W, I, x, row):
         p = f"layers.{l}."
         u = [nm(h[t], 2 * l) for t in range(H)]
         q = [mv(W[p + "q.w"], u[t]) for t in range(H)]
-        ks = [rot(mv(W[p + "k.w"], u[t]), P + t) for t in range(H)]
-        vs = [mv(W[p + "v.w"], u[t]) for t in range(H)]
+        ks = [rq(rot(mv(W[p + "k.w"], u[t]), P + t)) for t in range(H)]
+        vs = [rq(mv(W[p + "v.w"], u[t])) for t in range(H)]
         keys = I[f"prefix.k.{l}"][0, :, 0].astype(np.float64).tolist() + ks
         vals = I[f"prefix.v.{l}"][0, :, 0].astype(np.float64).tolist() + vs
         o = [[0.0] * (nq * dh) for _ in range(H)]
         for t in range(H):
             for n in range(nq):
-                qq = rot(q[t][n * dh:(n + 1) * dh], P + t)
+                qq = rq(rot(q[t][n * dh:(n + 1) * dh], P + t))
                 sc = [sum(qq[c] * kk[c] for c in range(dh)) / math.sqrt(dh) for kk in keys]
                 m = max(sc)
                 e = [math.exp(s - m) for s in sc]
                 z = sum(e)
                 for c in range(dh):
                     o[t][n * dh + c] = sum(e[j] * vals[j][c] for j in range(len(keys))) / z
+        o = [rq(o[t]) for t in range(H)]
         for t in range(H):
             y = mv(W[p + "o.w"], o[t])
             h[t] = [h[t][i] + row[2 * l][2 * D + i] * y[i] for i in range(D)]
         for t in range(H):
             u2 = nm(h[t], 2 * l + 1)
             g, up = mv(W[p + "gate.w"], u2), mv(W[p + "up.w"], u2)
-            a = [0.5 * g[f] * (1 + math.tanh(math.sqrt(2 / math.pi) * (g[f] + 0.044715 * g[f] ** 3))) * up[f] for f in range(F_)]
+            a = rq([0.5 * g[f] * (1 + math.tanh(math.sqrt(2 / math.pi) * (g[f] + 0.044715 * g[f] ** 3))) * up[f] for f in range(F_)])
             y = mv(W[p + "down.w"], a)
             h[t] = [h[t][i] + row[2 * l + 1][2 * D + i] * y[i] for i in range(D)]
     out = []
@@ -722,3 +732,64 @@ def test_increasing_schedule_constant_field():
     w["action_out.b"] = c
     xT = oracle.run(cfg, w, I, steps=T, tau=tau)
     np.testing.assert_allclose(xT, I["x0"].astype(np.float64) + c.astype(np.float64), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- bf16 operand reading
+def _torch_bf16(vec):
+    """float32, then bfloat16, both round-to-nearest-even, by torch's own conversions."""
+    return torch.tensor(vec, dtype=torch.float64).to(torch.float32).to(torch.bfloat16).to(torch.float64).tolist()
+
+
+def test_round_bf16_matches_torch_including_ties():
+    # exact ties (lower 16 bits 0x8000) on both parities of the kept bit, both signs, and the
+    # binade edges where rounding up carries into the exponent
+    hi = np.array([0x3F80, 0x3F81, 0x4049, 0xC2F7, 0x3F7F, 0x7F7E, 0x0080, 0x8001], dtype=np.uint32)
+    lo = np.array([0x0000, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    pats = (hi[:, None] << 16 | lo[None, :]).ravel()
+    x32 = pats.view(np.float32)
+    got = oracle.round_bf16(x32)
+    ref = torch.from_numpy(x32.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, ref)
+    # float64 input is held in float32 first, as the kernels' fp32 accumulators hold it
+    x64 = RNG.standard_normal(4096) * np.exp(RNG.uniform(-20, 20, 4096))
+    np.testing.assert_array_equal(oracle.round_bf16(x64), np.array(_torch_bf16(x64.tolist())))
+    # a tie goes to the even neighbour: 1 + 2^-8 (between 1 and 1 + 2^-7) rounds down to 1
+    assert oracle.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert oracle.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+def test_round_acts_time_conditioning_rounds_the_mlp_operands():
+    """The bf16 reading of the modulation table against torch with bf16 casts at the
+    embedding and both time-MLP activations (the table itself stays exact)."""
+    cfg = wl.workload("tiny_fp32")
+    W = oracle.cast_weights(wl.make_weights(cfg))
+    tau = oracle.schedule(4)
+    table, _ = oracle.modulation_table(cfg, W, tau, round_acts=True)
+    bf = lambda t: t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    e = bf(t64(oracle.sinusoidal_embedding(tau[:4], cfg["hidden"])))
+    c = bf(F.silu(e @ t64(W["time_in.w"]).T + t64(W["time_in.b"])))
+    c = bf(F.silu(c @ t64(W["time_out.w"]).T + t64(W["time_out.b"])))
+    S, O, D = W["mod.w"].shape
+    ref = (c @ t64(W["mod.w"]).reshape(S * O, D).T).reshape(4, S, O) + t64(W["mod.b"])
+    np.testing.assert_allclose(table, ref.numpy(), rtol=1e-12, atol=1e-12)
+    exact, _ = oracle.modulation_table(cfg, W, tau)
+    assert 0 < oracle.e_rel(table, exact) < 1e-2
+
+
+def test_round_acts_rounds_bf16_tensors_where_formed():
+    """round_acts against the scalar brute force with torch's bf16 rounding at the norm's scaled
+    input and shift, the chunk's queries and keys after RoPE, its values, the attention output
+    and the gated-GELU activation."""
+    cfg = wl.workload("tiny_fp32", n_layers=2, hidden=8, n_heads=2, head_dim=4, mlp_dim=6,
+                      action_horizon=3, action_dim=2, prefix_len=4, weight_std=0.5)
+    W, I = oracle.cast_weights(wl.make_weights(cfg)), wl.make_inputs(cfg)
+    bound = oracle.bind(cfg, W, I)
+    table, tb = oracle.modulation_table(cfg, W, oracle.schedule(2))
+    x = I["x0"].astype(np.float64)
+    v = oracle.velocity(cfg, W, bound, x, table, tb, 1, round_acts=True)
+    Wl = {k: np.asarray(a).tolist() for k, a in W.items()}
+    ref = _brute_velocity_pi05(cfg, Wl, I, x[0].tolist(), table[1].tolist(), rq=_torch_bf16)
+    np.testing.assert_allclose(v[0], np.array(ref), rtol=1e-10, atol=1e-12)
+    exact = oracle.velocity(cfg, W, bound, x, table, tb, 1)
+    e = oracle.e_rel(v, exact)
+    assert 0 < e < 2e-2, e   # the reading moves the result by bf16-sized amounts, not more
