@@ -112,8 +112,12 @@ def loop_traffic(workload):
 
 
 def cpu_baseline(cfg, W, I, budget_s=12.0):
-    """The oracle as it stands, timed on the host: whole chunks (all Euler steps) of the same
-    workload until about budget_s of CPU work has been done (at least one chunk)."""
+    """The oracle as it stands, timed on the host in float32 (numpy, BLAS threads = the
+    visible cores): Euler steps of the same workload, whole chunks one after another, until
+    about budget_s of CPU work has been done (at least one step). chunks/s = batch / (mean
+    step time x T); when the budget ends inside the first chunk the figure is extrapolated
+    from the steps done, and the sample says so. The schedule table and the binding are
+    computed before the timed region."""
     import numpy as np
     import oracle
     try:
@@ -122,21 +126,169 @@ def cpu_baseline(cfg, W, I, budget_s=12.0):
         blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info() if p.get("user_api") == "blas"}))
     except Exception:
         threads, blas = os.cpu_count(), "unknown"
-    w = oracle.cast_weights(W)
-    bound = oracle.bind(cfg, w, I)
-    t0 = time.perf_counter()
+    T, B = cfg["steps"], cfg["batch"]
+    f32 = np.float32
+    w = oracle.cast_weights(W, f32)
+    bound = oracle.bind(cfg, w, I, dtype=f32)
+    tau = oracle.schedule(T, dtype=f32)
+    table, tb = oracle.modulation_table(cfg, w, tau)
+    x = np.array(I["x0"], dtype=f32)
     n = 0
+    t0 = time.perf_counter()
     while True:
-        oracle.denoise(cfg, w, bound, I["x0"], cfg["steps"])
+        k = n % T
+        if k == 0:
+            x = np.array(I["x0"], dtype=f32)
+        x = x + (tau[k + 1] - tau[k]) * oracle.velocity(cfg, w, bound, x, table, tb, k)
         n += 1
-        if time.perf_counter() - t0 > budget_s:
+        if time.perf_counter() - t0 > budget_s and (n % T == 0 or n < T):
             break
     dt = time.perf_counter() - t0
+    whole = n // T
+    how = (f"{whole} whole chunk(s)" if n % T == 0 else
+           f"{n} of the {T} Euler steps of one chunk, extrapolated to the chunk")
     return {
-        "value": round(cfg["batch"] * n / dt, 4), "unit": "chunks/s", "cores": int(threads), "kind": "oracle",
-        "sample": f"{n} chunk(s) of {cfg['name']} ({cfg['steps']} Euler steps, batch {cfg['batch']}), float64 numpy "
-                  f"({blas}, {threads} threads; {os.cpu_count()} CPUs visible), table and bind excluded, {dt:.1f} s",
+        "value": round(B / (dt / n * T), 4), "unit": "chunks/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{how} of {cfg['name']} (batch {B}), float32 numpy ({blas}, {threads} threads; "
+                  f"{os.cpu_count()} CPUs visible), table and bind excluded, {dt:.1f} s",
     }
+
+
+def time_calls(ctx, x0, T, out, n, stream):
+    """n back-to-back fm_denoise calls with a HIP event on the context stream before each call
+    and after the last: per-call latencies (ms) between consecutive events, and the wall time
+    of the whole bracket (synchronized on both sides)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        evs[i].record(stream)
+        ctx.denoise(x0, T, out)
+    evs[n].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(n)], wall
+
+
+def latency_summary(lat):
+    import numpy as np
+    a = np.asarray(lat, float)
+    return {"p50_ms": round(float(np.percentile(a, 50)), 4), "p90_ms": round(float(np.percentile(a, 90)), 4),
+            "mean_ms": round(float(a.mean()), 4), "calls": int(a.size)}
+
+
+def bound_of(cfg, seconds_per_step):
+    """Fraction of the Euler step's own roofline bound: algorithmic bytes over 8 TB/s or flops
+    over the dtype's dense MFMA peak, whichever bound is larger."""
+    b, f = step_bytes_flops(cfg)
+    peak_f = (BF16_PEAK_TFLOPS if cfg["dtype"] == 1 else FP32_PEAK_TFLOPS) * 1e12
+    t_hbm, t_mfma = b / (HBM_PEAK_GBS * 1e9), f / peak_f
+    kind = "hbm" if t_hbm >= t_mfma else "mfma"
+    return {"bound": kind, "frac": round((t_hbm if kind == "hbm" else t_mfma) / seconds_per_step, 4),
+            "hbm_frac": round(t_hbm / seconds_per_step, 4), "mfma_frac": round(t_mfma / seconds_per_step, 4),
+            "alg_bytes_per_euler_step": int(b), "alg_flops_per_euler_step": int(f),
+            "floor_us_per_euler_step": round(max(t_hbm, t_mfma) * 1e6, 2)}
+
+
+def make_context(cfg, W, I, fmt_fp8=False):
+    """Context with weights loaded, the seeded prefix (or context and state) bound and the
+    schedule set; returns (ctx, bind callable)."""
+    import torch
+    from flow_matching_vla_amd import fm
+    dt, B = cfg["dtype"], cfg["batch"]
+    ctx = fm.Context(cfg)
+    if fmt_fp8:
+        ctx.set_weight_format(fm.WEIGHTS_FP8_E4M3)
+    wt = {n: fm.to_device(a, dt) for n, a in W.items()}
+    ctx.load_weights(wt)
+    del wt
+    if cfg["arch"] == 0:
+        L = cfg["n_layers"]
+        kk = [fm.to_device(I[f"prefix.k.{l}"], dt) for l in range(L)]
+        vv = [fm.to_device(I[f"prefix.v.{l}"], dt) for l in range(L)]
+
+        def bind():
+            ctx.bind_prefix_kv(B, cfg["prefix_len"], kk, vv)
+    else:
+        zc, st = fm.to_device(I["context"], dt), fm.to_device(I["state"], fm.F32)
+
+        def bind():
+            ctx.bind_prefix_kv(B, cfg["ctx_len"], context=zc, state=st)
+    bind()
+    torch.cuda.synchronize()
+    ctx.set_schedule(cfg["steps"], B)
+    return ctx, bind
+
+
+def dominant_role(ctx, cfg, x0, out):
+    """Per-operation roles timed with events around every launch (eager replay); the role with
+    the largest time per chunk and its fraction of its own bound."""
+    from flow_matching_vla_amd import fm
+    T, dt = cfg["steps"], cfg["dtype"]
+    roles = {}
+    for r in ("inproj", "qkv", "attn", "oproj", "mlp_up", "mlp_down", "out"):
+        tot, nl = 0.0, 0
+        for _ in range(3):
+            m, n = fm.profile_loop(ctx, x0, T, r, out)
+            tot += m
+            nl += n
+        roles[r] = (tot / nl, nl // 3)
+    dom = max(roles, key=lambda r: roles[r][0] * roles[r][1])
+    nbytes, nflops = role_bytes_flops(cfg, dom)
+    avg_s = roles[dom][0] * 1e-3
+    ridge = (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
+    if nflops / max(nbytes, 1) < ridge:
+        ach = nbytes / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel_role": dom,
+                "alg_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches_per_chunk": roles[dom][1]}
+    else:
+        peak = BF16_PEAK_TFLOPS if dt == 1 else FP32_PEAK_TFLOPS
+        ach = nflops / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "kernel_role": dom,
+                "alg_flops_per_launch": int(nflops), "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches_per_chunk": roles[dom][1]}
+    return {r: round(v[0] * 1000, 2) for r, v in roles.items()}, roof
+
+
+def bench_other(name, calls, cpu_budget):
+    """One of the other workloads, in the same run: chunks/s, p50 / p90 chunk latency, the
+    Euler step against its own roofline bound, the dominant kernel role where the per-operation
+    graph serves it, and the oracle on a bounded sample. Every device object is released
+    before returning."""
+    import torch
+    from flow_matching_vla_amd import workloads as wl
+    cfg = wl.workload(name)
+    T, B = cfg["steps"], cfg["batch"]
+    print(f"[bench] {name}: generating seeded inputs", file=sys.stderr, flush=True)
+    W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
+    ctx, _ = make_context(cfg, W, I)
+    x0 = torch.from_numpy(I["x0"]).cuda()
+    out = torch.empty_like(x0)
+    for _ in range(5):
+        ctx.denoise(x0, T, out)
+    lat, wall = time_calls(ctx, x0, T, out, calls, ctx.stream)
+    summ = latency_summary(lat)
+    persistent, _ = ctx.loop_status()
+    r = {"workload": f"{name}: {DESCRIPTIONS[name]}", "chunks_per_s": round(B * calls / wall, 3),
+         "latency": summ, "per_euler_step_us": round(1000 * summ["p50_ms"] / T, 2),
+         "path": "loop kernel (one launch per chunk)" if persistent else "hipGraph of per-operation kernels",
+         "step_roofline": bound_of(cfg, summ["p50_ms"] * 1e-3 / T)}
+    if not persistent:
+        roles, roof = dominant_role(ctx, cfg, x0, out)
+        r["roles_us_per_launch"], r["roofline"] = roles, roof
+    print(f"[bench] {name}: {summ['p50_ms']:.3f} ms per chunk (p50), {r['chunks_per_s']:.1f} chunks/s",
+          file=sys.stderr, flush=True)
+    ctx.close()
+    del x0, out, ctx
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu_budget > 0:
+        r["cpu_baseline"] = cpu_baseline(cfg, W, I, cpu_budget)
+    return r
 
 
 def main():
@@ -150,6 +302,7 @@ def main():
     ap.add_argument("--no-roles", action="store_true")
     ap.add_argument("--no-visibility", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weights line of pi0.5 workloads")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' entries")
     ap.add_argument("--weights", choices=("as-given", "fp8"), default="as-given",
                     help="fp8: the expert's per-layer matrices as FP8 E4M3 codes with per-row scales")
     ap.add_argument("--pmc-probe", action="store_true",
@@ -174,27 +327,7 @@ def main():
     print(f"[bench] {cfg['name']}: generating seeded inputs", file=sys.stderr, flush=True)
     W, I = wl.make_weights(cfg), wl.make_inputs(cfg)
     torch.cuda.set_device(0)
-    ctx = fm.Context(cfg)
-    if args.weights == "fp8":
-        ctx.set_weight_format(fm.WEIGHTS_FP8_E4M3)
-    wt = {n: fm.to_device(a, dt) for n, a in W.items()}
-    ctx.load_weights(wt)
-    del wt
-    if cfg["arch"] == 0:
-        L = cfg["n_layers"]
-        kk = [fm.to_device(I[f"prefix.k.{l}"], dt) for l in range(L)]
-        vv = [fm.to_device(I[f"prefix.v.{l}"], dt) for l in range(L)]
-
-        def bind():
-            ctx.bind_prefix_kv(B, cfg["prefix_len"], kk, vv)
-    else:
-        zc, st = fm.to_device(I["context"], dt), fm.to_device(I["state"], fm.F32)
-
-        def bind():
-            ctx.bind_prefix_kv(B, cfg["ctx_len"], context=zc, state=st)
-    bind()
-    torch.cuda.synchronize()
-    ctx.set_schedule(T, B)
+    ctx, bind = make_context(cfg, W, I, fmt_fp8=args.weights == "fp8")
     x0 = torch.from_numpy(I["x0"]).cuda()
     out = torch.empty_like(x0)
     stream = ctx.stream
@@ -217,16 +350,8 @@ def main():
         ctx.denoise(x0, T, out)
     torch.cuda.synchronize()
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        ctx.denoise(x0, T, out)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    lat, wall = time_calls(ctx, x0, T, out, args.steps, stream)
+    ms = sum(lat) / len(lat)
     value = B * args.steps / wall
     print(f"[bench] {ms:.3f} ms per chunk call ({value:.1f} chunks/s)", file=sys.stderr, flush=True)
 
@@ -240,6 +365,7 @@ def main():
                    "action_dim": cfg["action_dim"], "parallelism": "none (1 GPU)",
                    "weights": "fp8-e4m3, per-row power-of-two scale" if args.weights == "fp8" else "as given"},
         "per_euler_step_us": round(1000 * ms / T, 2),
+        "latency": latency_summary(lat),
         "loop": {"alg_bytes_per_euler_step": int(step_b), "alg_flops_per_euler_step": int(step_f),
                  "achieved_GBps": round(step_b * T / (ms * 1e-3) / 1e9, 1),
                  "hbm_frac": round(step_b * T / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -281,40 +407,14 @@ def main():
         nbytes, nflops = step_b * T, step_f * T
         ach = nbytes / avg_s / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": loop_traffic(cfg["name"] + ("_fp8" if args.weights == "fp8" else "")), "kernel": "k_loop",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": loop_traffic(cfg["name"] + ("_fp8" if args.weights == "fp8" else "")), "kernel": "k_xloop",
                            "alg_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2),
                            "launches_per_chunk": 1, "mfma_TFLOPs": round(nflops / avg_s / 1e12, 2)}
     if not args.no_roles and not persistent:
-        roles = {}
-        for r in ("inproj", "qkv", "attn", "oproj", "mlp_up", "mlp_down", "out"):
-            ctx.denoise(x0, T, out)
-            tot = 0.0
-            nl = 0
-            for _ in range(3):
-                m, n = fm.profile_loop(ctx, x0, T, r, out)
-                tot += m
-                nl += n
-            roles[r] = (tot / nl, nl // 3)
-        res["roles_us_per_launch"] = {r: round(v[0] * 1000, 2) for r, v in roles.items()}
-        dom = max(roles, key=lambda r: roles[r][0] * roles[r][1])
-        res["roofline_kernel_role"] = dom
-        nbytes, nflops = role_bytes_flops(cfg, dom)
-        avg_s = roles[dom][0] * 1e-3
-        intensity = nflops / max(nbytes, 1)
-        ridge = (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9)
-        if intensity < ridge:
-            ach = nbytes / avg_s / 1e9
-            res["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel_role": dom,
-                               "alg_bytes_per_launch": int(nbytes), "avg_launch_us": round(avg_s * 1e6, 2),
-                               "launches_per_chunk": roles[dom][1]}
-        else:
-            peak = BF16_PEAK_TFLOPS if dt == 1 else FP32_PEAK_TFLOPS
-            ach = nflops / avg_s / 1e12
-            res["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                               "frac": round(ach / peak, 4), "traffic": None, "kernel_role": dom,
-                               "alg_flops_per_launch": int(nflops), "avg_launch_us": round(avg_s * 1e6, 2),
-                               "launches_per_chunk": roles[dom][1]}
+        roles, roof = dominant_role(ctx, cfg, x0, out)
+        res["roles_us_per_launch"] = roles
+        res["roofline_kernel_role"] = roof["kernel_role"]
+        res["roofline"] = roof
     # per-request visibility: the workload's seeded mixed batch (ragged compact prefixes for
     # pi0.5, text / image masks for DiT), same binding, timed like the main loop
     vis = None if args.no_visibility else wl.make_visibility(cfg)
@@ -345,13 +445,7 @@ def main():
     # the same workload with the expert's per-layer matrices as FP8 codes (a separate model:
     # reported beside the bf16 line, never as its value)
     if cfg["arch"] == 0 and args.weights == "as-given" and not args.no_fp8:
-        c8 = fm.Context(cfg)
-        c8.set_weight_format(fm.WEIGHTS_FP8_E4M3)
-        c8.load_weights({n: fm.to_device(a, dt) for n, a in W.items()})
-        L = cfg["n_layers"]
-        c8.bind_prefix_kv(B, cfg["prefix_len"], [fm.to_device(I[f"prefix.k.{l}"], dt) for l in range(L)],
-                          [fm.to_device(I[f"prefix.v.{l}"], dt) for l in range(L)])
-        c8.set_schedule(T, B)
+        c8, _ = make_context(cfg, W, I, fmt_fp8=True)
         o8 = torch.empty_like(x0)
         for _ in range(5):
             c8.denoise(x0, T, o8)
@@ -371,6 +465,7 @@ def main():
                               "traffic": loop_traffic(cfg["name"] + "_fp8"),
                               "chunk_e_rel_vs_bf16_weights": round(float(torch.linalg.vector_norm(o8 - out) / torch.linalg.vector_norm(out)), 5)}
         c8.close()
+        del o8, c8
     # the step after the path: the chunk back to robot units (LIBERO width 7; GR00T's policy
     # keeps 16 of the model's 40 steps), timed with HIP events on the context stream
     post_kind = fm.UNNORM_QUANTILE_EPS if cfg["arch"] == 0 else fm.UNNORM_QUANTILE_CLIP
@@ -415,7 +510,16 @@ def main():
         for _ in range(100):
             oracle.quantile_unnormalize(chunk, q01, q99, post_kind, post_h, post_d)
         res["post"]["oracle_us"] = round((time.perf_counter() - t1) / 100 * 1e6, 2)
+    # release every device object of this workload before the next one (and before exit: the
+    # interpreter then tears down nothing of this library's)
     ctx.close()
+    del ctx, bind, x0, out, robot
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_configs and args.workload == "pi05_b1" and args.weights == "as-given":
+        res["configs"] = {}
+        for name, calls, cb in (("tiny_fp32", 50, 3.0), ("pi05_b8", 20, 4.0), ("dit_b1", 20, 4.0), ("pi05_b64", 10, 6.0)):
+            res["configs"][name] = bench_other(name, calls, 0.0 if args.no_cpu_baseline else cb)
     print(json.dumps(res), flush=True)
 
 

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfmvla.so")
-SOURCES = ["fm_gemm.hip", "fm_attn.hip", "fm_misc.hip", "fm_persist.hip", "fm_api.cpp"]
+SOURCES = ["fm_gemm.hip", "fm_attn.hip", "fm_misc.hip", "fm_xloop.hip", "fm_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-x", "hip",

@@ -13,7 +13,7 @@
 
 #include "../../include/fm.h"
 #include "fm_kernels.h"
-#include "fm_persist.h"
+#include "fm_xloop.h"
 
 using namespace fm;
 
@@ -176,6 +176,7 @@ struct fm_ctx {
   std::vector<float2> rope_pos;   // host [max_prefix_len + H][dh/2]: cos/sin of every position
   // per-request visibility: PREFIX_JOINT compact prefix lengths, DIT text / image masks
   int* plens = nullptr;       // [Bmax]
+  std::vector<int> plens_host;   // the same, on the host
   uint32_t* kmask = nullptr;  // [2][Bmax][ctx_words]: bit j % 32 of word j / 32 = key j visible
   int ctx_words = 0;
   // whether a request sees less than the whole binding (some P_b < P; a text / image mask
@@ -193,24 +194,27 @@ struct fm_ctx {
   float* ws = nullptr;
   size_t ws_bytes = 0;
   unsigned* counters = nullptr;
-  static constexpr int kCounters = 1 << 16;
 
-  // persistent loop kernel: per-step activation buffers (one set per step and layer, written
-  // once per launch), flag words, partial-result workspaces, per-step dt
+  // the loop kernel: XCD-local buffers (one region per XCD), the cross-XCD partial sums and
+  // norm operands, flag words and their counter bases, per-step dt
   int loop_mode = FM_LOOP_AUTO;
-  char* rot = nullptr;
-  size_t rot_bytes = 0;
+  char* xl = nullptr;
+  size_t xl_bytes = 0;
+  long xl_zeroed_stride = -1;   // layout the XCD-local buffers were last zeroed for
+  int xl_zeroed_batch = -1;
+  char* xag = nullptr;          // norm operands of every (step, site)
+  size_t xag_bytes = 0;
+  float* xpart = nullptr;       // [2][8][64][hidden] partial sums
   uint32_t* pflags = nullptr;
-  float *pws_attn = nullptr, *pws_ml = nullptr, *pws_split = nullptr;
   float* dts = nullptr;
-  uint32_t epoch = 0;
-  LoopArgs* loop_dev = nullptr;      // the loop description the kernel reads, and its host copy
-  LoopArgs loop_host;
+  uint32_t xb_base = 0, ag_base = 0, pe_base = 0;   // counter values at the next launch's start
+  XLoopArgs* loop_dev = nullptr;      // the loop description the kernel reads, and its host copy
+  XLoopArgs loop_host;
   bool loop_uploaded = false;
   int wformat = FM_WEIGHTS_AS_GIVEN;   // for the next fm_load_weights
   bool w8 = false;                     // the loaded per-layer weights have FP8 copies
-  LayerW* lw_dev = nullptr;          // [n_layers] weight pointers
-  std::vector<LayerW> lw_host;
+  XLayerW* lw_dev = nullptr;         // [n_layers] weight pointers
+  std::vector<XLayerW> lw_host;
 
   // the step after the path: action statistics of the robot's share of the chunk
   int unnorm_kind = -1, robot_h = 0, robot_d = 0;
@@ -450,7 +454,7 @@ fm_status plan_ops(fm_ctx* ctx, std::vector<Op>& ops) {
     if (op.kind == Op::GEMM) {
       gemm_plan(op.g, ctx->elem, ctx->num_cus);
       need = std::max(need, gemm_ws_bytes(op.g));
-      if (op.g.splits > 1 && gemm_num_tiles(op.g) > fm_ctx::kCounters) return fail(ctx, FM_ERR_UNSUPPORTED, "too many split tiles");
+      if (op.g.splits > 1 && gemm_num_tiles(op.g) > kGemmCounters) return fail(ctx, FM_ERR_UNSUPPORTED, "too many split tiles");
     } else if (op.kind == Op::ATTN) {
       attn_plan(op.at, ctx->elem, ctx->num_cus);
       need = std::max(need, attn_ws_bytes(op.at));
@@ -500,15 +504,17 @@ fm_status check_ready(fm_ctx* ctx) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Persistent loop kernel
+// The loop kernel (fm_xloop.hip)
 // ---------------------------------------------------------------------------------------
-LoopShape loop_shape(const fm_ctx* ctx) {
+XShape loop_shape(const fm_ctx* ctx) {
   const fm_config& c = ctx->c;
-  LoopShape sh;
-  sh.dtype_bf16 = c.dtype == FM_BF16;
-  sh.B = ctx->bound_batch; sh.H = c.action_horizon; sh.M = sh.B * sh.H;
-  sh.D = c.hidden; sh.nq = c.n_heads; sh.dh = c.head_dim; sh.F = c.mlp_dim; sh.da = c.action_dim;
-  sh.L = c.n_layers; sh.P = ctx->prefix_len; sh.qd = c.n_heads * c.head_dim;
+  XShape sh;
+  sh.bf16 = c.dtype == FM_BF16;
+  sh.B = ctx->bound_batch; sh.H = c.action_horizon; sh.D = c.hidden; sh.nq = c.n_heads; sh.dh = c.head_dim;
+  sh.F = c.mlp_dim; sh.da = c.action_dim; sh.L = c.n_layers;
+  sh.npairs = 0;
+  for (int b = 0; b < ctx->bound_batch && b < (int)ctx->plens_host.size(); ++b)
+    sh.npairs += ((ctx->plens_host[b] + 31) / 32 + (c.action_horizon + 31) / 32 + 1) / 2;
   return sh;
 }
 
@@ -518,53 +524,46 @@ const char* loop_unsupported(const fm_ctx* ctx) {
   if (ctx->loop_mode != FM_LOOP_AUTO) return "loop mode is FM_LOOP_GRAPH";
   if (c.arch != FM_ARCH_PREFIX_JOINT || !c.mlp_gated || c.n_kv_heads != 1) return "not a pi0.5-family expert";
   if (!ctx->pflags) return "no loop-kernel workspace (bf16, head_dim 256 only)";
-  if (c.action_dim % 4 != 0) return "action_dim must be a multiple of 4";
   if (ctx->steps < 1 || ctx->prefix_len < 0) return "no schedule or binding";
-  return loop_check(loop_shape(ctx), ctx->num_cus);
+  return xloop_check(loop_shape(ctx), ctx->num_cus);
 }
 
-// byte layout of one (step, layer) set of activation buffers, each aligned to 4 KB so
-// that no cache line is shared by buffers written in different phases
-struct RotLayout { long o_hs, o_st, o_q, o_sk, o_svt, o_ao, o_hsu, o_stu, o_act, layer; int Hp; };
-RotLayout rot_layout(const fm_ctx* ctx) {
-  const fm_config& c = ctx->c;
-  const long M = (long)ctx->bound_batch * c.action_horizon, D = c.hidden, qd = (long)c.n_heads * c.head_dim;
-  const long dh = c.head_dim, F = c.mlp_dim, B = ctx->bound_batch;
-  RotLayout r;
-  r.Hp = (int)round_up(c.action_horizon, 32);
-  long off = 0;
-  auto put = [&](long bytes) { const long o = off; off += round_up(std::max(bytes, 1L), 4096); return o; };
-  const long Mp = round_up(M, 16);   // the GEMM operands hs, ao, hsu, act: whole 16-row blocks
-  r.o_hs = put(Mp * D * 2);
-  r.o_st = put(M * (D / 16) * 4);
-  r.o_q = put(B * round_up((long)c.n_heads * c.action_horizon, 16) * dh * 2);   // folded rows
-  r.o_sk = put(B * r.Hp * dh * 2);
-  r.o_svt = put(B * dh * r.Hp * 2);
-  r.o_ao = put(Mp * qd * 2);
-  r.o_hsu = put(Mp * D * 2);
-  r.o_stu = put(M * (D / 16) * 4);
-  r.o_act = put(Mp * F * 2);
-  r.layer = off;
-  return r;
-}
-
-// the activation buffers for `steps` steps of the current binding
+// the buffers for `steps` steps of the current binding; the XCD-local ones are zeroed whenever
+// their layout changes: key slots past the horizon in the chunk's last key tile are never
+// written, and their zero softmax weight must not meet a stale NaN or Inf left by another layout
 fm_status loop_buffers(fm_ctx* ctx, int steps) {
-  const RotLayout r = rot_layout(ctx);
-  const size_t need = (size_t)steps * (ctx->c.n_layers + 1) * r.layer;
-  if (need <= ctx->rot_bytes) return FM_OK;
-  HIPCK(hipStreamSynchronize(ctx->stream));
-  dfree(ctx, ctx->rot);
-  ctx->rot = nullptr;
-  ctx->rot_bytes = 0;
-  void* p;
-  fm_status s = dalloc(ctx, &p, need);
-  if (s != FM_OK) return s;
-  // zeroed once: key slots past the horizon in the last suffix K / V^T tile are never
-  // written, and their zero softmax weight must not meet a stale NaN or Inf
-  HIPCK(hipMemsetAsync(p, 0, need, ctx->stream));
-  ctx->rot = (char*)p;
-  ctx->rot_bytes = need;
+  const fm_config& c = ctx->c;
+  const XShape sh = loop_shape(ctx);
+  const XLayout r = xloop_layout(sh.B, sh.H, sh.D, sh.F, sh.da, sh.npairs);
+  const size_t need_xl = 8 * (size_t)r.xl_stride;
+  const size_t need_ag = (size_t)steps * (2 * c.n_layers + 1) * r.ag_site;
+  if (need_xl > ctx->xl_bytes || need_ag > ctx->xag_bytes) HIPCK(hipStreamSynchronize(ctx->stream));
+  if (need_xl > ctx->xl_bytes) {
+    dfree(ctx, ctx->xl);
+    ctx->xl = nullptr;
+    ctx->xl_bytes = 0;
+    void* p;
+    fm_status s = dalloc(ctx, &p, need_xl);
+    if (s != FM_OK) return s;
+    ctx->xl = (char*)p;
+    ctx->xl_bytes = need_xl;
+    ctx->xl_zeroed_stride = -1;
+  }
+  if (need_ag > ctx->xag_bytes) {
+    dfree(ctx, ctx->xag);
+    ctx->xag = nullptr;
+    ctx->xag_bytes = 0;
+    void* p;
+    fm_status s = dalloc(ctx, &p, need_ag);
+    if (s != FM_OK) return s;
+    ctx->xag = (char*)p;
+    ctx->xag_bytes = need_ag;
+  }
+  if (ctx->xl_zeroed_stride != r.xl_stride || ctx->xl_zeroed_batch != ctx->bound_batch) {
+    HIPCK(hipMemsetAsync(ctx->xl, 0, ctx->xl_bytes, ctx->stream));
+    ctx->xl_zeroed_stride = r.xl_stride;
+    ctx->xl_zeroed_batch = ctx->bound_batch;
+  }
   return FM_OK;
 }
 
@@ -574,60 +573,75 @@ fm_status loop_run(fm_ctx* ctx, int k0, int nsteps, float* vout) {
   const fm_config& c = ctx->c;
   fm_status s = loop_buffers(ctx, ctx->steps);
   if (s != FM_OK) return s;
-  const RotLayout r = rot_layout(ctx);
-  LoopArgs a;
+  const XShape sh = loop_shape(ctx);
+  const XLayout r = xloop_layout(sh.B, sh.H, sh.D, sh.F, sh.da, sh.npairs);
+  XLoopArgs a;
   memset(&a, 0, sizeof a);
   a.B = ctx->bound_batch; a.H = c.action_horizon; a.M = a.B * a.H; a.D = c.hidden; a.nq = c.n_heads;
-  a.dh = c.head_dim; a.F = c.mlp_dim; a.da = c.action_dim; a.L = c.n_layers; a.P = ctx->prefix_len; a.cap = ctx->cap;
-  a.qd = a.nq * a.dh; a.nqkv = a.qd + 2 * a.dh; a.Hp = r.Hp; a.S = n_sites(c); a.csum = ctx->csum;
-  a.cq4 = (int)round_up(a.nqkv, 4); a.cg4 = (int)round_up(2 * a.F, 4); a.cout4 = (int)round_up(a.da, 4);
-  a.eps = c.norm_eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)a.dh));
+  a.F = c.mlp_dim; a.da = c.action_dim; a.L = c.n_layers; a.P = ctx->prefix_len; a.cap = ctx->cap;
+  a.Hp = r.Hp; a.S = n_sites(c); a.csum = ctx->csum;
+  const int nqkv = c.n_heads * c.head_dim + 2 * c.head_dim;
+  a.cq4 = (int)round_up(nqkv, 4); a.cg4 = (int)round_up(2 * a.F, 4); a.cout4 = (int)round_up(a.da, 4);
+  a.eps = c.norm_eps; a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
   a.rope = c.rope_base > 0.f;
-  a.RT = (a.nq * a.H + 63) / 64; a.TP = (a.P + 31) / 32; a.TS = (a.H + 31) / 32; a.SA = (a.TP + a.TS + 1) / 2;
   a.max_steps = std::max(c.max_steps, 1); a.dts = ctx->dts;
+  // attention key-tile pairs of one head: request b's prefix tiles, then its chunk's tiles, two
+  // by two
+  a.npairs = 0;
+  for (int b = 0; b < a.B; ++b) {
+    a.poff[b] = a.npairs;
+    a.plen[b] = ctx->plens_host[b];
+    const int nt = (a.plen[b] + 31) / 32 + (a.H + 31) / 32;
+    for (int j = 0; j < nt; j += 2) a.pair[a.npairs++] = XPair{b, j};
+  }
+  a.poff[a.B] = a.npairs;
   a.w_in = ctx->w_in; a.b_in = ctx->b_in; a.w_out = ctx->w_out; a.b_out = ctx->b_out;
-  std::vector<LayerW> lw(c.n_layers);
+  std::vector<XLayerW> lw(c.n_layers);
   for (int l = 0; l < c.n_layers; ++l) {
     const auto& W = ctx->L[l];
-    lw[l] = ctx->w8 ? LayerW{W.qkv8, W.o8, W.gu8, W.down8, W.sqkv, W.so, W.sgu, W.sdown}
-                    : LayerW{W.qkv, W.o, W.gu, W.down, nullptr, nullptr, nullptr, nullptr};
+    lw[l] = ctx->w8 ? XLayerW{W.qkv8, W.o8, W.gu8, W.down8, W.sqkv, W.so, W.sgu, W.sdown}
+                    : XLayerW{W.qkv, W.o, W.gu, W.down, nullptr, nullptr, nullptr, nullptr};
   }
   a.lw = ctx->lw_dev;
   auto wbytes = [&](int N, int K) { return (uint32_t)(ctx->w8 ? swizzled_fp8_bytes(N, K) : swizzled_bytes(N, K, ET_BF16)); };
-  a.wb_qkv = wbytes(a.nqkv, a.D);
-  a.wb_o = wbytes(a.D, a.qd);
+  a.wb_qkv = wbytes(nqkv, a.D);
+  a.wb_o = wbytes(a.D, c.n_heads * c.head_dim);
   a.wb_gu = wbytes(2 * a.F, a.D);
   a.wb_down = wbytes(a.D, a.F);
   a.wb_out = (uint32_t)swizzled_bytes(a.da, a.D, ET_BF16);
-  a.table = ctx->table; a.cbuf = ctx->cbuf; a.rope_cs = ctx->rope_cs; a.plens = ctx->plens;
-  a.x = ctx->x; a.h = ctx->h;
+  a.table = ctx->table; a.cbuf = ctx->cbuf; a.rope_cs = ctx->rope_cs;
   a.pool = (const __bf16*)ctx->pool; a.plane = (long)c.max_batch * ctx->cap * c.head_dim;
-  a.rot = ctx->rot; a.rot_layer = r.layer; a.rot_step = (long)(c.n_layers + 1) * r.layer;
-  a.o_hs = r.o_hs; a.o_st = r.o_st; a.o_q = r.o_q; a.o_sk = r.o_sk; a.o_svt = r.o_svt; a.o_ao = r.o_ao;
-  a.o_hsu = r.o_hsu; a.o_stu = r.o_stu; a.o_act = r.o_act;
-  a.ws_attn = ctx->pws_attn; a.ws_attn_ml = ctx->pws_ml; a.ws_split = ctx->pws_split;
+  a.xl = ctx->xl; a.xl_stride = r.xl_stride;
+  a.o_xx = r.o_xx; a.o_q = r.o_q; a.o_sk = r.o_sk; a.o_svt = r.o_svt; a.o_ap = r.o_ap; a.o_ml = r.o_ml;
+  a.o_ax = r.o_ax; a.o_act = r.o_act;
+  a.part = ctx->xpart;
+  a.ag = ctx->xag; a.ag_site = r.ag_site; a.ag_step = (long)(2 * c.n_layers + 1) * r.ag_site; a.o_agst = r.o_agst;
   a.flags = ctx->pflags;
   // the description lives in device memory; it is uploaded again only when it changed
   if (!ctx->loop_uploaded || memcmp(&a, &ctx->loop_host, sizeof a) != 0 || lw.size() != ctx->lw_host.size() ||
-      memcmp(lw.data(), ctx->lw_host.data(), lw.size() * sizeof(LayerW)) != 0) {
+      memcmp(lw.data(), ctx->lw_host.data(), lw.size() * sizeof(XLayerW)) != 0) {
     HIPCK(hipStreamSynchronize(ctx->stream));
     ctx->loop_host = a;
     ctx->lw_host = lw;
     HIPCK(hipMemcpy(ctx->loop_dev, &ctx->loop_host, sizeof a, hipMemcpyHostToDevice));
-    HIPCK(hipMemcpy(ctx->lw_dev, ctx->lw_host.data(), lw.size() * sizeof(LayerW), hipMemcpyHostToDevice));
+    HIPCK(hipMemcpy(ctx->lw_dev, ctx->lw_host.data(), lw.size() * sizeof(XLayerW), hipMemcpyHostToDevice));
     ctx->loop_uploaded = true;
   }
-  LaunchArgs la;
-  la.k0 = k0; la.nsteps = nsteps; la.vout = vout;
-  const uint32_t nbar = (uint32_t)loop_barriers(c.n_layers, nsteps);
-  if (ctx->epoch > 0xf0000000u - nbar) {
-    // epochs only grow within a flag generation: start a new one
-    HIPCK(hipMemsetAsync(ctx->pflags, 0, kFlagWords * sizeof(uint32_t), ctx->stream));
-    ctx->epoch = 0;
+  uint32_t nxb, nag, npe;
+  xloop_counts(c.n_layers, nsteps, &nxb, &nag, &npe);
+  if (ctx->xb_base > 0x70000000u - 32u * nxb || ctx->ag_base > 0x70000000u - 32u * nag || ctx->pe_base > 0x70000000u - npe) {
+    // counters only grow within a flag generation: start a new one
+    HIPCK(hipMemsetAsync(ctx->pflags, 0, kXFlagWords * sizeof(uint32_t), ctx->stream));
+    ctx->xb_base = ctx->ag_base = ctx->pe_base = 0;
   }
-  la.e0 = ctx->epoch;
-  ctx->epoch += nbar;
-  HIPCK(loop_launch(ctx->loop_dev, la, ctx->num_cus, ctx->w8, ctx->stream));
+  XLaunch la;
+  la.k0 = k0; la.nsteps = nsteps;
+  la.xb0 = ctx->xb_base; la.ag0 = ctx->ag_base; la.pe0 = ctx->pe_base;
+  la.xin = ctx->x; la.xout = ctx->x; la.vout = vout;
+  ctx->xb_base += 32u * nxb;
+  ctx->ag_base += 32u * nag;
+  ctx->pe_base += npe;
+  HIPCK(xloop_launch(ctx->loop_dev, la, ctx->w8, ctx->stream));
   return FM_OK;
 }
 
@@ -637,6 +651,24 @@ fm_status loop_run(fm_ctx* ctx, int k0, int nsteps, float* vout) {
 // C ABI
 // =======================================================================================
 extern "C" {
+
+fm_status fm_device_supported(const char* gcn_arch, int32_t num_xcc, int32_t num_cus, char* msg, int32_t msg_len) {
+  std::string m;
+  fm_status s = FM_OK;
+  if (!gcn_arch) { m = "gcn_arch is NULL"; s = FM_ERR_INVALID_ARG; }
+  else if (strncmp(gcn_arch, "gfx950", 6) != 0) { m = fmt("device is %s; this library is built for gfx950", gcn_arch); s = FM_ERR_UNSUPPORTED; }
+  else if (num_xcc != 8) {
+    m = fmt("the device reports %d XCDs; the split-K and loop-kernel exchanges assume the 8 XCDs of a whole MI355X "
+            "partition (workgroup b on XCD b mod 8)", num_xcc);
+    s = FM_ERR_UNSUPPORTED;
+  } else if (num_cus < 8 || num_cus % 8 != 0) {
+    m = fmt("the device reports %d CUs, not a multiple of its 8 XCDs", num_cus);
+    s = FM_ERR_UNSUPPORTED;
+  }
+  if (msg && msg_len > 0) { strncpy(msg, m.c_str(), msg_len - 1); msg[msg_len - 1] = 0; }
+  if (s != FM_OK) g_err = m;
+  return s;
+}
 
 fm_status fm_query(const fm_config* cfg, fm_plan_info* info, char* msg, int32_t msg_len) {
   std::string m;
@@ -698,8 +730,34 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, ctx->device);
   if (e != hipSuccess) { ctx->err = fmt("hipGetDeviceProperties: %s", hipGetErrorString(e)); return bail(FM_ERR_DEVICE); }
-  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) { ctx->err = fmt("device is %s; this library is built for gfx950", prop.gcnArchName); return bail(FM_ERR_UNSUPPORTED); }
+  int n_xcc = 0;
+  e = hipDeviceGetAttribute(&n_xcc, hipDeviceAttributeNumberOfXccs, ctx->device);
+  if (e != hipSuccess) { ctx->err = fmt("hipDeviceGetAttribute(NumberOfXccs): %s", hipGetErrorString(e)); return bail(FM_ERR_DEVICE); }
+  {
+    char msg[256];
+    fm_status ds = fm_device_supported(prop.gcnArchName, n_xcc, prop.multiProcessorCount, msg, (int32_t)sizeof msg);
+    if (ds != FM_OK) { ctx->err = msg; return bail(ds); }
+  }
   ctx->num_cus = prop.multiProcessorCount;
+  {
+    // The XCD-local exchanges need each residue of blockIdx mod 8 on one XCD: check that the
+    // dispatcher deals a launch round-robin over the XCDs (from whichever XCD it starts on).
+    const int n = 2048;
+    uint32_t* d = nullptr;
+    std::vector<uint32_t> h(n);
+    e = hipMalloc(&d, n * sizeof(uint32_t));
+    if (e == hipSuccess) e = xcc_probe(d, n, ctx->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(h.data(), d, n * sizeof(uint32_t), hipMemcpyDeviceToHost, ctx->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(ctx->stream);
+    if (d) (void)hipFree(d);
+    if (e != hipSuccess) { ctx->err = fmt("workgroup placement probe: %s", hipGetErrorString(e)); return bail(FM_ERR_DEVICE); }
+    for (int b = 0; b < n; ++b)
+      if (h[b] >= 8u || ((h[b] - (uint32_t)b) & 7u) != (h[0] & 7u)) {
+        ctx->err = fmt("workgroup %d of a %d-workgroup launch ran on XCD %u: the dispatch is not round-robin over the 8 XCDs, "
+                       "which the split-K and loop-kernel exchanges need", b, n, h[b]);
+        return bail(FM_ERR_UNSUPPORTED);
+      }
+  }
   e = hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) { ctx->err = fmt("hipStreamCreate: %s", hipGetErrorString(e)); return bail(FM_ERR_DEVICE); }
 
@@ -750,15 +808,13 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
     ALLOC(dbuf, (size_t)c.max_steps * ctx->csum * 4, float*);
     ALLOC(dff, (size_t)c.n_layers * F * 4, float*);
   }
-  ALLOC(counters, fm_ctx::kCounters * sizeof(unsigned), unsigned*);
-  if (c.arch == FM_ARCH_PREFIX_JOINT && c.dtype == FM_BF16 && c.head_dim == 256) {
-    ALLOC(pflags, kFlagWords * sizeof(uint32_t), uint32_t*);
-    ALLOC(pws_attn, (size_t)kMaxAttnItems * 64 * 256 * sizeof(float), float*);
-    ALLOC(pws_ml, (size_t)kMaxAttnItems * 64 * 2 * sizeof(float), float*);
-    ALLOC(pws_split, (size_t)kMaxSplitItems * 64 * 16 * sizeof(float), float*);
+  ALLOC(counters, kGemmCounters * sizeof(unsigned), unsigned*);
+  if (c.arch == FM_ARCH_PREFIX_JOINT && c.dtype == FM_BF16 && c.head_dim == 256 && c.n_layers <= kXMaxLayers) {
+    ALLOC(pflags, kXFlagWords * sizeof(uint32_t), uint32_t*);
+    ALLOC(xpart, 2 * 8 * 64 * D * sizeof(float), float*);
     ALLOC(dts, (size_t)std::max(c.max_steps, 1) * sizeof(float), float*);
-    ALLOC(loop_dev, sizeof(LoopArgs), LoopArgs*);
-    ALLOC(lw_dev, (size_t)c.n_layers * sizeof(LayerW), LayerW*);
+    ALLOC(loop_dev, sizeof(XLoopArgs), XLoopArgs*);
+    ALLOC(lw_dev, (size_t)c.n_layers * sizeof(XLayerW), XLayerW*);
   }
   if (c.arch == FM_ARCH_PREFIX_JOINT) {
     ctx->cap = pool_capacity(c);
@@ -791,11 +847,11 @@ fm_status fm_create(const fm_config* cfg, void* stream, fm_ctx** out) {
         ctx->rope_pos[(size_t)p * (dh / 2) + j] = make_float2((float)std::cos(p * th), (float)std::sin(p * th));
     }
   }
-  e = hipMemsetAsync(ctx->counters, 0, fm_ctx::kCounters * sizeof(unsigned), ctx->stream);
+  e = hipMemsetAsync(ctx->counters, 0, kGemmCounters * sizeof(unsigned), ctx->stream);
   if (e == hipSuccess) e = hipMemsetAsync(ctx->zeros, 0, kVecPad * sizeof(float), ctx->stream);
   if (e == hipSuccess) e = fill_f32(ctx->ones, 1.f, kVecPad, ctx->stream);
   if (e == hipSuccess) e = hipMemsetAsync(ctx->stats, 0, ((D / kStatCols) * rows + 2 * kMaxStatSlots) * sizeof(float2), ctx->stream);
-  if (e == hipSuccess && ctx->pflags) e = hipMemsetAsync(ctx->pflags, 0, kFlagWords * sizeof(uint32_t), ctx->stream);
+  if (e == hipSuccess && ctx->pflags) e = hipMemsetAsync(ctx->pflags, 0, kXFlagWords * sizeof(uint32_t), ctx->stream);
   if (e == hipSuccess && ctx->pool) e = hipMemsetAsync(ctx->pool, 0, (size_t)c.n_layers * 2 * B * ctx->cap * c.head_dim * esz, ctx->stream);
   if (e == hipSuccess && ctx->vtself) e = hipMemsetAsync(ctx->vtself, 0, B * D * ctx->tpad * esz, ctx->stream);
   if (e == hipSuccess && ctx->cross_vt) e = hipMemsetAsync(ctx->cross_vt, 0, ((c.n_layers + 1) / 2) * B * D * ctx->spad * esz, ctx->stream);
@@ -1149,6 +1205,7 @@ static fm_status upload_lengths(fm_ctx* ctx, const std::vector<int>& lens, int P
     memcpy(&cs[(size_t)b * H * hd], &ctx->rope_pos[(size_t)lens[b] * hd], (size_t)H * hd * sizeof(float2));
   HIPCK(hipMemcpyAsync(ctx->rope_cs, cs.data(), cs.size() * sizeof(float2), hipMemcpyHostToDevice, ctx->stream));
   HIPCK(hipMemcpyAsync(ctx->plens, lens.data(), (size_t)B * sizeof(int), hipMemcpyHostToDevice, ctx->stream));
+  ctx->plens_host = lens;
   HIPCK(hipStreamSynchronize(ctx->stream));
   bool ragged = false;
   for (int b = 0; b < B; ++b) ragged |= lens[b] != P;
@@ -1499,12 +1556,14 @@ fm_status fm_loop_status(fm_ctx* ctx, int32_t* persistent, uint32_t* fault) {
   HIPCK(hipStreamSynchronize(ctx->stream));
   if (persistent) *persistent = (ctx->loaded && !loop_unsupported(ctx)) ? 1 : 0;
   uint32_t f = 0;
-  if (ctx->pflags) HIPCK(hipMemcpy(&f, ctx->pflags + kFlagErr, sizeof f, hipMemcpyDeviceToHost));
+  if (ctx->pflags) HIPCK(hipMemcpy(&f, ctx->pflags + kXErr, sizeof f, hipMemcpyDeviceToHost));
   if (fault) *fault = f;
   if (f != 0) {
-    (void)hipMemset(ctx->pflags, 0, kFlagWords * sizeof(uint32_t));
-    ctx->epoch = 0;
-    return fail(ctx, FM_ERR_DEVICE, fmt("loop kernel: a grid-barrier wait expired (fault word %u)", f));
+    (void)hipMemset(ctx->pflags, 0, kXFlagWords * sizeof(uint32_t));
+    ctx->xb_base = ctx->ag_base = ctx->pe_base = 0;
+    if (f == kXFaultSlot)
+      return fail(ctx, FM_ERR_DEVICE, "loop kernel: two workgroups ran on one (XCD, rank) slot (the dispatch was not round-robin over the XCDs); results are invalid");
+    return fail(ctx, FM_ERR_DEVICE, fmt("loop kernel: a bounded wait expired (fault word %u); results are invalid", f));
   }
   return FM_OK;
 }
@@ -1543,11 +1602,11 @@ fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const voi
     g.bias = (const float*)bpad;
   }
   if (e == hipSuccess && wsb) e = hipMalloc(&ws, wsb);
-  if (e == hipSuccess) e = hipMalloc(&cnt, fm_ctx::kCounters * sizeof(unsigned));
-  if (e == hipSuccess) e = hipMemsetAsync(cnt, 0, fm_ctx::kCounters * sizeof(unsigned), s);
+  if (e == hipSuccess) e = hipMalloc(&cnt, kGemmCounters * sizeof(unsigned));
+  if (e == hipSuccess) e = hipMemsetAsync(cnt, 0, kGemmCounters * sizeof(unsigned), s);
   if (e == hipSuccess) e = swizzle_weight(wsw, W, nullptr, N, K, K, elem, s);
   g.W = wsw; g.ws = (float*)ws; g.counters = (unsigned*)cnt;
-  if (e == hipSuccess && g.splits > 1 && gemm_num_tiles(g) > fm_ctx::kCounters) e = hipErrorInvalidValue;
+  if (e == hipSuccess && g.splits > 1 && gemm_num_tiles(g) > kGemmCounters) e = hipErrorInvalidValue;
   if (e == hipSuccess) e = gemm_launch(g, elem, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   hipError_t e2 = hipSuccess;

@@ -17,12 +17,6 @@
 #include "fm_common.h"
 #include "fm_kernels.h"
 
-#ifdef FM_PHASE_TIMING
-extern __device__ unsigned long long* g_phase;
-#define FM_PHASE(i) do { if (threadIdx.x == 0 && g_phase) g_phase[blockIdx.x * 8 + (i)] = __builtin_amdgcn_s_memrealtime(); } while (0)
-#else
-#define FM_PHASE(i) do { } while (0)
-#endif
 
 namespace fm {
 
@@ -112,7 +106,6 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   const int ntile = n1 + n2;
   auto tile_start = [&](int t) { return (!VIS || t < n1) ? key_beg + t * BK : s2 + (t - n1) * BK; };
 
-  FM_PHASE(0);
   // K / V^T tile copies: fragment f of a tile is 64 lanes x 16 bytes. K fragment (kb, c):
   // lane l carries key kb 16 + l % 16, d = c KC + (l / 16) VEC ... (A operand of S^T).
   // V^T fragment (db, kc): lane l carries d = db 16 + l % 16, stored key slots
@@ -158,7 +151,6 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
 #pragma unroll
   for (int p = 1; p < NST - 1; ++p)
     if (p < ntile) issue(tile_start(p), p);
-  FM_PHASE(1);
 
   f32x4 o[QB][DB];   // O^T: lane l, element e holds d = 16 db + 4 (l / 16) + e of query l % 16
 #pragma unroll
@@ -187,7 +179,6 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
     // tile t's copies are done once at most the tiles issued after it are in flight
     wait_tiles<FPW, NST>(min(NST - 1, ntile - 1 - t));
     __syncthreads();
-    if (t == 0) FM_PHASE(2);
     const V16* sK = sbuf[t % NST];
     const V16* sV = sK + FK * 64;
 
@@ -296,7 +287,6 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
           o[qb][db] = MT::mma(__builtin_bit_cast(frag, vf[db * KCH + kc]), pf[qb][kc], o[qb][db]);
     __syncthreads();   // this buffer is refilled by the next iteration's copies
   }
-  FM_PHASE(3);
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -328,7 +318,6 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
       wml[blk * 16 + lane] = make_float2(m_run[qb], l_run[qb]);
     }
   }
-  FM_PHASE(4);
 }
 
 // Merge of the key splits: thread = (row tile, wave, d-block, lane) of the partial layout,

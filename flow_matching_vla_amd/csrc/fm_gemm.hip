@@ -7,14 +7,6 @@
 #include "fm_common.h"
 #include "fm_kernels.h"
 
-#ifdef FM_PHASE_TIMING
-extern __device__ unsigned long long* g_phase;
-#define FM_PHASE_INIT unsigned long long* const fm_ph = g_phase
-#define FM_PHASE(i) do { if (threadIdx.x == 0 && fm_ph) ((__attribute__((address_space(1))) unsigned long long*)fm_ph)[blockIdx.x * 16 + (i)] = __builtin_amdgcn_s_memrealtime(); } while (0)
-#else
-#define FM_PHASE_INIT do { } while (0)
-#define FM_PHASE(i) do { } while (0)
-#endif
 
 namespace fm {
 
@@ -129,12 +121,13 @@ __device__ __forceinline__ f32x4 ld_dev(const Rsrc& r, uint32_t off) {
 }
 // XCD-local exchange (all parties on one XCD, which has one L2): plain stores (the vector
 // L1 writes through to L2), an arrival counter updated by atomics that execute in L2, and
-// plain loads after the reader has invalidated its own L1.
+// device-scope (sc1) loads, which miss the reader's L1 (an L1 invalidate does not serve: the
+// workgroup-scope form drops nothing, and the agent-scope form also drops the L2's lines).
 __device__ __forceinline__ void st_l2(const Rsrc& r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(V16, v), r, off, 0, 0);
 }
 __device__ __forceinline__ f32x4 ld_l2(const Rsrc& r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1));
 }
 __device__ __forceinline__ uint32_t l2_fetch_add(unsigned* p, uint32_t v) {
   uint32_t old;
@@ -144,7 +137,6 @@ __device__ __forceinline__ uint32_t l2_fetch_add(unsigned* p, uint32_t v) {
 __device__ __forceinline__ void l2_put(unsigned* p, uint32_t v) {
   __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void inv_l1() { asm volatile("buffer_inv sc0" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------
 // Epilogue over a BM x BN fp32 tile held in LDS (row stride ldc). Items are 4-column runs;
@@ -643,12 +635,13 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / WNW, wn = w % WNW;
   const int ntn = (a.N + BN - 1) / BN, ntm = (a.M + BM - 1) / BM, tiles = ntn * ntm;
-  // The grid is padded to a multiple of 8 x splits, so each XCD (workgroup b runs on XCD
-  // b mod 8) takes a contiguous range of logical items made of whole tiles: the splits of a
-  // tile are consecutive items, so they run on one XCD and exchange partial tiles through
-  // its L2. Tiles are ordered in groups of 8 row tiles walked column by column, so the tiles
-  // an XCD runs together share a few weight column tiles and activation row tiles in its L2.
-  const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
+  // The grid is padded to a multiple of 8 x splits, so each XCD takes a contiguous range of
+  // logical items made of whole tiles (xcd_range_item: the range of the XCD the workgroup runs
+  // on): the splits of a tile are consecutive items, so they run on one XCD and exchange
+  // partial tiles through its L2. Tiles are ordered in groups of 8 row tiles walked column by
+  // column, so the tiles an XCD runs together share a few weight column tiles and activation
+  // row tiles in its L2.
+  const int bid = xcd_range_item(gridDim.x);
   if (bid >= tiles * a.splits) return;
   const int split = bid % a.splits, t = bid / a.splits;
   constexpr int GM = 8;
@@ -659,8 +652,6 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
   const int kbeg = split * a.k_split;
   const int kend = min(a.K, kbeg + a.k_split);
   const int nks = (kend - kbeg) / BK;
-  FM_PHASE_INIT;
-  FM_PHASE(0);
 
   // this wave's copies: fragments f = w FPW + i; f < FA: A row block f, else W column
   // block f - FA. Per-copy lane offsets without the k part.
@@ -709,7 +700,6 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
   for (int i = 0; i < WRB; ++i)
 #pragma unroll
     for (int j = 0; j < WCB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  FM_PHASE(1);
 
   // One barrier per stage: it makes stage ks visible to every wave and also proves that
   // every wave has finished reading stage ks - 1, whose buffer the copies issued right after
@@ -720,7 +710,6 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
     wait_stages<FPW, 0, NST>(min(NST - 2, nks - 1 - ks));   // stage ks has landed
     __syncthreads();
     if (ks + NST - 1 < nks) issue(kbeg + (ks + NST - 1) * BK, (ks + NST - 1) % NST);
-    if (ks < 8) FM_PHASE(2 + ks);
     const V16* sA = lds + (ks % NST) * FS * 64;
     const V16* sB = sA + FA * 64;
     V16 af[WRB], bfr[WCB];
@@ -736,7 +725,6 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
         acc[i][j] = MT::mma(__builtin_bit_cast(frag, af[i]), __builtin_bit_cast(frag, bfr[j]), acc[i][j]);
   }
   __syncthreads();   // every wave is done with the operand stages (the epilogue reuses LDS)
-  FM_PHASE(10);
   float* C = (float*)lds;
   typedef Epilogue<T, 64, BN, NT, EPI> EP;
   // Row inputs (residual h, state x, RoPE cos/sin) of every slab are loaded before the
@@ -800,7 +788,6 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
       if (tid == 0) s_last = l2_fetch_add(a.counters + t, 1u) == (unsigned)a.splits - 1u;
       __syncthreads();
       if (!s_last) return;
-      inv_l1();
 #pragma unroll 2
       for (int q = 0; q < Q4; ++q) {
         const int it = tid + q * NT;
@@ -813,29 +800,23 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
       }
       if (tid == 0) l2_put(a.counters + t, 0u);
       __syncthreads();
-      FM_PHASE(12);
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl) {
         if (m0 + 64 * sl >= a.M) break;   // uniform
         apply_slab(sl, C + 64 * sl * LDC);
       }
-      FM_PHASE(11);
       return;
     }
   }
   // no split: slab by slab through one 64-row C buffer
-  FM_PHASE(12);
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl) {
     if (m0 + 64 * sl >= a.M) break;   // uniform
     write_slab(sl, C);
     __syncthreads();
-    if (sl == 0) FM_PHASE(13);
     apply_slab(sl, C);
     __syncthreads();
-    if (sl == 0) FM_PHASE(14);
   }
-  FM_PHASE(11);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -868,9 +849,9 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntn = (a.N + BN - 1) / BN;
   // The grid is padded to a multiple of 8 x splits and the splits of a column tile are
-  // consecutive logical items, so they run on one XCD (workgroup b runs on XCD b mod 8) and
+  // consecutive logical items of one XCD's range (xcd_range_item), so they run on one XCD and
   // exchange partial tiles through its L2.
-  const int bid = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int bid = xcd_range_item(gridDim.x);
   if (bid >= ntn * a.splits) return;
   const int tile = bid / a.splits, split = bid % a.splits;
   const int n0 = tile * BN;
@@ -883,8 +864,6 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   const int c_lo = split * span, c_hi = min(KCt, c_lo + span);
   const int nst = (c_hi - c_lo + SPC - 1) / SPC;
 
-  FM_PHASE_INIT;
-  FM_PHASE(0);
   // activation fragments: lane l reads row 16 mb + l % 16, k run l / 16 of every chunk
   const Rsrc ra = make_rsrc(a.A, a.a_bytes);
   uint32_t aoff[MB];
@@ -920,7 +899,6 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   // all loads are in flight before the first MFMA waits on one (the scheduler would
   // otherwise interleave them with the MFMAs and keep only a few outstanding)
   __builtin_amdgcn_sched_barrier(0);
-  FM_PHASE(1);
 
   f32x4 acc[MB][NB];
 #pragma unroll
@@ -957,7 +935,6 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     }
   }
   if constexpr (NORM) st.merge(a, 0, s_mean, s_rinv);
-  FM_PHASE(2);
 
   // wave partials -> LDS, summed in wave order
 #pragma unroll
@@ -980,7 +957,6 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
       for (int w2 = 0; w2 < KW; ++w2) part[q] += *(const f32x4*)(red + (w2 * BM + r) * LDR + c4 * 4);
     }
   }
-  FM_PHASE(3);
   if (a.splits > 1) {
     const Rsrc rws = make_rsrc(a.ws, a.ws_bytes);
     const uint32_t tbase = (uint32_t)tile * (uint32_t)a.splits * (BM * BN * 4);
@@ -994,7 +970,6 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     if (tid == 0) s_last = l2_fetch_add(a.counters + tile, 1u) == (unsigned)a.splits - 1u;
     __syncthreads();
     if (!s_last) return;
-    inv_l1();
 #pragma unroll
     for (int q = 0; q < Q4; ++q) {
       const int i = tid + q * NT;
@@ -1012,7 +987,6 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     }
     if (tid == 0) l2_put(a.counters + tile, 0u);
   }
-  FM_PHASE(4);
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < Q4; ++q) {
@@ -1025,7 +999,6 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   __syncthreads();
   ep.settle();
   ep.apply(a, red, LDR, 0, n0, s_mean, s_rinv);
-  FM_PHASE(5);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -67,6 +67,8 @@ struct GemmArgs {
   int col_group; long col_gstride;
 };
 constexpr long kVecPad = 1L << 18;   // floats in the zeros / ones buffers
+// Split-K arrival counters (GemmArgs::counters): one per output tile.
+constexpr int kGemmCounters = 1 << 16;
 
 enum GemmKind { GEMM_SKINNY = 0, GEMM_TILED = 1, GEMM_BIG = 2 };
 enum GemmCfg { GEMM_64x64 = 0, GEMM_128x128 = 1, GEMM_32x64 = 2 };
@@ -133,6 +135,8 @@ hipError_t prefix_k_copy(void* pool, long pool_bs, const void* src, int B, int P
 hipError_t prefix_v_copy_t(void* pool, long pool_bs, int cap, const void* src, int B, int P, int dh,
                            int elem, hipStream_t s);
 hipError_t fill_f32(float* dst, float v, long n, hipStream_t s);
+// out[b] = the XCC id workgroup b of an n-workgroup launch runs on (n <= 65536)
+hipError_t xcc_probe(uint32_t* out, int n, hipStream_t s);
 // FP8 E4M3 weights, one power-of-two scale per row: codes [N x K] bytes, scale [N], and the
 // dequantized bf16 matrix deq [N x K] (exact). src bf16 rows of stride ld; K even.
 hipError_t quantize_fp8_rows(const void* src, long ld, int N, int K, uint8_t* codes, float* scale, void* deq, hipStream_t s);

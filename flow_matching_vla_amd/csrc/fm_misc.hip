@@ -135,6 +135,15 @@ __global__ void k_rows_from_f32(T* dst, long dld, const float* src, long sld, in
     dst[r * dld + c] = from_f32<T>(src[r * sld + c] + add);
   }
 }
+__global__ void k_xcc_probe(uint32_t* out, int n) {
+  if (threadIdx.x == 0 && (int)blockIdx.x < n) out[blockIdx.x] = hw_xcc_id();
+}
+hipError_t xcc_probe(uint32_t* out, int n, hipStream_t s) {
+  if (n < 1 || n > 65536) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_xcc_probe, dim3(n), dim3(64), 0, s, out, n);
+  return hipGetLastError();
+}
+
 __global__ void k_fill(float* dst, float v, long n) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) dst[i] = v;
 }

@@ -60,6 +60,7 @@ def lib():
     P, I32, VP = C.POINTER, C.c_int32, C.c_void_p
     sig = {
         "fm_query": ([P(fm_config), P(fm_plan_info), C.c_char_p, I32], I32),
+        "fm_device_supported": ([C.c_char_p, I32, I32, C.c_char_p, I32], I32),
         "fm_weight_spec": ([P(fm_config), I32, P(C.c_char_p), P(I32), P(C.c_int64)], I32),
         "fm_create": ([P(fm_config), VP, P(VP)], I32),
         "fm_destroy": ([VP], I32),
@@ -98,7 +99,10 @@ def quantize_fp8(w):
     """The library's FP8 weight quantizer on a device bf16 [N, K] tensor: (codes uint8 [N, K],
     per-row scales fp32 [N], dequantized bf16 [N, K]), all device tensors."""
     torch = _torch()
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        raise ValueError("quantize_fp8: w must be a 2-D tensor")
     N, K = w.shape
+    check_tensor(w, "w", torch.bfloat16, (N, K))
     codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     scale = torch.empty((N,), dtype=torch.float32, device=w.device)
     deq = torch.empty_like(w)
@@ -148,6 +152,42 @@ def _check(st: int, ctx=None):
     if st != FM_OK:
         msg = lib().fm_last_error(ctx)
         raise FMError(st, msg.decode() if msg else "")
+
+
+def device_supported(gcn_arch: str, num_xcc: int, num_cus: int):
+    """(True, "") when the library can run on a device with these properties, else (False,
+    reason). Host only: no GPU is touched."""
+    buf = C.create_string_buffer(512)
+    st = lib().fm_device_supported(gcn_arch.encode() if gcn_arch is not None else None, num_xcc, num_cus, buf, 512)
+    return st == FM_OK, buf.value.decode()
+
+
+def check_tensor(t, name: str, dtype, shape, device_index=None, on_device: bool = True):
+    """Raise ValueError unless `t` is a contiguous torch tensor of `dtype` and exactly `shape`,
+    on the GPU (the context's device when device_index is given) when on_device. The C ABI
+    receives bare pointers and cannot check what they point at: a host tensor, a short buffer
+    or a strided view would make the library read or write past an allocation on the GPU."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if on_device:
+        if not t.is_cuda:
+            raise ValueError(f"{name}: must be a device tensor, got one on {t.device}")
+        if device_index is not None and t.device.index != device_index:
+            raise ValueError(f"{name}: on {t.device}, the context runs on cuda:{device_index}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(d) for d in shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def torch_dtype(code: int):
+    """The torch dtype of a config dtype code (F32 / BF16)."""
+    torch = _torch()
+    return torch.bfloat16 if code == BF16 else torch.float32
 
 
 def query(cfg: dict) -> dict:
@@ -204,6 +244,9 @@ class Context:
         self.h = h
         self._keep = []
         self._bound = (0, 0)   # (batch, prefix or context length) of the binding
+        self._robot = None     # (robot_horizon, robot_dim) of the action statistics
+        self.device_index = torch.cuda.current_device()
+        self._tdtype = torch_dtype(self.dtype)
 
     def close(self):
         if self.h:
@@ -229,6 +272,10 @@ class Context:
         """weights: name -> device tensor (config dtype, contiguous)."""
         arr = (fm_tensor * len(weights))()
         names = []
+        for n, t in weights.items():
+            # names and shapes are the library's to check (it reports expected vs got); where
+            # the data lives and how it is laid out are not visible through the pointer
+            check_tensor(t, f"weight '{n}'", self._tdtype, tuple(t.shape), self.device_index)
         for i, (n, t) in enumerate(weights.items()):
             nb = n.encode()
             names.append(nb)
@@ -248,6 +295,17 @@ class Context:
         _check(lib().fm_set_schedule(self.h, steps, batch, tp), self.h)
 
     def bind_prefix_kv(self, batch: int, prefix_len: int, k=None, v=None, context=None, state=None):
+        c, di = self._c, self.device_index
+        if k is not None or v is not None:
+            if k is None or v is None or len(k) != c.n_layers or len(v) != c.n_layers:
+                raise ValueError(f"k and v need one tensor per layer ({c.n_layers})")
+            for l in range(c.n_layers):
+                check_tensor(k[l], f"prefix k[{l}]", self._tdtype, (batch, prefix_len, 1, c.head_dim), di)
+                check_tensor(v[l], f"prefix v[{l}]", self._tdtype, (batch, prefix_len, 1, c.head_dim), di)
+        if context is not None:
+            check_tensor(context, "context", self._tdtype, (batch, prefix_len, c.ctx_dim), di)
+        if state is not None:
+            check_tensor(state, "state", _torch().float32, (batch, c.state_tokens, c.state_dim), di)
         kp = vp = None
         if k is not None:
             kp = (C.c_void_p * len(k))(*[t.data_ptr() for t in k])
@@ -319,17 +377,28 @@ class Context:
             ptrs.append(a.ctypes.data_as(C.POINTER(C.c_uint8)))
         _check(lib().fm_bind_context_masks(self.h, ptrs[0], ptrs[1]), self.h)
 
+    def chunk_shape(self):
+        """[bound batch, H, d_a]: the shape of x0, out, x and v of the bound batch."""
+        return (self._bound[0], self._c.action_horizon, self._c.action_dim)
+
+    def _check_chunk(self, t, name):
+        check_tensor(t, name, _torch().float32, self.chunk_shape(), self.device_index)
+
     def denoise(self, x0, steps: int, out=None):
         torch = _torch()
+        self._check_chunk(x0, "x0")
         if out is None:
             out = torch.empty_like(x0)
+        self._check_chunk(out, "out")
         _check(lib().fm_denoise(self.h, _ptr(x0), steps, _ptr(out)), self.h)
         return out
 
     def step_velocity(self, x, k: int, v=None):
         torch = _torch()
+        self._check_chunk(x, "x")
         if v is None:
             v = torch.empty_like(x)
+        self._check_chunk(v, "v")
         _check(lib().fm_step_velocity(self.h, _ptr(x), k, _ptr(v)), self.h)
         return v
 
@@ -347,12 +416,17 @@ class Context:
         fp = C.POINTER(C.c_float)
         _check(lib().fm_set_action_stats(self.h, kind, robot_horizon, robot_dim, lo.ctypes.data_as(fp),
                                          hi.ctypes.data_as(fp)), self.h)
+        self._robot = (robot_horizon, robot_dim)
 
     def unnormalize(self, x, robot_horizon: int, robot_dim: int, out=None):
         """Model-space chunk (device fp32 [B, H, d_a]) -> robot units [B, robot_horizon, robot_dim]."""
         torch = _torch()
+        if self._robot is not None and (robot_horizon, robot_dim) != self._robot:
+            raise ValueError(f"robot horizon / dim {(robot_horizon, robot_dim)}, the action statistics hold {self._robot}")
+        self._check_chunk(x, "x")
         if out is None:
             out = torch.empty((x.shape[0], robot_horizon, robot_dim), dtype=torch.float32, device=x.device)
+        check_tensor(out, "out", torch.float32, (self._bound[0], robot_horizon, robot_dim), self.device_index)
         _check(lib().fm_unnormalize(self.h, _ptr(x), _ptr(out)), self.h)
         return out
 
@@ -365,6 +439,7 @@ class Context:
     def step_trace(self, x, k: int):
         torch = _torch()
         c = self.cfg
+        self._check_chunk(x, "x")
         rows = x.shape[0] * (c.get("state_tokens", 0) + c["action_horizon"])
         tr = torch.empty((c["n_layers"] + 1, rows, c["hidden"]), dtype=torch.float32, device=x.device)
         v = torch.empty_like(x)
@@ -380,8 +455,10 @@ UNNORM_QUANTILE_EPS, UNNORM_QUANTILE_CLIP = 0, 1
 def profile_loop(ctx: "Context", x0, steps: int, role: str, out=None):
     """Eager run of the loop with events around every launch of `role`; (total ms, launches)."""
     torch = _torch()
+    ctx._check_chunk(x0, "x0")
     if out is None:
         out = torch.empty_like(x0)
+    ctx._check_chunk(out, "out")
     ms, n = C.c_float(), C.c_int32()
     _check(lib().fm_profile_loop(ctx.h, _ptr(x0), steps, _ptr(out), OP_ROLES[role], C.byref(ms), C.byref(n)), ctx.h)
     return ms.value, n.value
@@ -389,9 +466,15 @@ def profile_loop(ctx: "Context", x0, steps: int, role: str, out=None):
 
 def op_linear(A, W, bias=None, act: int = 0, out_f32: bool = False):
     torch = _torch()
+    if not isinstance(A, torch.Tensor) or not isinstance(W, torch.Tensor) or A.dim() != 2 or W.dim() != 2:
+        raise ValueError("op_linear: A and W must be 2-D tensors")
     dt = BF16 if A.dtype == torch.bfloat16 else F32
     M, K = A.shape
     N = W.shape[0]
+    check_tensor(A, "A", torch_dtype(dt), (M, K))
+    check_tensor(W, "W", torch_dtype(dt), (N, K), A.device.index)
+    if bias is not None:
+        check_tensor(bias, "bias", torch.float32, (N,), A.device.index)
     out = torch.empty((M, N), dtype=torch.float32 if out_f32 else A.dtype, device=A.device)
     s = torch.cuda.current_stream().cuda_stream
     _check(lib().fm_op_linear(dt, M, N, K, _ptr(A), _ptr(W), _ptr(bias), act, _ptr(out), int(out_f32), C.c_void_p(s)))
@@ -401,9 +484,14 @@ def op_linear(A, W, bias=None, act: int = 0, out_f32: bool = False):
 def op_attention(q, k, v):
     """q [B, Tq, nh, dh]; k, v [B, nkv, nk, dh]."""
     torch = _torch()
+    if not all(isinstance(t, torch.Tensor) and t.dim() == 4 for t in (q, k, v)):
+        raise ValueError("op_attention: q, k and v must be 4-D tensors")
     dt = BF16 if q.dtype == torch.bfloat16 else F32
     B, Tq, nh, dh = q.shape
     nkv, nk = k.shape[1], k.shape[2]
+    check_tensor(q, "q", torch_dtype(dt), (B, Tq, nh, dh))
+    check_tensor(k, "k", torch_dtype(dt), (B, nkv, nk, dh), q.device.index)
+    check_tensor(v, "v", torch_dtype(dt), (B, nkv, nk, dh), q.device.index)
     o = torch.empty_like(q)
     s = torch.cuda.current_stream().cuda_stream
     _check(lib().fm_op_attention(dt, B, Tq, nh, nkv, nk, dh, _ptr(q), _ptr(k), _ptr(v), _ptr(o), C.c_void_p(s)))

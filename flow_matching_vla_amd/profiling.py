@@ -78,7 +78,7 @@ def source_hash(files: list[str]) -> str:
     return h.hexdigest()
 
 
-LOOP_SOURCES = ["csrc/fm_persist.hip", "csrc/fm_persist.h", "csrc/fm_common.h"]
+LOOP_SOURCES = ["csrc/fm_xloop.hip", "csrc/fm_xloop.h", "csrc/fm_common.h"]
 
 
 def loop_source_hash() -> str:

@@ -108,22 +108,44 @@ fm_status fm_query(const fm_config* cfg, fm_plan_info* info, char* msg, int32_t 
  * shape. Host only. Returns FM_ERR_INVALID_ARG for i out of range. */
 fm_status fm_weight_spec(const fm_config* cfg, int32_t i, const char** name, int32_t* ndim, int64_t shape[4]);
 
-/* Create a context on the current HIP device. hip_stream: a hipStream_t (NULL = the
- * default stream) on which all of this context's work runs. Allocates the pool and the
- * activation buffers for max_batch. */
+/* Whether a device can run this library, from its properties alone (host only, no GPU
+ * needed): gcn_arch the agent name (hipDeviceProp_t::gcnArchName), num_xcc the XCD count
+ * (hipDeviceAttributeNumberOfXccs), num_cus the compute units. The split-K GEMMs and the loop
+ * kernel exchange partial results through one XCD's L2 and rely on the whole-GPU dispatch
+ * that deals a launch's workgroups round-robin over the XCDs (each residue of the workgroup
+ * index mod 8 on one XCD), so a gfx950 with 8 XCDs (a whole MI355X) is required;
+ * FM_ERR_UNSUPPORTED with a message in msg (may be NULL) otherwise, and FM_ERR_INVALID_ARG for
+ * a NULL gcn_arch. fm_create applies this check to its device, and also launches a probe
+ * whose workgroups report their XCD, refusing the device unless the placement is round-robin.
+ * The loop kernel verifies it again on every launch (see fm_loop_status). */
+fm_status fm_device_supported(const char* gcn_arch, int32_t num_xcc, int32_t num_cus, char* msg, int32_t msg_len);
+
+/* Create a context on the current HIP device (refused with FM_ERR_UNSUPPORTED unless
+ * fm_device_supported accepts it). hip_stream: a hipStream_t (NULL = the default stream) on
+ * which all of this context's work runs, in order (pi0.5 Design, "Runtime boundary": one
+ * caller stream per engine, and a context is not safe to share between threads). Allocates
+ * the pool and the activation buffers for max_batch. */
 fm_status fm_create(const fm_config* cfg, void* hip_stream, fm_ctx** out);
 
-/* Synchronize the context stream and release every device allocation. NULL is a no-op. */
+/* Synchronize the context stream and release every device allocation (GR00T N1.7, "Who
+ * runs what": the runner owns execution and the lifetime of its buffers). NULL is a no-op. */
 fm_status fm_destroy(fm_ctx* ctx);
 
-/* Message of the last failed call on ctx (or of the last failed fm_create / fm_query when
- * ctx is NULL). Valid until the next call on the same context. */
+/* Message of the last failed call on ctx (or of the last failed fm_create / fm_query /
+ * fm_device_supported / kernel-level call when ctx is NULL). Valid until the next call on the
+ * same context. What this build does not implement is refused with a status and a message
+ * instead of being run (pi0.5 Design, "Runtime boundary": an unimplemented configuration is
+ * refused at load rather than run; GR00T N1.7, "Who runs what": a mismatch fails at load).
+ * That a device error poisons the context is this library's own rule. */
 const char* fm_last_error(const fm_ctx* ctx);
 
 /* Load all weights (fm_weight_spec lists names and shapes). Each tensor is validated
  * (name, dtype, rank, shape: a mismatch names expected vs got and returns FM_ERR_SHAPE)
- * and then copied into the library's layout. Biases are converted to fp32. Calling it
- * again replaces the weights and invalidates schedule and captured graphs. */
+ * and then copied into the library's layout; nothing is loaded that does not match, and no
+ * tensor is silently cast, reshaped or skipped (GR00T N1.7, "Checkpoint": a checkpoint whose
+ * tensors do not fit the build is refused at load; pi0.5 Design, "Component contract": the
+ * expert's tensor names and shapes are part of the contract). Biases are converted to fp32.
+ * Calling it again replaces the weights and invalidates schedule and captured graphs. */
 fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* tensors, int32_t n);
 
 /* Build the per-step modulation table for `steps` Euler steps and `batch` requests
@@ -293,10 +315,12 @@ enum { FM_LOOP_AUTO = 0, FM_LOOP_GRAPH = 1 };
 fm_status fm_set_loop_mode(fm_ctx* ctx, int32_t mode);
 
 /* Synchronize the context stream. *persistent = 1 when the loop kernel serves the current
- * weights, schedule and binding (0 otherwise). *fault is the loop kernel's fault word: 0,
- * or nonzero when one of its bounded grid-barrier waits expired since the last query (its
- * results are then invalid; the context is poisoned and FM_ERR_DEVICE is returned). Either
- * pointer may be NULL. */
+ * weights, schedule and binding (0 otherwise). *fault: 0, or what went wrong since the last
+ * query: 1, 2, 3 or 5 when one of the loop kernel's bounded waits expired (barrier gather,
+ * release, split-K, attention split); 6 when the loop kernel's workgroups of one residue of
+ * blockIdx.x mod 8 did not all run on one XCD. Results since then are invalid: the context is poisoned and FM_ERR_DEVICE is returned (the
+ * words are cleared). A loop-kernel launch that starts with its fault word set writes NaN to
+ * its output and does nothing else. Either pointer may be NULL. */
 fm_status fm_loop_status(fm_ctx* ctx, int32_t* persistent, uint32_t* fault);
 
 /* Run the same loop as fm_denoise, eagerly, with a hipEvent pair on the context stream

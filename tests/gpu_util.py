@@ -16,7 +16,7 @@ def say(*a):
 class Case:
     """One workload: host weights/inputs, the oracle's bound state, and a GPU context."""
 
-    def __init__(self, cfg, W=None, I=None, steps=None, tau=None, vis=None):
+    def __init__(self, cfg, W=None, I=None, steps=None, tau=None, vis=None, oracle_dtype=np.float64):
         import torch
         from flow_matching_vla_amd import fm
 
@@ -43,11 +43,14 @@ class Case:
         torch.cuda.synchronize()
         del wt
         self.x0 = torch.from_numpy(self.I["x0"]).cuda()
-        # oracle state (float64)
-        self.w64 = oracle.cast_weights(self.W)
+        # oracle state (float64; float32 for the largest batches, whose oracle agrees with the
+        # float64 one to ~1e-6, far inside the 1e-2 bar)
+        self.odt = oracle_dtype
+        self.w64 = oracle.cast_weights(self.W, oracle_dtype)
         self.set_visibility(vis)
-        self.tau64 = oracle.schedule(self.steps, tau)
+        self.tau64 = oracle.schedule(self.steps, tau, dtype=self.odt)
         self.table, self.tb = oracle.modulation_table(cfg, self.w64, self.tau64) if self.steps else (None, None)
+        self._table_r = None   # the bf16 reading's table, on first use
 
     def set_visibility(self, vis):
         """Per-request visibility on both sides: {"prefix_lens"} or {"text_mask", "image_mask"}
@@ -58,11 +61,19 @@ class Case:
         else:
             self.ctx.bind_context_masks(vis.get("text_mask"), vis.get("image_mask"))
         self.vis = vis
-        self.bound = oracle.bind(self.cfg, self.w64, dict(self.I, **vis))
+        self.bound = oracle.bind(self.cfg, self.w64, dict(self.I, **vis), dtype=self.odt)
 
-    def oracle_velocity(self, x, k, trace=None, requests=None):
+    def oracle_velocity(self, x, k, trace=None, requests=None, round_acts=False):
+        """The oracle's velocity at x for step k (of the given requests only); round_acts: the
+        bf16 reading (its own modulation table, computed on first use)."""
+        table, tb = self.table, self.tb
+        if round_acts:
+            if self._table_r is None:
+                self._table_r = oracle.modulation_table(self.cfg, self.w64, self.tau64, round_acts=True)
+            table, tb = self._table_r
+        x = np.asarray(x, self.odt)
         if requests is None:
-            return oracle.velocity(self.cfg, self.w64, self.bound, np.asarray(x, np.float64), self.table, self.tb, k, trace)
+            return oracle.velocity(self.cfg, self.w64, self.bound, x, table, tb, k, trace, round_acts=round_acts)
         cfg = dict(self.cfg, batch=len(requests))
         bound = {}
         for key, val in self.bound.items():
@@ -74,7 +85,7 @@ class Case:
                 bound[key] = val[requests]
             else:
                 bound[key] = val
-        return oracle.velocity(cfg, self.w64, bound, np.asarray(x, np.float64)[requests], self.table, self.tb, k, trace)
+        return oracle.velocity(cfg, self.w64, bound, x[requests], table, tb, k, trace, round_acts=round_acts)
 
     def gpu_velocity(self, x_np, k):
         import torch
@@ -93,23 +104,43 @@ class Case:
         self.ctx.close()
 
 
-def teacher_forced(case, tol_v, requests=None, layers_trace=False):
-    """GPU velocity at the GPU's own trajectory x_k vs the oracle velocity at the same x_k."""
+def per_request(got, ref, tol_rel, tol_inf, what):
+    """e_rel (vla.cpp Eq. (5)) of every request on its own, each within tol_rel, and its largest
+    element error within tol_inf of the request's largest reference magnitude; returns the
+    worst (e_rel, e_inf / max|ref|)."""
+    worst_rel, worst_inf = 0.0, 0.0
+    for b in range(ref.shape[0]):
+        er = oracle.e_rel(got[b], ref[b])
+        ei = oracle.e_inf(got[b], ref[b]) / float(np.max(np.abs(ref[b])))
+        worst_rel, worst_inf = max(worst_rel, er), max(worst_inf, ei)
+        assert er <= tol_rel, (what, b, er)
+        assert ei <= tol_inf, (what, b, ei)
+    return worst_rel, worst_inf
+
+
+def teacher_forced(case, tol_v, requests=None, layers_trace=False, steps=None, tol_inf=None, round_acts=False):
+    """GPU velocity at the GPU's own trajectory x_k vs the oracle velocity at the same x_k, for
+    the first `steps` steps (all by default). With tol_inf, every request is checked on its
+    own (per_request); else the compared requests together."""
     x = case.I["x0"].astype(np.float32)
     worst = 0.0
-    for k in range(case.steps):
+    for k in range(case.steps if steps is None else steps):
         v_gpu = case.gpu_velocity(x, k)
-        v_ref = case.oracle_velocity(x, k, requests=requests)
+        v_ref = case.oracle_velocity(x, k, requests=requests, round_acts=round_acts)
         vg = v_gpu if requests is None else v_gpu[requests]
         e = oracle.e_rel(vg, v_ref)
         say(f"  step {k}: velocity e_rel {e:.3e} e_inf {oracle.e_inf(vg, v_ref):.3e}")
+        if tol_inf is not None:
+            wr, wi = per_request(vg, v_ref, tol_v, tol_inf, f"velocity step {k}")
+            say(f"  step {k}: worst request e_rel {wr:.3e}, worst e_inf / max|v| {wi:.3e}")
+            e = wr
         worst = max(worst, e)
         x = (x + np.float32(case.tau64[k + 1] - case.tau64[k]) * v_gpu).astype(np.float32)
     assert worst <= tol_v, worst
     return worst
 
 
-def chunk(case, tol_x, requests=None):
+def chunk(case, tol_x, requests=None, tol_inf=None):
     x_gpu = case.gpu_denoise()
     I = case.I
     if requests is not None:
@@ -118,11 +149,14 @@ def chunk(case, tol_x, requests=None):
                                     ({i: a[requests] for i, a in v.items()} if isinstance(v, dict) else
                                      (v[requests] if isinstance(v, np.ndarray) else v)))
                                 for k, v in case.bound.items()},
-                               I["x0"][requests], case.steps, tau=case.tau)
+                               I["x0"][requests], case.steps, tau=case.tau, dtype=case.odt)
         x_gpu = x_gpu[requests]
     else:
-        x_ref = oracle.denoise(case.cfg, case.w64, case.bound, I["x0"], case.steps, tau=case.tau)
+        x_ref = oracle.denoise(case.cfg, case.w64, case.bound, I["x0"], case.steps, tau=case.tau, dtype=case.odt)
     e = oracle.e_rel(x_gpu, x_ref)
     say(f"  chunk e_rel {e:.3e} e_inf {oracle.e_inf(x_gpu, x_ref):.3e}")
+    if tol_inf is not None:
+        wr, wi = per_request(x_gpu, x_ref, tol_x, tol_inf, "chunk")
+        say(f"  chunk: worst request e_rel {wr:.3e}, worst e_inf / max|x| {wi:.3e}")
     assert e <= tol_x, e
     return x_gpu

@@ -83,18 +83,63 @@ def test_loop_kernel_matches_graph_path_pi05_b1():
 
 
 def test_loop_kernel_leaves_prefix_pool_untouched():
+    # the pool's prefix rows [0, P) of every layer, read through the pool's own memory before
+    # and after two loops on the same binding (no re-bind in between), must be bitwise equal:
+    # the loop kernel writes only the chunk's own slots
     import torch
     cfg = wl.workload("pi05_b1", n_layers=2, steps=3)
     c = Case(cfg)
+    assert c.ctx.loop_status()[0]
+    P = cfg["prefix_len"]
+
+    def rows():
+        out = []
+        for l in range(cfg["n_layers"]):
+            kt, vt = c.ctx.prefix_pool_views(l)
+            cols = fm.pool_v_slot(np.arange(P), cfg["dtype"])
+            out.append((kt[0, :P].clone(), vt[0][:, torch.from_numpy(cols).cuda()].clone()))
+        torch.cuda.synchronize()
+        return out
+
+    before = rows()
     a = c.gpu_denoise()
-    # rebinding the same prefix and running again must reproduce the chunk bitwise: the
-    # loop kernel never writes the bound K/V
-    L = cfg["n_layers"]
-    k = [fm.to_device(c.I[f"prefix.k.{l}"], cfg["dtype"]) for l in range(L)]
-    v = [fm.to_device(c.I[f"prefix.v.{l}"], cfg["dtype"]) for l in range(L)]
-    c.ctx.bind_prefix_kv(1, cfg["prefix_len"], k, v)
-    torch.cuda.synchronize()
     b = c.gpu_denoise()
+    after = rows()
+    for (k0, v0), (k1, v1) in zip(before, after):
+        assert torch.equal(k0.view(torch.int16), k1.view(torch.int16))
+        assert torch.equal(v0.view(torch.int16), v1.view(torch.int16))
     np.testing.assert_array_equal(a, b)
     assert c.ctx.loop_status()[1] == 0
+    c.close()
+
+
+@pytest.mark.parametrize("mode", [fm.LOOP_AUTO, fm.LOOP_GRAPH])
+def test_rebinding_another_batch_on_one_context(mode):
+    # one context bound to batch 2 (horizon 16: 32 action rows), run, then bound to batch 1 and
+    # batch 2 again: every binding of the context must match the oracle. The loop kernel places
+    # its per-step buffers by the bound batch, so a new batch moves them onto bytes the previous
+    # layout wrote (statistics among them).
+    import torch
+    cfg = wl.workload("pi05_b1", n_layers=2, steps=2, batch=2, action_horizon=16, prefix_len=100)
+    c = Case(cfg)
+    c.ctx.set_loop_mode(mode)
+    assert c.ctx.loop_status()[0] == (mode == fm.LOOP_AUTO)
+    L, dt = cfg["n_layers"], cfg["dtype"]
+    for B in (2, 1, 2):
+        k = [fm.to_device(c.I[f"prefix.k.{l}"][:B], dt) for l in range(L)]
+        v = [fm.to_device(c.I[f"prefix.v.{l}"][:B], dt) for l in range(L)]
+        c.ctx.bind_prefix_kv(B, cfg["prefix_len"], k, v)
+        c.ctx.set_schedule(c.steps, B)
+        x0 = torch.from_numpy(np.ascontiguousarray(c.I["x0"][:B])).cuda()
+        got = c.ctx.denoise(x0, c.steps)
+        torch.cuda.synchronize()
+        assert c.ctx.loop_status() == (mode == fm.LOOP_AUTO, 0)
+        got = got.cpu().numpy()
+        ref = oracle.denoise(dict(cfg, batch=B), c.w64, {**c.bound, "k": [a[:B] for a in c.bound["k"]],
+                                                         "v": [a[:B] for a in c.bound["v"]],
+                                                         "prefix_lens": c.bound["prefix_lens"][:B]},
+                             c.I["x0"][:B], c.steps, tau=c.tau)
+        e = oracle.e_rel(got, ref)
+        say(f"  mode {mode}, batch {B}: chunk e_rel {e:.3e}")
+        assert np.all(np.isfinite(got)) and e <= 2e-2, e
     c.close()

@@ -121,23 +121,49 @@ def test_pi05_b1():
 
 def test_pi05_sharp_attention_two_layers():
     # Larger query and output weights make the softmax peaky and the velocity lean on
-    # attention. Logits reach ~20 here, so the bf16 rounding of q and k (relative 2^-9)
-    # moves them by ~0.04 and the softmax weights by a few percent: the bound is the bf16
-    # workloads' 1e-2 widened by the 8x query scale (3e-2), not a kernel allowance.
+    # attention: logits reach ~20, so the bf16 rounding of the chunk's q and k (relative 2^-9)
+    # moves them by ~0.04 and the softmax weights by a few percent. Against the oracle's bf16
+    # reading of the attention (q, k, v and the attention output rounded where formed,
+    # round_acts) the kernels must meet the bf16 bar of 1e-2; against the exact oracle the gap
+    # that this rounding alone opens is logged and bounded by 3e-2.
     cfg = wl.workload("pi05_b1", n_layers=2, steps=3)
     W = wl.make_weights(cfg)
     for l in range(2):
         W[f"layers.{l}.q.w"] = wl.round_bf16(W[f"layers.{l}.q.w"] * 8)
         W[f"layers.{l}.o.w"] = wl.round_bf16(W[f"layers.{l}.o.w"] * 8)
     c = Case(cfg, W=W)
-    _teacher_forced(c, 3e-2)
+    w_read = _teacher_forced(c, 1e-2, round_acts=True)
+    w_exact = _teacher_forced(c, 3e-2)
+    say(f"  sharp attention: worst velocity e_rel {w_read:.3e} vs the bf16 reading, {w_exact:.3e} vs exact")
     c.close()
 
 
-def test_pi05_b8_sampled_requests():
-    c = Case(wl.workload("pi05_b8"))
-    _teacher_forced(c, 1e-2, requests=[0, 5])
-    _chunk(c, 2e-2, requests=[0, 5])
+def _permuted_rebind_is_bitwise(c, perm):
+    """Bind the same requests in another order on the same context: every request's chunk is
+    computed by the same kernels with the same plans, so the outputs permute bitwise."""
+    import torch
+    from flow_matching_vla_amd import fm
+    cfg = c.cfg
+    a = c.gpu_denoise()
+    L, B, dt = cfg["n_layers"], cfg["batch"], cfg["dtype"]
+    k = [fm.to_device(c.I[f"prefix.k.{l}"][perm], dt) for l in range(L)]
+    v = [fm.to_device(c.I[f"prefix.v.{l}"][perm], dt) for l in range(L)]
+    c.ctx.bind_prefix_kv(B, cfg["prefix_len"], k, v)
+    del k, v
+    x0p = torch.from_numpy(np.ascontiguousarray(c.I["x0"][perm])).cuda()
+    b = c.ctx.denoise(x0p, c.steps)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(b.cpu().numpy(), a[perm])
+    say(f"  permuted requests {list(perm[:8])}...: chunks permute bitwise")
+
+
+def test_pi05_b8_every_request():
+    # full-size batch 8: every request on its own against the oracle (two teacher-forced
+    # steps and the whole chunk), then a permuted binding on the same context
+    c = Case(wl.workload("pi05_b8"), oracle_dtype=np.float32)
+    _teacher_forced(c, 1e-2, steps=2, tol_inf=5e-2)
+    _chunk(c, 2e-2, tol_inf=2e-2)
+    _permuted_rebind_is_bitwise(c, np.array([5, 0, 7, 2, 1, 6, 3, 4]))
     c.close()
 
 
@@ -148,8 +174,12 @@ def test_dit_b1():
     c.close()
 
 
-def test_pi05_b64_sampled_requests():
-    c = Case(wl.workload("pi05_b64"))
-    _teacher_forced(c, 1e-2, requests=[0, 37, 63])
-    _chunk(c, 2e-2, requests=[0, 63])
+@pytest.mark.timeout(900)
+def test_pi05_b64_every_request():
+    # full-size batch 64, prefix 1024: every request on its own against the (float32) oracle,
+    # two teacher-forced steps and the whole chunk, then a permuted binding on the same context
+    c = Case(wl.workload("pi05_b64"), oracle_dtype=np.float32)
+    _teacher_forced(c, 1e-2, steps=2, tol_inf=5e-2)
+    _chunk(c, 2e-2, tol_inf=2e-2)
+    _permuted_rebind_is_bitwise(c, np.random.default_rng(64).permutation(64))
     c.close()

@@ -102,3 +102,60 @@ def test_pool_layout_helpers_are_permutations():
     assert sorted(s.tolist()) == j.tolist()
     assert np.array_equal(s // 32, j // 32)
     assert np.array_equal(fm.pool_v_slot(j, fm.F32), j)
+
+
+# ----------------------------------------------------------------------------- argument checks
+def test_check_tensor_rejects_what_a_pointer_cannot_show(lib):
+    """The binding's argument check (runs before any library call that takes a pointer)."""
+    import torch
+    from flow_matching_vla_amd import fm
+    x = torch.zeros((2, 50, 32), dtype=torch.float32)
+    # host memory is refused outright
+    with pytest.raises(ValueError, match="device tensor"):
+        fm.check_tensor(x, "x0", torch.float32, (2, 50, 32))
+    # the remaining checks, independent of where the tensor lives
+    fm.check_tensor(x, "x0", torch.float32, (2, 50, 32), on_device=False)
+    with pytest.raises(ValueError, match="dtype"):
+        fm.check_tensor(x.to(torch.bfloat16), "x0", torch.float32, (2, 50, 32), on_device=False)
+    with pytest.raises(ValueError, match="shape"):
+        fm.check_tensor(x[:1], "x0", torch.float32, (2, 50, 32), on_device=False)   # a batch-1 x0 on a batch-2 binding
+    with pytest.raises(ValueError, match="shape"):
+        fm.check_tensor(x, "x0", torch.float32, (2, 50, 7), on_device=False)
+    with pytest.raises(ValueError, match="contiguous"):
+        fm.check_tensor(x.transpose(0, 1).contiguous().transpose(0, 1), "x0", torch.float32, (2, 50, 32), on_device=False)
+    with pytest.raises(ValueError, match="torch tensor"):
+        fm.check_tensor(np.zeros((2, 50, 32), np.float32), "x0", torch.float32, (2, 50, 32), on_device=False)
+    # prefix K of one layer: [batch, prefix_len, 1, head_dim] in the config dtype
+    k = torch.zeros((1, 816, 1, 256), dtype=torch.bfloat16)
+    fm.check_tensor(k, "k", fm.torch_dtype(fm.BF16), (1, 816, 1, 256), on_device=False)
+    with pytest.raises(ValueError, match="shape"):
+        fm.check_tensor(k[:, :800], "k", fm.torch_dtype(fm.BF16), (1, 816, 1, 256), on_device=False)
+
+
+def test_kernel_level_helpers_refuse_host_tensors(lib):
+    import torch
+    from flow_matching_vla_amd import fm
+    a = torch.zeros((64, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        fm.op_linear(a, a)
+    q = torch.zeros((1, 4, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensor"):
+        fm.op_attention(q, q, q)
+    with pytest.raises(ValueError, match="device tensor"):
+        fm.quantize_fp8(a)
+
+
+@pytest.mark.parametrize("arch,xcc,cus,ok", [
+    ("gfx950", 8, 256, True),
+    ("gfx950:sramecc+:xnack-", 8, 256, True),
+    ("gfx950", 1, 32, False),    # a compute partition of one XCD: the exchanges' placement does not hold
+    ("gfx950", 4, 128, False),
+    ("gfx942", 8, 304, False),
+    ("gfx950", 8, 252, False),
+])
+def test_device_precondition(lib, arch, xcc, cus, ok):
+    from flow_matching_vla_amd import fm
+    got, msg = fm.device_supported(arch, xcc, cus)
+    assert got == ok, msg
+    if not ok:
+        assert msg
