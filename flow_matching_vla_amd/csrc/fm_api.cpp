@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1656,6 +1657,95 @@ fm_status fm_op_attention(int32_t dtype, int32_t B, int32_t Tq, int32_t nh, int3
   if (vt) (void)hipFree(vt);
   if (ws) (void)hipFree(ws);
   if (e != hipSuccess) { g_err = fmt("fm_op_attention: %s", hipGetErrorString(e)); return FM_ERR_DEVICE; }
+  return FM_OK;
+}
+
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Attention without allocation: the transposed V plane and the split partials of
+// fm_op_attention live in one file-scope device array (one copy per GPU, held until the process
+// ends). Host code never passes the array's name to a kernel: its address on the current device
+// comes from hipGetSymbolAddress, taken once per device on the first call there.
+// ---------------------------------------------------------------------------------------
+
+namespace {
+constexpr size_t kNoAllocScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices];
+int g_scratch_cus[kNoAllocMaxDevices];
+
+// this device's copy of `scratch` and its CU count (hipGetSymbolAddress with the device current)
+hipError_t scratch_of_current_device(void** ptr, int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_cus[dev] = prop.multiProcessorCount;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *cus = g_scratch_cus[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+fm_status fm_op_attention_noalloc(int32_t dtype, int32_t B, int32_t Tq, int32_t nh, int32_t nkv, int32_t nk,
+                                  int32_t dh, const void* q, const void* k, const void* v, void* o, void* stream) {
+  const int elem = dtype == FM_BF16 ? ET_BF16 : ET_F32;
+  if ((dtype != FM_F32 && dtype != FM_BF16) || B < 1 || Tq < 1 || nh < 1 || nk < 1 || (nkv != 1 && nkv != nh) ||
+      !q || !k || !v || !o || (dh != 64 && dh != 128 && dh != 256) || (dtype == FM_F32 && dh == 256)) {
+    g_err = "fm_op_attention_noalloc: bad arguments";
+    return FM_ERR_INVALID_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  void* base = nullptr;
+  int cus = 0;
+  hipError_t e = scratch_of_current_device(&base, &cus);
+  if (e != hipSuccess) { g_err = fmt("fm_op_attention_noalloc: scratch address: %s", hipGetErrorString(e)); return FM_ERR_DEVICE; }
+  const size_t esz = elem == ET_BF16 ? 2 : 4;
+  const int kpad = (int)round_up(nk, 64);
+  AttnArgs at;
+  memset(&at, 0, sizeof at);
+  at.q = q; at.q_bs = (long)Tq * nh * dh; at.q_rs = (long)nh * dh;
+  at.k = k; at.k_bs = (long)nkv * nk * dh; at.k_rs = dh; at.k_hs = (long)nk * dh;
+  at.o = o; at.o_bs = at.q_bs; at.o_rs = at.q_rs;
+  at.v_bs = (long)nkv * dh * kpad; at.v_hs = (long)dh * kpad; at.v_ds = kpad;
+  at.B = B; at.Tq = Tq; at.n_heads = nh; at.heads_per_kv = nh / nkv; at.n_keys = nk; at.dh = dh;
+  at.k_len = (long)B * nkv * nk * dh; at.v_len = (long)B * nkv * dh * kpad;
+  at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  attn_plan(at, elem, cus);
+  // scratch layout: the V plane, then (256-byte aligned) the split partials
+  const size_t vt_bytes = (size_t)B * nkv * dh * kpad * esz;
+  const size_t ws_off = (size_t)round_up((long)vt_bytes, 256);
+  const size_t need = ws_off + attn_ws_bytes(at);
+  if (need > kNoAllocScratchBytes) {
+    g_err = fmt("fm_op_attention_noalloc: needs %zu bytes of scratch, more than its fixed %zu", need,
+                kNoAllocScratchBytes);
+    return FM_ERR_INVALID_ARG;
+  }
+  char* sc = (char*)base;
+  at.vt = sc;
+  at.ws = attn_ws_bytes(at) ? (float*)(sc + ws_off) : nullptr;
+  // the plane's padding keys must read zero (a fill kernel: this call may be captured in a graph)
+  e = fill_f32((float*)sc, 0.f, (long)(vt_bytes / 4), s);
+  if (e == hipSuccess) e = prefix_v_copy_t(sc, (long)dh * kpad, kpad, v, B * nkv, nk, dh, elem, s);
+  if (e == hipSuccess) e = attn_launch(at, elem, s);
+  if (e != hipSuccess) { g_err = fmt("fm_op_attention_noalloc: %s", hipGetErrorString(e)); return FM_ERR_DEVICE; }
   return FM_OK;
 }
 

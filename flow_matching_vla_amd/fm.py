@@ -82,6 +82,7 @@ def lib():
         "fm_unnormalize": ([VP, VP, VP], I32),
         "fm_op_linear": ([I32, I32, I32, I32, VP, VP, VP, I32, VP, I32, VP], I32),
         "fm_op_attention": ([I32, I32, I32, I32, I32, I32, I32, VP, VP, VP, VP, VP], I32),
+        "fm_op_attention_noalloc": ([I32, I32, I32, I32, I32, I32, I32, VP, VP, VP, VP, VP], I32),
         "fm_op_quantize_fp8": ([I32, I32, VP, VP, VP, VP, VP], I32),
         "fm_set_weight_format": ([VP, I32], I32),
     }
@@ -495,4 +496,23 @@ def op_attention(q, k, v):
     o = torch.empty_like(q)
     s = torch.cuda.current_stream().cuda_stream
     _check(lib().fm_op_attention(dt, B, Tq, nh, nkv, nk, dh, _ptr(q), _ptr(k), _ptr(v), _ptr(o), C.c_void_p(s)))
+    return o
+
+
+def op_attention_noalloc(q, k, v, o):
+    """op_attention into the caller's o, with the library's fixed scratch: no allocation and no
+    synchronization (the work is enqueued on torch's current stream)."""
+    torch = _torch()
+    if not all(isinstance(t, torch.Tensor) and t.dim() == 4 for t in (q, k, v, o)):
+        raise ValueError("op_attention_noalloc: q, k, v and o must be 4-D tensors")
+    dt = BF16 if q.dtype == torch.bfloat16 else F32
+    B, Tq, nh, dh = q.shape
+    nkv, nk = k.shape[1], k.shape[2]
+    check_tensor(q, "q", torch_dtype(dt), (B, Tq, nh, dh))
+    check_tensor(k, "k", torch_dtype(dt), (B, nkv, nk, dh), q.device.index)
+    check_tensor(v, "v", torch_dtype(dt), (B, nkv, nk, dh), q.device.index)
+    check_tensor(o, "o", torch_dtype(dt), (B, Tq, nh, dh), q.device.index)
+    s = torch.cuda.current_stream().cuda_stream
+    _check(lib().fm_op_attention_noalloc(dt, B, Tq, nh, nkv, nk, dh, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                         C.c_void_p(s)))
     return o

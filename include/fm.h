@@ -345,6 +345,17 @@ fm_status fm_op_linear(int32_t dtype, int32_t M, int32_t N, int32_t K, const voi
                        const float* bias, int32_t act, void* out, int32_t out_f32, void* hip_stream);
 fm_status fm_op_attention(int32_t dtype, int32_t B, int32_t Tq, int32_t n_heads, int32_t n_kv, int32_t n_keys,
                           int32_t dh, const void* q, const void* k, const void* v, void* o, void* hip_stream);
+/* fm_op_attention_noalloc: fm_op_attention for callers that cannot allocate device memory
+ *   (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ *   Same arguments, kernels and results as fm_op_attention; it calls no hipMalloc / hipFree and
+ *   does not synchronize: the work is enqueued on hip_stream. Its scratch (the transposed V
+ *   plane, B * n_kv * dh * round_up(n_keys, 64) elements, then the split partials) lives in a
+ *   fixed 16 MiB device array per GPU, held until the process ends; a call needing more
+ *   returns FM_ERR_INVALID_ARG with the byte counts in fm_last_error(NULL). Every call on one GPU
+ *   shares that array: calls that overlap on one GPU (two streams, two threads) race. */
+fm_status fm_op_attention_noalloc(int32_t dtype, int32_t B, int32_t Tq, int32_t n_heads, int32_t n_kv,
+                                  int32_t n_keys, int32_t dh, const void* q, const void* k, const void* v, void* o,
+                                  void* hip_stream);
 /* fm_op_quantize_fp8: the FP8 weight quantizer alone (see fm_set_weight_format), for parity.
  *   src DEVICE bf16 [N, K] row-major (K even); codes DEVICE bytes [N, K]; scale DEVICE fp32 [N]
  *   (2^e of each row); deq DEVICE bf16 [N, K] = code value x 2^e (exact). Synchronizes
