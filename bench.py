@@ -294,7 +294,7 @@ def bench_other(name, calls, cpu_budget):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50, help="timed fm_denoise calls")
+    ap.add_argument("--steps", type=int, default=100, help="timed fm_denoise calls")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="pi05_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -518,7 +518,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_configs and args.workload == "pi05_b1" and args.weights == "as-given":
         res["configs"] = {}
-        for name, calls, cb in (("tiny_fp32", 50, 3.0), ("pi05_b8", 20, 4.0), ("dit_b1", 20, 4.0), ("pi05_b64", 10, 6.0)):
+        for name, calls, cb in (("tiny_fp32", 100, 3.0), ("pi05_b8", 100, 4.0), ("dit_b1", 100, 4.0), ("pi05_b64", 100, 6.0)):
             res["configs"][name] = bench_other(name, calls, 0.0 if args.no_cpu_baseline else cb)
     print(json.dumps(res), flush=True)
 

@@ -88,6 +88,16 @@ fm_status check_config(const fm_config* c, std::string& msg) {
     msg = "n_layers, hidden (>= 64), heads, head_dim, mlp_dim, action_horizon, action_dim, n_kv_heads, max_batch and max_steps must be positive";
     return FM_ERR_INVALID_ARG;
   }
+  // upper limits far above any expert the pages describe, so that every derived count and size
+  // (weight list, pool and buffer bytes, products of fields) stays small and within range
+  if (c->n_layers > 1024 || c->n_heads > 256 || c->n_kv_heads > 256 || c->mlp_dim > (1 << 16) ||
+      c->action_horizon > 4096 || c->action_dim > 4096 || c->max_batch > 4096 || c->max_steps > 4096 ||
+      c->max_prefix_len > (1 << 20) || c->state_tokens > 8 || c->state_dim > (1 << 16) || c->ctx_len_max > (1 << 20) ||
+      c->ctx_dim > (1 << 16) || c->mlp_gated < 0) {
+    msg = "a config field is out of range (n_layers <= 1024, heads <= 256, mlp_dim, state_dim, ctx_dim <= 65536, "
+          "action_horizon, action_dim, max_batch, max_steps <= 4096, max_prefix_len, ctx_len_max <= 2^20)";
+    return FM_ERR_INVALID_ARG;
+  }
   if (c->hidden % 64 != 0 || c->hidden / kStatCols > kMaxStatSlots) { msg = fmt("hidden %d must be a multiple of 64 and at most %d", c->hidden, kStatCols * kMaxStatSlots); return FM_ERR_UNSUPPORTED; }
   if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) {
     msg = fmt("head_dim %d not in {64, 128, 256}", c->head_dim);

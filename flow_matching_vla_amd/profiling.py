@@ -50,6 +50,41 @@ def per_dispatch(d: str, counter: str) -> list[tuple[int, str, float]]:
     return [(i, names[i], v) for i, v in sorted(per.items())]
 
 
+def per_dispatch_max(d: str, counter: str) -> dict[int, float]:
+    """dispatch id -> largest value of the counter over its instances (a per-XCC clock count)."""
+    per = defaultdict(float)
+    for r in _rows(d, "counter_collection.csv"):
+        if r.get("Counter_Name") == counter:
+            i = int(r["Dispatch_Id"])
+            per[i] = max(per[i], float(r["Counter_Value"]))
+    return per
+
+
+def mfma(d: str, simds: int = 1024, clock_ghz: float = 2.4) -> list[dict]:
+    """Per kernel, from one run with SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE: bf16 MFMA flops per dispatch (MOPS x 512), MFMA busy share of the SIMDs
+    (busy cycles summed over SIMDs / (active cycles x SIMDs), rocprofv3's MfmaUtil), and the
+    flop rate over the active cycles at clock_ghz."""
+    mops = {i: (k, v) for i, k, v in per_dispatch(d, "SQ_INSTS_VALU_MFMA_MOPS_BF16")}
+    busy = {i: v for i, _, v in per_dispatch(d, "SQ_VALU_MFMA_BUSY_CYCLES")}
+    gui = per_dispatch_max(d, "GRBM_GUI_ACTIVE")
+    acc = defaultdict(lambda: [0, 0.0, 0.0, 0.0])
+    for i, (k, m) in mops.items():
+        if i not in busy or gui.get(i, 0.0) <= 0:
+            continue
+        a = acc[k]
+        a[0] += 1
+        a[1] += 512.0 * m
+        a[2] += busy[i]
+        a[3] += gui[i]
+    out = []
+    for k, (n, fl, bu, gu) in acc.items():
+        t = gu / n / (clock_ghz * 1e9)
+        out.append({"kernel": k, "dispatches": n, "flops_per_dispatch": fl / n, "mfma_busy_pct": 100.0 * bu / (gu * simds),
+                    "active_us": t * 1e6, "tflops": fl / n / t / 1e12 if t > 0 else 0.0})
+    return sorted(out, key=lambda r: -r["flops_per_dispatch"] * r["dispatches"])
+
+
 def traffic(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int) -> dict:
     """HBM bytes per dispatch of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by copy_bytes over what the counter reads for the plain device copy of
@@ -87,7 +122,7 @@ def loop_source_hash() -> str:
 
 
 def main(argv):
-    """profiling.py stats DIR | counters DIR COUNTER | traffic FETCH_DIR WRITE_DIR KERNEL COPY_BYTES"""
+    """profiling.py stats DIR | counters DIR COUNTER | mfma DIR | traffic FETCH_DIR WRITE_DIR KERNEL COPY_BYTES"""
     if argv[0] == "stats":
         rows = kernel_stats(argv[1])
         tot = sum(c * a for _, c, a, _, _ in rows)
@@ -98,6 +133,12 @@ def main(argv):
     elif argv[0] == "counters":
         for k, (n, m) in sorted(counter_means(argv[1], argv[2]).items(), key=lambda x: -x[1][1]):
             print(f"{argv[2]} {m:14.1f} KiB/dispatch x{n:3d}  {k[:100]}")
+    elif argv[0] == "mfma":
+        rows = mfma(argv[1])
+        print(f"{'kernel':80s} {'disp':>5s} {'GFLOP/disp':>11s} {'active_us':>10s} {'TFLOP/s':>8s} {'busy%':>6s}")
+        for r in rows:
+            print(f"{r['kernel'][:80]:80s} {r['dispatches']:5d} {r['flops_per_dispatch'] / 1e9:11.3f} "
+                  f"{r['active_us']:10.2f} {r['tflops']:8.1f} {r['mfma_busy_pct']:6.1f}")
     elif argv[0] == "traffic":
         t = traffic(argv[1], argv[2], argv[3], int(argv[4]))
         for c in ("FETCH_SIZE", "WRITE_SIZE"):

@@ -304,10 +304,12 @@ enum {
 };
 
 /* Implementation of fm_denoise / fm_step_velocity.
- * FM_LOOP_AUTO: the persistent loop kernel wherever it applies - bf16 pi0.5-family expert
- *   (PREFIX_JOINT, one K/V head, gated MLP) with head_dim 256, hidden a multiple of 512 up to
- *   1024, action_dim a multiple of 4 up to 32, batch * H <= 64 action rows, and every phase
- *   within two work items per CU - and the per-operation graph elsewhere.
+ * FM_LOOP_AUTO: the loop kernel wherever it applies, the per-operation graph elsewhere. It
+ *   applies to the bf16 pi0.5-family expert (PREFIX_JOINT, one K/V head, gated MLP) with
+ *   head_dim 256, 1 to 8 query heads (one per XCD), hidden 512 or 1024, mlp_dim a multiple of
+ *   512 up to 4096, action_dim a multiple of 4 up to 32, batch * H <= 64 action rows, at most
+ *   64 layers and at most 32 attention key-tile pairs per head (64 key tiles of 32 over the
+ *   requests' compact prefixes and chunks), on a device of 256 CUs in 8 XCDs.
  * FM_LOOP_GRAPH: always the captured graph of per-operation kernels.
  * Both compute the same function (reduction orders differ). Default FM_LOOP_AUTO.
  * FM_ERR_INVALID_ARG for another mode. */
@@ -316,11 +318,12 @@ fm_status fm_set_loop_mode(fm_ctx* ctx, int32_t mode);
 
 /* Synchronize the context stream. *persistent = 1 when the loop kernel serves the current
  * weights, schedule and binding (0 otherwise). *fault: 0, or what went wrong since the last
- * query: 1, 2, 3 or 5 when one of the loop kernel's bounded waits expired (barrier gather,
- * release, split-K, attention split); 6 when the loop kernel's workgroups of one residue of
- * blockIdx.x mod 8 did not all run on one XCD. Results since then are invalid: the context is poisoned and FM_ERR_DEVICE is returned (the
- * words are cleared). A loop-kernel launch that starts with its fault word set writes NaN to
- * its output and does nothing else. Either pointer may be NULL. */
+ * query: 1, 2 or 3 when one of the loop kernel's bounded waits expired (1 an XCD barrier, 2 the
+ * wait for a norm operand from every XCD, 3 the wait for the O or down partial sums); 4 when two
+ * of its workgroups took one (XCD, rank) slot, i.e. the launch was not dealt round-robin over
+ * the XCDs. Results since then are invalid: the context is poisoned and FM_ERR_DEVICE is
+ * returned (the word is cleared). A loop-kernel launch that starts with its fault word set
+ * writes NaN to its output and does nothing else. Either pointer may be NULL. */
 fm_status fm_loop_status(fm_ctx* ctx, int32_t* persistent, uint32_t* fault);
 
 /* Run the same loop as fm_denoise, eagerly, with a hipEvent pair on the context stream

@@ -62,6 +62,20 @@ def test_config_validation(lib, field, value, status):
     assert str(e.value).startswith(status)
 
 
+@pytest.mark.parametrize("field", ["n_layers", "n_heads", "mlp_dim", "action_horizon", "action_dim", "max_batch",
+                                   "max_steps", "max_prefix_len"])
+def test_config_fields_are_bounded(lib, field):
+    # every field has an upper limit, so that a config cannot make the host build a weight list
+    # or size arithmetic of billions of entries (found by the AddressSanitizer sweep)
+    import time
+    t0 = time.perf_counter()
+    with pytest.raises(fm.FMError) as e:
+        fm.query(dict(wl.workload("pi05_b1"), **{field: 1 << 30}))
+    assert str(e.value).startswith(fm.STATUS[1])
+    assert time.perf_counter() - t0 < 1.0
+    fm.query(dict(wl.workload("pi05_b1"), n_layers=1024))   # the limit itself is accepted
+
+
 def test_dit_config_validation(lib):
     with pytest.raises(fm.FMError):
         fm.query(dict(wl.workload("dit_b1"), n_kv_heads=1))
