@@ -90,7 +90,9 @@ def step_bytes_flops(cfg):
     return tb, tf
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "{}_loop_kernel_hbm_traffic.txt")
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "{}_loop_kernel_hbm_traffic.txt")
+MFMA_FILE = os.path.join(HERE, "profiles", "{}_mfma_counters.txt")
 
 
 def loop_traffic(workload):
@@ -109,6 +111,25 @@ def loop_traffic(workload):
     if vals.get("source_sha256") != profiling.loop_source_hash() or "traffic_bytes_per_launch" not in vals:
         return None
     return int(float(vals["traffic_bytes_per_launch"]))
+
+
+def mfma_counters(workload):
+    """MFMA busy share of the per-operation kernels from the committed rocprofv3 counter
+    summary of this workload (time-weighted over the kernels that issue MFMAs), or None when
+    there is none or the kernel sources have changed since the counters were taken."""
+    from flow_matching_vla_amd import profiling
+    path = MFMA_FILE.format(workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for ln in open(path):
+        if ":" in ln and not ln.startswith("#") and not ln.startswith("void") and not ln.startswith("_Z"):
+            k, v = ln.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != profiling.graph_source_hash() or "mfma_busy_pct_time_weighted" not in vals:
+        return None
+    return {"busy_frac_time_weighted": round(float(vals["mfma_busy_pct_time_weighted"]) / 100, 4),
+            "counters": "SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16", "file": os.path.relpath(path, HERE)}
 
 
 def cpu_baseline(cfg, W, I, budget_s=12.0):
@@ -280,6 +301,9 @@ def bench_other(name, calls, cpu_budget):
     if not persistent:
         roles, roof = dominant_role(ctx, cfg, x0, out)
         r["roles_us_per_launch"], r["roofline"] = roles, roof
+        mc = mfma_counters(name)
+        if mc is not None:
+            r["mfma_counters"] = mc
     print(f"[bench] {name}: {summ['p50_ms']:.3f} ms per chunk (p50), {r['chunks_per_s']:.1f} chunks/s",
           file=sys.stderr, flush=True)
     ctx.close()

@@ -50,38 +50,37 @@ def per_dispatch(d: str, counter: str) -> list[tuple[int, str, float]]:
     return [(i, names[i], v) for i, v in sorted(per.items())]
 
 
-def per_dispatch_max(d: str, counter: str) -> dict[int, float]:
-    """dispatch id -> largest value of the counter over its instances (a per-XCC clock count)."""
-    per = defaultdict(float)
+def dispatch_ns(d: str) -> dict[int, float]:
+    """dispatch id -> its duration in ns, from the start / end timestamps of the counter rows."""
+    out = {}
     for r in _rows(d, "counter_collection.csv"):
-        if r.get("Counter_Name") == counter:
-            i = int(r["Dispatch_Id"])
-            per[i] = max(per[i], float(r["Counter_Value"]))
-    return per
+        out[int(r["Dispatch_Id"])] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
 
 
 def mfma(d: str, simds: int = 1024, clock_ghz: float = 2.4) -> list[dict]:
-    """Per kernel, from one run with SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and
-    GRBM_GUI_ACTIVE: bf16 MFMA flops per dispatch (MOPS x 512), MFMA busy share of the SIMDs
-    (busy cycles summed over SIMDs / (active cycles x SIMDs), rocprofv3's MfmaUtil), and the
-    flop rate over the active cycles at clock_ghz."""
+    """Per kernel, from one run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_VALU_MFMA_BUSY_CYCLES:
+    bf16 MFMA flops per dispatch (MOPS x 512), the flop rate over the dispatch's own duration
+    (its timestamps), and the MFMA busy share of the SIMDs (busy cycles summed over the SIMDs /
+    (duration x clock_ghz x simds)). GRBM_GUI_ACTIVE is not used as the denominator: in a
+    counter run it also counts cycles outside the dispatch."""
     mops = {i: (k, v) for i, k, v in per_dispatch(d, "SQ_INSTS_VALU_MFMA_MOPS_BF16")}
     busy = {i: v for i, _, v in per_dispatch(d, "SQ_VALU_MFMA_BUSY_CYCLES")}
-    gui = per_dispatch_max(d, "GRBM_GUI_ACTIVE")
+    dur = dispatch_ns(d)
     acc = defaultdict(lambda: [0, 0.0, 0.0, 0.0])
     for i, (k, m) in mops.items():
-        if i not in busy or gui.get(i, 0.0) <= 0:
+        if i not in busy or dur.get(i, 0.0) <= 0:
             continue
         a = acc[k]
         a[0] += 1
         a[1] += 512.0 * m
         a[2] += busy[i]
-        a[3] += gui[i]
+        a[3] += dur[i]
     out = []
-    for k, (n, fl, bu, gu) in acc.items():
-        t = gu / n / (clock_ghz * 1e9)
-        out.append({"kernel": k, "dispatches": n, "flops_per_dispatch": fl / n, "mfma_busy_pct": 100.0 * bu / (gu * simds),
-                    "active_us": t * 1e6, "tflops": fl / n / t / 1e12 if t > 0 else 0.0})
+    for k, (n, fl, bu, ns) in acc.items():
+        t = ns / n * 1e-9
+        out.append({"kernel": k, "dispatches": n, "flops_per_dispatch": fl / n, "duration_us": t * 1e6,
+                    "tflops": fl / n / t / 1e12, "mfma_busy_pct": 100.0 * bu / (ns * clock_ghz * simds)})
     return sorted(out, key=lambda r: -r["flops_per_dispatch"] * r["dispatches"])
 
 
@@ -114,11 +113,18 @@ def source_hash(files: list[str]) -> str:
 
 
 LOOP_SOURCES = ["csrc/fm_xloop.hip", "csrc/fm_xloop.h", "csrc/fm_common.h"]
+GRAPH_SOURCES = ["csrc/fm_gemm.hip", "csrc/fm_attn.hip", "csrc/fm_kernels.h", "csrc/fm_common.h"]
 
 
 def loop_source_hash() -> str:
     here = os.path.dirname(os.path.abspath(__file__))
     return source_hash([os.path.join(here, f) for f in LOOP_SOURCES])
+
+
+def graph_source_hash() -> str:
+    """sha256 of the per-operation kernels' sources (the GEMMs and the attention)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    return source_hash([os.path.join(here, f) for f in GRAPH_SOURCES])
 
 
 def main(argv):
@@ -135,10 +141,14 @@ def main(argv):
             print(f"{argv[2]} {m:14.1f} KiB/dispatch x{n:3d}  {k[:100]}")
     elif argv[0] == "mfma":
         rows = mfma(argv[1])
-        print(f"{'kernel':80s} {'disp':>5s} {'GFLOP/disp':>11s} {'active_us':>10s} {'TFLOP/s':>8s} {'busy%':>6s}")
+        print(f"{'kernel':80s} {'disp':>5s} {'GFLOP/disp':>11s} {'us/disp':>9s} {'TFLOP/s':>8s} {'%2.5PF':>7s} {'busy%':>6s}")
         for r in rows:
             print(f"{r['kernel'][:80]:80s} {r['dispatches']:5d} {r['flops_per_dispatch'] / 1e9:11.3f} "
-                  f"{r['active_us']:10.2f} {r['tflops']:8.1f} {r['mfma_busy_pct']:6.1f}")
+                  f"{r['duration_us']:9.2f} {r['tflops']:8.1f} {100 * r['tflops'] / 2500:7.2f} {r['mfma_busy_pct']:6.1f}")
+        mm = [r for r in rows if r["flops_per_dispatch"] > 0]
+        tt = sum(r["duration_us"] * r["dispatches"] for r in mm)
+        print(f"mfma_busy_pct_time_weighted: {sum(r['mfma_busy_pct'] * r['duration_us'] * r['dispatches'] for r in mm) / tt:.2f}")
+        print(f"source_sha256: {graph_source_hash()}")
     elif argv[0] == "traffic":
         t = traffic(argv[1], argv[2], argv[3], int(argv[4]))
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
