@@ -154,6 +154,9 @@ __device__ __forceinline__ XLayerW layer_at(XA& a, int l) {
 // launch round-robin over the 8 XCDs, so the workgroups of one XCD are one residue class of
 // blockIdx mod 8 and their blockIdx / 8 are 0..31).
 struct Who { int x, r; };
+// The attention's key-tile pair of a CU: pair p runs on rank 31 - p, so the pairs take the ranks
+// with one QKV tile (16-31) and, at horizon <= 50 and batch 1, no rows of the reduce.
+__device__ __forceinline__ int pair_of(const Who& me) { return 31 - me.r; }
 
 // ---------------------------------------------------------------------------------------
 // Waits
@@ -397,7 +400,7 @@ __device__ __forceinline__ void ag_arrive(XA& a, const Who& me) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Attention of one key-tile pair: CU rank p of XCD x takes pair p of head x; the waves of half h
+// Attention of one key-tile pair: CU rank 31 - p of XCD x takes pair p of head x; the waves of half h
 // (waves 4 h .. 4 h + 3) take tile j + h of the pair, wave w4 the query rows 16 w4 .. + 15 of the
 // request. S^T = K Q^T and O^T = V^T P^T on MFMA with the tile's K / V^T in LDS (32 KB at
 // slotB + 32 KB h). The two halves are merged in LDS, and the pair's unnormalised output O
@@ -413,9 +416,10 @@ __device__ __forceinline__ int req_tiles(XA& a, int b) { return (a.plen[b] + 31)
 // tiles from the pool when suffix == false, the chunk's own tiles from this step's K / V^T when
 // suffix == true. Returns the copies issued.
 __device__ __forceinline__ int tile_issue(XA& a, const Who& me, int l, int h, bool suffix, int w, XSmem& sm) {
-  if (me.r >= a.npairs) return 0;
+  const int p = pair_of(me);
+  if (p >= a.npairs) return 0;
   const int lane = threadIdx.x & 63;
-  const XPair pr = pair_at(a, me.r);
+  const XPair pr = pair_at(a, p);
   const int b = pr.b, j = pr.j + h, tp = (a.plen[b] + 31) / 32;
   if (j >= req_tiles(a, b)) return 0;
   const bool is_suf = j >= tp;
@@ -458,8 +462,9 @@ __device__ __forceinline__ int tile_issue(XA& a, const Who& me, int l, int h, bo
 __device__ __forceinline__ void attn_pair(XA& a, const Who& me, XSmem& sm) {
   typedef Mma<bf16>::frag frag;
   const int lane = threadIdx.x & 63, w = wave_id(), w4 = w & 3, h = w >> 2;
-  const bool valid = me.r < a.npairs;
-  const XPair pr = valid ? pair_at(a, me.r) : XPair{0, 0};
+  const int pi = pair_of(me);
+  const bool valid = pi < a.npairs;
+  const XPair pr = valid ? pair_at(a, pi) : XPair{0, 0};
   const int b = pr.b, j = pr.j + h, tp = (a.plen[b] + 31) / 32;
   const bool has = valid && j < req_tiles(a, b) && 16 * w4 < a.H;   // a tile and query rows for this wave
   const bool is_suf = j >= tp;
@@ -532,7 +537,7 @@ __device__ __forceinline__ void attn_pair(XA& a, const Who& me, XSmem& sm) {
     const int row = 16 * w4 + (lane & 15);
     if (row < a.H) {
       const Rsrc rw = make_rsrc(xl + a.o_ap, (uint32_t)(a.npairs * 64 * kDH * 4));
-      const uint32_t rb = (uint32_t)((me.r * 64 + row) * kDH * 4);
+      const uint32_t rb = (uint32_t)((pi * 64 + row) * kDH * 4);
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         const f32x4 v = a1 * o[db] + a2 * mrg[(w4 * kDB + db) * 64 + lane];
@@ -540,7 +545,7 @@ __device__ __forceinline__ void attn_pair(XA& a, const Who& me, XSmem& sm) {
       }
       if (lane < 16) {
         const Rsrc rm = make_rsrc(xl + a.o_ml, (uint32_t)(a.npairs * 64 * 8));
-        st8<0>(rm, (uint32_t)((me.r * 64 + row) * 8), u32x2{__float_as_uint(mx), __float_as_uint(a1 * lsum + a2 * p2.y)});
+        st8<0>(rm, (uint32_t)((pi * 64 + row) * 8), u32x2{__float_as_uint(mx), __float_as_uint(a1 * lsum + a2 * p2.y)});
       }
     }
   }
@@ -576,9 +581,20 @@ __global__ void __launch_bounds__(kT, 1) k_xloop(const XLoopArgs* __restrict__ p
   auto xa = [&](XA& a) { ++nxb; xarrive(a, me); };
   auto xw = [&](XA& a) { xwait(a, me, la.xb0 + 32u * nxb, sm); };
   auto xb = [&](XA& a) { xa(a); xw(a); };
+  const bool has_head = me.x < pa->nq;
+  const bool acu = has_head && pair_of(me) < pa->npairs;   // this CU takes a key-tile pair of the attention
 
-  // copy-wave bookkeeping: this wave's gate/up, down and next-QKV copies not yet waited for
-  int c_gu = 0, c_dn = 0, c_qk = 0;
+  // copy-wave bookkeeping: this wave's gate/up, down, next-QKV and prefix-tile copies not yet
+  // waited for
+  int c_gu = 0, c_dn = 0, c_qk = 0, c_tl = 0;
+  // copy waves of a CU with a tile pair: layer l's prefix key tiles into slot B. The prefix is
+  // bound for the whole chunk, so they are issued a phase group early: after the previous
+  // layer's down GEMM (or with the first layer's QKV weights), and land during the reduce and
+  // the QKV phase; the attention waits for them.
+  auto issue_tiles = [&](XA& a, int l) {
+    c_tl = 0;
+    if (copy_wave() && acu) c_tl = tile_issue(a, me, l, 0, false, wave_id() - 4, sm) + tile_issue(a, me, l, 1, false, wave_id() - 4, sm);
+  };
 
   // (XCD, rank) slot check: two workgroups on one slot mean the dispatch was not round-robin
   if (t == 0) sm.dead = 0;
@@ -593,8 +609,6 @@ __global__ void __launch_bounds__(kT, 1) k_xloop(const XLoopArgs* __restrict__ p
     __syncthreads();
   }
 
-  const bool has_head = me.x < pa->nq;
-  const bool acu = has_head && me.r < pa->npairs;   // this CU takes a key-tile pair of the attention
   for (int kk = 0; kk < la.nsteps; ++kk) {
     XA& a = launder(pa);
     const int k = la.k0 + kk;
@@ -662,10 +676,11 @@ __global__ void __launch_bounds__(kT, 1) k_xloop(const XLoopArgs* __restrict__ p
       }
       ag_arrive(a, me);
       ++nag;
-      // copy waves: the first layer's QKV weights, behind the arrival
+      // copy waves: the first layer's QKV weights and prefix key tiles, behind the arrival
       __syncthreads();
       if (copy_wave() && has_head)
         prefetch_w<W8>(layer_at(a, 0).qkv, a.wb_qkv, D / 32, nqkv, nt_q, 0, D / 32, sm.slotA);
+      issue_tiles(a, 0);
     }
 
     for (int l = 0; l < a.L; ++l) {
@@ -673,7 +688,7 @@ __global__ void __launch_bounds__(kT, 1) k_xloop(const XLoopArgs* __restrict__ p
       const XLayerW lw = layer_at(a, l);
       const int sq = 2 * l, su = 2 * l + 1, sn = 2 * l + 2;   // norm sites: QKV, gate/up, next
       // ================= QKV + RoPE (XCD x: head x's q, and k, v) =================
-      if (copy_wave()) vm_wait_le(0);   // this layer's QKV weights have landed
+      if (copy_wave()) vm_wait_le(c_tl);   // this layer's QKV weights have landed (the key tiles may fly)
       ag_wait(a, me, la.ag0 + 32u * nag, sm);
       {
         char* ab = agb(sq);
@@ -730,21 +745,16 @@ __global__ void __launch_bounds__(kT, 1) k_xloop(const XLoopArgs* __restrict__ p
         // A CU's vector memory operations complete in issue order, whichever wave issued them,
         // and the weight streams of all CUs share the XCD's L2 and the HBM: copies are issued
         // after each phase's own loads, stores and barrier arrival, one phase's worth at a time.
-        // Copy waves: this layer's prefix key tiles (on a CU with a tile pair) and O weights.
+        // Copy waves: this layer's O weights.
         xa(a);
-        if (copy_wave() && has_head) {
-          if (acu) {
-            tile_issue(a, me, l, 0, false, w - 4, sm);
-            tile_issue(a, me, l, 1, false, w - 4, sm);
-          }
+        if (copy_wave() && has_head)
           prefetch_w<W8>(lw.o, a.wb_o, a.nq * kDH / 32, nod, nt_od, me.x * (kDH / 32), kDH / 32, sm.slotO);
-        }
         xw(a);
       }
       // ================= attention: pair me.r of head x (a CU with a pair) =================
       {
         // the chunk's own key tiles are this phase's inputs; the prefix tiles were copied
-        // during the QKV phase
+        // since the previous layer's down GEMM
         if (acu) {
           tile_issue(a, me, l, w >> 2, true, w & 3, sm);
           wait_all();
@@ -913,6 +923,12 @@ __global__ void __launch_bounds__(kT, 1) k_xloop(const XLoopArgs* __restrict__ p
         if (!copy_wave()) wait_all();
         __syncthreads();
         if (t == 0) flag_st(a.flags + kXFd + me.r * 8 + me.x, la.pe0 + npe);
+        // copy waves: the next layer's prefix key tiles (slot B is free after the down GEMM),
+        // behind the flag
+        if (l + 1 < a.L) {
+          __syncthreads();
+          issue_tiles(a, l + 1);
+        }
       }
       // ================= reduce the down partials + residual; publish the next norm operand ==
       {
