@@ -113,6 +113,39 @@ def loop_traffic(workload):
     return int(float(vals["traffic_bytes_per_launch"]))
 
 
+def measured_ceilings():
+    """Ceilings measured on this device with the platform's own routines, beside the nominal
+    peaks: a 1 GiB device-to-device copy (bytes read + written per second) and a bf16
+    8192 x 8192 x 8192 matrix product (torch.matmul), each the best of 20 timed runs."""
+    import torch
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+
+    def best(fn, n=20):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e-3)
+        return min(out)
+    t_copy = best(lambda: dst.copy_(src))
+    t_mm = best(lambda: torch.matmul(a, b))
+    r = {"copy_GBps": round(2 * nb / t_copy / 1e9, 1), "bf16_gemm_TFLOPs": round(2 * 8192 ** 3 / t_mm / 1e12, 1),
+         "how": "1 GiB device copy (read + write) and torch.matmul bf16 8192^3, best of 20"}
+    del src, dst, a, b
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return r
+
+
 def mfma_counters(workload):
     """MFMA busy share of the per-operation kernels from the committed rocprofv3 counter
     summary of this workload (time-weighted over the kernels that issue MFMAs), or None when
@@ -319,7 +352,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100, help="timed fm_denoise calls")
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pi05_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fit", action="store_true")
@@ -524,6 +557,7 @@ def main():
         torch.cuda.synchronize()
         return round((time.perf_counter() - t0) / n * 1e3, 3)
     res["bind_ms"] = per_call_ms(bind, 5)
+    res["measured_ceilings"] = measured_ceilings()
     res["schedule_ms"] = per_call_ms(lambda: ctx.set_schedule(T, B), 3)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
