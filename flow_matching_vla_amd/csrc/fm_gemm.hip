@@ -668,21 +668,28 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
     }
   }
   const uint32_t lds0 = lds_addr(lds) + (uint32_t)(w * FPW) * 1024u;
-  auto issue = [&](int k0, int st) {
+  // Per copy: its buffer descriptor and the byte step per k-stage, both wave-uniform, so the
+  // stage's copies issue without branches. An absent row's offset (kOob) stays past every
+  // extent as it advances (K * 2 bytes < 2^31), so it needs no select.
+  V16 cdesc[FPW];
+  uint32_t cstep[FPW];
 #pragma unroll
-    for (int i = 0; i < FPW; ++i) {
-      const int f = w * FPW + i;
-      const uint32_t dst = lds0 + (uint32_t)(st * FS + i) * 1024u;
-      if (f < FA) {   // uniform per wave
-        dma16_lds(da, dst, coff[i] == kOob ? kOob : coff[i] + (uint32_t)(k0 * sizeof(T)));
-      } else {
-        dma16_lds(dw, dst, coff[i] + (uint32_t)((k0 / KC) * 1024));
-      }
-    }
+  for (int i = 0; i < FPW; ++i) {
+    const bool isA = w * FPW + i < FA;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cdesc[i][q] = __builtin_amdgcn_readfirstlane(isA ? da[q] : dw[q]);
+    cstep[i] = __builtin_amdgcn_readfirstlane(isA ? (uint32_t)(BK * sizeof(T)) : 1024u);
+    coff[i] += isA ? (coff[i] == kOob ? 0u : (uint32_t)(kbeg * sizeof(T))) : (uint32_t)((kbeg / KC) * 1024);
+  }
+  // copies of k-stage s (relative to kbeg) into ring slot st
+  auto issue = [&](int s, int st) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i)
+      dma16_lds(cdesc[i], lds0 + (uint32_t)(st * FS + i) * 1024u, coff[i] + (uint32_t)s * cstep[i]);
   };
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < nks) issue(kbeg + p * BK, p);
+    if (p < nks) issue(p, p);
   Epilogue<T, 64, BN, NT, EPI> ep0;   // per-column inputs, loaded before the main loop
   ep0.prefetch_cols(a, n0);
   if constexpr (NORM) {
@@ -703,14 +710,13 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
 
   // One barrier per stage: it makes stage ks visible to every wave and also proves that
   // every wave has finished reading stage ks - 1, whose buffer the copies issued right after
-  // it refill (with stage ks + NST - 1). (Reading the next stage's fragments during this
-  // stage's MFMAs measured 2-7% slower: the stage time is set by the copies, not by the
-  // LDS reads.)
-  for (int ks = 0; ks < nks; ++ks) {
-    wait_stages<FPW, 0, NST>(min(NST - 2, nks - 1 - ks));   // stage ks has landed
-    __syncthreads();
-    if (ks + NST - 1 < nks) issue(kbeg + (ks + NST - 1) * BK, (ks + NST - 1) % NST);
-    const V16* sA = lds + (ks % NST) * FS * 64;
+  // it refill (with stage ks + NST - 1). Measured on MI355X: the steady loop without any
+  // branch (no per-copy operand choice, no wait switch) is ~10% faster than with them;
+  // carrying the next stage's fragments in registers during this stage's MFMAs, two stages
+  // per barrier, and copies whose sources stay in cache all measured no faster.
+  // Stage ks's fragments from LDS, then its MFMAs.
+  auto compute = [&](int slot) {
+    const V16* sA = lds + slot * FS * 64;
     const V16* sB = sA + FA * 64;
     V16 af[WRB], bfr[WCB];
 #pragma unroll
@@ -723,6 +729,25 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
 #pragma unroll
       for (int j = 0; j < WCB; ++j)
         acc[i][j] = MT::mma(__builtin_bit_cast(frag, af[i]), __builtin_bit_cast(frag, bfr[j]), acc[i][j]);
+  };
+  // Steady state (a stage left to issue): NST - 2 later stages may still be in flight, and
+  // the copies of stage ks + NST - 1 refill stage ks - 1's slot. Ring slots advance by
+  // counters (NST need not be a power of two).
+  int ks = 0, slot = 0, fill = NST - 1;
+  for (; ks + NST - 1 < nks; ++ks) {
+    FM_WAIT_VM((NST - 2) * FPW);   // stage ks has landed
+    __syncthreads();
+    issue(ks + NST - 1, fill);
+    fill = fill + 1 == NST ? 0 : fill + 1;
+    compute(slot);
+    slot = slot + 1 == NST ? 0 : slot + 1;
+  }
+  // the last NST - 1 (or fewer) stages: nothing left to issue
+  for (; ks < nks; ++ks) {
+    wait_stages<FPW, 0, NST>(nks - 1 - ks);
+    __syncthreads();
+    compute(slot);
+    slot = slot + 1 == NST ? 0 : slot + 1;
   }
   __syncthreads();   // every wave is done with the operand stages (the epilogue reuses LDS)
   float* C = (float*)lds;
