@@ -116,20 +116,25 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   const uint32_t k_lane = (uint32_t)(((long)b * a.k_bs + (long)g * a.k_hs + (long)(lane % 16) * a.k_rs + (lane / 16) * VEC) * sizeof(T));
   const uint32_t v_lane = (uint32_t)(((long)b * a.v_bs + (long)g * a.v_hs + (long)(lane % 16) * a.v_ds + (lane / 16) * VEC) * sizeof(T));
   const uint32_t k_row = (uint32_t)(a.k_rs * sizeof(T)), v_row16 = (uint32_t)(16 * a.v_ds * sizeof(T));
+  // Per copy: its descriptor, its lane offset at key 0 and its bytes per key, all but the
+  // lane offset wave-uniform, so a tile's copies issue without branches.
+  V16 cdesc[FPW];
+  uint32_t cbase[FPW], cper[FPW];
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    const int f = wave * FPW + i;
+    const bool isK = f < FK;
+    const int kb = f / DCH, c = f % DCH, fv = f - FK, db = fv / KCH, kc = fv % KCH;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cdesc[i][q] = __builtin_amdgcn_readfirstlane(isK ? rk[q] : rv[q]);
+    cbase[i] = isK ? k_lane + (uint32_t)(16 * kb) * k_row + (uint32_t)(c * KC * sizeof(T))
+                   : v_lane + (uint32_t)db * v_row16 + (uint32_t)(kc * KC * sizeof(T));
+    cper[i] = __builtin_amdgcn_readfirstlane(isK ? k_row : (uint32_t)sizeof(T));
+  }
   auto issue = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < FPW; ++i) {
-      const int f = wave * FPW + i;
-      if (f < FK) {   // uniform per wave
-        const int kb = f / DCH, c = f % DCH;
-        const uint32_t off = k_lane + (uint32_t)(kt + 16 * kb) * k_row + (uint32_t)(c * KC * sizeof(T));
-        dma16_lds(rk, lds0 + (uint32_t)buf * (FT * 1024u) + i * 1024u, off);
-      } else {
-        const int fv = f - FK, db = fv / KCH, kc = fv % KCH;
-        const uint32_t off = v_lane + (uint32_t)db * v_row16 + (uint32_t)((kt + kc * KC) * sizeof(T));
-        dma16_lds(rv, lds0 + (uint32_t)buf * (FT * 1024u) + i * 1024u, off);
-      }
-    }
+    for (int i = 0; i < FPW; ++i)
+      dma16_lds(cdesc[i], lds0 + (uint32_t)buf * (FT * 1024u) + i * 1024u, cbase[i] + (uint32_t)kt * cper[i]);
   };
   if (ntile > 0) issue(tile_start(0), 0);   // tile 0 first, the other prefetched tiles after Q
 
@@ -177,7 +182,8 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
       vis &= ~(bits_below(a.seg_end - kt) & ~bits_below(pb - kt));   // the keys in [pb, seg_end)
     }
     // tile t's copies are done once at most the tiles issued after it are in flight
-    wait_tiles<FPW, NST>(min(NST - 1, ntile - 1 - t));
+    if (t + NST - 1 < ntile) FM_WAIT_VMCNT((NST - 1) * FPW);
+    else wait_tiles<FPW, NST>(ntile - 1 - t);
     __syncthreads();
     const V16* sK = sbuf[t % NST];
     const V16* sV = sK + FK * 64;
