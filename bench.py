@@ -65,14 +65,15 @@ def role_bytes_flops(cfg, role):
     # DiT: per-role averages over the two block kinds
     S = cfg["ctx_len"]
     if role == "qkv":
-        w = (D * D + 3 * D * D) / 2
-        return w * e + 2 * D * 4, 2 * w * M
+        w, rows = (D * D + 3 * D * D) / 2, (D + 3 * D) / 2
+        return (w + 4 * rows if w8 else w * e) + 2 * D * 4, 2 * w * M
     if role == "attn":
         kv = (B * S * D * 2 * e + 0) / 2
         fl = (4 * B * (st + H) * S * D + 4 * B * (st + H) ** 2 * D) / 2
         return kv, fl
-    w = {"oproj": D * D, "mlp_up": F * D, "mlp_down": D * F, "out": da * D, "inproj": D * da}[role]
-    return w * e, 2 * w * M
+    w, rows = {"oproj": (D * D, D), "mlp_up": (F * D, F), "mlp_down": (D * F, D), "out": (da * D, 0),
+               "inproj": (D * da, 0)}[role]
+    return (w + 4 * rows if (w8 and rows) else w * e), 2 * w * M
 
 
 def step_bytes_flops(cfg):
@@ -358,7 +359,7 @@ def main():
     ap.add_argument("--no-fit", action="store_true")
     ap.add_argument("--no-roles", action="store_true")
     ap.add_argument("--no-visibility", action="store_true")
-    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weights line of pi0.5 workloads")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-weights line of bf16 workloads")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' entries")
     ap.add_argument("--weights", choices=("as-given", "fp8"), default="as-given",
                     help="fp8: the expert's per-layer matrices as FP8 E4M3 codes with per-row scales")
@@ -499,9 +500,9 @@ def main():
             ctx.bind_prefix_lengths(None)
         else:
             ctx.bind_context_masks(None, None)
-    # the same workload with the expert's per-layer matrices as FP8 codes (a separate model:
-    # reported beside the bf16 line, never as its value)
-    if cfg["arch"] == 0 and args.weights == "as-given" and not args.no_fp8:
+    # the same workload with the per-layer matrices as FP8 codes (a separate model: reported
+    # beside the bf16 line, never as its value)
+    if dt == 1 and args.weights == "as-given" and not args.no_fp8:
         c8, _ = make_context(cfg, W, I, fmt_fp8=True)
         o8 = torch.empty_like(x0)
         for _ in range(5):

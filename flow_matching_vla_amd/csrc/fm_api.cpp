@@ -3,6 +3,7 @@
 // prefix length).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -154,9 +155,10 @@ struct fm_ctx {
   struct Layer {
     void *qkv = nullptr, *q = nullptr, *kx = nullptr, *vx = nullptr, *o = nullptr, *gu = nullptr, *down = nullptr;
     // FP8 weights (FM_WEIGHTS_FP8_E4M3): codes fragment-major and per-row scales of the same
-    // four matrices, streamed by the loop kernel; qkv .. down then hold the dequantized bf16
-    void *qkv8 = nullptr, *o8 = nullptr, *gu8 = nullptr, *down8 = nullptr;
-    float *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sdown = nullptr;
+    // matrices, streamed by the loop kernel and by the skinny GEMMs of the per-operation graph;
+    // q, qkv .. down then hold the dequantized bf16 (for the large-M GEMMs and the schedule)
+    void *q8 = nullptr, *qkv8 = nullptr, *o8 = nullptr, *gu8 = nullptr, *down8 = nullptr;
+    float *sq = nullptr, *sqkv = nullptr, *so = nullptr, *sgu = nullptr, *sdown = nullptr;
   };
   std::vector<Layer> L;
   void *w_tin = nullptr, *w_tout = nullptr, *w_mod = nullptr, *w_tb = nullptr, *w_in = nullptr, *w_out = nullptr, *w_state = nullptr;
@@ -354,6 +356,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       char* vpl = (char*)ctx->pool + (size_t)(2 * l + 1) * plane;
       // QKV + RoPE + append into pool slots [P, P+H)
       GemmArgs g = gemm_base(Ma, qd + 2 * dh, D, W.qkv);
+      g.w8 = W.qkv8; g.wscale = W.sqkv;
       set_consumer(ctx, g, NORM_RMS, k, 2 * l, nullptr, Mh);
       g.epi = EPI_QKV; g.out = ctx->qbuf; g.ldo = qd;
       g.q_cols = qd; g.kv_cols = dh; g.tq = H; g.kv_off = ctx->prefix_len;
@@ -375,18 +378,21 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.role = FM_OP_ATTN; op.at = at; ops.push_back(op);
       // O projection + gated residual
       g = gemm_base(Ma, D, qd, W.o);
+      g.w8 = W.o8; g.wscale = W.so;
       g.A = ctx->obuf; g.lda = qd;
       g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l, 2); g.stats_out = ctx->stats; g.stats_out_ld = D / kStatCols;
       g.hs = ctx->hs; g.hscale = site(2 * l + 1, 0);
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_OPROJ; op.g = g; ops.push_back(op);
       // gate/up + GELU * up
       g = gemm_base(Ma, c.mlp_gated ? 2 * F : F, D, W.gu);
+      g.w8 = W.gu8; g.wscale = W.sgu;
       set_consumer(ctx, g, NORM_RMS, k, 2 * l + 1, nullptr, Mh);
       g.out = ctx->abuf; g.ldo = F;
       if (c.mlp_gated) g.epi = EPI_GELU_MUL; else { g.epi = EPI_STORE; g.act = ACT_GELU; }
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_UP; op.g = g; ops.push_back(op);
       // down + gated residual
       g = gemm_base(Ma, D, F, W.down);
+      g.w8 = W.down8; g.wscale = W.sdown;
       g.A = ctx->abuf; g.lda = F;
       g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(2 * l + 1, 2); g.stats_out = ctx->stats; g.stats_out_ld = D / kStatCols;
       g.hs = ctx->hs; g.hscale = site(2 * l + 2, 0);
@@ -404,6 +410,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       if (cross) {
         const int ci = l / 2;
         g = gemm_base(Mh, D, D, W.q);
+        g.w8 = W.q8; g.wscale = W.sq;
         set_consumer(ctx, g, NORM_LN, k, l, nullptr, Mh);
         g.epi = EPI_STORE; g.out = ctx->qbuf; g.ldo = D;
         memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_QKV; op.g = g; ops.push_back(op);
@@ -418,6 +425,7 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
         if (ctx->masked[mi]) { at.kmask = ctx->kmask + (size_t)mi * c.max_batch * ctx->ctx_words; at.km_bs = ctx->ctx_words; }
       } else {
         g = gemm_base(Mh, 3 * D, D, W.qkv);
+        g.w8 = W.qkv8; g.wscale = W.sqkv;
         set_consumer(ctx, g, NORM_LN, k, l, nullptr, Mh);
         g.epi = EPI_QKV; g.out = ctx->qbuf; g.ldo = D;
         g.q_cols = D; g.kv_cols = D; g.tq = Tq; g.kv_off = 0; g.rope = 0;
@@ -431,15 +439,18 @@ std::vector<Op> build_step(fm_ctx* ctx, int k, float* vout, float* trace) {
       }
       memset(&op, 0, sizeof op); op.kind = Op::ATTN; op.role = FM_OP_ATTN; op.at = at; ops.push_back(op);
       g = gemm_base(Mh, D, D, W.o);
+      g.w8 = W.o8; g.wscale = W.so;
       g.A = ctx->obuf; g.lda = D;
       g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = site(l, 2); g.stats_out = ctx->stats; g.stats_out_ld = D / kStatCols;
       g.hs = ctx->hs; g.hscale = nullptr;  // the feed-forward LayerNorm carries no modulation
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_OPROJ; op.g = g; ops.push_back(op);
       g = gemm_base(Mh, F, D, W.gu);
+      g.w8 = W.gu8; g.wscale = W.sgu;
       set_consumer(ctx, g, NORM_LN, k, -1, ctx->dff + (size_t)l * F, Mh);
       g.epi = EPI_STORE; g.act = ACT_GELU; g.out = ctx->abuf; g.ldo = F;
       memset(&op, 0, sizeof op); op.kind = Op::GEMM; op.role = FM_OP_MLP_UP; op.g = g; ops.push_back(op);
       g = gemm_base(Mh, D, F, W.down);
+      g.w8 = W.down8; g.wscale = W.sdown;
       g.A = ctx->abuf; g.lda = F;
       g.epi = EPI_RESID; g.h = ctx->h; g.ldh_out = D; g.gate = nullptr; g.stats_out = ctx->stats; g.stats_out_ld = D / kStatCols;
       g.hs = ctx->hs; g.hscale = site(l + 1, 0);
@@ -921,9 +932,9 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
   auto drop = [&](void*& p) { dfree(ctx, p); p = nullptr; };
   for (auto& l : ctx->L) {
     drop(l.qkv); drop(l.q); l.kx = l.vx = nullptr; drop(l.o); drop(l.gu); drop(l.down);
-    drop(l.qkv8); drop(l.o8); drop(l.gu8); drop(l.down8);
-    { void* sp[] = {l.sqkv, l.so, l.sgu, l.sdown}; for (void* q : sp) dfree(ctx, q); }
-    l.sqkv = l.so = l.sgu = l.sdown = nullptr;
+    drop(l.q8); drop(l.qkv8); drop(l.o8); drop(l.gu8); drop(l.down8);
+    { void* sp[] = {l.sq, l.sqkv, l.so, l.sgu, l.sdown}; for (void* q : sp) dfree(ctx, q); }
+    l.sq = l.sqkv = l.so = l.sgu = l.sdown = nullptr;
   }
   ctx->w8 = false;
   drop(ctx->wkx_all); drop(ctx->wvx_all);   // kx / vx point into these
@@ -981,14 +992,20 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
   // FP8 weights: the matrix quantized row by row (codes, row scales, dequantized bf16), then
   // the dequantized matrix laid out for the per-operation kernels and the schedule, and the
   // codes and scales for the loop kernel, all in the same output-row order (rows)
-  const bool w8 = c.arch == FM_ARCH_PREFIX_JOINT && ctx->wformat == FM_WEIGHTS_FP8_E4M3;
+  const bool w8 = ctx->wformat == FM_WEIGHTS_FP8_E4M3;
   void *st8 = nullptr, *stsc = nullptr, *stdq = nullptr;
+  // the largest quantized matrix: the staged row blocks, or a feed-forward matrix (F x D or
+  // D x F), or the pi0.5 output projection (D x n_heads head_dim)
+  const size_t qrows = std::max({stage_rows, (size_t)F, (size_t)D});
+  size_t qelems = std::max(stage_rows * D, (size_t)F * D);
+  if (c.arch == FM_ARCH_PREFIX_JOINT) qelems = std::max(qelems, (size_t)D * c.n_heads * c.head_dim);
   if (w8) {
-    if ((s = dalloc(ctx, &st8, stage_rows * D)) != FM_OK) return s;
-    if ((s = dalloc(ctx, &stsc, stage_rows * 4)) != FM_OK) return s;
-    if ((s = dalloc(ctx, &stdq, stage_rows * D * esz)) != FM_OK) return s;
+    if ((s = dalloc(ctx, &st8, qelems)) != FM_OK) return s;
+    if ((s = dalloc(ctx, &stsc, qrows * 4)) != FM_OK) return s;
+    if ((s = dalloc(ctx, &stdq, qelems * esz)) != FM_OK) return s;
   }
   auto q8 = [&](void** dbf, void** d8, float** dsc, const void* src, const int* rws, int N, int K) -> fm_status {
+    if ((size_t)N > qrows || (size_t)N * K > qelems) return fail(ctx, FM_ERR_SHAPE, "FP8 staging smaller than a matrix");
     HIPCK(quantize_fp8_rows(src, K, N, K, (uint8_t*)st8, (float*)stsc, stdq, ctx->stream));
     fm_status st2 = swz(dbf, stdq, rws, N, K);
     if (st2 != FM_OK) return st2;
@@ -1055,7 +1072,8 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
       const std::string p = "blocks." + std::to_string(i) + ".";
       auto& W = ctx->L[i];
       if (i % 2 == 0) {
-        if ((s = swz(&W.q, data((p + "q.w").c_str()), nullptr, D, D)) != FM_OK) return s;
+        const void* qw = data((p + "q.w").c_str());
+        if ((s = w8 ? q8(&W.q, &W.q8, &W.sq, qw, nullptr, D, D) : swz(&W.q, qw, nullptr, D, D)) != FM_OK) return s;
         W.kx = (char*)ctx->wkx_all + (size_t)(i / 2) * xb;
         W.vx = (char*)ctx->wvx_all + (size_t)(i / 2) * xb;
         HIPCK(swizzle_weight(W.kx, data((p + "k.w").c_str()), nullptr, D, c.ctx_dim, c.ctx_dim, elem, ctx->stream));
@@ -1064,12 +1082,15 @@ fm_status fm_load_weights(fm_ctx* ctx, const fm_tensor* t, int32_t n) {
         HIPCK(hipMemcpyAsync(stage, data((p + "q.w").c_str()), (size_t)D * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
         HIPCK(hipMemcpyAsync((char*)stage + (size_t)D * D * esz, data((p + "k.w").c_str()), (size_t)D * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
         HIPCK(hipMemcpyAsync((char*)stage + (size_t)2 * D * D * esz, data((p + "v.w").c_str()), (size_t)D * D * esz, hipMemcpyDeviceToDevice, ctx->stream));
-        if ((s = swz(&W.qkv, stage, nullptr, 3 * D, D)) != FM_OK) return s;
+        if ((s = w8 ? q8(&W.qkv, &W.qkv8, &W.sqkv, stage, nullptr, 3 * D, D) : swz(&W.qkv, stage, nullptr, 3 * D, D)) != FM_OK) return s;
         HIPCK(hipStreamSynchronize(ctx->stream));
       }
-      if ((s = swz(&W.o, data((p + "o.w").c_str()), nullptr, D, D)) != FM_OK) return s;
-      if ((s = swz(&W.gu, data((p + "ff1.w").c_str()), nullptr, F, D)) != FM_OK) return s;
-      if ((s = swz(&W.down, data((p + "ff2.w").c_str()), nullptr, D, F)) != FM_OK) return s;
+      const void* ow = data((p + "o.w").c_str());
+      const void* f1 = data((p + "ff1.w").c_str());
+      const void* f2 = data((p + "ff2.w").c_str());
+      if ((s = w8 ? q8(&W.o, &W.o8, &W.so, ow, nullptr, D, D) : swz(&W.o, ow, nullptr, D, D)) != FM_OK) return s;
+      if ((s = w8 ? q8(&W.gu, &W.gu8, &W.sgu, f1, nullptr, F, D) : swz(&W.gu, f1, nullptr, F, D)) != FM_OK) return s;
+      if ((s = w8 ? q8(&W.down, &W.down8, &W.sdown, f2, nullptr, D, F) : swz(&W.down, f2, nullptr, D, F)) != FM_OK) return s;
     }
   }
   if (c.arch == FM_ARCH_DIT_CROSS) {
@@ -1104,8 +1125,9 @@ fm_status fm_set_weight_format(fm_ctx* ctx, int32_t format) {
   const fm_config& c = ctx->c;
   if (format != FM_WEIGHTS_AS_GIVEN && format != FM_WEIGHTS_FP8_E4M3)
     return fail(ctx, FM_ERR_INVALID_ARG, fmt("weight format %d", format));
-  if (format == FM_WEIGHTS_FP8_E4M3 && (c.arch != FM_ARCH_PREFIX_JOINT || c.dtype != FM_BF16 || c.mlp_dim % 64 != 0))
-    return fail(ctx, FM_ERR_UNSUPPORTED, "FP8 weights need the prefix-joint expert in bf16 with mlp_dim a multiple of 64");
+  if (format == FM_WEIGHTS_FP8_E4M3 &&
+      (c.dtype != FM_BF16 || c.mlp_dim % 64 != 0 || (c.arch == FM_ARCH_DIT_CROSS && c.hidden % 64 != 0)))
+    return fail(ctx, FM_ERR_UNSUPPORTED, "FP8 weights need bf16, mlp_dim a multiple of 64 and (DiT head) hidden a multiple of 64");
   ctx->wformat = format;
   return FM_OK;
 }

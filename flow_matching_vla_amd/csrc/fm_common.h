@@ -82,6 +82,15 @@ template <> __device__ __forceinline__ V16 pack<bf16>(const float* in) {
 }
 __device__ __forceinline__ V16 vzero() { return V16{0u, 0u, 0u, 0u}; }
 
+// Eight FP8 E4M3 codes (two words, k order) to the bf16 MFMA operand, exactly (a row's
+// power-of-two scale is applied to the sums instead).
+__device__ __forceinline__ V16 fp8x8_bf16(uint32_t w0, uint32_t w1) {
+  return V16{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+}
+
 // GELU, tanh form: 0.5 x (1 + tanh z) with z = sqrt(2/pi) (x + 0.044715 x^3), evaluated as
 // x / (1 + e^(-2z)) (the same function: 0.5 (1 + tanh z) = 1 / (1 + e^(-2z))), one
 // exponential and one division instead of a full tanh.

@@ -859,8 +859,14 @@ __global__ void __launch_bounds__(WMW * WNW * 64, big_pair(BM, BN, WMW * WNW) ? 
 // ---------------------------------------------------------------------------------------
 // ST: the range can hold more than one stage (a second register set, double buffering);
 // without it the range is exactly one stage and the kernel keeps half the registers.
-template <typename T, int KW, int NB, int CPW, int EPI, bool NORM, bool ST>
+// W8: the weights are FP8 E4M3 codes (a.W as swizzle_fp8 lays them out: one 1 KB fragment
+// holds 16 rows x 64 k, i.e. the chunk pair a wave takes per stage with CPW = 2), converted to
+// bf16 exactly in registers, and the sums are scaled by the rows' powers of two before the
+// epilogue. With the same chunk pairs per wave and the same split ranges as the bf16 kernel,
+// the result equals the bf16 kernel's on the dequantized weights bit for bit.
+template <typename T, int KW, int NB, int CPW, int EPI, bool NORM, bool ST, bool W8>
 __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
+  static_assert(!W8 || (CPW == 2 && sizeof(T) == 2), "FP8 weights: chunk pairs of bf16");
   typedef Mma<T> MT;
   typedef typename MT::frag frag;
   constexpr int NT = KW * 64, VEC = MT::VEC, KC = MT::KC;
@@ -897,9 +903,10 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     const int r = 16 * mb + (lane % 16);
     aoff[mb] = r < a.M ? (uint32_t)(((long)a_row(a, r) * a.lda + (lane / 16) * VEC) * sizeof(T)) : kOob;
   }
-  // weight fragments: fragment (nb, c) is 1 KB at ((nb * KCt + c) * 64 + lane) * 16 bytes
+  // weight fragments: fragment (nb, c) is 1 KB at ((nb * KCt + c) * 64 + lane) * 16 bytes;
+  // FP8: fragment (nb, c / 2) at ((nb * KCt / 2 + c / 2) * 64 + lane) * 16 bytes
   const Rsrc rw = make_rsrc(a.W, a.w_bytes);
-  const uint32_t wbase = (uint32_t)((n0 / 16) * KCt * 1024 + lane * 16);
+  const uint32_t wbase = W8 ? (uint32_t)((n0 / 16) * (KCt / 2) * 1024 + lane * 16) : (uint32_t)((n0 / 16) * KCt * 1024 + lane * 16);
 
   V16 ra0[CPW][MB], rb0[CPW][NB], ra1[CPW][MB], rb1[CPW][NB];
   auto issue = [&](int stg, V16 (&xa)[CPW][MB], V16 (&xb)[CPW][NB]) {
@@ -909,8 +916,16 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
       const bool cok = cc < c_hi;   // uniform per wave
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) xa[c][mb] = bload16(ra, cok ? aoff[mb] + (uint32_t)(cc * KC * sizeof(T)) : kOob);
+      if constexpr (W8) {
+        // the pair's codes (chunk c_lo + ... is even: ranges and stages hold whole pairs)
+        if (c == 0) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) xb[c][nb] = bload16(rw, cok ? wbase + (uint32_t)((nb * KCt + cc) * 1024) : kOob);
+          for (int nb = 0; nb < NB; ++nb) xb[0][nb] = bload16(rw, cok ? wbase + (uint32_t)((nb * (KCt / 2) + cc / 2) * 1024) : kOob);
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) xb[c][nb] = bload16(rw, cok ? wbase + (uint32_t)((nb * KCt + cc) * 1024) : kOob);
+      }
     }
   };
   issue(0, ra0, rb0);
@@ -931,13 +946,19 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto mma = [&](const V16 (&xa)[CPW][MB], const V16 (&xb)[CPW][NB]) {
+    V16 wb[CPW][NB];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        wb[c][nb] = W8 ? (c == 0 ? fp8x8_bf16(xb[0][nb][0], xb[0][nb][1]) : fp8x8_bf16(xb[0][nb][2], xb[0][nb][3])) : xb[c][nb];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = MT::mma(__builtin_bit_cast(frag, xa[c][mb]), __builtin_bit_cast(frag, xb[c][nb]), acc[mb][nb]);
+          acc[mb][nb] = MT::mma(__builtin_bit_cast(frag, xa[c][mb]), __builtin_bit_cast(frag, wb[c][nb]), acc[mb][nb]);
   };
   if constexpr (!ST) {
     mma(ra0, rb0);
@@ -1018,6 +1039,10 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     const int i = tid + q * NT;
     if (i < BM * BN / 4) {
       const int r = i / (BN / 4), c4 = i % (BN / 4);
+      if constexpr (W8) {   // the rows' scales of these four output columns (padded to N, 4)
+        const int n = n0 + 4 * c4;
+        part[q] *= n < a.N ? *(const f32x4*)(a.wscale + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       *(f32x4*)(red + r * LDR + c4 * 4) = part[q];
     }
   }
@@ -1055,6 +1080,7 @@ int gemm_num_tiles(const GemmArgs& a) {
 
 void gemm_plan(GemmArgs& a, int elem, int num_cus) {
   const int kq = elem == ET_BF16 ? 32 : 16;
+  a.fp8 = 0;   // set below where the skinny kernel streams FP8 weights
   const int esz = elem == ET_BF16 ? 2 : 4;
   if (a.M <= 64 && elem == ET_BF16 && a.K % 32 == 0) {
     // Weight streaming in bf16: eight waves, two chunks per wave and stage (double-buffered
@@ -1073,9 +1099,13 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
     if (splits > kct / 8) splits = kct / 8;
     if (splits > 16) splits = 16;
     if (splits < 1) splits = 1;
-    const int span = (kct + splits - 1) / splits;
+    int span = (kct + splits - 1) / splits;
+    // whole chunk pairs per range when K allows (the FP8 weights hold pairs; the bf16 kernel
+    // takes the same ranges, so the two add the same partial sums in the same order)
+    if (a.K % 64 == 0) span = (span + 1) & ~1;
     a.splits = (kct + span - 1) / span;
     a.k_split = span * kq;
+    a.fp8 = a.w8 && a.wscale && a.K % 64 == 0 ? 1 : 0;
     return;
   }
   if (a.M <= 64) {
@@ -1215,13 +1245,13 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
 }
 
 // Skinny instantiations: the residual epilogue never consumes a norm; the others can.
-template <typename T, int KW, int NB, int CPW, bool ST>
+template <typename T, int KW, int NB, int CPW, bool ST, bool W8>
 static hipError_t launch_skinny_st(const GemmArgs& a, hipStream_t s) {
   const int per_round = 8 * a.splits;   // whole column tiles per XCD range
   const int items = ((a.N + 16 * NB - 1) / (16 * NB)) * a.splits;
   const dim3 grid((items + per_round - 1) / per_round * per_round), block(KW * 64);
   const bool norm = a.norm != NORM_NONE;
-#define K_SK(E, NRM) hipLaunchKernelGGL((k_gemm_skinny<T, KW, NB, CPW, E, NRM, ST>), grid, block, 0, s, a)
+#define K_SK(E, NRM) hipLaunchKernelGGL((k_gemm_skinny<T, KW, NB, CPW, E, NRM, ST, W8>), grid, block, 0, s, a)
   switch (a.epi) {
     case EPI_STORE: if (norm) K_SK(EPI_STORE, true); else K_SK(EPI_STORE, false); break;
     case EPI_GELU_MUL: if (norm) K_SK(EPI_GELU_MUL, true); else K_SK(EPI_GELU_MUL, false); break;
@@ -1242,12 +1272,18 @@ static hipError_t launch_skinny_st(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// a range of more than one stage needs the double-buffered kernel (CPW 2 only: registers)
+// a range of more than one stage needs the double-buffered kernel (CPW 2 only: registers);
+// FP8 weights run with eight waves and chunk pairs only
 template <typename T, int KW, int NB, int CPW>
 static hipError_t launch_skinny_cpw(const GemmArgs& a, hipStream_t s) {
   const int kc = sizeof(T) == 2 ? 32 : 16;
-  if (a.k_split <= KW * CPW * kc) return launch_skinny_st<T, KW, NB, CPW, false>(a, s);
-  if constexpr (CPW == 2) return launch_skinny_st<T, KW, NB, CPW, true>(a, s);
+  const bool one = a.k_split <= KW * CPW * kc;
+  if constexpr (sizeof(T) == 2 && KW == 8 && CPW == 2) {
+    if (a.fp8) return one ? launch_skinny_st<T, KW, NB, CPW, false, true>(a, s) : launch_skinny_st<T, KW, NB, CPW, true, true>(a, s);
+  }
+  if (a.fp8) return hipErrorInvalidValue;
+  if (one) return launch_skinny_st<T, KW, NB, CPW, false, false>(a, s);
+  if constexpr (CPW == 2) return launch_skinny_st<T, KW, NB, CPW, true, false>(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -1317,7 +1353,11 @@ hipError_t gemm_launch(const GemmArgs& in, int elem, hipStream_t s) {
   const int esz = elem == ET_BF16 ? 2 : 4;
   const long rows = (long)((a.M - 1) / a.row_group) * a.row_gstride + a.row_off + (a.M - 1) % a.row_group + 1;
   const long a_bytes = rows * a.lda * esz;
-  const long w_bytes = (long)swizzled_bytes(a.N, a.K, elem);
+  if (a.fp8) {
+    if (a.kind != GEMM_SKINNY || elem != ET_BF16 || !a.w8 || !a.wscale || a.K % 64 != 0 || a.k_split % 64 != 0) return hipErrorInvalidValue;
+    a.W = a.w8;
+  }
+  const long w_bytes = a.fp8 ? (long)swizzled_fp8_bytes(a.N, a.K) : (long)swizzled_bytes(a.N, a.K, elem);
   const long ws_bytes = (long)gemm_ws_bytes(a);
   if (a_bytes >= (1L << 31) || w_bytes >= (1L << 31) || ws_bytes >= (1L << 31)) return hipErrorInvalidValue;
   a.a_bytes = (uint32_t)a_bytes; a.w_bytes = (uint32_t)w_bytes; a.ws_bytes = (uint32_t)ws_bytes;

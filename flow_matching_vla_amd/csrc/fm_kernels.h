@@ -65,6 +65,11 @@ struct GemmArgs {
   // n / col_group, the planes col_gstride elements apart (col_group 0: one plane). Kept last,
   // so that the fields above keep their offsets in the kernel arguments.
   int col_group; long col_gstride;
+  // Optional FP8 E4M3 copy of the weights (codes fragment-major as swizzle_fp8, with the
+  // matrix's per-row power-of-two scales by output column, padded to N rounded up to 4). The
+  // planner sets fp8 when the skinny kernel then streams the codes instead of W (bf16, K a
+  // multiple of 64); the sums are scaled per column before the epilogue.
+  const void* w8; const float* wscale; int fp8;
 };
 constexpr long kVecPad = 1L << 18;   // floats in the zeros / ones buffers
 // Split-K arrival counters (GemmArgs::counters): one per output tile.

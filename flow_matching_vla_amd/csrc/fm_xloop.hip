@@ -258,15 +258,6 @@ __device__ __forceinline__ int prefetch_w(const void* W, uint32_t wbytes, int kb
   return issued;
 }
 
-// Eight FP8 codes (two words, k order) to the bf16 MFMA operand, exactly (the row scale is
-// applied in the epilogue).
-__device__ __forceinline__ V16 fp8x8_bf16(uint32_t w0, uint32_t w1) {
-  return V16{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
-             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
-             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
-             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
-}
-
 // ---------------------------------------------------------------------------------------
 // GEMM of one phase: nt (1 or 2) tiles of 16 output columns over this CU's K range of nch
 // 32-wide chunks, weights in LDS at `slot` (as prefetch_w put them), A fragment-major with kba

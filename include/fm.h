@@ -207,16 +207,21 @@ static inline int32_t fm_pool_v_slot(int32_t j, int32_t dtype) {
   return dtype != FM_BF16 ? j : ((j & ~31) | (((j >> 2) & 3) << 3) | (((j >> 4) & 1) << 2) | (j & 3));
 }
 
-/* Storage of the expert's per-layer matrices (q, k, v, o, gate, up, down), applied by the next
+/* Storage of the expert's per-layer matrices (listed below), applied by the next
  * fm_load_weights (vla.cpp Sec. IV-D, Table V: quantized action-head weights; pi0.5 Design
  * names FP8 for the expert).
  *   FM_WEIGHTS_AS_GIVEN  the config dtype (default).
  *   FM_WEIGHTS_FP8_E4M3  each row (output feature) becomes OCP FP8 E4M3 codes times one
  *     power-of-two scale 2^e, e the smallest exponent with max |row| <= 448 2^e; codes round
- *     to nearest, ties to even. The loop kernel streams the codes (half the bytes) and turns
- *     them into bf16 exactly; the per-operation kernels use the dequantized bf16 weights. Both
- *     therefore compute the same function of the dequantized weights, which is the model.
- *     PREFIX_JOINT in FM_BF16 with mlp_dim a multiple of 64 (FM_ERR_UNSUPPORTED otherwise).
+ *     to nearest, ties to even. The loop kernel and the per-operation graph's weight-streaming
+ *     GEMMs (64 rows or fewer: batch 1) stream the codes (half the bytes) and turn them into
+ *     bf16 exactly, scaling each output column's sums by its row's 2^e; the larger GEMMs use
+ *     the dequantized bf16 weights. All therefore compute the same function of the
+ *     dequantized weights, which is the model. Quantized: the per-layer q / k / v, o and MLP
+ *     matrices (PREFIX_JOINT), and every block's q, the self blocks' k and v, o, ff1 and ff2
+ *     (DIT_CROSS; the cross blocks' context projections, applied once per binding, stay in
+ *     the config dtype). FM_BF16 with mlp_dim, and for DIT_CROSS hidden, a multiple of 64
+ *     (FM_ERR_UNSUPPORTED otherwise).
  * FM_ERR_INVALID_ARG for another format. */
 enum { FM_WEIGHTS_AS_GIVEN = 0, FM_WEIGHTS_FP8_E4M3 = 1 };
 fm_status fm_set_weight_format(fm_ctx* ctx, int32_t format);

@@ -462,13 +462,25 @@ def quantize_fp8_rows(w):
     return codes, e, np.ldexp(fp8_e4m3_value(codes), e[:, None])
 
 
+FP8_BLOCK_WEIGHTS = ("q.w", "o.w", "ff1.w", "ff2.w")        # every DiT block
+FP8_SELF_BLOCK_WEIGHTS = ("k.w", "v.w")                      # self-attention blocks only
+
+
 def fp8_weights(cfg, w):
-    """The expert's per-layer matrices replaced by their FP8-dequantized values (pi0.5-shaped
-    expert); everything else unchanged."""
+    """The action head's per-layer matrices replaced by their FP8-dequantized values, everything
+    else unchanged. pi0.5-shaped expert: q, k, v, o, gate, up, down of every layer. DiT head:
+    the matrices applied to the action tokens inside the loop, namely q, o, ff1, ff2 of every
+    block and k, v of the self-attention (odd) blocks; the cross blocks' k, v act on the
+    context once per observation (bind), outside the loop, and keep the configured dtype
+    (reading: the low-bit format serves the streamed weights of the denoise loop)."""
     out = dict(w)
     for l in range(cfg["n_layers"]):
-        for nm in FP8_LAYER_WEIGHTS:
-            key = f"layers.{l}.{nm}"
+        if cfg["arch"] == ARCH_PREFIX_JOINT:
+            keys = [f"layers.{l}.{nm}" for nm in FP8_LAYER_WEIGHTS]
+        else:
+            names = FP8_BLOCK_WEIGHTS + (FP8_SELF_BLOCK_WEIGHTS if l % 2 == 1 else ())
+            keys = [f"blocks.{l}.{nm}" for nm in names]
+        for key in keys:
             if key in out:
                 out[key] = quantize_fp8_rows(out[key])[2].astype(np.asarray(w[key]).dtype)
     return out

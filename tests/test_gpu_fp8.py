@@ -8,10 +8,12 @@ weights, pi0.5 Design FP8 for the expert).
     integer decision, taken in the same precision on both sides: the scaled value is exact).
   * The loop: the FP8 context computes the model whose weights are the dequantized values.
     A bf16 context loaded with exactly those values must give bit-identical chunks, since a
-    power-of-two row scale commutes with every fp32 rounding. This holds on the loop kernel,
-    which streams the codes, and on the per-operation graph, which reads the dequantized
-    bf16 copies. Against the oracle on the dequantized weights the tolerances are the bf16
-    ones: <= 1e-2 per teacher-forced step velocity, <= 2e-2 on the chunk."""
+    power-of-two row scale commutes with every fp32 rounding and the codes convert to bf16
+    exactly. This holds on the loop kernel and on the per-operation graph's GEMMs of at most
+    64 rows, which stream the codes, and on the larger graph GEMMs, which read dequantized
+    bf16 copies; for the pi0.5-shaped expert and the DiT head (whose cross blocks' context
+    projections stay bf16). Against the oracle on the dequantized weights the tolerances are
+    the bf16 ones: <= 1e-2 per teacher-forced step velocity, <= 2e-2 on the chunk."""
 import numpy as np
 import pytest
 
@@ -52,24 +54,34 @@ def _context(cfg, W, I, fp8, steps):
         ctx.set_weight_format(fm.WEIGHTS_FP8_E4M3)
     ctx.load_weights({n: fm.to_device(a, dt) for n, a in W.items()})
     L, B = cfg["n_layers"], cfg["batch"]
-    ctx.bind_prefix_kv(B, cfg["prefix_len"], [fm.to_device(I[f"prefix.k.{l}"], dt) for l in range(L)],
-                       [fm.to_device(I[f"prefix.v.{l}"], dt) for l in range(L)])
+    if cfg["arch"] == wl.ARCH_PREFIX_JOINT:
+        ctx.bind_prefix_kv(B, cfg["prefix_len"], [fm.to_device(I[f"prefix.k.{l}"], dt) for l in range(L)],
+                           [fm.to_device(I[f"prefix.v.{l}"], dt) for l in range(L)])
+    else:
+        ctx.bind_prefix_kv(B, cfg["ctx_len"], context=fm.to_device(I["context"], dt),
+                           state=fm.to_device(I["state"], fm.F32))
     ctx.set_schedule(steps, B)
     torch.cuda.synchronize()
     return ctx
 
 
-@pytest.mark.parametrize("name,over", [
-    ("pi05_b1", dict(n_layers=2, steps=2)),               # the loop kernel streams the codes
-    ("pi05_b8", dict(n_layers=2, steps=2, batch=3)),      # the per-operation graph
+@pytest.mark.parametrize("name,over,graph", [
+    ("pi05_b1", dict(n_layers=2, steps=2), False),            # the loop kernel streams the codes
+    ("pi05_b1", dict(n_layers=2, steps=2), True),             # graph GEMMs of 50 rows stream them
+    ("pi05_b8", dict(n_layers=2, steps=2, batch=3), False),   # graph GEMMs of 150 rows: bf16 copies
+    ("dit_b1", dict(n_layers=4, steps=2), False),             # DiT head, 41 rows: codes streamed
+    ("dit_b1", dict(n_layers=2, steps=2, batch=2), False),    # two requests, 82 rows: bf16 copies
 ])
-def test_fp8_context_equals_dequantized_bf16(name, over):
+def test_fp8_context_equals_dequantized_bf16(name, over, graph):
     import torch
     cfg = wl.workload(name, **over)
     W = wl.make_weights(cfg)
     Wq = oracle.fp8_weights(cfg, W)          # the model an FP8 context computes (exact in bf16)
     c = Case(cfg, W=Wq)                       # bf16 context holding the dequantized weights
     a8 = _context(cfg, W, c.I, True, c.steps)
+    if graph:
+        a8.set_loop_mode(fm.LOOP_GRAPH)
+        c.ctx.set_loop_mode(fm.LOOP_GRAPH)
     assert a8.loop_status()[0] == c.ctx.loop_status()[0]
     x8 = a8.denoise(c.x0, c.steps)
     torch.cuda.synchronize()
@@ -96,7 +108,9 @@ def test_fp8_context_equals_dequantized_bf16(name, over):
 
 
 def test_fp8_weight_format_errors():
-    for cfg in (wl.workload("tiny_fp32"), wl.workload("dit_b1", n_layers=2)):
+    # fp32 configurations, and an MLP width that is not a multiple of 64
+    for cfg in (wl.workload("tiny_fp32"), wl.workload("dit_b1", n_layers=2, dtype=wl.DTYPE_F32),
+                wl.workload("dit_b1", n_layers=2, mlp_dim=6144 + 32)):
         ctx = fm.Context(cfg)
         with pytest.raises(fm.FMError) as e:
             ctx.set_weight_format(fm.WEIGHTS_FP8_E4M3)

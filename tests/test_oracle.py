@@ -659,17 +659,35 @@ def test_fp8_row_scales_and_error_bound():
     np.testing.assert_array_equal(e2, e[:4] + 5)
 
 
-def test_fp8_weights_replace_only_layer_matrices():
-    cfg = _tiny()
+def _fp8_expected(cfg, key):
+    """The matrices the low-bit format covers, listed by hand: every per-layer matrix of the
+    pi0.5-shaped expert; in the DiT head q, o, ff1, ff2 of every block and k, v of the
+    self-attention (odd) blocks only."""
+    parts = key.split(".")
+    if cfg["arch"] == wl.ARCH_PREFIX_JOINT:
+        return parts[0] == "layers" and parts[2] in ("q", "k", "v", "o", "gate", "up", "down") and parts[3] == "w"
+    if parts[0] != "blocks" or parts[3] != "w":
+        return False
+    return parts[2] in ("q", "o", "ff1", "ff2") or (parts[2] in ("k", "v") and int(parts[1]) % 2 == 1)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "dit_b1"])
+def test_fp8_weights_replace_only_layer_matrices(name):
+    cfg = _tiny() if name == "tiny_fp32" else wl.workload(name, n_layers=4, hidden=64, n_heads=2, head_dim=32,
+                                                          n_kv_heads=2, mlp_dim=128, ctx_dim=48)
     W = wl.make_weights(cfg)
     Q = oracle.fp8_weights(cfg, W)
+    n = 0
     for k in W:
-        if any(k.endswith(nm) for nm in oracle.FP8_LAYER_WEIGHTS) and k.startswith("layers."):
+        if _fp8_expected(cfg, k):
+            n += 1
             assert not np.array_equal(Q[k], W[k])
             e = oracle.fp8_row_exponents(W[k])[:, None]   # half a quantum: relative 2^-4, or 2^(e-10) for subnormals
             assert np.all(np.abs(Q[k] - W[k]) <= np.maximum(np.abs(W[k]) / 16, np.ldexp(1.0, e - 10)))
         else:
             np.testing.assert_array_equal(Q[k], W[k])
+    L = cfg["n_layers"]
+    assert n == (7 * L if cfg["arch"] == wl.ARCH_PREFIX_JOINT else 4 * L + 2 * (L // 2))
 
 
 # ----------------------------------------------------------------------------- after the path
