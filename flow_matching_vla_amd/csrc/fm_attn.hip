@@ -169,6 +169,10 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m_run[qb] = VIS ? -1e30f : -INFINITY; l_run[qb] = 0.f; }
 
+  // a wave whose query rows all lie past R (the row tile's unused tail, e.g. 41 DiT tokens in
+  // a 128-row tile) still copies its share of every tile and meets every barrier, but reads
+  // no fragment and computes nothing (wave-uniform)
+  const bool active = rt * ROWS + wave * QB * 16 < R;
   for (int t = 0; t < ntile; ++t) {
     const int kt = tile_start(t);
     if (t + NST - 1 < ntile) issue(tile_start(t + NST - 1), (t + NST - 1) % NST);
@@ -187,6 +191,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
     __syncthreads();
     const V16* sK = sbuf[t % NST];
     const V16* sV = sK + FK * 64;
+    if (active) {
 
     // S^T = K Q^T: 16 keys x 16 queries per (kb, qb), two partial chains each. A key
     // block's fragments are all read from LDS before its MFMAs, so the reads overlap each
@@ -291,6 +296,7 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = MT::mma(__builtin_bit_cast(frag, vf[db * KCH + kc]), pf[qb][kc], o[qb][db]);
+    }
     __syncthreads();   // this buffer is refilled by the next iteration's copies
   }
 
@@ -315,7 +321,9 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
       continue;
     }
     // split keys: unnormalised O^T in the MFMA output layout ([block][db][lane][e], one
-    // 16-byte store per lane and d-block) and (m, l) of each query row
+    // 16-byte store per lane and d-block) and (m, l) of each query row; an inactive wave's
+    // rows are past R, and the merge never stores them
+    if (!active) continue;
     float* wo = a.ws + ((long)tile_id * a.splits + sp) * (ROWS * DH);
 #pragma unroll
     for (int db = 0; db < DB; ++db) *(f32x4*)(wo + ((blk * DB + db) * 64 + lane) * 4) = o[qb][db];
