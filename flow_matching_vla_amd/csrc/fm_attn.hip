@@ -173,9 +173,10 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
   // a 128-row tile) still copies its share of every tile and meets every barrier, but reads
   // no fragment and computes nothing (wave-uniform)
   const bool active = rt * ROWS + wave * QB * 16 < R;
+  // One barrier per tile: after it, tile t is visible to every wave and every wave has left
+  // tile t - 1, whose buffer then takes tile t + NST - 1 (the copies run during the compute).
   for (int t = 0; t < ntile; ++t) {
     const int kt = tile_start(t);
-    if (t + NST - 1 < ntile) issue(tile_start(t + NST - 1), (t + NST - 1) % NST);
     // visibility bits of the tile's 32 keys (a scalar load: its wait does not count the
     // tile copies)
     uint32_t vis = 0xffffffffu;
@@ -185,10 +186,12 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
       vis &= bits_below(key_end - kt);
       vis &= ~(bits_below(a.seg_end - kt) & ~bits_below(pb - kt));   // the keys in [pb, seg_end)
     }
-    // tile t's copies are done once at most the tiles issued after it are in flight
-    if (t + NST - 1 < ntile) FM_WAIT_VMCNT((NST - 1) * FPW);
+    // tile t's copies are done once at most the tiles issued after it (t + 1 .. t + NST - 2)
+    // are in flight
+    if (t + NST - 2 < ntile) FM_WAIT_VMCNT((NST - 2) * FPW);
     else wait_tiles<FPW, NST>(ntile - 1 - t);
     __syncthreads();
+    if (t + NST - 1 < ntile) issue(tile_start(t + NST - 1), (t + NST - 1) % NST);
     const V16* sK = sbuf[t % NST];
     const V16* sV = sK + FK * 64;
     if (active) {
@@ -297,7 +300,6 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = MT::mma(__builtin_bit_cast(frag, vf[db * KCH + kc]), pf[qb][kc], o[qb][db]);
     }
-    __syncthreads();   // this buffer is refilled by the next iteration's copies
   }
 
 #pragma unroll
