@@ -466,23 +466,30 @@ FP8_BLOCK_WEIGHTS = ("q.w", "o.w", "ff1.w", "ff2.w")        # every DiT block
 FP8_SELF_BLOCK_WEIGHTS = ("k.w", "v.w")                      # self-attention blocks only
 
 
-def fp8_weights(cfg, w):
-    """The action head's per-layer matrices replaced by their FP8-dequantized values, everything
-    else unchanged. pi0.5-shaped expert: q, k, v, o, gate, up, down of every layer. DiT head:
-    the matrices applied to the action tokens inside the loop, namely q, o, ff1, ff2 of every
-    block and k, v of the self-attention (odd) blocks; the cross blocks' k, v act on the
-    context once per observation (bind), outside the loop, and keep the configured dtype
-    (reading: the low-bit format serves the streamed weights of the denoise loop)."""
-    out = dict(w)
+def fp8_weight_names(cfg):
+    """Names of the matrices the low-bit format covers. pi0.5-shaped expert: q, k, v, o, gate,
+    up, down of every layer. DiT head: the matrices applied to the action tokens inside the
+    loop, namely q, o, ff1, ff2 of every block and k, v of the self-attention (odd) blocks; the
+    cross blocks' k, v act on the context once per observation (bind), outside the loop, and
+    keep the configured dtype (reading: the low-bit format serves the streamed weights of the
+    denoise loop)."""
+    keys = []
     for l in range(cfg["n_layers"]):
         if cfg["arch"] == ARCH_PREFIX_JOINT:
-            keys = [f"layers.{l}.{nm}" for nm in FP8_LAYER_WEIGHTS]
+            keys += [f"layers.{l}.{nm}" for nm in FP8_LAYER_WEIGHTS]
         else:
             names = FP8_BLOCK_WEIGHTS + (FP8_SELF_BLOCK_WEIGHTS if l % 2 == 1 else ())
-            keys = [f"blocks.{l}.{nm}" for nm in names]
-        for key in keys:
-            if key in out:
-                out[key] = quantize_fp8_rows(out[key])[2].astype(np.asarray(w[key]).dtype)
+            keys += [f"blocks.{l}.{nm}" for nm in names]
+    return keys
+
+
+def fp8_weights(cfg, w):
+    """The matrices fp8_weight_names lists replaced by their FP8-dequantized values, everything
+    else unchanged."""
+    out = dict(w)
+    for key in fp8_weight_names(cfg):
+        if key in out:
+            out[key] = quantize_fp8_rows(out[key])[2].astype(np.asarray(w[key]).dtype)
     return out
 
 

@@ -107,6 +107,57 @@ def test_fp8_context_equals_dequantized_bf16(name, over, graph):
     c.close()
 
 
+def _fp8_exact(cfg, W, seed):
+    """The same weights with every matrix the format covers replaced by FP8-exact rows: random
+    finite E4M3 codes of either sign times a per-row power of two, each row holding a code of
+    value 448 (so the quantizer's exponent is that power and its codes are these). The
+    dequantized weights are then these weights themselves: no full-size quantization on the
+    host is needed (the quantizer is pinned against the oracle above)."""
+    rng = np.random.default_rng(seed)
+    table = oracle.fp8_e4m3_value(np.arange(256))          # value of every code byte
+    out = dict(W)
+    for key in oracle.fp8_weight_names(cfg):
+        N, K = W[key].shape
+        codes = rng.integers(0x18, 0x7F, size=(N, K), dtype=np.int64)   # exponent field >= 3, no NaN
+        codes |= rng.integers(0, 2, size=(N, K), dtype=np.int64) << 7
+        codes[:, 0] = 0x7E | (codes[:, 0] & 0x80)                         # |value| 448 in every row
+        e = rng.integers(-13, -11, size=(N, 1))
+        out[key] = np.ldexp(table[codes], e).astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("name", ["dit_b1", "pi05_b1"])
+def test_fp8_full_size_equals_bf16_on_fp8_exact_weights(name):
+    # the whole head at its bench size: the FP8 context (codes streamed by the skinny GEMMs for
+    # DiT, by the loop kernel for pi0.5) against a bf16 context on the same FP8-exact weights,
+    # bitwise, and against the oracle over two teacher-forced steps
+    import torch
+    cfg = wl.workload(name, steps=2)
+    W8 = _fp8_exact(cfg, wl.make_weights(cfg), seed=17)
+    say(f"  {name}: FP8-exact weights built")
+    c = Case(cfg, W=W8)
+    a8 = _context(cfg, W8, c.I, True, c.steps)
+    assert a8.loop_status()[0] == c.ctx.loop_status()[0]
+    x8 = a8.denoise(c.x0, c.steps)
+    torch.cuda.synchronize()
+    x8 = x8.cpu().numpy()
+    xq = c.gpu_denoise()
+    say(f"  {name}: FP8 context vs bf16 on the same weights, max |diff| {np.max(np.abs(x8 - xq)):.3e}")
+    np.testing.assert_array_equal(x8, xq)
+    x = c.I["x0"].astype(np.float32)
+    worst = 0.0
+    for k in range(c.steps):
+        v = a8.step_velocity(torch.from_numpy(x).cuda(), k)
+        torch.cuda.synchronize()
+        v = v.cpu().numpy()
+        worst = max(worst, oracle.e_rel(v, c.oracle_velocity(x, k)))
+        x = (x + np.float32(c.tau64[k + 1] - c.tau64[k]) * v).astype(np.float32)
+    say(f"  worst step velocity e_rel {worst:.3e}")
+    assert worst <= 1e-2, worst
+    a8.close()
+    c.close()
+
+
 def test_fp8_weight_format_errors():
     # fp32 configurations, and an MLP width that is not a multiple of 64
     for cfg in (wl.workload("tiny_fp32"), wl.workload("dit_b1", n_layers=2, dtype=wl.DTYPE_F32),
