@@ -473,6 +473,9 @@ def main():
         res["roles_us_per_launch"] = roles
         res["roofline_kernel_role"] = roof["kernel_role"]
         res["roofline"] = roof
+    mc = mfma_counters(cfg["name"]) if args.weights == "as-given" and not persistent else None
+    if mc is not None:
+        res["mfma_counters"] = mc
     # per-request visibility: the workload's seeded mixed batch (ragged compact prefixes for
     # pi0.5, text / image masks for DiT), same binding, timed like the main loop
     vis = None if args.no_visibility else wl.make_visibility(cfg)
