@@ -1,4 +1,5 @@
 """Kernel-level parity through the C ABI: the library GEMM (tiles, ragged tails, split-K,
+the weight-streaming kernel at the row counts where it computes three or four 16-row blocks,
 fused bias/activation) and the attention kernel (head fold onto one K/V head, MHA,
 split over keys, ragged key counts) against the CPU oracle's float64 routines."""
 import numpy as np
@@ -19,7 +20,8 @@ def _dev(a, bf16):
 
 @pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("M,N,K", [(50, 2560, 1024), (50, 1024, 4096), (1, 64, 64), (7, 37, 96), (130, 200, 320),
-                                   (400, 1024, 2048), (3200, 2560, 1024), (16, 7, 1024), (41, 4608, 1536)])
+                                   (400, 1024, 2048), (3200, 2560, 1024), (16, 7, 1024), (41, 4608, 1536),
+                                   (48, 512, 256), (49, 512, 256), (33, 96, 64), (64, 160, 4096)])
 def test_linear_matches_oracle(bf16, M, N, K):
     from flow_matching_vla_amd import fm
     import torch
