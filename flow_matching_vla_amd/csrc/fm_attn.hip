@@ -370,6 +370,8 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
   const int lane = w % 64, db = (w / 64) % DB, wave = w / (64 * DB);
   const int rt = tile_id % rtiles, g = (tile_id / rtiles) % groups, b = tile_id / (rtiles * groups);
   const int rl = wave * 16 + (lane % 16);
+  const int r = rt * ROWS + rl;
+  if (r >= R) return;   // a row tile's tail past R: its partials were never stored
   const int S = a.splits;
   const float* wo = a.ws + (long)tile_id * S * (ROWS * DH) + (long)w * 4;
   const float2* wml = (const float2*)(a.ws + ntiles * S * (ROWS * DH)) + (long)tile_id * S * ROWS + rl;
@@ -392,8 +394,6 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
     num += wgt * ov[s];
     den += wgt * ml[s].y;
   }
-  const int r = rt * ROWS + rl;
-  if (r >= R) return;
   const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
   T* op = (T*)a.o + (long)b * a.o_bs + (long)t * a.o_rs + (long)n * a.dh + db * 16 + 4 * (lane / 16);
   const float inv = 1.f / den;
