@@ -880,6 +880,14 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float red[RED];
   __shared__ float s_mean[BM], s_rinv[BM];
   __shared__ int s_last;
+  // AL (bf16, chunk pairs): a wave's activations of a stage are 16 MB rows x 128 bytes (its two
+  // chunks), loaded as whole rows (8 rows x 128 bytes per load: full cache lines) and turned
+  // into MFMA fragments through the wave's own LDS region. Loaded as fragments, each load read
+  // 16 rows x 64 bytes, which measured ~2.3 us slower per 41 x 6144 x 1536 launch from L2.
+  // In LDS, row r's 16-byte piece p sits at piece p ^ ((r / 2) % 8), so that the fragment
+  // reads (16 rows, one piece) and the row writes (2 rows, 8 pieces) hit 16 bank groups.
+  constexpr bool AL = sizeof(T) == 2 && CPW == 2;
+  __shared__ __attribute__((aligned(16))) V16 sa[AL ? KW * MB * 128 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntn = (a.N + BN - 1) / BN;
@@ -901,11 +909,22 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
 
   // activation fragments: lane l reads row 16 mb + l % 16, k run l / 16 of every chunk
   const Rsrc ra = make_rsrc(a.A, a.a_bytes);
-  uint32_t aoff[MB];
+  uint32_t aoff[MB], arow[AL ? 2 * MB : 1];
+  if constexpr (AL) {
+    // row-load j: rows 8 j .. 8 j + 7, lane l takes row 8 j + l / 8 and its piece l % 8 (chunk
+    // (l % 8) / 4 of the wave's pair, quarter l % 4); rows past M read row M - 1 (finite values
+    // whose products land only in output rows that are never stored)
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int r = 16 * mb + (lane % 16);
-    aoff[mb] = r < a.M ? (uint32_t)(((long)a_row(a, r) * a.lda + (lane / 16) * VEC) * sizeof(T)) : kOob;
+    for (int j = 0; j < 2 * MB; ++j) {
+      const int r = min(8 * j + lane / 8, a.M - 1);
+      arow[j] = (uint32_t)(((long)a_row(a, r) * a.lda + (lane % 4) * VEC) * sizeof(T));
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = 16 * mb + (lane % 16);
+      aoff[mb] = r < a.M ? (uint32_t)(((long)a_row(a, r) * a.lda + (lane / 16) * VEC) * sizeof(T)) : kOob;
+    }
   }
   // weight fragments: fragment (nb, c) is 1 KB at ((nb * KCt + c) * 64 + lane) * 16 bytes;
   // FP8: fragment (nb, c / 2) at ((nb * KCt / 2 + c / 2) * 64 + lane) * 16 bytes
@@ -918,8 +937,16 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     for (int c = 0; c < CPW; ++c) {
       const int cc = c_lo + stg * SPC + w * CPW + c;
       const bool cok = cc < c_hi;   // uniform per wave
+      if constexpr (AL) {
+        // row-loads 2 c + {0 .. MB}: chunk min(pair start + (l % 8) / 4, last chunk) of each row;
+        // a chunk outside the range multiplies zero weights
+        const int ci = min(c_lo + stg * SPC + w * CPW + (lane % 8) / 4, KCt - 1);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) xa[c][mb] = bload16(ra, cok ? aoff[mb] + (uint32_t)(cc * KC * sizeof(T)) : kOob);
+        for (int mb = 0; mb < MB; ++mb) xa[c][mb] = bload16(ra, arow[c * MB + mb] + (uint32_t)(ci * KC * sizeof(T)));
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) xa[c][mb] = bload16(ra, cok ? aoff[mb] + (uint32_t)(cc * KC * sizeof(T)) : kOob);
+      }
       if constexpr (W8) {
         // the pair's codes (chunk c_lo + ... is even: ranges and stages hold whole pairs)
         if (c == 0) {
@@ -949,7 +976,29 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const V16 (&xa)[CPW][MB], const V16 (&xb)[CPW][NB]) {
+  auto mma = [&](const V16 (&xr)[CPW][MB], const V16 (&xb)[CPW][NB]) {
+    V16 xa[CPW][MB];
+    if constexpr (AL) {
+      // the stage's rows into this wave's region, then the fragments back out
+      V16* reg = sa + w * (MB * 128);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int j = c * MB + mb, r = 8 * j + lane / 8;
+          reg[r * 8 + ((lane % 8) ^ ((r / 2) % 8))] = xr[c][mb];
+        }
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          xa[c][mb] = reg[(16 * mb + lane % 16) * 8 + ((c * 4 + lane / 16) ^ ((lane % 16) / 2))];
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) xa[c][mb] = xr[c][mb];
+    }
     V16 wb[CPW][NB];
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
