@@ -894,9 +894,13 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   // The grid is padded to a multiple of 8 x splits and the splits of a column tile are
   // consecutive logical items of one XCD's range (xcd_range_item), so they run on one XCD and
   // exchange partial tiles through its L2.
+  // Items are (column tile, 64-row group, split), splits innermost, then row groups, so a
+  // column tile's row groups share its weights in one XCD's L2.
+  const int RG = a.rgroups > 1 ? a.rgroups : 1;
   const int bid = xcd_range_item(gridDim.x);
-  if (bid >= ntn * a.splits) return;
-  const int tile = bid / a.splits, split = bid % a.splits;
+  if (bid >= ntn * RG * a.splits) return;
+  const int tr = bid / a.splits, split = bid % a.splits;   // tr: (column tile, row group)
+  const int tile = tr / RG, m0 = (tr % RG) * 64;
   const int n0 = tile * BN;
   const int KCt = a.K / KC;
   // this workgroup's K range: chunks [c_lo, c_hi), walked in stages of KW x CPW chunks (wave w
@@ -916,13 +920,13 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     // whose products land only in output rows that are never stored)
 #pragma unroll
     for (int j = 0; j < 2 * MB; ++j) {
-      const int r = min(8 * j + lane / 8, a.M - 1);
+      const int r = min(m0 + 8 * j + lane / 8, a.M - 1);
       arow[j] = (uint32_t)(((long)a_row(a, r) * a.lda + (lane % 4) * VEC) * sizeof(T));
     }
   } else {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int r = 16 * mb + (lane % 16);
+      const int r = m0 + 16 * mb + (lane % 16);
       aoff[mb] = r < a.M ? (uint32_t)(((long)a_row(a, r) * a.lda + (lane / 16) * VEC) * sizeof(T)) : kOob;
     }
   }
@@ -961,9 +965,9 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   };
   issue(0, ra0, rb0);
   RowStats<BM, NT> st;
-  if constexpr (NORM) st.load(a, 0);
+  if constexpr (NORM) st.load(a, m0);
   Epilogue<T, BM, BN, NT, EPI> ep;
-  ep.prefetch(a, 0, n0);
+  ep.prefetch(a, m0, n0);
   if constexpr (ST) {
     if (nst > 1) issue(1, ra1, rb1);
   }
@@ -1033,7 +1037,7 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
       }
     }
   }
-  if constexpr (NORM) st.merge(a, 0, s_mean, s_rinv);
+  if constexpr (NORM) st.merge(a, m0, s_mean, s_rinv);
 
   // wave partials -> LDS, summed in wave order
 #pragma unroll
@@ -1058,7 +1062,7 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   }
   if (a.splits > 1) {
     const Rsrc rws = make_rsrc(a.ws, a.ws_bytes);
-    const uint32_t tbase = (uint32_t)tile * (uint32_t)a.splits * (BM * BN * 4);
+    const uint32_t tbase = (uint32_t)tr * (uint32_t)a.splits * (BM * BN * 4);
 #pragma unroll
     for (int q = 0; q < Q4; ++q) {
       const int i = tid + q * NT;
@@ -1066,7 +1070,7 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0);   // this workgroup's partial is in L2
     __syncthreads();
-    if (tid == 0) s_last = l2_fetch_add(a.counters + tile, 1u) == (unsigned)a.splits - 1u;
+    if (tid == 0) s_last = l2_fetch_add(a.counters + tr, 1u) == (unsigned)a.splits - 1u;
     __syncthreads();
     if (!s_last) return;
 #pragma unroll
@@ -1084,7 +1088,7 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
       }
       part[q] = sum;
     }
-    if (tid == 0) l2_put(a.counters + tile, 0u);
+    if (tid == 0) l2_put(a.counters + tr, 0u);
   }
   __syncthreads();
 #pragma unroll
@@ -1101,7 +1105,7 @@ __global__ void __launch_bounds__(KW * 64) k_gemm_skinny(GemmArgs a) {
   }
   __syncthreads();
   ep.settle();
-  ep.apply(a, red, LDR, 0, n0, s_mean, s_rinv);
+  ep.apply(a, red, LDR, m0, n0, s_mean, s_rinv);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1125,7 +1129,7 @@ static int big_bm(int cfg) { return cfg == 4 || (cfg & 2) ? 128 : 256; }
 static int big_bn(int cfg) { return cfg != 4 && (cfg & 1) ? 256 : 128; }
 
 int gemm_num_tiles(const GemmArgs& a) {
-  if (a.kind == GEMM_SKINNY) return (a.N + skinny_bn(a.cfg) - 1) / skinny_bn(a.cfg);
+  if (a.kind == GEMM_SKINNY) return (a.N + skinny_bn(a.cfg) - 1) / skinny_bn(a.cfg) * (a.rgroups > 1 ? a.rgroups : 1);
   if (a.kind == GEMM_BIG) return ((a.M + big_bm(a.cfg) - 1) / big_bm(a.cfg)) * ((a.N + big_bn(a.cfg) - 1) / big_bn(a.cfg));
   const CfgShape c = cfg_shape(a.cfg, ET_BF16);
   return ((a.M + c.bm - 1) / c.bm) * ((a.N + c.bn - 1) / c.bn);
@@ -1133,7 +1137,8 @@ int gemm_num_tiles(const GemmArgs& a) {
 
 void gemm_plan(GemmArgs& a, int elem, int num_cus) {
   const int kq = elem == ET_BF16 ? 32 : 16;
-  a.fp8 = 0;   // set below where the skinny kernel streams FP8 weights
+  a.fp8 = 0;       // set below where the skinny kernel streams FP8 weights
+  a.rgroups = 1;   // set below where it runs over groups of 64 rows
   const int esz = elem == ET_BF16 ? 2 : 4;
   if (a.M <= 64 && elem == ET_BF16 && a.K % 32 == 0) {
     // Weight streaming in bf16: eight waves, two chunks per wave and stage (double-buffered
@@ -1199,6 +1204,29 @@ void gemm_plan(GemmArgs& a, int elem, int num_cus) {
     a.splits = bs;
     a.k_split = bkw * bc * kq;
     return;
+  }
+  if (elem == ET_BF16 && a.K % 32 == 0 && a.M <= 64 * num_cus) {
+    // A few hundred rows and a narrow output: the weight-streaming kernel over 64-row groups,
+    // one workgroup per (column tile, row group), when those fit in one round on the CUs (the
+    // row groups of a column tile share its weights in one XCD's L2). Measured on MI355X at
+    // 400 rows: 400 x 1024 x 2048 8.1 us against 17.3 for the large-M kernel, 400 x 1024 x
+    // 4096 12.3 against 22.3, 400 x 2560 x 1024 (560 items, two rounds) 14.6 against 15.0
+    // and 400 x 8192 x 1024 35.4 against 17.1: so only one round. 16-column tiles where they
+    // also fit (not for residual epilogues, whose statistic slots are 32 columns).
+    const int rg = (a.M + 63) / 64;
+    const int t1 = (a.N + 15) / 16, t2 = (a.N + 31) / 32;
+    const int nb = (a.epi != EPI_RESID && t1 * rg <= num_cus) ? 1 : 2;
+    if ((nb == 1 ? t1 : t2) * rg <= num_cus) {
+      a.kind = GEMM_SKINNY;
+      a.kw = 8;
+      a.cpw = 2;
+      a.cfg = nb == 2 ? SK_N32 : SK_N16;
+      a.rgroups = rg;
+      a.splits = 1;
+      a.k_split = a.K;
+      a.fp8 = a.w8 && a.wscale && a.K % 64 == 0 ? 1 : 0;
+      return;
+    }
   }
   if (elem == ET_BF16 && a.K % 32 == 0) {
     // Large-M kernel: the tile shape and K split with the lowest estimated time. Per
@@ -1301,7 +1329,7 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t s) {
 template <typename T, int KW, int NB, int CPW, int MB, bool ST, bool W8>
 static hipError_t launch_skinny_st(const GemmArgs& a, hipStream_t s) {
   const int per_round = 8 * a.splits;   // whole column tiles per XCD range
-  const int items = ((a.N + 16 * NB - 1) / (16 * NB)) * a.splits;
+  const int items = ((a.N + 16 * NB - 1) / (16 * NB)) * (a.rgroups > 1 ? a.rgroups : 1) * a.splits;
   const dim3 grid((items + per_round - 1) / per_round * per_round), block(KW * 64);
   const bool norm = a.norm != NORM_NONE;
 #define K_SK(E, NRM) hipLaunchKernelGGL((k_gemm_skinny<T, KW, NB, CPW, MB, E, NRM, ST, W8>), grid, block, 0, s, a)
@@ -1420,7 +1448,9 @@ hipError_t gemm_launch(const GemmArgs& in, int elem, hipStream_t s) {
   if (a_bytes >= (1L << 31) || w_bytes >= (1L << 31) || ws_bytes >= (1L << 31)) return hipErrorInvalidValue;
   a.a_bytes = (uint32_t)a_bytes; a.w_bytes = (uint32_t)w_bytes; a.ws_bytes = (uint32_t)ws_bytes;
   if (a.kind == GEMM_SKINNY) {
-    if (a.M > 64) return hipErrorInvalidValue;
+    // more than 64 rows: bf16 row groups of 64 (rgroups of them, covering M)
+    const int rg = a.rgroups > 1 ? a.rgroups : 1;
+    if (a.M > 64 * rg || (rg > 1 && (elem != ET_BF16 || a.kw != 8 || a.cpw != 2))) return hipErrorInvalidValue;
     return elem == ET_BF16 ? launch_skinny<bf16>(a, s) : launch_skinny<float>(a, s);
   }
   if (a.kind == GEMM_BIG) {

@@ -70,6 +70,9 @@ struct GemmArgs {
   // planner sets fp8 when the skinny kernel then streams the codes instead of W (bf16, K a
   // multiple of 64); the sums are scaled per column before the epilogue.
   const void* w8; const float* wscale; int fp8;
+  // Weight-streaming kernel over more than 64 rows: rgroups groups of 64 rows, each a workgroup
+  // of its own per column tile and split (0 or 1: one group, M <= 64).
+  int rgroups;
 };
 constexpr long kVecPad = 1L << 18;   // floats in the zeros / ones buffers
 // Split-K arrival counters (GemmArgs::counters): one per output tile.

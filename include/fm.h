@@ -214,9 +214,9 @@ static inline int32_t fm_pool_v_slot(int32_t j, int32_t dtype) {
  *   FM_WEIGHTS_FP8_E4M3  each row (output feature) becomes OCP FP8 E4M3 codes times one
  *     power-of-two scale 2^e, e the smallest exponent with max |row| <= 448 2^e; codes round
  *     to nearest, ties to even. The loop kernel and the per-operation graph's weight-streaming
- *     GEMMs (64 rows or fewer: batch 1) stream the codes (half the bytes) and turn them into
- *     bf16 exactly, scaling each output column's sums by its row's 2^e; the larger GEMMs use
- *     the dequantized bf16 weights. All therefore compute the same function of the
+ *     GEMMs (64 rows, or groups of 64 rows over a narrow output) stream the codes (half the
+ *     bytes) and turn them into bf16 exactly, scaling each output column's sums by its row's
+ *     2^e; the large-M GEMMs use the dequantized bf16 weights. All therefore compute the same function of the
  *     dequantized weights, which is the model. Quantized: the per-layer q / k / v, o and MLP
  *     matrices (PREFIX_JOINT), and every block's q, the self blocks' k and v, o, ff1 and ff2
  *     (DIT_CROSS; the cross blocks' context projections, applied once per binding, stay in

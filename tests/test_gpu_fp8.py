@@ -9,10 +9,10 @@ weights, pi0.5 Design FP8 for the expert).
   * The loop: the FP8 context computes the model whose weights are the dequantized values.
     A bf16 context loaded with exactly those values must give bit-identical chunks, since a
     power-of-two row scale commutes with every fp32 rounding and the codes convert to bf16
-    exactly. This holds on the loop kernel and on the per-operation graph's GEMMs of at most
-    64 rows, which stream the codes, and on the larger graph GEMMs, which read dequantized
-    bf16 copies; for the pi0.5-shaped expert and the DiT head (whose cross blocks' context
-    projections stay bf16). Against the oracle on the dequantized weights the tolerances are
+    exactly. This holds on the loop kernel and on the per-operation graph's weight-streaming
+    GEMMs (64 rows, or 64-row groups that fit one round on the CUs), which stream the codes,
+    and on the large-M GEMMs, which read dequantized bf16 copies; for the pi0.5-shaped expert
+    and the DiT head (whose cross blocks' context projections stay bf16). Against the oracle on the dequantized weights the tolerances are
     the bf16 ones: <= 1e-2 per teacher-forced step velocity, <= 2e-2 on the chunk."""
 import numpy as np
 import pytest
@@ -68,7 +68,7 @@ def _context(cfg, W, I, fp8, steps):
 @pytest.mark.parametrize("name,over,graph", [
     ("pi05_b1", dict(n_layers=2, steps=2), False),            # the loop kernel streams the codes
     ("pi05_b1", dict(n_layers=2, steps=2), True),             # graph GEMMs of 50 rows stream them
-    ("pi05_b8", dict(n_layers=2, steps=2, batch=3), False),   # graph GEMMs of 150 rows: bf16 copies
+    ("pi05_b8", dict(n_layers=2, steps=2, batch=3), False),   # 150 rows: codes streamed in 64-row groups, gate/up on bf16 copies
     ("dit_b1", dict(n_layers=4, steps=2), False),             # DiT head, 41 rows: codes streamed
     ("dit_b1", dict(n_layers=2, steps=2, batch=2), False),    # two requests, 82 rows: bf16 copies
 ])
