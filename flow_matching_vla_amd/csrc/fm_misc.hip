@@ -76,8 +76,18 @@ __global__ void __launch_bounds__(256) k_inproj(InProjArgs a) {
     for (int c = 0; c < 16; c += 4) *(f32x4*)(hp + c) = f32x4{y[c], y[c + 1], y[c + 2], y[c + 3]};
     if (a.hs) {
       T* hq = (T*)a.hs + (long)hr * a.D + n0 + g * 16;
+      if constexpr (sizeof(T) == 2) {   // two 16-byte stores (the row piece is 32-byte aligned)
 #pragma unroll
-      for (int c = 0; c < 16; ++c) hq[c] = from_f32<T>(y[c] * (1.f + hsc[c]));
+        for (int c = 0; c < 16; c += 8) {
+          bf16x8 v;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (bf16)(y[c + e] * (1.f + hsc[c + e]));
+          *(bf16x8*)(hq + c) = v;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) hq[c] = from_f32<T>(y[c] * (1.f + hsc[c]));
+      }
     }
   }
   if (a.stats) {   // uniform (kernel argument)
