@@ -45,6 +45,15 @@ __device__ __forceinline__ uint32_t bits_below(int n) {
   return n >= 32 ? 0xffffffffu : (n <= 0 ? 0u : (1u << n) - 1u);
 }
 
+// Element type of the key splits' partial O. Heads of 128 and 256 dims in bf16 store each
+// split's O normalised by its own row sum, rounded to bf16 (the merged output is rounded to
+// bf16 as well): half the bytes of the partial stores and of the merge's reads, which at
+// 128 KB per 128-row tile of 256-wide heads took a large part of both launches (+3% at 8
+// requests of 400 folded rows). 64-dim heads and fp32 keep the unnormalised fp32 sums.
+template <typename T, int DH> struct SplitPartial { typedef float type; };
+template <> struct SplitPartial<bf16, 128> { typedef bf16 type; };
+template <> struct SplitPartial<bf16, 256> { typedef bf16 type; };
+
 // WAVES waves of QB query blocks (16 rows each): ROWS = 16 WAVES QB rows per workgroup.
 // Every K and V^T fragment a wave reads from LDS feeds QB MFMAs, so QB = 2 halves the LDS
 // reads per MFMA (one wave per SIMD then holds twice the accumulators). VIS: the per-request
@@ -340,15 +349,26 @@ __global__ void __launch_bounds__(WAVES * 64) k_attn(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int blk = wave * QB + qb;                      // 16-row block of the row tile
-    // split keys: unnormalised O^T in the MFMA output layout ([block][db][lane][e], one
-    // 16-byte store per lane and d-block) and (m, l) of each query row; an inactive wave's
-    // rows are past R, and the merge never stores them
+    // split keys: O^T (SplitPartial: unnormalised fp32, or normalised by the split's own row
+    // sum in bf16) in the MFMA output layout ([block][db][lane][e], one store per lane and
+    // d-block), and (m, l) of each query row; a split that sees none of a row's keys (l = 0)
+    // stores zeros, which the merge weighs by l = 0. An inactive wave's rows are past R, and
+    // the merge never stores them.
     if (!active) continue;
-    float* wo = a.ws + ((long)tile_id * a.splits + sp) * (ROWS * DH);
+    typedef typename SplitPartial<T, DH>::type P;
+    P* wo = (P*)a.ws + ((long)tile_id * a.splits + sp) * (ROWS * DH);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *(f32x4*)(wo + ((blk * DB + db) * 64 + lane) * 4) = o[qb][db];
+    for (int db = 0; db < DB; ++db) {
+      P* p = wo + ((blk * DB + db) * 64 + lane) * 4;
+      if constexpr (sizeof(P) == 2) {
+        const float inv = l_run[qb] > 0.f ? 1.f / l_run[qb] : 0.f;
+        *(bf16x4*)p = bf16x4{(bf16)(o[qb][db][0] * inv), (bf16)(o[qb][db][1] * inv), (bf16)(o[qb][db][2] * inv), (bf16)(o[qb][db][3] * inv)};
+      } else {
+        *(f32x4*)p = o[qb][db];
+      }
+    }
     if (lane < 16) {
-      float2* wml = (float2*)(a.ws + (long)a.B * groups * rtiles * a.splits * (ROWS * DH)) + ((long)tile_id * a.splits + sp) * ROWS;
+      float2* wml = (float2*)((P*)a.ws + (long)a.B * groups * rtiles * a.splits * (ROWS * DH)) + ((long)tile_id * a.splits + sp) * ROWS;
       wml[blk * 16 + lane] = make_float2(m_run[qb], l_run[qb]);
     }
   }
@@ -373,26 +393,34 @@ __global__ void __launch_bounds__(256) k_attn_combine(AttnArgs a) {
   const int r = rt * ROWS + rl;
   if (r >= R) return;   // a row tile's tail past R: its partials were never stored
   const int S = a.splits;
-  const float* wo = a.ws + (long)tile_id * S * (ROWS * DH) + (long)w * 4;
-  const float2* wml = (const float2*)(a.ws + ntiles * S * (ROWS * DH)) + (long)tile_id * S * ROWS + rl;
+  typedef typename SplitPartial<T, DH>::type P;
+  const P* wo = (const P*)a.ws + (long)tile_id * S * (ROWS * DH) + (long)w * 4;
+  const float2* wml = (const float2*)((const P*)a.ws + ntiles * S * (ROWS * DH)) + (long)tile_id * S * ROWS + rl;
   f32x4 ov[NS];
   float2 ml[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int sc = min(s, S - 1);
-    ov[s] = *(const f32x4*)(wo + (long)sc * (ROWS * DH));
+    if constexpr (sizeof(P) == 2) {
+      const bf16x4 v = *(const bf16x4*)(wo + (long)sc * (ROWS * DH));
+      ov[s] = f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    } else {
+      ov[s] = *(const f32x4*)(wo + (long)sc * (ROWS * DH));
+    }
     ml[s] = wml[(long)sc * ROWS];
   }
   float mx = ml[0].x;
 #pragma unroll
   for (int s = 1; s < NS; ++s) mx = fmaxf(mx, ml[s].x);   // clamped copies repeat a real split
+  // a normalised partial weighs by its split's share of the row's exponential sum
   f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const float wgt = s < S ? exp2f(ml[s].x - mx) : 0.f;
+    const float e = s < S ? exp2f(ml[s].x - mx) : 0.f;
+    const float wgt = sizeof(P) == 2 ? e * ml[s].y : e;
     num += wgt * ov[s];
-    den += wgt * ml[s].y;
+    den += e * ml[s].y;
   }
   const int n = g * a.heads_per_kv + r / a.Tq, t = r % a.Tq;
   T* op = (T*)a.o + (long)b * a.o_bs + (long)t * a.o_rs + (long)n * a.dh + db * 16 + 4 * (lane / 16);
@@ -433,6 +461,7 @@ void attn_plan(AttnArgs& a, int elem, int num_cus) {
   (void)elem;
 }
 
+// sized for fp32 partials (bf16 ones use half of the first part)
 size_t attn_ws_bytes(const AttnArgs& a) {
   if (a.splits <= 1) return 0;
   return (size_t)attn_num_items(a) * a.splits * ((size_t)kAttnRows * a.dh + 2 * kAttnRows) * sizeof(float);
