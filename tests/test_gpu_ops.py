@@ -50,6 +50,7 @@ def test_linear_matches_oracle(bf16, M, N, K):
     (True, 2, 50, 8, 1, 1074, 256),    # P = 1024
     (True, 1, 41, 24, 24, 600, 64),    # DiT cross-attention
     (True, 1, 41, 24, 24, 41, 64),     # DiT self-attention
+    (True, 2, 20, 4, 1, 300, 128),     # 128-dim heads folded onto one K/V head: five key splits (bf16 partials)
     (True, 1, 3, 8, 1, 1, 256),        # a single key
     (True, 1, 5, 4, 1, 65, 64),        # one key past a tile
     (False, 1, 16, 4, 1, 80, 64),      # fp32 tiny expert
